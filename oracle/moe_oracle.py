@@ -1,0 +1,405 @@
+"""Plain float64 CPU oracle of the MoE expert layer, forward and backward.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py.  It shares no code, header, table or helper with
+the HIP library under mixture_experts_layer_02_amd/, and neither imports the
+other.
+
+Sources ("the pages"):
+  [Aurora] "Scalable Pretraining of Large Mixture of Experts Language Models on
+           Aurora Super Computer": section 3.1 (FastSparseMoE), its Algorithm 1
+           (FastSparseMoEBlock with expert parallelism, stages 1-5) and Figure 5.
+  [Domyn]  "Training a 1T-Params MoE on EU public infrastructure": the model
+           table (hidden 6144, 384 routed experts, top-8, expert hidden 1792).
+
+Arithmetic: every input is widened to float64 and every step runs in float64
+with no intermediate rounding.  Matrix products use numpy's matmul as a
+library step; everything else is written out as its definition.
+
+Readings taken where the pages leave a step open (each is also listed in the
+design notes):
+  * Selection is made on the logits (softmax is strictly increasing, so the
+    selected set equals the top-k of the probabilities), ties go to the lower
+    expert index, +0.0 and -0.0 compare equal, and slot j holds the j-th
+    selection in that order.
+  * renormalize=1 (the default): the top-k probabilities are divided by their
+    sum.  renormalize=0 keeps Algorithm 1's literal TopK(Softmax(logits)).
+  * Local experts are the block [e0, e0 + NL).  Selections of other experts
+    are counted but produce no row; their slots contribute nothing to y.
+  * Rows of one expert's segment are in ascending token order (the order that
+    Algorithm 1's blocked count/index kernels produce).
+  * No capacity limit, no biases in the experts; the router may get an added
+    per-expert logit bias (the Zipf-skewed workload).
+  * The backward pass is not written out on the pages beyond stage 5; it is
+    derived here by differentiating stages 1, 4 and 5.
+
+Every function is pinned by a test in tests/test_oracle_*.py against brute
+force, closed forms, invariants or finite differences; none is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "topk_route", "count_tokens", "generate_indices", "permute",
+    "silu", "silu_grad", "expert_ffn_rows", "expert_ffn", "combine",
+    "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd", "unpermute_bwd",
+    "route_bwd", "router_bwd", "layer_forward", "layer_backward",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Stage 1 of Algorithm 1 [Aurora]: router, softmax, top-k.
+# --------------------------------------------------------------------------
+
+def router_logits(x, wr, bias=None):
+    """logits[t][e] = sum_i x[t][i] * W_r[e][i]  (+ bias[e]).
+
+    [Aurora] Algorithm 1, stage 1: the router is a linear layer mapping each of
+    the tokens to one logit per expert.  W_r is stored out x in, i.e. [E][d].
+    """
+    L = _f64(x) @ _f64(wr).T
+    if bias is not None:
+        L = L + _f64(bias)[None, :]
+    return L
+
+
+def topk_route(logits, k, renormalize=1):
+    """Per token: the k experts with the largest logits, and their weights.
+
+    [Aurora] Algorithm 1, stage 1: probs = Softmax(logits); weights, indices =
+    TopK(probs).  Returns idx [T][k] int32 (slot j = j-th largest, ties to the
+    lower expert index) and w [T][k] float64: the softmax probabilities of the
+    selected experts, divided by their sum when ``renormalize`` is 1.
+    """
+    L = _f64(logits)
+    if not np.isfinite(L).all():
+        raise ValueError("oracle: logits must be finite")
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("oracle: need 1 <= k <= E")
+    # A stable sort of the negated logits keeps equal logits (including +0.0
+    # against -0.0) in ascending expert order.
+    order = np.argsort(-L, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    # Softmax over all experts, written out.
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    probs = z / z.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+# --------------------------------------------------------------------------
+# Stages 2 and 3 of Algorithm 1 [Aurora]: token counting, prefix sums and
+# index generation, written as their plain definition (a stable counting sort
+# of the local (token, slot) selections by expert).
+# --------------------------------------------------------------------------
+
+def count_tokens(idx, E, e0, NL):
+    """counts[e] for every expert e, and the local boundaries offsets[0..NL].
+
+    [Aurora] Algorithm 1, stage 2: the per-expert token counts of the experts
+    held locally, followed by a prefix sum that gives each expert's segment
+    boundaries (cum_token_counts).  counts covers all E experts (selections
+    of non-local experts are counted too); offsets[n] is the number of
+    selections of local experts e0 .. e0+n-1, so offsets[NL] is the number of
+    routed rows R.
+    """
+    idx = np.asarray(idx)
+    counts = np.zeros(E, np.int64)
+    for e in idx.reshape(-1):
+        counts[int(e)] += 1
+    offsets = np.zeros(NL + 1, np.int64)
+    for n in range(NL):
+        offsets[n + 1] = offsets[n] + counts[e0 + n]
+    return counts, offsets
+
+
+def generate_indices(idx, e0, NL, offsets):
+    """row_token[R] and slot_row[T][k] of the permuted (expert-major) layout.
+
+    [Aurora] Algorithm 1, stage 3: each selection of a local expert gets a row
+    in that expert's segment; input_indices maps the row to its token and
+    output_indices maps the token's local selection back to the row.
+    Here slot_row[t][j] is the row of slot j of token t, or -1 when the slot's
+    expert is not local; row_token[row] = t.  Tokens are visited in ascending
+    order, so every segment lists its tokens in ascending order.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    R = int(offsets[NL])
+    next_row = [int(offsets[n]) for n in range(NL)]
+    row_token = np.full(R, -1, np.int64)
+    slot_row = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            n = int(idx[t, j]) - e0
+            if 0 <= n < NL:
+                row = next_row[n]
+                next_row[n] += 1
+                row_token[row] = t
+                slot_row[t, j] = row
+    return row_token, slot_row
+
+
+def permute(x, row_token):
+    """mlp_in[row] = x[row_token[row]] ([Aurora] Algorithm 1, stage 4 gather)."""
+    return np.asarray(x)[np.asarray(row_token, np.int64)]
+
+
+# --------------------------------------------------------------------------
+# Stage 4 of Algorithm 1 [Aurora]: the SwiGLU expert MLP on each segment.
+# --------------------------------------------------------------------------
+
+def silu(g):
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
+    g = _f64(g)
+    return g / (1.0 + np.exp(-g))
+
+
+def silu_grad(g):
+    """d silu / dg = s * (1 + g * (1 - s)) with s = sigmoid(g)."""
+    g = _f64(g)
+    s = 1.0 / (1.0 + np.exp(-g))
+    return s * (1.0 + g * (1.0 - s))
+
+
+def expert_ffn_rows(xr, w1e, w3e, w2e):
+    """One expert's MLP on rows xr [m][d]: gate, up, silu(gate)*up, down.
+
+    [Aurora] Algorithm 1, stage 4: gate_out = X W_gate, up_out = X W_up,
+    mul_out = Silu(gate_out) * up_out, mlp_out = mul_out W_down, with the
+    weights of a linear layer (out x in): w1e, w3e [f][d], w2e [d][f].
+    """
+    X = _f64(xr)
+    G = X @ _f64(w1e).T
+    U = X @ _f64(w3e).T
+    H = silu(G) * U
+    Y = H @ _f64(w2e).T
+    return G, U, H, Y
+
+
+def expert_ffn(x_perm, offsets, w1, w3, w2):
+    """Stage 4 over all local experts: segment n is rows offsets[n]:offsets[n+1].
+
+    [Aurora] Algorithm 1, stage 4 (Grouped_mm over the concatenated per-rank
+    expert weights with the cum_token_counts boundaries).
+    Returns G, U, H [R][f] and y_perm [R][d].
+    """
+    x_perm = _f64(x_perm)
+    NL = len(offsets) - 1
+    R = int(offsets[NL])
+    f = np.asarray(w1).shape[1]
+    d = np.asarray(w1).shape[2]
+    G = np.zeros((R, f))
+    U = np.zeros((R, f))
+    H = np.zeros((R, f))
+    Y = np.zeros((R, d))
+    for n in range(NL):
+        a, b = int(offsets[n]), int(offsets[n + 1])
+        if b > a:
+            G[a:b], U[a:b], H[a:b], Y[a:b] = expert_ffn_rows(x_perm[a:b], w1[n], w3[n], w2[n])
+    return G, U, H, Y
+
+
+# --------------------------------------------------------------------------
+# Stage 5 of Algorithm 1 [Aurora]: weighted output reduction.
+# --------------------------------------------------------------------------
+
+def combine(y_perm, slot_row, w):
+    """y[t] = sum over local slots j (ascending) of w[t][j] * y_perm[slot_row[t][j]].
+
+    [Aurora] Algorithm 1, stage 5, ExpertOutputReductionForward: each output
+    element accumulates the token's locally computed expert outputs scaled by
+    their routing weights.  A token with no local slot gets y = 0.
+    """
+    y_perm = _f64(y_perm)
+    w = _f64(w)
+    slot_row = np.asarray(slot_row)
+    T, k = slot_row.shape
+    y = np.zeros((T, y_perm.shape[1]))
+    for j in range(k):
+        rows = slot_row[:, j]
+        m = rows >= 0
+        y[m] += w[m, j][:, None] * y_perm[rows[m]]
+    return y
+
+
+def combine_bwd(dy, y_perm, slot_row, w):
+    """dy_perm[row] = w[t][j] dy[t];  dw[t][j] = <y_perm[row], dy[t]> (0 if non-local).
+
+    [Aurora] Algorithm 1, stage 5, ExpertOutputReductionBackward (with the
+    row/token indices read as the forward defines them).
+    """
+    dy = _f64(dy)
+    y_perm = _f64(y_perm)
+    w = _f64(w)
+    slot_row = np.asarray(slot_row)
+    T, k = slot_row.shape
+    dy_perm = np.zeros_like(y_perm)
+    dw = np.zeros((T, k))
+    for j in range(k):
+        rows = slot_row[:, j]
+        m = rows >= 0
+        t = np.nonzero(m)[0]
+        dy_perm[rows[m]] = w[t, j][:, None] * dy[t]
+        dw[t, j] = np.einsum("rd,rd->r", y_perm[rows[m]], dy[t])
+    return dy_perm, dw
+
+
+# --------------------------------------------------------------------------
+# Backward of stage 4 (derived by differentiating the expert MLP).
+# --------------------------------------------------------------------------
+
+def expert_ffn_bwd_rows(xr, w1e, w3e, w2e, dyr):
+    """Gradients of one expert's MLP for rows xr with upstream dyr [m][d].
+
+    dH = dY W2, dU = dH * silu(G), dG = dH * U * silu'(G), dX = dG W1 + dU W3,
+    dW1 = dG^T X, dW3 = dU^T X, dW2 = dY^T H (weights out x in).
+    """
+    X = _f64(xr)
+    dY = _f64(dyr)
+    G, U, H, _ = expert_ffn_rows(X, w1e, w3e, w2e)
+    dH = dY @ _f64(w2e)
+    dU = dH * silu(G)
+    dG = dH * U * silu_grad(G)
+    dX = dG @ _f64(w1e) + dU @ _f64(w3e)
+    dW1 = dG.T @ X
+    dW3 = dU.T @ X
+    dW2 = dY.T @ H
+    return dG, dU, dX, dW1, dW3, dW2
+
+
+def expert_ffn_bwd(x_perm, offsets, w1, w3, w2, dy_perm):
+    """Backward of stage 4 over all local experts.
+
+    Returns dG, dU [R][f], dx_perm [R][d], dW1, dW3 [NL][f][d], dW2 [NL][d][f].
+    An expert with no rows gets exactly zero weight gradients.
+    """
+    x_perm = _f64(x_perm)
+    dy_perm = _f64(dy_perm)
+    NL = len(offsets) - 1
+    R = int(offsets[NL])
+    NLw, f, d = np.asarray(w1).shape
+    dG = np.zeros((R, f))
+    dU = np.zeros((R, f))
+    dX = np.zeros((R, d))
+    dW1 = np.zeros((NLw, f, d))
+    dW3 = np.zeros((NLw, f, d))
+    dW2 = np.zeros((NLw, d, f))
+    for n in range(NL):
+        a, b = int(offsets[n]), int(offsets[n + 1])
+        if b > a:
+            dG[a:b], dU[a:b], dX[a:b], dW1[n], dW3[n], dW2[n] = expert_ffn_bwd_rows(
+                x_perm[a:b], w1[n], w3[n], w2[n], dy_perm[a:b])
+    return dG, dU, dX, dW1, dW3, dW2
+
+
+def unpermute_bwd(dx_perm, slot_row):
+    """dx[t] = sum over local slots j of dx_perm[slot_row[t][j]] (adjoint of the gather)."""
+    dx_perm = _f64(dx_perm)
+    slot_row = np.asarray(slot_row)
+    T, k = slot_row.shape
+    dx = np.zeros((T, dx_perm.shape[1]))
+    for j in range(k):
+        rows = slot_row[:, j]
+        m = rows >= 0
+        dx[m] += dx_perm[rows[m]]
+    return dx
+
+
+# --------------------------------------------------------------------------
+# Backward of stage 1 (derived).
+# --------------------------------------------------------------------------
+
+def route_bwd(idx, w, dw, E, renormalize=1, logits=None):
+    """dlogits [T][E] from the gradient dw [T][k] of the routing weights.
+
+    renormalize=1: w_j = exp(L_j) / sum_{i in S} exp(L_i) over the selected set
+    S, so dL_m = w_m (dw_m - <w, dw>) for m in S and 0 elsewhere (including
+    selected experts that are not local: their dw is 0 but the normaliser
+    still couples them).
+    renormalize=0: w_j = p_{idx_j} with p the softmax over all E, so
+    dL_e = p_e (g_e - <w, dw>) with g_e = dw_j where e = idx_j, else 0; this
+    needs the logits.
+    """
+    idx = np.asarray(idx, np.int64)
+    w = _f64(w)
+    dw = _f64(dw)
+    T, k = idx.shape
+    s = (w * dw).sum(axis=1)
+    dL = np.zeros((T, E))
+    if renormalize:
+        for j in range(k):
+            dL[np.arange(T), idx[:, j]] = w[:, j] * (dw[:, j] - s)
+    else:
+        L = _f64(logits)
+        z = np.exp(L - L.max(axis=1, keepdims=True))
+        p = z / z.sum(axis=1, keepdims=True)
+        g = np.zeros((T, E))
+        for j in range(k):
+            g[np.arange(T), idx[:, j]] = dw[:, j]
+        dL = p * (g - s[:, None])
+    return dL
+
+
+def router_bwd(x, wr, dlogits):
+    """dx_router = dlogits W_r  [T][d];  dW_r = dlogits^T x  [E][d]."""
+    dL = _f64(dlogits)
+    return dL @ _f64(wr), dL.T @ _f64(x)
+
+
+# --------------------------------------------------------------------------
+# The whole layer.
+# --------------------------------------------------------------------------
+
+def layer_forward(x, wr, w1, w3, w2, k, e0, NL, renormalize=1, bias=None,
+                  logits=None, routing=None):
+    """Stages 1-5 on one GPU's share.  Returns a dict of every intermediate.
+
+    ``logits`` (optional) replaces stage 1's matmul, so that routing can be
+    taken from a given logit tensor; ``routing=(idx, w)`` (optional) replaces
+    stage 1 altogether (forced routing).
+    """
+    out = {}
+    E = np.asarray(wr).shape[0]
+    if routing is not None:
+        idx, w = routing
+        idx = np.asarray(idx, np.int32)
+        w = _f64(w)
+    else:
+        L = router_logits(x, wr, bias) if logits is None else _f64(logits)
+        out["logits"] = L
+        idx, w = topk_route(L, k, renormalize)
+    out["idx"], out["w"] = idx, w
+    counts, offsets = count_tokens(idx, E, e0, NL)
+    row_token, slot_row = generate_indices(idx, e0, NL, offsets)
+    out.update(counts=counts, offsets=offsets, row_token=row_token, slot_row=slot_row)
+    x_perm = permute(_f64(x), row_token)
+    G, U, H, Yp = expert_ffn(x_perm, offsets, w1, w3, w2)
+    out.update(x_perm=x_perm, G=G, U=U, H=H, y_perm=Yp)
+    out["y"] = combine(Yp, slot_row, w)
+    return out
+
+
+def layer_backward(fwd, x, wr, w1, w3, w2, dy, renormalize=1):
+    """Gradients of <dy, y> with the routing (idx) held fixed.
+
+    Returns dict with dy_perm, dw, dG, dU, dx_perm, dW1, dW3, dW2, dlogits,
+    dx (expert path + router path) and dWr.
+    """
+    E = np.asarray(wr).shape[0]
+    dy_perm, dw = combine_bwd(dy, fwd["y_perm"], fwd["slot_row"], fwd["w"])
+    dG, dU, dXp, dW1, dW3, dW2 = expert_ffn_bwd(fwd["x_perm"], fwd["offsets"], w1, w3, w2, dy_perm)
+    dx_moe = unpermute_bwd(dXp, fwd["slot_row"])
+    dL = route_bwd(fwd["idx"], fwd["w"], dw, E, renormalize, fwd.get("logits"))
+    dx_r, dWr = router_bwd(x, wr, dL)
+    return dict(dy_perm=dy_perm, dw=dw, dG=dG, dU=dU, dx_perm=dXp, dW1=dW1, dW3=dW3,
+                dW2=dW2, dlogits=dL, dx_router=dx_r, dx=dx_moe + dx_r, dWr=dWr)
