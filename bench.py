@@ -1,0 +1,220 @@
+"""Throughput of the MoE expert layer (forward + backward) on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fwdbwd_1t]
+
+A step is one pass of the whole hot path over one batch: router logits,
+top-k routing, counting + permutation, the gate/up and down grouped GEMMs,
+the weighted combine, and the backward of each (combine, dH, dX, dW, route,
+router, unpermute).  Inputs are seeded synthetic tensors already resident in
+HBM when the timed region starts.  Every entry point is bracketed by HIP
+events on the stream it is launched on; the dominant kernel's average
+duration gives the roofline fraction.  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def _cpu_baseline(cfg, inp, sample_tokens):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of the workload."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    Ts = sample_tokens
+    dt = cfg.dtype
+    x = synth.as_f32(inp["x"][:Ts], dt).astype(np.float64)
+    dy = synth.as_f32(inp["dy"][:Ts], dt).astype(np.float64)
+    wr = synth.as_f32(inp["wr"], dt)
+    w1 = synth.as_f32(inp["w1"], dt)
+    w3 = synth.as_f32(inp["w3"], dt)
+    w2 = synth.as_f32(inp["w2"], dt)
+    t0 = time.perf_counter()
+    fwd = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize)
+    if cfg.backward:
+        oracle.layer_backward(fwd, x, wr, w1, w3, w2, dy, cfg.renormalize)
+    dt_s = time.perf_counter() - t0
+    return {"value": Ts / dt_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {Ts} of {cfg.T} tokens of {cfg.name}, all {cfg.num_local} local experts' "
+                      f"weights, {'forward+backward' if cfg.backward else 'forward'}, float64 numpy; "
+                      f"{dt_s:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fwdbwd_1t")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_02_amd as moe
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+
+    def note(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(cfg)
+    gen_s = time.perf_counter() - t_gen
+    note(f"inputs of {cfg.name} drawn in {gen_s:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    g = {n: up(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
+    bias = up(inp["bias"]) if "bias" in inp else None
+    routing = (up(inp["idx"]), up(inp["w"])) if cfg.routing == "roundrobin" else None
+    D = moe.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype,
+                      cfg.renormalize)
+    b = moe.Buffers(D, backward=cfg.backward)
+    stream = torch.cuda.current_stream()
+
+    rows = ["A1_router_logits", "A2_route", "A34_permute", "A5_gate_up", "A6_down", "A7_combine"]
+    if cfg.backward:
+        rows += ["B1_combine_bwd", "B2_dh", "B3_dx", "B4_dw", "B5_route_bwd", "B5_router_bwd", "B5_unpermute"]
+    ev = {r: [] for r in rows}
+
+    def timed(name, fn, rec):
+        if rec:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            ev[name].append((s, e))
+        else:
+            fn()
+
+    def step(rec):
+        if routing is None:
+            timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits), rec)
+            timed("A2_route", lambda: moe.route(D, b.logits, b.topk_idx, b.topk_w), rec)
+            idx, w = b.topk_idx, b.topk_w
+        else:
+            idx, w = routing
+        timed("A34_permute", lambda: moe.permute(D, idx, g["x"], b.counts, b.offsets, b.row_token, b.slot_row,
+                                                 b.x_perm, b.ws_permute), rec)
+        timed("A5_gate_up", lambda: moe.expert_gate_up(D, b.offsets, b.x_perm, g["w1"], g["w3"], b.gu, b.h), rec)
+        timed("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), rec)
+        timed("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), rec)
+        if not cfg.backward:
+            return
+        timed("B1_combine_bwd", lambda: moe.combine_bwd(D, b.slot_row, w, b.y_perm, g["dy"], b.dy_perm,
+                                                        b.dtopk_w), rec)
+        timed("B2_dh", lambda: moe.expert_bwd_dh(D, b.offsets, g["w2"], b.gu, b.dy_perm, b.dgu), rec)
+        timed("B3_dx", lambda: moe.expert_bwd_dx(D, b.offsets, g["w1"], g["w3"], b.dgu, b.dx_perm), rec)
+        timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1,
+                                                      b.dW3, b.dW2), rec)
+        timed("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), rec)
+        timed("B5_router_bwd", lambda: moe.router_bwd(D, g["x"], g["wr"], b.dlogits, b.dx_router, b.dWr,
+                                                      b.ws_router_bwd), rec)
+        timed("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, b.dx_router, b.dx), rec)
+
+    note("inputs resident in HBM; warming up")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    note(f"{args.warmup} warmup steps done; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    R = int(b.offsets[-1].item())
+    T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
+    bb = 2 if cfg.dtype == "bf16" else 4
+    avg_ms = {r: float(np.mean([s.elapsed_time(e) for s, e in ev[r]])) for r in rows if ev[r]}
+    flops = {"A1_router_logits": 2.0 * T * d * E, "A5_gate_up": 4.0 * R * d * f, "A6_down": 2.0 * R * d * f,
+             "B2_dh": 2.0 * R * d * f, "B3_dx": 4.0 * R * d * f, "B4_dw": 6.0 * R * d * f,
+             "B5_router_bwd": 4.0 * T * d * E}
+    ntok_local = int((b.slot_row >= 0).any(dim=1).sum().item())
+    hbm_bytes = {"A2_route": T * E * 4 + T * cfg.k * 8,
+                 "A34_permute": ntok_local * d * bb + R * d * bb + T * cfg.k * 12 + R * 4,
+                 "A7_combine": R * d * bb + T * d * bb + T * cfg.k * 8,
+                 "B1_combine_bwd": T * d * bb + 2 * R * d * bb + T * cfg.k * 12,
+                 "B5_route_bwd": T * E * 4 + T * cfg.k * 12,
+                 "B5_unpermute": R * d * bb + T * d * (4 + bb) + T * cfg.k * 4}
+    per_row = {}
+    for r, ms in avg_ms.items():
+        ent = {"ms": round(ms, 4)}
+        if r in flops:
+            ent["TFLOP/s"] = round(flops[r] / ms / 1e9, 1)
+            ent["frac_mfma"] = round(flops[r] / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+        if r in hbm_bytes:
+            ent["GB/s"] = round(hbm_bytes[r] / ms / 1e6, 1)
+            ent["frac_hbm"] = round(hbm_bytes[r] / ms / 1e6 / PEAK_HBM_GBS, 4)
+        per_row[r] = ent
+    gemm_rows = [r for r in ("A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw") if r in avg_ms]
+    gemm_tflops = sum(flops[r] for r in gemm_rows) / sum(avg_ms[r] for r in gemm_rows) / 1e9
+    # dominant single-kernel row: the largest time among rows that launch one kernel
+    single = [r for r in ("A1_router_logits", "A2_route", "A5_gate_up", "A6_down", "A7_combine", "B1_combine_bwd",
+                          "B2_dh", "B3_dx", "B5_route_bwd", "B5_unpermute") if r in avg_ms]
+    dom = max(single, key=lambda r: avg_ms[r])
+    if dom in flops:
+        ach = flops[dom] / avg_ms[dom] / 1e9
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        ach = hbm_bytes[dom] / avg_ms[dom] / 1e6
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+
+    note(f"timed region: {ms_step:.3f} ms/step")
+    cpu = None
+    if not args.no_cpu_baseline:
+        note(f"cpu baseline: oracle on {min(args.cpu_sample_tokens, cfg.T)} tokens")
+        del g, b
+        torch.cuda.empty_cache()
+        cpu = _cpu_baseline(cfg, inp, min(args.cpu_sample_tokens, cfg.T))
+
+    out = {
+        "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} ({cfg.num_local} local from {cfg.expert_begin}) "
+                               f"top-{cfg.k} f={f} {'fwd+bwd' if cfg.backward else 'fwd'}",
+                   "routed_rows": R, "global_batch": T, "parallelism": "single GPU"},
+        "grouped_gemm_tflops": round(gemm_tflops, 1),
+        "grouped_gemm_frac_mfma": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "rows": per_row,
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert-layer library, libmoe.so.
+ *
+ * The layer is the sparse MoE block of one GPU's expert-parallel share, as
+ * described by the Aurora page ("Scalable Pretraining of Large Mixture of
+ * Experts Language Models on Aurora Super Computer", section 3.1
+ * FastSparseMoE, Algorithm 1): router, softmax + top-k, per-expert token
+ * counting with a prefix sum, index generation and gather, a grouped SwiGLU
+ * expert MLP over all local experts, and the weighted output reduction; plus
+ * the backward of each step.  Shapes of the 1T model come from the Domyn page
+ * ("Training a 1T-Params MoE on EU public infrastructure", model table:
+ * hidden 6144, 384 experts, top-8, expert hidden 1792).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `desc` is a DEVICE pointer, owned by the
+ *    caller, which allocates and frees it.  The library never allocates,
+ *    frees or synchronises, keeps no per-call global state and is
+ *    re-entrant; calls are asynchronous on `stream` (a hipStream_t, NULL =
+ *    the default stream).
+ *  - Matrices are row-major.  "dtype" tensors are float32 (MOE_F32) or
+ *    bfloat16 bits (MOE_BF16) per desc->dtype; logits, routing weights,
+ *    dlogits, dtopk_w and every weight gradient are always float32.
+ *  - Weights use the layout of a linear layer (out x in), concatenated over
+ *    the local experts (the page concatenates each expert's gate_proj,
+ *    up_proj and down_proj weights per rank):  Wr [E][d],
+ *    W1 = gate [NL][f][d], W3 = up [NL][f][d], W2 = down [NL][d][f].
+ *  - NL = desc->num_local experts [expert_begin, expert_begin+NL) are local.
+ *    R = offsets[NL] (on the device) is the number of routed rows; row
+ *    buffers are sized R_cap = T * min(k, NL) rows and rows >= R are never
+ *    written.  No entry point needs R on the host.
+ *  - Every call validates its arguments on the host before any launch and
+ *    returns MOE_OK or a negative error code; no exception crosses the ABI.
+ *    Device inputs must hold finite values (not checked).
+ *  - Pointers must be 16-byte aligned.  d and f must be multiples of 64,
+ *    E a multiple of 8 and at most 1024, 1 <= k <= min(E, 32), T >= 1,
+ *    0 <= expert_begin,
+ *    1 <= num_local, expert_begin + num_local <= E.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad sizes, wrong struct_size */
+  MOE_ERR_UNSUPPORTED = -2, /* dtype or shape outside the supported set above */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -4          /* a HIP launch failed; see moe_last_error() */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Which call a workspace size is asked for. */
+enum moe_op {
+  MOE_OP_ROUTER_LOGITS = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_GROUPED_FFN = 2,
+  MOE_OP_FFN_BWD_DX = 3,
+  MOE_OP_FFN_BWD_DW = 4,
+  MOE_OP_ROUTER_BWD = 5
+};
+
+typedef struct moe_desc {
+  uint32_t struct_size;     /* = sizeof(moe_desc) */
+  int32_t T;                /* tokens on this GPU (Algorithm 1's T) */
+  int32_t d;                /* hidden size (the page's H) */
+  int32_t f;                /* expert hidden size */
+  int32_t E;                /* router width: experts in the whole layer (the page's N) */
+  int32_t k;                /* experts selected per token (the page's K) */
+  int32_t expert_begin;     /* first local expert (the page's n_start) */
+  int32_t num_local;        /* local experts (the page's NR) */
+  int32_t dtype;            /* enum moe_dtype */
+  int32_t renormalize;      /* 1: top-k probabilities divided by their sum; 0: raw softmax probabilities */
+} moe_desc;
+
+/* Host-only query: bytes of device workspace that call `op` needs for desc
+ * (0 when it needs none).  Returns MOE_ERR_INVALID_ARG on a bad desc/op. */
+int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes);
+
+/* A1, router scores (Aurora page, Algorithm 1 stage 1: the router is a linear
+ * layer producing one logit per token and expert).
+ *   x [T][d] dtype, Wr [E][d] dtype, bias [E] float32 or NULL (added to every
+ *   token's logits), logits [T][E] float32 out.  Accumulation is float32. */
+int moe_router_logits(const moe_desc* desc, const void* x, const void* Wr, const float* bias,
+                      float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* A2, softmax + top-k (+ renormalisation) (Algorithm 1 stage 1).
+ *   logits [T][E] float32 -> topk_idx [T][k] int32, topk_w [T][k] float32.
+ *   Slot j holds the j-th largest logit; equal logits (and +0.0 / -0.0) go to
+ *   the lower expert index.  renormalize=1: w_j = exp(L_j - L_0) / sum over
+ *   the k selected of exp(L_i - L_0); renormalize=0: w_j = softmax over all
+ *   E experts at the selected index. */
+int moe_route(const moe_desc* desc, const float* logits, int32_t* topk_idx, float* topk_w,
+              void* stream);
+
+/* A3 + A4, token counting, prefix sum, index generation and gather
+ * (Algorithm 1 stages 2, 3 and the stage-4 gather).
+ *   topk_idx [T][k] int32 (values in [0, E)), x [T][d] dtype (may be NULL:
+ *   indices only);
+ *   counts [E] int32: selections of every expert, local or not;
+ *   offsets [NL+1] int32: exclusive prefix sum of the local counts
+ *     (offsets[NL] = R), the page's cum_token_counts;
+ *   row_token [R_cap] int32: token of each routed row (the page's
+ *     input_indices); rows of one expert are in ascending token order;
+ *   slot_row [T][k] int32: row of each slot, or -1 when its expert is not
+ *     local (the page's output_indices / selected_expert_indices);
+ *   x_perm [R_cap][d] dtype: x_perm[r] = x[row_token[r]] (bit copy).
+ *   ws: moe_workspace_size(MOE_OP_PERMUTE) bytes. */
+int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* A5 + A6, the grouped SwiGLU expert MLP (Algorithm 1 stage 4: Grouped_mm of
+ * gate and up, Silu(gate) * up, Grouped_mm of down, with segment boundaries
+ * offsets).  For each local expert n and row r in [offsets[n], offsets[n+1]):
+ *   G = x_perm[r] W1[n]^T, U = x_perm[r] W3[n]^T, h[r] = silu(G) * U,
+ *   y_perm[r] = h[r] W2[n]^T.
+ *   x_perm [R_cap][d], h [R_cap][f], y_perm [R_cap][d] dtype;
+ *   gu [R_cap][2f] dtype or NULL: when given, G is saved in columns [0, f)
+ *   and U in [f, 2f) for the backward.  Accumulation is float32; h, gu and
+ *   y_perm are rounded to dtype. */
+int moe_grouped_ffn(const moe_desc* desc, const int32_t* offsets, const void* x_perm,
+                    const void* W1, const void* W3, const void* W2, void* gu, void* h,
+                    void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* A5 alone: the gate/up grouped GEMM with the fused SwiGLU epilogue, i.e. the
+ * first half of moe_grouped_ffn (h and, when gu != NULL, G | U as above). */
+int moe_expert_gate_up(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* W1,
+                       const void* W3, void* gu, void* h, void* stream);
+
+/* A6 alone: the down grouped GEMM, y_perm[r] = h[r] W2[n]^T (second half of
+ * moe_grouped_ffn). */
+int moe_expert_down(const moe_desc* desc, const int32_t* offsets, const void* h, const void* W2,
+                    void* y_perm, void* stream);
+
+/* A7, weighted output reduction (Algorithm 1 stage 5 forward):
+ *   y[t] = sum over slots j = 0..k-1 with slot_row[t][j] >= 0 of
+ *          topk_w[t][j] * y_perm[slot_row[t][j]], summed in float32 in slot
+ *   order; y [T][d] dtype (0 for a token without a local slot). */
+int moe_combine(const moe_desc* desc, const int32_t* slot_row, const float* topk_w,
+                const void* y_perm, void* y, void* stream);
+
+/* B1, backward of the output reduction (Algorithm 1 stage 5 backward):
+ *   dy_perm[slot_row[t][j]] = topk_w[t][j] * dy[t]    ([R_cap][d] dtype),
+ *   dtopk_w[t][j] = <y_perm[slot_row[t][j]], dy[t]>   ([T][k] float32; 0 for
+ *   non-local slots).  dy [T][d] dtype. */
+int moe_combine_bwd(const moe_desc* desc, const int32_t* slot_row, const float* topk_w,
+                    const void* y_perm, const void* dy, void* dy_perm, float* dtopk_w,
+                    void* stream);
+
+/* B2 + B3, backward of the expert MLP with respect to its input (derived from
+ * Algorithm 1 stage 4 by differentiation):
+ *   dH = dy_perm W2[n], dU = dH * silu(G), dG = dH * U * silu'(G),
+ *   dx_perm = dG W1[n] + dU W3[n].
+ *   gu [R_cap][2f] dtype (as saved by moe_grouped_ffn), dy_perm [R_cap][d];
+ *   dgu [R_cap][2f] dtype out (dG in [0, f), dU in [f, 2f)),
+ *   dx_perm [R_cap][d] dtype out. */
+int moe_grouped_ffn_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* W1,
+                           const void* W3, const void* W2, const void* gu, const void* dy_perm,
+                           void* dgu, void* dx_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* B2 alone: dH = dy_perm W2[n] with the SwiGLU backward fused into the
+ * epilogue -> dgu (first half of moe_grouped_ffn_bwd_dx). */
+int moe_expert_bwd_dh(const moe_desc* desc, const int32_t* offsets, const void* W2, const void* gu,
+                      const void* dy_perm, void* dgu, void* stream);
+
+/* B3 alone: dx_perm = dG W1[n] + dU W3[n], one grouped GEMM with K = 2f over
+ * dgu (second half of moe_grouped_ffn_bwd_dx). */
+int moe_expert_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* W1, const void* W3,
+                      const void* dgu, void* dx_perm, void* stream);
+
+/* B4, weight gradients of the expert MLP (variable-K grouped GEMMs):
+ *   dW1[n] = dG_n^T x_perm_n, dW3[n] = dU_n^T x_perm_n  ([NL][f][d] float32),
+ *   dW2[n] = dy_perm_n^T h_n                           ([NL][d][f] float32),
+ *   where _n is the row segment of expert n.  They are overwritten, not
+ *   accumulated; an expert with no rows gets exact zeros. */
+int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const void* x_perm,
+                           const void* h, const void* dgu, const void* dy_perm, float* dW1,
+                           float* dW3, float* dW2, void* ws, size_t ws_bytes, void* stream);
+
+/* B5a, backward of the gather: dx[t] = dx_add[t] + sum over local slots j of
+ *   dx_perm[slot_row[t][j]], summed in float32; dx [T][d] dtype out;
+ *   dx_add [T][d] float32 or NULL (e.g. the router path's input gradient). */
+int moe_unpermute_bwd(const moe_desc* desc, const int32_t* slot_row, const void* dx_perm,
+                      const float* dx_add, void* dx, void* stream);
+
+/* B5b, backward of softmax + top-k (+ renormalisation):
+ *   renormalize=1: dlogits[t][m] = w_m (dw_m - sum_j w_j dw_j) for the k
+ *   selected m (local or not), 0 elsewhere;
+ *   renormalize=0: dlogits[t][e] = p_e (g_e - sum_j w_j dw_j) with p the
+ *   softmax of logits over all E and g_e = dw_j at e = topk_idx[t][j], else
+ *   0 (needs logits; it may be NULL when renormalize=1).
+ *   dlogits [T][E] float32 out. */
+int moe_route_bwd(const moe_desc* desc, const float* logits, const int32_t* topk_idx,
+                  const float* topk_w, const float* dtopk_w, float* dlogits, void* stream);
+
+/* B5c, backward of the router linear layer:
+ *   dx_router = dlogits Wr   ([T][d] float32 out),
+ *   dWr = dlogits^T x        ([E][d] float32 out, overwritten).
+ *   On the bf16 path dlogits is rounded to bf16 for the matrix cores. */
+int moe_router_bwd(const moe_desc* desc, const void* x, const void* Wr, const float* dlogits,
+                   float* dx_router, float* dWr, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(int status);
+
+/* Text of the last HIP error seen by a failing call on this thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

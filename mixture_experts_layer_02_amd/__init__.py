@@ -1,0 +1,283 @@
+"""Python binding of libmoe.so, the MI355X MoE expert-layer library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The
+functions mirror the C ABI in include/moe.h one to one; ``Buffers``,
+``forward`` and ``backward`` allocate the tensors of one layer pass and chain
+the entry points in order.
+
+There is no fallback: if libmoe.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported before libmoe.so so that the process holds one HIP runtime
+
+__all__ = [
+    "MoeError", "MoeDesc", "lib", "make_desc", "workspace_size", "router_logits", "route", "permute",
+    "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
+    "unpermute_bwd", "route_bwd", "router_bwd", "Buffers", "forward", "backward",
+    "MOE_F32", "MOE_BF16",
+]
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+OP_ROUTER_LOGITS, OP_PERMUTE, OP_GROUPED_FFN, OP_FFN_BWD_DX, OP_FFN_BWD_DW, OP_ROUTER_BWD = range(6)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("T", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("f", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("expert_begin", ctypes.c_int32),
+        ("num_local", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("renormalize", ctypes.c_int32),
+    ]
+
+    @property
+    def R_cap(self) -> int:
+        return self.T * min(self.k, self.num_local)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == MOE_BF16 else torch.float32
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, rc):
+        l = lib()
+        msg = l.moe_status_str(rc).decode()
+        if rc == MOE_ERR_HIP:
+            msg += ": " + l.moe_last_error().decode()
+        super().__init__(f"{fn} failed ({rc}): {msg}")
+        self.rc = rc
+
+
+# name -> argtypes (after the leading const moe_desc*)
+_SIGS = {
+    "moe_router_logits": [_vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_route": [_vp, _vp, _vp, _vp],
+    "moe_permute": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_grouped_ffn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_expert_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_down": [_vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dh": [_vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_combine": [_vp, _vp, _vp, _vp, _vp],
+    "moe_combine_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_grouped_ffn_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_grouped_ffn_bwd_dw": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_unpermute_bwd": [_vp, _vp, _vp, _vp, _vp],
+    "moe_route_bwd": [_vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+}
+EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error"])
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build()")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(l, name)
+            fn.argtypes = [ctypes.POINTER(MoeDesc)] + args
+            fn.restype = ctypes.c_int
+        l.moe_workspace_size.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        l.moe_workspace_size.restype = ctypes.c_int
+        l.moe_status_str.argtypes = [ctypes.c_int]
+        l.moe_status_str.restype = ctypes.c_char_p
+        l.moe_last_error.argtypes = []
+        l.moe_last_error.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def make_desc(T, d, f, E, k, expert_begin=0, num_local=None, dtype=MOE_BF16, renormalize=1) -> MoeDesc:
+    if isinstance(dtype, str):
+        dtype = MOE_BF16 if dtype == "bf16" else MOE_F32
+    return MoeDesc(ctypes.sizeof(MoeDesc), T, d, f, E, k, expert_begin, E if num_local is None else num_local,
+                   dtype, renormalize)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("libmoe needs contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _call(name, desc, *args):
+    rc = getattr(lib(), name)(ctypes.byref(desc), *[_p(a) for a in args])
+    if rc != MOE_OK:
+        raise MoeError(name, rc)
+
+
+def workspace_size(desc: MoeDesc, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    rc = lib().moe_workspace_size(ctypes.byref(desc), op, ctypes.byref(n))
+    if rc != MOE_OK:
+        raise MoeError("moe_workspace_size", rc)
+    return n.value
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (ws, ws.numel() * ws.element_size())
+
+
+def router_logits(desc, x, wr, bias, logits, ws=None):
+    w, n = _ws(ws)
+    _call("moe_router_logits", desc, x, wr, bias, logits, w, n, _stream())
+
+
+def route(desc, logits, topk_idx, topk_w):
+    _call("moe_route", desc, logits, topk_idx, topk_w, _stream())
+
+
+def permute(desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws):
+    w, n = _ws(ws)
+    _call("moe_permute", desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, w, n, _stream())
+
+
+def grouped_ffn(desc, offsets, x_perm, w1, w3, w2, gu, h, y_perm, ws=None):
+    w, n = _ws(ws)
+    _call("moe_grouped_ffn", desc, offsets, x_perm, w1, w3, w2, gu, h, y_perm, w, n, _stream())
+
+
+def expert_gate_up(desc, offsets, x_perm, w1, w3, gu, h):
+    _call("moe_expert_gate_up", desc, offsets, x_perm, w1, w3, gu, h, _stream())
+
+
+def expert_down(desc, offsets, h, w2, y_perm):
+    _call("moe_expert_down", desc, offsets, h, w2, y_perm, _stream())
+
+
+def expert_bwd_dh(desc, offsets, w2, gu, dy_perm, dgu):
+    _call("moe_expert_bwd_dh", desc, offsets, w2, gu, dy_perm, dgu, _stream())
+
+
+def expert_bwd_dx(desc, offsets, w1, w3, dgu, dx_perm):
+    _call("moe_expert_bwd_dx", desc, offsets, w1, w3, dgu, dx_perm, _stream())
+
+
+def combine(desc, slot_row, topk_w, y_perm, y):
+    _call("moe_combine", desc, slot_row, topk_w, y_perm, y, _stream())
+
+
+def combine_bwd(desc, slot_row, topk_w, y_perm, dy, dy_perm, dtopk_w):
+    _call("moe_combine_bwd", desc, slot_row, topk_w, y_perm, dy, dy_perm, dtopk_w, _stream())
+
+
+def grouped_ffn_bwd_dx(desc, offsets, w1, w3, w2, gu, dy_perm, dgu, dx_perm, ws=None):
+    w, n = _ws(ws)
+    _call("moe_grouped_ffn_bwd_dx", desc, offsets, w1, w3, w2, gu, dy_perm, dgu, dx_perm, w, n, _stream())
+
+
+def grouped_ffn_bwd_dw(desc, offsets, x_perm, h, dgu, dy_perm, dw1, dw3, dw2, ws=None):
+    w, n = _ws(ws)
+    _call("moe_grouped_ffn_bwd_dw", desc, offsets, x_perm, h, dgu, dy_perm, dw1, dw3, dw2, w, n, _stream())
+
+
+def unpermute_bwd(desc, slot_row, dx_perm, dx_add, dx):
+    _call("moe_unpermute_bwd", desc, slot_row, dx_perm, dx_add, dx, _stream())
+
+
+def route_bwd(desc, logits, topk_idx, topk_w, dtopk_w, dlogits):
+    _call("moe_route_bwd", desc, logits, topk_idx, topk_w, dtopk_w, dlogits, _stream())
+
+
+def router_bwd(desc, x, wr, dlogits, dx_router, dwr, ws):
+    w, n = _ws(ws)
+    _call("moe_router_bwd", desc, x, wr, dlogits, dx_router, dwr, w, n, _stream())
+
+
+class Buffers:
+    """Every device tensor of one forward (+ backward) pass of a layer, allocated once."""
+
+    def __init__(self, desc: MoeDesc, device="cuda", backward=False):
+        dt = desc.torch_dtype
+        T, d, f, E, k, NL, Rc = desc.T, desc.d, desc.f, desc.E, desc.k, desc.num_local, desc.R_cap
+        z = dict(device=device)
+        i32 = torch.int32
+        self.desc = desc
+        self.logits = torch.empty(T, E, dtype=torch.float32, **z)
+        self.topk_idx = torch.empty(T, k, dtype=i32, **z)
+        self.topk_w = torch.empty(T, k, dtype=torch.float32, **z)
+        self.counts = torch.empty(E, dtype=i32, **z)
+        self.offsets = torch.empty(NL + 1, dtype=i32, **z)
+        self.row_token = torch.empty(Rc, dtype=i32, **z)
+        self.slot_row = torch.empty(T, k, dtype=i32, **z)
+        self.x_perm = torch.empty(Rc, d, dtype=dt, **z)
+        self.gu = torch.empty(Rc, 2 * f, dtype=dt, **z) if backward else None
+        self.h = torch.empty(Rc, f, dtype=dt, **z)
+        self.y_perm = torch.empty(Rc, d, dtype=dt, **z)
+        self.y = torch.empty(T, d, dtype=dt, **z)
+        self.ws_permute = torch.empty(max(16, workspace_size(desc, OP_PERMUTE)), dtype=torch.uint8, **z)
+        if backward:
+            self.dy_perm = torch.empty(Rc, d, dtype=dt, **z)
+            self.dtopk_w = torch.empty(T, k, dtype=torch.float32, **z)
+            self.dgu = torch.empty(Rc, 2 * f, dtype=dt, **z)
+            self.dx_perm = torch.empty(Rc, d, dtype=dt, **z)
+            self.dW1 = torch.empty(NL, f, d, dtype=torch.float32, **z)
+            self.dW3 = torch.empty(NL, f, d, dtype=torch.float32, **z)
+            self.dW2 = torch.empty(NL, d, f, dtype=torch.float32, **z)
+            self.dlogits = torch.empty(T, E, dtype=torch.float32, **z)
+            self.dx_router = torch.empty(T, d, dtype=torch.float32, **z)
+            self.dWr = torch.empty(E, d, dtype=torch.float32, **z)
+            self.dx = torch.empty(T, d, dtype=dt, **z)
+            self.ws_router_bwd = torch.empty(max(16, workspace_size(desc, OP_ROUTER_BWD)), dtype=torch.uint8, **z)
+
+
+def forward(b: Buffers, x, wr, w1, w3, w2, bias=None, routing=None):
+    """Stages A1-A7.  ``routing=(topk_idx, topk_w)`` device tensors skip A1-A2."""
+    D = b.desc
+    if routing is None:
+        router_logits(D, x, wr, bias, b.logits)
+        route(D, b.logits, b.topk_idx, b.topk_w)
+        idx, w = b.topk_idx, b.topk_w
+    else:
+        idx, w = routing
+    permute(D, idx, x, b.counts, b.offsets, b.row_token, b.slot_row, b.x_perm, b.ws_permute)
+    grouped_ffn(D, b.offsets, b.x_perm, w1, w3, w2, b.gu, b.h, b.y_perm)
+    combine(D, b.slot_row, w, b.y_perm, b.y)
+    return b.y
+
+
+def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None):
+    """Stages B1-B5 for upstream gradient dy (needs Buffers(backward=True))."""
+    D = b.desc
+    idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
+    combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
+    grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
+    grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
+    if routing is None:
+        route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits)
+        router_bwd(D, x, wr, b.dlogits, b.dx_router, b.dWr, b.ws_router_bwd)
+        unpermute_bwd(D, b.slot_row, b.dx_perm, b.dx_router, b.dx)
+    else:
+        unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx)
+    return b.dx

@@ -1,0 +1,217 @@
+// The extern "C" entry points of libmoe.so (declared in include/moe.h):
+// argument validation on the host, then the kernel launches of each step.
+#include <string.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  strncpy(g_last_error, hipGetErrorString(e), sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = 0;
+  return MOE_ERR_HIP;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? MOE_OK : hip_fail(e); }
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool need(const void* p) { return p != nullptr && aligned(p); }
+bool opt(const void* p) { return p == nullptr || aligned(p); }
+
+int check_desc(const moe_desc* d) {
+  if (!d || d->struct_size != sizeof(moe_desc)) return MOE_ERR_INVALID_ARG;
+  if (d->T < 1 || d->d < 1 || d->f < 1 || d->E < 1 || d->k < 1 || d->num_local < 1 || d->expert_begin < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (d->k > d->E || (int64_t)d->expert_begin + d->num_local > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (d->d % 64 || d->f % 64 || d->E % 8 || d->E > 1024 || d->k > 32) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d->T * d->k >= (1ll << 31) || (int64_t)d->T * d->E >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  switch (op) {
+    case MOE_OP_ROUTER_LOGITS:
+    case MOE_OP_GROUPED_FFN:
+    case MOE_OP_FFN_BWD_DX:
+    case MOE_OP_FFN_BWD_DW: *bytes = 0; return MOE_OK;
+    case MOE_OP_PERMUTE: *bytes = moe::permute_workspace(*desc); return MOE_OK;
+    case MOE_OP_ROUTER_BWD: *bytes = moe::router_bwd_workspace(*desc); return MOE_OK;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+}
+
+int moe_router_logits(const moe_desc* desc, const void* x, const void* Wr, const float* bias, float* logits,
+                      void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(x) || !need(Wr) || !need(logits) || !opt(bias)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_router_logits(*desc, x, Wr, bias, logits, S(stream)));
+}
+
+int moe_route(const moe_desc* desc, const float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(logits) || !need(topk_idx) || !need(topk_w)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_route(*desc, logits, topk_idx, topk_w, S(stream)));
+}
+
+int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,
+                int32_t* row_token, int32_t* slot_row, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(topk_idx) || !need(counts) || !need(offsets) || !need(row_token) || !need(slot_row) || !opt(x))
+    return MOE_ERR_INVALID_ARG;
+  if (x && !need(x_perm)) return MOE_ERR_INVALID_ARG;
+  if (!need(ws) || ws_bytes < moe::permute_workspace(*desc)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_permute(*desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws,
+                                    S(stream)));
+}
+
+int moe_grouped_ffn(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* W1,
+                    const void* W3, const void* W2, void* gu, void* h, void* y_perm, void* ws, size_t ws_bytes,
+                    void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(x_perm) || !need(W1) || !need(W3) || !need(W2) || !opt(gu) || !need(h) ||
+      !need(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  hipError_t e = moe::launch_gate_up(*desc, offsets, x_perm, W1, W3, gu, h, S(stream));
+  if (e == hipSuccess) e = moe::launch_down(*desc, offsets, h, W2, y_perm, S(stream));
+  return finish(e);
+}
+
+int moe_expert_gate_up(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* W1,
+                       const void* W3, void* gu, void* h, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(x_perm) || !need(W1) || !need(W3) || !opt(gu) || !need(h)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_gate_up(*desc, offsets, x_perm, W1, W3, gu, h, S(stream)));
+}
+
+int moe_expert_down(const moe_desc* desc, const int32_t* offsets, const void* h, const void* W2, void* y_perm,
+                    void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(h) || !need(W2) || !need(y_perm)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_down(*desc, offsets, h, W2, y_perm, S(stream)));
+}
+
+int moe_combine(const moe_desc* desc, const int32_t* slot_row, const float* topk_w, const void* y_perm, void* y,
+                void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(topk_w) || !need(y_perm) || !need(y)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_combine(*desc, slot_row, topk_w, y_perm, y, S(stream)));
+}
+
+int moe_combine_bwd(const moe_desc* desc, const int32_t* slot_row, const float* topk_w, const void* y_perm,
+                    const void* dy, void* dy_perm, float* dtopk_w, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(topk_w) || !need(y_perm) || !need(dy) || !need(dy_perm) || !need(dtopk_w))
+    return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_combine_bwd(*desc, slot_row, topk_w, y_perm, dy, dy_perm, dtopk_w, S(stream)));
+}
+
+int moe_grouped_ffn_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* W1, const void* W3,
+                           const void* W2, const void* gu, const void* dy_perm, void* dgu, void* dx_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(W1) || !need(W3) || !need(W2) || !need(gu) || !need(dy_perm) || !need(dgu) ||
+      !need(dx_perm))
+    return MOE_ERR_INVALID_ARG;
+  hipError_t e = moe::launch_bwd_dh(*desc, offsets, W2, gu, dy_perm, dgu, S(stream));
+  if (e == hipSuccess) e = moe::launch_bwd_dxp(*desc, offsets, W1, W3, dgu, dx_perm, S(stream));
+  return finish(e);
+}
+
+int moe_expert_bwd_dh(const moe_desc* desc, const int32_t* offsets, const void* W2, const void* gu,
+                      const void* dy_perm, void* dgu, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(W2) || !need(gu) || !need(dy_perm) || !need(dgu)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_bwd_dh(*desc, offsets, W2, gu, dy_perm, dgu, S(stream)));
+}
+
+int moe_expert_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* W1, const void* W3,
+                      const void* dgu, void* dx_perm, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(W1) || !need(W3) || !need(dgu) || !need(dx_perm)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_bwd_dxp(*desc, offsets, W1, W3, dgu, dx_perm, S(stream)));
+}
+
+int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* h,
+                           const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2, void* ws,
+                           size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(x_perm) || !need(h) || !need(dgu) || !need(dy_perm) || !need(dW1) || !need(dW3) ||
+      !need(dW2))
+    return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_ffn_bwd_dw(*desc, offsets, x_perm, h, dgu, dy_perm, dW1, dW3, dW2, S(stream)));
+}
+
+int moe_unpermute_bwd(const moe_desc* desc, const int32_t* slot_row, const void* dx_perm, const float* dx_add,
+                      void* dx, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(dx_perm) || !opt(dx_add) || !need(dx)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_unpermute_bwd(*desc, slot_row, dx_perm, dx_add, dx, S(stream)));
+}
+
+int moe_route_bwd(const moe_desc* desc, const float* logits, const int32_t* topk_idx, const float* topk_w,
+                  const float* dtopk_w, float* dlogits, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(topk_idx) || !need(topk_w) || !need(dtopk_w) || !need(dlogits)) return MOE_ERR_INVALID_ARG;
+  if (desc->renormalize == 0 ? !need(logits) : !opt(logits)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_route_bwd(*desc, logits, topk_idx, topk_w, dtopk_w, dlogits, S(stream)));
+}
+
+int moe_router_bwd(const moe_desc* desc, const void* x, const void* Wr, const float* dlogits, float* dx_router,
+                   float* dWr, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(x) || !need(Wr) || !need(dlogits) || !opt(dx_router) || !opt(dWr)) return MOE_ERR_INVALID_ARG;
+  if (dWr && (!need(ws) || ws_bytes < moe::router_bwd_workspace(*desc)))
+    return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_router_bwd(*desc, x, Wr, dlogits, dx_router, dWr, ws, S(stream)));
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+}  // extern "C"

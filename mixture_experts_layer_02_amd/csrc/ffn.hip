@@ -1,0 +1,282 @@
+// Launchers of the grouped GEMMs: the SwiGLU expert MLP (Aurora page,
+// section 3.1, Algorithm 1 stage 4: Grouped_mm of gate and up, Silu(gate) * up,
+// Grouped_mm of down over the cum_token_counts segments), its backward, and
+// the router's linear layer and its backward.
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+
+#include "gemm.h"
+#include "internal.h"
+
+namespace moe {
+
+int num_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+namespace {
+
+GemmParams blank() {
+  GemmParams p{};
+  return p;
+}
+
+template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
+hipError_t run_mfma(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
+  const int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus() * 2);
+  if (grid <= 0) return hipSuccess;
+  gemm_mfma_kernel<ALAY, BLAY, AT, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int ALAY, int BLAY, int GRP, int EPI, bool DUAL>
+hipError_t run_f32(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
+  const int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus() * 4);
+  if (grid <= 0) return hipSuccess;
+  gemm_f32_kernel<ALAY, BLAY, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t r_cap(const moe_desc& d) { return (int64_t)d.T * std::min(d.k, d.num_local); }
+
+// Upper bound on the m-tiles of a variable-M grouped product.
+int64_t mtiles_ub(const moe_desc& d, int bm) { return cdiv(r_cap(d), bm) + d.num_local; }
+
+// Split-K factor of the router-weight gradient (K = T is long, M x N small):
+// enough chunks for two workgroups per compute unit of a 256-CU part.  It
+// depends on the shape only, so the summation order (and the result) is the
+// same on every device and the workspace query needs no device.
+int router_splits(const moe_desc& d) {
+  const int64_t tiles = cdiv(d.E, 128) * cdiv(d.d, 128);
+  int64_t s = cdiv((int64_t)256 * 2, tiles);
+  s = std::min<int64_t>(s, cdiv(d.T, 256));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+
+__global__ void __launch_bounds__(256) sum_splits_kernel(const float* __restrict__ part, int S, int64_t n,
+                                                         float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += part[(int64_t)s * n + i];
+    out[i] = acc;
+  }
+}
+
+}  // namespace
+
+size_t router_bwd_workspace(const moe_desc& d) {
+  return (size_t)router_splits(d) * (size_t)d.E * (size_t)d.d * sizeof(float);
+}
+
+hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
+                                float* logits, hipStream_t s) {
+  GemmParams p = blank();
+  p.A = x;
+  p.lda = d.d;
+  p.B = Wr;
+  p.ldb = d.d;
+  p.C = logits;
+  p.ldc = d.E;
+  p.M = d.T;
+  p.N = d.E;
+  p.K = d.d;
+  p.bias = bias;
+  p.c_f32 = 1;
+  if (d.dtype == MOE_BF16)
+    return run_mfma<LAY_K, LAY_K, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 128) * cdiv(d.E, 128), s);
+  return run_f32<LAY_K, LAY_K, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.E, 64), s);
+}
+
+hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,
+                          const void* W3, void* gu, void* h, hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
+  GemmParams p = blank();
+  p.A = x_perm;
+  p.lda = d.d;
+  p.B = W1;
+  p.B2 = W3;
+  p.ldb = d.d;
+  p.b_gstride = (int64_t)d.f * d.d;
+  p.C = h;
+  p.ldc = d.f;
+  p.gu_out = gu;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.N = d.f;
+  p.K = d.d;
+  p.c_f32 = bf ? 0 : 1;
+  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 128) * cdiv(d.f, 64), s);
+  return run_f32<LAY_K, LAY_K, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
+}
+
+hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h, const void* W2, void* y_perm,
+                       hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
+  GemmParams q = blank();
+  q.A = h;
+  q.lda = d.f;
+  q.B = W2;
+  q.ldb = d.f;
+  q.b_gstride = (int64_t)d.d * d.f;
+  q.C = y_perm;
+  q.ldc = d.d;
+  q.offsets = offsets;
+  q.ngroups = d.num_local;
+  q.N = d.d;
+  q.K = d.f;
+  q.c_f32 = bf ? 0 : 1;
+  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 128) * cdiv(d.d, 128), s);
+  return run_f32<LAY_K, LAY_K, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
+}
+
+hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* W2, const void* gu,
+                         const void* dy_perm, void* dgu, hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
+  // dH = dY W2 (W2 stored [d][f]: N-contiguous in k = d), SwiGLU backward epilogue -> dgu
+  GemmParams p = blank();
+  p.A = dy_perm;
+  p.lda = d.d;
+  p.B = W2;
+  p.ldb = d.f;
+  p.b_gstride = (int64_t)d.d * d.f;
+  p.C = dgu;
+  p.ldc = 2 * (int64_t)d.f;
+  p.gu_in = gu;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.N = d.f;
+  p.K = d.d;
+  p.c_f32 = bf ? 0 : 1;
+  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, 128) * cdiv(d.f, 128), s);
+  return run_f32<LAY_K, LAY_MN, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
+}
+
+hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void* W1, const void* W3,
+                          const void* dgu, void* dx_perm, hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
+  // dX = [dG | dU] [W1 ; W3]  (K = 2f; rows k < f of W1, k >= f of W3, both [f][d])
+  GemmParams q = blank();
+  q.A = dgu;
+  q.lda = 2 * (int64_t)d.f;
+  q.B = W1;
+  q.B2 = W3;
+  q.ksplit = d.f;
+  q.ldb = d.d;
+  q.b_gstride = (int64_t)d.f * d.d;
+  q.C = dx_perm;
+  q.ldc = d.d;
+  q.offsets = offsets;
+  q.ngroups = d.num_local;
+  q.N = d.d;
+  q.K = 2 * d.f;
+  q.c_f32 = bf ? 0 : 1;
+  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 128) * cdiv(d.d, 128), s);
+  return run_f32<LAY_K, LAY_MN, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
+}
+
+hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
+                             const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
+                             hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
+  // dW1 | dW3 [f][d] = [dG | dU]^T x_perm over each expert's rows (M = 2f split at f)
+  GemmParams p = blank();
+  p.A = dgu;
+  p.lda = 2 * (int64_t)d.f;
+  p.B = x_perm;
+  p.ldb = d.d;
+  p.C = dW1;
+  p.C2 = dW3;
+  p.msplit = d.f;
+  p.ldc = d.d;
+  p.c_gstride = (int64_t)d.f * d.d;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.M = 2 * d.f;
+  p.N = d.d;
+  p.c_f32 = 1;
+  hipError_t e;
+  if (bf) e = run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 128) * cdiv(d.d, 128), s);
+  else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
+  if (e != hipSuccess) return e;
+  // dW2 [d][f] = dy_perm^T h
+  GemmParams q = blank();
+  q.A = dy_perm;
+  q.lda = d.d;
+  q.B = h;
+  q.ldb = d.f;
+  q.C = dW2;
+  q.ldc = d.f;
+  q.c_gstride = (int64_t)d.d * d.f;
+  q.offsets = offsets;
+  q.ngroups = d.num_local;
+  q.M = d.d;
+  q.N = d.f;
+  q.c_f32 = 1;
+  if (bf) return run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 128) * cdiv(d.f, 128), s);
+  return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 64) * cdiv(d.f, 64), s);
+}
+
+hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
+                             float* dx_router, float* dWr, void* ws, hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
+  hipError_t e = hipSuccess;
+  if (dx_router) {
+    // dx_router [T][d] = dlogits [T][E] Wr [E][d]
+    GemmParams p = blank();
+    p.A = dlogits;
+    p.lda = d.E;
+    p.B = Wr;
+    p.ldb = d.d;
+    p.C = dx_router;
+    p.ldc = d.d;
+    p.M = d.T;
+    p.N = d.d;
+    p.K = d.E;
+    p.c_f32 = 1;
+    if (bf) e = run_mfma<LAY_K, LAY_MN, float, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 128) * cdiv(d.d, 128), s);
+    else e = run_f32<LAY_K, LAY_MN, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.d, 64), s);
+    if (e != hipSuccess) return e;
+  }
+  if (dWr) {
+    // dWr [E][d] = dlogits^T x, split over T into S chunks, then summed in chunk order
+    const int S = router_splits(d);
+    float* part = reinterpret_cast<float*>(ws);
+    GemmParams q = blank();
+    q.A = dlogits;
+    q.lda = d.E;
+    q.B = x;
+    q.ldb = d.d;
+    q.C = part;
+    q.ldc = d.d;
+    q.c_gstride = (int64_t)d.E * d.d;
+    q.offsets = nullptr;
+    q.ngroups = S;
+    q.kchunk = (int)cdiv(d.T, S);
+    q.M = d.E;
+    q.N = d.d;
+    q.K = d.T;
+    q.c_f32 = 1;
+    if (bf) e = run_mfma<LAY_MN, LAY_MN, float, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, 128) * cdiv(d.d, 128), s);
+    else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, 64) * cdiv(d.d, 64), s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)d.E * d.d;
+    const int64_t blocks = std::min<int64_t>(cdiv(n, 256), (int64_t)num_cus() * 8);
+    sum_splits_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, S, n, dWr);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace moe

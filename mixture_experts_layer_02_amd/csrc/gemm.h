@@ -1,0 +1,549 @@
+// Grouped GEMM kernels of the expert MLP, its backward and the router.
+//
+// One template covers every matrix product of the layer:
+//   C[m][n] = sum_k A(m, k) B(k, n)
+// with A stored K-contiguous (A[m*lda + k]) or M-contiguous (A[k*lda + m]),
+// B stored K-contiguous (B[n*ldb + k]) or N-contiguous (B[k*ldb + n]), and
+// three kinds of grouping:
+//   GRP_NONE  one plain product (router);
+//   GRP_M     variable-M groups: group g owns rows [offsets[g], offsets[g+1])
+//             of A and C and its own B (the expert segments of the Aurora
+//             page's Grouped_mm with cum_token_counts boundaries);
+//   GRP_K     variable-K groups: group g reduces over k in [offsets[g],
+//             offsets[g+1]) and owns its own C (expert weight gradients),
+//             or uniform K chunks when offsets is NULL (split-K).
+// The tile loop is persistent: the grid is sized to the machine and each
+// workgroup walks tile ids blockIdx.x, blockIdx.x + gridDim.x, ...; the tile
+// count is computed on the device from offsets, so no host sync is needed.
+// Within an expert, tiles are ordered m-tile fastest so that the workgroups
+// running together share one expert's weights and rows in L2 / MALL.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+enum { LAY_K = 0, LAY_MN = 1 };
+enum { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
+
+constexpr int MAXG = 1024;
+
+struct GemmParams {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  const void* B2;       // DUAL: second B (same layout); ksplit: B for k >= ksplit
+  int64_t ldb;
+  int64_t b_gstride;    // elements between groups' B (GRP_M)
+  int ksplit;           // 0 = off; else k >= ksplit reads B2 at k - ksplit
+  void* C;
+  void* C2;             // msplit: rows >= msplit go to C2 at row - msplit
+  int64_t ldc;
+  int64_t c_gstride;    // elements between groups' C (GRP_K)
+  int msplit;
+  const int32_t* offsets;
+  int ngroups;
+  int M, N, K;
+  int kchunk;           // GRP_K with offsets == NULL: group g = [g*kchunk, (g+1)*kchunk) of K
+  const float* bias;    // EPI_STORE: C += bias[n] (NULL = none)
+  const void* gu_in;    // EPI_SWIGLU_BWD: [rows][2N], G | U
+  void* gu_out;         // EPI_SWIGLU: [rows][2N], G | U (NULL = not saved)
+  int c_f32;            // 1: C is float, 0: C is bf16
+};
+
+struct TileCtx {
+  int g;
+  int64_t m0;   // first row of the tile in C's row space (GRP_M: global row)
+  int mlim;     // valid rows in the tile
+  int n0;
+  int nlim;     // valid columns in the tile
+  int64_t k0, k1;  // K range of the tile
+  int mtile;    // m-tile index within the group (GRP_K: within M)
+};
+
+// ---------------------------------------------------------------------------
+// Tile scheduling (shared by the MFMA and the FMA kernels).
+// ---------------------------------------------------------------------------
+template <int GRP, int BM, int BN>
+struct Scheduler {
+  int total;
+  int NT, MT;
+
+  // Must be called by all threads of the block.
+  __device__ void init(const GemmParams& p, int* s_pref, int* s_scan) {
+    NT = (p.N + BN - 1) / BN;
+    if (GRP == GRP_M) {
+      const int tid = threadIdx.x;
+      const int G = p.ngroups;
+      int loc[4];
+      int sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = tid * 4 + i;
+        int c = 0;
+        if (g < G) {
+          const int m = p.offsets[g + 1] - p.offsets[g];
+          c = (m + BM - 1) / BM * NT;
+        }
+        loc[i] = c;
+        sum += c;
+      }
+      s_scan[tid] = sum;
+      __syncthreads();
+      for (int off = 1; off < 256; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+      }
+      int ex = s_scan[tid] - sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = tid * 4 + i;
+        if (g < G) s_pref[g] = ex;
+        ex += loc[i];
+      }
+      if (tid == 0) s_pref[G] = s_scan[255];
+      __syncthreads();
+      total = s_pref[G];
+      MT = 0;
+    } else {
+      MT = (p.M + BM - 1) / BM;
+      total = MT * NT * (GRP == GRP_K ? p.ngroups : 1);
+    }
+  }
+
+  __device__ TileCtx tile(const GemmParams& p, const int* s_pref, int id) const {
+    TileCtx t;
+    if (GRP == GRP_M) {
+      int lo = 0, hi = p.ngroups;  // s_pref[lo] <= id < s_pref[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= id) lo = mid; else hi = mid;
+      }
+      const int g = lo;
+      const int r0 = p.offsets[g], r1 = p.offsets[g + 1];
+      const int mt_g = (r1 - r0 + BM - 1) / BM;
+      const int local = id - s_pref[g];
+      const int mt = local % mt_g, nt = local / mt_g;
+      t.g = g;
+      t.mtile = mt;
+      t.m0 = (int64_t)r0 + (int64_t)mt * BM;
+      t.mlim = min(BM, r1 - (int)t.m0);
+      t.n0 = nt * BN;
+      t.nlim = min(BN, p.N - t.n0);
+      t.k0 = 0;
+      t.k1 = p.K;
+    } else {
+      const int per = MT * NT;
+      const int g = GRP == GRP_K ? id / per : 0;
+      const int local = id - g * per;
+      const int mt = local % MT, nt = local / MT;
+      t.g = g;
+      t.mtile = mt;
+      t.m0 = (int64_t)mt * BM;
+      t.mlim = min(BM, p.M - (int)t.m0);
+      t.n0 = nt * BN;
+      t.nlim = min(BN, p.N - t.n0);
+      if (GRP == GRP_K) {
+        if (p.offsets) {
+          t.k0 = p.offsets[g];
+          t.k1 = p.offsets[g + 1];
+        } else {
+          t.k0 = (int64_t)g * p.kchunk;
+          t.k1 = min((int64_t)p.K, t.k0 + p.kchunk);
+        }
+      } else {
+        t.k0 = 0;
+        t.k1 = p.K;
+      }
+    }
+    return t;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Epilogue: one output element (and its DUAL partner) of a tile.
+// r, c are tile-local; the caller has checked r < mlim, c < nlim.
+// ---------------------------------------------------------------------------
+template <int GRP, int EPI>
+__device__ __forceinline__ void epi_store(const GemmParams& p, const TileCtx& t, int r, int c,
+                                          float v, float v2) {
+  const int64_t row = t.m0 + r;
+  const int64_t col = (int64_t)t.n0 + c;
+  if (EPI == EPI_STORE) {
+    if (p.bias) v += p.bias[col];
+    int64_t crow = row;
+    void* Cb = p.C;
+    if (p.msplit && row >= p.msplit) {
+      crow = row - p.msplit;
+      Cb = p.C2;
+    }
+    int64_t off = crow * p.ldc + col;
+    if (GRP == GRP_K) off += (int64_t)t.g * p.c_gstride;
+    if (p.c_f32) reinterpret_cast<float*>(Cb)[off] = v;
+    else reinterpret_cast<uint16_t*>(Cb)[off] = f2bf(v);
+  } else if (EPI == EPI_SWIGLU) {
+    // v = gate (G), v2 = up (U); h = silu(G) * U
+    const float h = v / (1.0f + __expf(-v)) * v2;
+    if (p.c_f32) {
+      reinterpret_cast<float*>(p.C)[row * p.ldc + col] = h;
+      if (p.gu_out) {
+        float* gu = reinterpret_cast<float*>(p.gu_out) + row * (2 * (int64_t)p.N);
+        gu[col] = v;
+        gu[p.N + col] = v2;
+      }
+    } else {
+      reinterpret_cast<uint16_t*>(p.C)[row * p.ldc + col] = f2bf(h);
+      if (p.gu_out) {
+        uint16_t* gu = reinterpret_cast<uint16_t*>(p.gu_out) + row * (2 * (int64_t)p.N);
+        gu[col] = f2bf(v);
+        gu[p.N + col] = f2bf(v2);
+      }
+    }
+  } else {  // EPI_SWIGLU_BWD: v = dH; C = dgu [rows][2N]
+    float g, u;
+    const int64_t gi = row * (2 * (int64_t)p.N) + col;
+    if (p.c_f32) {
+      g = reinterpret_cast<const float*>(p.gu_in)[gi];
+      u = reinterpret_cast<const float*>(p.gu_in)[gi + p.N];
+    } else {
+      g = bf2f(reinterpret_cast<const uint16_t*>(p.gu_in)[gi]);
+      u = bf2f(reinterpret_cast<const uint16_t*>(p.gu_in)[gi + p.N]);
+    }
+    const float s = 1.0f / (1.0f + __expf(-g));
+    const float du = v * g * s;
+    const float dg = v * u * s * (1.0f + g * (1.0f - s));
+    if (p.c_f32) {
+      reinterpret_cast<float*>(p.C)[gi] = dg;
+      reinterpret_cast<float*>(p.C)[gi + p.N] = du;
+    } else {
+      reinterpret_cast<uint16_t*>(p.C)[gi] = f2bf(dg);
+      reinterpret_cast<uint16_t*>(p.C)[gi + p.N] = f2bf(du);
+    }
+  }
+}
+
+// Pointer to operand element (mn, k) for the current k-tile, honouring the
+// group offset, the K split and the layout.  Returns the base such that
+// element (mn_local, k_local) of the tile is base[mn_local*smn + k_local*sk].
+template <typename T>
+struct OpView {
+  const T* base;
+  int64_t smn, sk;
+};
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel: 128 x 128 tile, BK = 64, 4 waves in 2 x 2, each wave a
+// 64 x 64 sub-tile of 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.  Operand tiles
+// are staged through LDS (double buffered) as [row][k] bf16 rows padded to 72
+// elements; M/N-contiguous operands are transposed on their way into LDS.
+// DUAL: the 128 B rows are 64 columns of B followed by the same 64 columns
+// of B2, and each wave's two n-blocks are (B, B2) at the same columns.
+// ---------------------------------------------------------------------------
+namespace mf {
+constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8, THREADS = 256;
+}
+
+template <int LAY, typename ST>
+struct MfLoader {
+  u32x4 v[4];
+
+  // Element (mn, k) of the operand for this k-tile lives at
+  //   K-contig: base[mn * ld + k],  MN-contig: base[k * ld + mn].
+  // base2 replaces base for rows mn >= 64 when dual (rows 64.. read base2 at mn - 64).
+  __device__ __forceinline__ void load(const ST* base, const ST* base2, int64_t ld, int mnlim,
+                                       int klim, bool dual) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int mn, k;
+      if (LAY == LAY_K) {
+        mn = tid / 8 + 32 * i;
+        k = (tid % 8) * 8;
+      } else {
+        k = tid / 16 + 16 * i;
+        mn = (tid % 16) * 8;
+      }
+      const ST* b = base;
+      int mn_eff = mn;
+      if (dual && mn >= 64) {
+        b = base2;
+        mn_eff = mn - 64;
+      }
+      const int lim = dual ? min(mnlim, 64) : mnlim;
+      const bool ok = (LAY == LAY_K) ? (mn_eff < lim && k < klim) : (k < klim && mn_eff < lim);
+      if (!ok) {
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+        continue;
+      }
+      const ST* ptr = (LAY == LAY_K) ? b + (int64_t)mn_eff * ld + k : b + (int64_t)k * ld + mn_eff;
+      if constexpr (sizeof(ST) == 2) {
+        v[i] = *reinterpret_cast<const u32x4*>(ptr);
+      } else {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(ptr);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(ptr + 4);
+        v[i] = u32x4{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]),
+                     pack_bf2(hi[2], hi[3])};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* S) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (LAY == LAY_K) {
+        const int mn = tid / 8 + 32 * i;
+        const int k = (tid % 8) * 8;
+        *reinterpret_cast<u32x4*>(S + mn * mf::LDK + k) = v[i];
+      } else {
+        const int k = tid / 16 + 16 * i;
+        const int mn = (tid % 16) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          S[(mn + 2 * e) * mf::LDK + k] = (uint16_t)(v[i][e] & 0xffffu);
+          S[(mn + 2 * e + 1) * mf::LDK + k] = (uint16_t)(v[i][e] >> 16);
+        }
+      }
+    }
+  }
+};
+
+template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
+__global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
+  using namespace mf;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+  __shared__ int s_pref[MAXG + 1];
+  __shared__ int s_scan[256];
+
+  Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
+  sched.init(p, s_pref, s_scan);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const AT* Ag = reinterpret_cast<const AT*>(p.A);
+  const uint16_t* Bg = reinterpret_cast<const uint16_t*>(p.B);
+  const uint16_t* B2g = reinterpret_cast<const uint16_t*>(p.B2);
+
+  for (int id = blockIdx.x; id < sched.total; id += gridDim.x) {
+    const TileCtx t = sched.tile(p, s_pref, id);
+    const int64_t klen = t.k1 - t.k0;
+    const int nk = (int)((klen + BK - 1) / BK);
+
+    // A operand base for this tile (element (m_local, k_local) at k-tile 0).
+    const AT* a_base;
+    if (ALAY == LAY_K) a_base = Ag + t.m0 * p.lda + t.k0;
+    else a_base = Ag + t.k0 * p.lda + t.m0;
+    // B operand bases.
+    const uint16_t* b_grp = Bg;
+    const uint16_t* b2_grp = B2g;
+    if (GRP == GRP_M) {
+      b_grp += (int64_t)t.g * p.b_gstride;
+      if (B2g) b2_grp += (int64_t)t.g * p.b_gstride;
+    }
+
+    MfLoader<ALAY, AT> la;
+    MfLoader<BLAY, uint16_t> lb;
+
+    auto b_ptrs = [&](int kt, const uint16_t*& b1, const uint16_t*& b2) {
+      const int64_t kg = t.k0 + (int64_t)kt * BK;  // global k of the k-tile start
+      if (BLAY == LAY_K) {
+        b1 = b_grp + (int64_t)t.n0 * p.ldb + kg;
+        b2 = DUAL ? b2_grp + (int64_t)t.n0 * p.ldb + kg : nullptr;
+      } else {
+        if (p.ksplit && kg >= p.ksplit) b1 = b2_grp + (kg - p.ksplit) * p.ldb + t.n0;
+        else b1 = b_grp + kg * p.ldb + t.n0;
+        b2 = nullptr;
+      }
+    };
+    auto a_ptr = [&](int kt) -> const AT* {
+      const int64_t ko = (int64_t)kt * BK;
+      return ALAY == LAY_K ? a_base + ko : a_base + ko * p.lda;
+    };
+    auto klim_of = [&](int kt) -> int { return (int)min((int64_t)BK, klen - (int64_t)kt * BK); };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    if (nk > 0) {
+      const uint16_t *b1, *b2;
+      b_ptrs(0, b1, b2);
+      la.load(a_ptr(0), nullptr, p.lda, t.mlim, klim_of(0), false);
+      lb.load(b1, b2, p.ldb, t.nlim, klim_of(0), DUAL);
+      la.store(As[0]);
+      lb.store(Bs[0]);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        const uint16_t *b1, *b2;
+        b_ptrs(kt + 1, b1, b2);
+        la.load(a_ptr(kt + 1), nullptr, p.lda, t.mlim, klim_of(kt + 1), false);
+        lb.load(b1, b2, p.ldb, t.nlim, klim_of(kt + 1), DUAL);
+      }
+      const uint16_t* as = As[cur];
+      const uint16_t* bs = Bs[cur];
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[2], bf[2];
+        const int kof = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          af[mi] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + mi * 32 + (lane & 31)) * LDK + kof);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int brow = DUAL ? (ni * 64 + wn * 32) : (wn * 64 + ni * 32);
+          bf[ni] = *reinterpret_cast<const bf16x8*>(bs + (brow + (lane & 31)) * LDK + kof);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+      }
+      if (more) {
+        la.store(As[cur ^ 1]);
+        lb.store(Bs[cur ^ 1]);
+      }
+      __syncthreads();
+    }
+
+    // Epilogue: acc[mi][ni][r] is C[row][col] with
+    //   row = wm*64 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = lane%32 (+ n-block base).
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row >= t.mlim) continue;
+        if (DUAL) {
+          const int col = wn * 32 + (lane & 31);
+          if (col < t.nlim) epi_store<GRP, EPI>(p, t, row, col, acc[mi][0][r], acc[mi][1][r]);
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) {
+            const int col = wn * 64 + ni * 32 + (lane & 31);
+            if (col < t.nlim) epi_store<GRP, EPI>(p, t, row, col, acc[mi][ni][r], 0.f);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 FMA kernel (the fp32 path): 64 x 64 tile, BK = 16, 256 threads with
+// a 4 x 4 micro-tile each.  LDS holds both operands as [k][mn] rows.
+// DUAL: the tile is 64 rows x 64 columns of B and the same columns of B2.
+// ---------------------------------------------------------------------------
+namespace ff {
+constexpr int BM = 64, BN = 64, BK = 16, LDM = 64 + 4;
+}
+
+template <int LAY>
+__device__ __forceinline__ void ff_load(float* S, const float* base, int64_t ld, int mnlim, int klim) {
+  using namespace ff;
+  const int tid = threadIdx.x;
+  if (LAY == LAY_K) {
+    const int mn = tid / 4, k = (tid % 4) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = mn < mnlim && k + e < klim;
+      S[(k + e) * LDM + mn] = ok ? base[(int64_t)mn * ld + k + e] : 0.f;
+    }
+  } else {
+    const int k = tid / 16, mn = (tid % 16) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = k < klim && mn + e < mnlim;
+      S[k * LDM + mn + e] = ok ? base[(int64_t)k * ld + mn + e] : 0.f;
+    }
+  }
+}
+
+template <int ALAY, int BLAY, int GRP, int EPI, bool DUAL>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmParams p) {
+  using namespace ff;
+  __shared__ float As[BK * LDM];
+  __shared__ float Bs[BK * LDM];
+  __shared__ float B2s[DUAL ? BK * LDM : 1];
+  __shared__ int s_pref[MAXG + 1];
+  __shared__ int s_scan[256];
+
+  Scheduler<GRP, BM, BN> sched;
+  sched.init(p, s_pref, s_scan);
+  const int tid = threadIdx.x;
+  const int ty = tid / 16, tx = tid % 16;
+  const float* Ag = reinterpret_cast<const float*>(p.A);
+  const float* Bg = reinterpret_cast<const float*>(p.B);
+  const float* B2g = reinterpret_cast<const float*>(p.B2);
+
+  for (int id = blockIdx.x; id < sched.total; id += gridDim.x) {
+    const TileCtx t = sched.tile(p, s_pref, id);
+    const int64_t klen = t.k1 - t.k0;
+    float acc[4][4] = {}, acc2[4][4] = {};
+    const float* b_grp = Bg;
+    const float* b2_grp = B2g;
+    if (GRP == GRP_M) {
+      b_grp += (int64_t)t.g * p.b_gstride;
+      if (B2g) b2_grp += (int64_t)t.g * p.b_gstride;
+    }
+    for (int64_t ko = 0; ko < klen; ko += BK) {
+      const int klim = (int)min((int64_t)BK, klen - ko);
+      const int64_t kg = t.k0 + ko;
+      const float* a = ALAY == LAY_K ? Ag + t.m0 * p.lda + kg : Ag + kg * p.lda + t.m0;
+      const float* b;
+      const float* b2 = nullptr;
+      if (BLAY == LAY_K) {
+        b = b_grp + (int64_t)t.n0 * p.ldb + kg;
+        if (DUAL) b2 = b2_grp + (int64_t)t.n0 * p.ldb + kg;
+      } else {
+        if (p.ksplit && kg >= p.ksplit) b = b2_grp + (kg - p.ksplit) * p.ldb + t.n0;
+        else b = b_grp + kg * p.ldb + t.n0;
+      }
+      ff_load<ALAY>(As, a, p.lda, t.mlim, klim);
+      ff_load<BLAY>(Bs, b, p.ldb, t.nlim, klim);
+      if (DUAL) ff_load<BLAY>(B2s, b2, p.ldb, t.nlim, klim);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BK; ++kk) {
+        float a4[4], b4[4], c4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a4[i] = As[kk * LDM + ty * 4 + i];
+          b4[i] = Bs[kk * LDM + tx * 4 + i];
+          if (DUAL) c4[i] = B2s[kk * LDM + tx * 4 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
+            if (DUAL) acc2[i][j] = fmaf(a4[i], c4[j], acc2[i][j]);
+          }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = ty * 4 + i, col = tx * 4 + j;
+        if (row < t.mlim && col < t.nlim) epi_store<GRP, EPI>(p, t, row, col, acc[i][j], acc2[i][j]);
+      }
+  }
+}
+
+}  // namespace moe

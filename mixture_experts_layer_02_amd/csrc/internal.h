@@ -1,0 +1,41 @@
+// Host-side interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+int num_cus();
+
+size_t permute_workspace(const moe_desc& d);
+size_t router_bwd_workspace(const moe_desc& d);
+
+hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
+                                float* logits, hipStream_t s);
+hipError_t launch_route(const moe_desc& d, const float* logits, int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_route_bwd(const moe_desc& d, const float* logits, const int32_t* idx, const float* w,
+                            const float* dw, float* dlogits, hipStream_t s);
+hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm, void* ws,
+                          hipStream_t s);
+hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
+                          void* y, hipStream_t s);
+hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
+                              const void* dy, void* dy_perm, float* dw, hipStream_t s);
+hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
+                                const float* dx_add, void* dx, hipStream_t s);
+hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,
+                          const void* W3, void* gu, void* h, hipStream_t s);
+hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h, const void* W2, void* y_perm,
+                       hipStream_t s);
+hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* W2, const void* gu,
+                         const void* dy_perm, void* dgu, hipStream_t s);
+hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void* W1, const void* W3,
+                          const void* dgu, void* dx_perm, hipStream_t s);
+hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
+                             const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
+                             hipStream_t s);
+hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
+                             float* dx_router, float* dWr, void* ws, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,343 @@
+// Token counting, prefix sums, index generation, gather, weighted combine and
+// their backward (Aurora page, section 3.1, Algorithm 1 stages 2, 3, the
+// stage-4 gather and stage 5).
+//
+// Counting and placement.  The page gives each GPU thread a block of 8 tokens,
+// counts per (local expert, thread) into an expert-major array, prefix-sums it
+// and places every selection at base + per-(expert, thread) counter, which
+// makes every expert's rows ascend in token order.  Here a 256-thread
+// workgroup owns a block of 256 tokens (one per lane): each wave builds, in
+// LDS, a 64-bit mask per expert of the lanes that selected it (ds_or_b64, an
+// order-free operation), the block count of an expert is the popcount of its
+// four wave masks, and a selection's rank inside the block is the popcount of
+// the masks of earlier waves plus the bits of lower lanes in its own wave.
+// The result is the same stable, deterministic placement, without a global
+// sort and without float or order-dependent atomics.
+//
+// Data movement (gather, combine and the backward scatter/sum) is token
+// major: one wavefront per token reads the token's row once and writes or
+// reads its routed rows with 16-byte vector accesses.
+#include "internal.h"
+
+namespace moe {
+
+constexpr int BLK_TOK = 256;
+
+// counts per (expert, token block), expert-major: blk_counts[e * nblk + b].
+__global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                    int32_t* __restrict__ blk_counts, int nblk) {
+  extern __shared__ uint64_t masks[];  // [4][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * E; i += 256) masks[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * BLK_TOK + tid;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicOr((unsigned long long*)&masks[wave * E + e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    const int c = __popcll(masks[e]) + __popcll(masks[E + e]) + __popcll(masks[2 * E + e]) +
+                  __popcll(masks[3 * E + e]);
+    blk_counts[(int64_t)e * nblk + blockIdx.x] = c;
+  }
+}
+
+// One workgroup of 1024 threads: counts[e] for every expert, and the exclusive
+// prefix sum of the local experts' block counts in expert-major order
+// (the page's partial_cum_token_counts); offsets[n] = base of expert n's
+// first block, offsets[NL] = R.
+__global__ void __launch_bounds__(1024) scan_kernel(const int32_t* __restrict__ blk_counts, int E, int nblk,
+                                                    int e0, int NL, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ base) {
+  __shared__ int sh[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = wv; e < E; e += 16) {
+    int s = 0;
+    for (int b = lane; b < nblk; b += 64) s += blk_counts[(int64_t)e * nblk + b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) counts[e] = s;
+  }
+  const int64_t n_loc = (int64_t)NL * nblk;
+  const int32_t* src = blk_counts + (int64_t)e0 * nblk;
+  const int64_t per = (n_loc + 1023) / 1024;
+  const int64_t lo = min(n_loc, (int64_t)tid * per), hi = min(n_loc, lo + per);
+  int s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += src[i];
+  sh[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  int run = sh[tid] - s;
+  for (int64_t i = lo; i < hi; ++i) {
+    base[i] = run;
+    if (i % nblk == 0) offsets[i / nblk] = run;
+    run += src[i];
+  }
+  if (tid == 0) offsets[NL] = sh[1023];
+}
+
+// row_token and slot_row from the block bases (the page's index generation).
+__global__ void __launch_bounds__(256) place_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                    int e0, int NL, const int32_t* __restrict__ base, int nblk,
+                                                    int32_t* __restrict__ row_token,
+                                                    int32_t* __restrict__ slot_row) {
+  extern __shared__ uint64_t masks[];  // [4][NL]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * NL; i += 256) masks[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * BLK_TOK + tid;
+  const bool live = t < T;
+  if (live) {
+    for (int j = 0; j < k; ++j) {
+      const int n = idx[(int64_t)t * k + j] - e0;
+      if ((unsigned)n < (unsigned)NL) atomicOr((unsigned long long*)&masks[wave * NL + n], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int n = idx[(int64_t)t * k + j] - e0;
+    int row = -1;
+    if ((unsigned)n < (unsigned)NL) {
+      int before = __popcll(masks[wave * NL + n] & below);
+      for (int w = 0; w < wave; ++w) before += __popcll(masks[w * NL + n]);
+      row = base[(int64_t)n * nblk + blockIdx.x] + before;
+      row_token[row] = t;
+    }
+    slot_row[(int64_t)t * k + j] = row;
+  }
+}
+
+// x_perm[slot_row[t][j]] = x[t] for every local slot: one wave per token,
+// 16-byte vectors, the token's row read once.
+__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ x,
+                                                     const int32_t* __restrict__ slot_row, int T, int k,
+                                                     int64_t row_bytes, uint8_t* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const uint64_t live = __ballot(r >= 0);
+  if (!live) return;
+  const int64_t nvec = row_bytes / 16;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * row_bytes);
+  constexpr int U = 4;
+  for (int64_t c0 = 0; c0 < nvec; c0 += 64 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * 64 + lane;
+      if (c < nvec) v[u] = src[c];
+    }
+    uint64_t m = live;
+    while (m) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int row = __shfl(r, j, 64);
+      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (int64_t)row * row_bytes);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < nvec) dst[c] = v[u];
+      }
+    }
+  }
+}
+
+// y[t] = sum_j w[t][j] y_perm[slot_row[t][j]] in slot order, float32 sums.
+template <typename T>
+__global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ w, const T* __restrict__ y_perm,
+                                                      int Tn, int k, int d, T* __restrict__ y) {
+  using V = Vec16<T>;
+  constexpr int VN = V::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const float wl = lane < k ? w[(int64_t)t * k + lane] : 0.f;
+  const uint64_t live = __ballot(r >= 0);
+  constexpr int U = 2;
+  for (int c0 = 0; c0 < d; c0 += 64 * VN * U) {
+    float acc[U][VN];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[u][e] = 0.f;
+    uint64_t m = live;
+    while (m) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int row = __shfl(r, j, 64);
+      const float wj = __shfl(wl, j, 64);
+      const T* src = y_perm + (int64_t)row * d;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + (u * 64 + lane) * VN;
+        if (c < d) {
+          float v[VN];
+          V::load(src + c, v);
+#pragma unroll
+          for (int e = 0; e < VN; ++e) acc[u][e] = fmaf(wj, v[e], acc[u][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + (u * 64 + lane) * VN;
+      if (c < d) V::store(y + (int64_t)t * d + c, acc[u]);
+    }
+  }
+}
+
+// dy_perm[row] = w dy[t];  dw[t][j] = <y_perm[row], dy[t]> (0 for non-local slots).
+template <typename T>
+__global__ void __launch_bounds__(256) combine_bwd_kernel(const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ w,
+                                                          const T* __restrict__ y_perm,
+                                                          const T* __restrict__ dy, int Tn, int k, int d,
+                                                          T* __restrict__ dy_perm, float* __restrict__ dw) {
+  using V = Vec16<T>;
+  constexpr int VN = V::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const float wl = lane < k ? w[(int64_t)t * k + lane] : 0.f;
+  const uint64_t live = __ballot(r >= 0);
+  float mydot = 0.f;  // lane j ends with slot j's dot product
+  uint64_t m = live;
+  while (m) {
+    const int j = __ffsll((unsigned long long)m) - 1;
+    m &= m - 1;
+    const int row = __shfl(r, j, 64);
+    const float wj = __shfl(wl, j, 64);
+    const T* yp = y_perm + (int64_t)row * d;
+    const T* g = dy + (int64_t)t * d;
+    T* out = dy_perm + (int64_t)row * d;
+    float part = 0.f;
+    for (int c = lane * VN; c < d; c += 64 * VN) {
+      float gv[VN], yv[VN], ov[VN];
+      V::load(g + c, gv);
+      V::load(yp + c, yv);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        part = fmaf(yv[e], gv[e], part);
+        ov[e] = wj * gv[e];
+      }
+      V::store(out + c, ov);
+    }
+    part = wave_sum(part);
+    if (lane == j) mydot = part;
+  }
+  if (lane < k) dw[(int64_t)t * k + lane] = mydot;
+}
+
+// dx[t] = dx_add[t] + sum_j dx_perm[slot_row[t][j]] (float32 sums).
+template <typename T>
+__global__ void __launch_bounds__(256) unpermute_bwd_kernel(const int32_t* __restrict__ slot_row,
+                                                            const T* __restrict__ dx_perm,
+                                                            const float* __restrict__ dx_add, int Tn, int k,
+                                                            int d, T* __restrict__ dx) {
+  using V = Vec16<T>;
+  constexpr int VN = V::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const uint64_t live = __ballot(r >= 0);
+  for (int c = lane * VN; c < d; c += 64 * VN) {
+    float acc[VN];
+    if (dx_add) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] = dx_add[(int64_t)t * d + c + e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] = 0.f;
+    }
+    uint64_t m = live;
+    while (m) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int row = __shfl(r, j, 64);
+      float v[VN];
+      V::load(dx_perm + (int64_t)row * d + c, v);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] += v[e];
+    }
+    V::store(dx + (int64_t)t * d + c, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+size_t permute_workspace(const moe_desc& d) {
+  const int64_t nblk = (d.T + BLK_TOK - 1) / BLK_TOK;
+  // blk_counts [E][nblk] + base [NL][nblk]
+  return (size_t)((int64_t)d.E * nblk + (int64_t)d.num_local * nblk) * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm, void* ws,
+                          hipStream_t s) {
+  const int nblk = (d.T + BLK_TOK - 1) / BLK_TOK;
+  int32_t* blk_counts = reinterpret_cast<int32_t*>(ws);
+  int32_t* base = blk_counts + (int64_t)d.E * nblk;
+  count_kernel<<<nblk, 256, 4 * d.E * sizeof(uint64_t), s>>>(idx, d.T, d.k, d.E, blk_counts, nblk);
+  scan_kernel<<<1, 1024, 0, s>>>(blk_counts, d.E, nblk, d.expert_begin, d.num_local, counts, offsets, base);
+  place_kernel<<<nblk, 256, 4 * d.num_local * sizeof(uint64_t), s>>>(idx, d.T, d.k, d.E, d.expert_begin,
+                                                                      d.num_local, base, nblk, row_token,
+                                                                      slot_row);
+  if (x) {
+    const int64_t row_bytes = (int64_t)d.d * (d.dtype == MOE_BF16 ? 2 : 4);
+    gather_kernel<<<(d.T + 3) / 4, 256, 0, s>>>(reinterpret_cast<const uint8_t*>(x), slot_row, d.T, d.k,
+                                                row_bytes, reinterpret_cast<uint8_t*>(x_perm));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
+                          void* y, hipStream_t s) {
+  const dim3 grid((d.T + 3) / 4), block(256);
+  if (d.dtype == MOE_BF16)
+    combine_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm, d.T, d.k, d.d,
+                                                    (uint16_t*)y);
+  else
+    combine_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, d.T, d.k, d.d, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
+                              const void* dy, void* dy_perm, float* dw, hipStream_t s) {
+  const dim3 grid((d.T + 3) / 4), block(256);
+  if (d.dtype == MOE_BF16)
+    combine_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm,
+                                                        (const uint16_t*)dy, d.T, d.k, d.d,
+                                                        (uint16_t*)dy_perm, dw);
+  else
+    combine_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, (const float*)dy, d.T,
+                                                     d.k, d.d, (float*)dy_perm, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
+                                const float* dx_add, void* dx, hipStream_t s) {
+  const dim3 grid((d.T + 3) / 4), block(256);
+  if (d.dtype == MOE_BF16)
+    unpermute_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, (const uint16_t*)dx_perm, dx_add, d.T,
+                                                          d.k, d.d, (uint16_t*)dx);
+  else
+    unpermute_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, dx_add, d.T, d.k, d.d,
+                                                       (float*)dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

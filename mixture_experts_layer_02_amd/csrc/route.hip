@@ -1,0 +1,170 @@
+// Softmax + top-k routing and its backward (Aurora page, section 3.1,
+// Algorithm 1 stage 1: probs = Softmax(logits); weights, indices = TopK(probs),
+// with the top-k probabilities renormalised over the selection by default).
+//
+// One wavefront owns one token: lane l holds logits l, l+64, l+128, ... of the
+// token's row (coalesced 256-byte loads), and each of the k rounds is a
+// lane-local arg-max followed by a 6-step butterfly over the wave.  The order
+// is (logit descending, expert index ascending), so equal logits - including
+// +0.0 against -0.0 - go to the lower expert.  The whole pass reads T*E*4
+// bytes and writes T*k*8; it is bound by HBM.
+#include "internal.h"
+
+namespace moe {
+
+template <int MAXV>
+__global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict__ logits, int T, int E,
+                                                         int k, int renorm, int32_t* __restrict__ idx_out,
+                                                         float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  float v[MAXV];
+  uint32_t taken = 0;  // bit i: element i is selected already or absent
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = i * 64 + lane;
+    if (e < E) v[i] = row[e];
+    else {
+      v[i] = 0.f;
+      taken |= 1u << i;
+    }
+  }
+  float my_v = 0.f, v0 = 0.f;
+  int my_i = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      if (!((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
+        bv = v[i];
+        bi = i * 64 + lane;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      const bool better = (oi != 0x7fffffff) && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+      if (better) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) {
+      my_v = bv;
+      my_i = bi;
+    }
+    if (j == 0) v0 = bv;
+  }
+  float w;
+  if (renorm) {
+    const float ex = lane < k ? expf(my_v - v0) : 0.f;
+    w = ex / wave_sum(ex);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i * 64 + lane < E) s += expf(v[i] - v0);
+    s = wave_sum(s);
+    w = expf(my_v - v0) / s;
+  }
+  if (lane < k) {
+    idx_out[(int64_t)t * k + lane] = my_i;
+    w_out[(int64_t)t * k + lane] = w;
+  }
+}
+
+// dlogits for one token per wave.  renorm: dL_m = w_m (dw_m - <w, dw>) on the
+// selected experts (local or not), 0 elsewhere.  raw softmax: dL_e = p_e (g_e -
+// <w, dw>) with g_e = dw_j at e = idx_j.
+template <int MAXV>
+__global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict__ logits,
+                                                        const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ dw, int T, int E, int k,
+                                                        int renorm, float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int my_i = -1;
+  float my_w = 0.f, my_dw = 0.f;
+  if (lane < k) {
+    my_i = idx[(int64_t)t * k + lane];
+    my_w = w[(int64_t)t * k + lane];
+    my_dw = dw[(int64_t)t * k + lane];
+  }
+  const float s = wave_sum(my_w * my_dw);
+  float* out = dlogits + (int64_t)t * E;
+  if (renorm) {
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      float g = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int ij = __shfl(my_i, j, 64);
+        const float wj = __shfl(my_w, j, 64);
+        const float dwj = __shfl(my_dw, j, 64);
+        if (ij == e) g = wj * (dwj - s);
+      }
+      if (e < E) out[e] = g;
+    }
+  } else {
+    const float* row = logits + (int64_t)t * E;
+    float v[MAXV];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      v[i] = e < E ? row[e] : -INFINITY;
+      mx = fmaxf(mx, v[i]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i * 64 + lane < E) z += expf(v[i] - mx);
+    z = wave_sum(z);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      float g = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int ij = __shfl(my_i, j, 64);
+        const float dwj = __shfl(my_dw, j, 64);
+        if (ij == e) g = dwj;
+      }
+      if (e < E) out[e] = expf(v[i] - mx) / z * (g - s);
+    }
+  }
+}
+
+hipError_t launch_route(const moe_desc& d, const float* logits, int32_t* idx, float* w,
+                        hipStream_t s) {
+  const dim3 grid((d.T + 3) / 4), block(256);
+  const int nv = (d.E + 63) / 64;
+  if (nv <= 1) topk_route_kernel<1><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
+  else if (nv <= 2) topk_route_kernel<2><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
+  else if (nv <= 4) topk_route_kernel<4><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
+  else if (nv <= 8) topk_route_kernel<8><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
+  else topk_route_kernel<16><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const moe_desc& d, const float* logits, const int32_t* idx, const float* w,
+                            const float* dw, float* dlogits, hipStream_t s) {
+  const dim3 grid((d.T + 3) / 4), block(256);
+  const int nv = (d.E + 63) / 64;
+  if (nv <= 1) route_bwd_kernel<1><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
+  else if (nv <= 2) route_bwd_kernel<2><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
+  else if (nv <= 4) route_bwd_kernel<4><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
+  else if (nv <= 8) route_bwd_kernel<8><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
+  else route_bwd_kernel<16><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
+  return hipGetLastError();
+}
+
+}  // namespace moe
