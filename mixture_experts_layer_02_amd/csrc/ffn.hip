@@ -31,11 +31,15 @@ GemmParams blank() {
   return p;
 }
 
+// Tile edge of the bf16 kernels: 256 x 256 (one workgroup per CU).
+constexpr int MT = 256;
+
 template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
 hipError_t run_mfma(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
-  const int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus() * 2);
+  int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus());
+  if (grid >= 8) grid -= grid % 8;  // whole XCD groups for the tile remap
   if (grid <= 0) return hipSuccess;
-  gemm_mfma_kernel<ALAY, BLAY, AT, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
+  gemm_mfma_kernel<MT, MT, ALAY, BLAY, AT, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -59,7 +63,7 @@ int64_t mtiles_ub(const moe_desc& d, int bm) { return cdiv(r_cap(d), bm) + d.num
 // depends on the shape only, so the summation order (and the result) is the
 // same on every device and the workspace query needs no device.
 int router_splits(const moe_desc& d) {
-  const int64_t tiles = cdiv(d.E, 128) * cdiv(d.d, 128);
+  const int64_t tiles = cdiv(d.E, MT) * cdiv(d.d, MT);
   int64_t s = cdiv((int64_t)256 * 2, tiles);
   s = std::min<int64_t>(s, cdiv(d.T, 256));
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
@@ -95,7 +99,7 @@ hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr
   p.bias = bias;
   p.c_f32 = 1;
   if (d.dtype == MOE_BF16)
-    return run_mfma<LAY_K, LAY_K, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 128) * cdiv(d.E, 128), s);
+    return run_mfma<LAY_K, LAY_K, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.E, MT), s);
   return run_f32<LAY_K, LAY_K, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.E, 64), s);
 }
 
@@ -117,7 +121,7 @@ hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void*
   p.N = d.f;
   p.K = d.d;
   p.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 128) * cdiv(d.f, 64), s);
+  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
   return run_f32<LAY_K, LAY_K, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
 }
 
@@ -137,7 +141,7 @@ hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h,
   q.N = d.d;
   q.K = d.f;
   q.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 128) * cdiv(d.d, 128), s);
+  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
   return run_f32<LAY_K, LAY_K, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
 }
 
@@ -159,7 +163,7 @@ hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* 
   p.N = d.f;
   p.K = d.d;
   p.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, 128) * cdiv(d.f, 128), s);
+  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
 }
 
@@ -182,7 +186,7 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
   q.N = d.d;
   q.K = 2 * d.f;
   q.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 128) * cdiv(d.d, 128), s);
+  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
 }
 
@@ -207,7 +211,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   p.N = d.d;
   p.c_f32 = 1;
   hipError_t e;
-  if (bf) e = run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 128) * cdiv(d.d, 128), s);
+  if (bf) e = run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
   else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
   if (e != hipSuccess) return e;
   // dW2 [d][f] = dy_perm^T h
@@ -224,7 +228,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   q.M = d.d;
   q.N = d.f;
   q.c_f32 = 1;
-  if (bf) return run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 128) * cdiv(d.f, 128), s);
+  if (bf) return run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 64) * cdiv(d.f, 64), s);
 }
 
@@ -245,7 +249,7 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
     p.N = d.d;
     p.K = d.E;
     p.c_f32 = 1;
-    if (bf) e = run_mfma<LAY_K, LAY_MN, float, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 128) * cdiv(d.d, 128), s);
+    if (bf) e = run_mfma<LAY_K, LAY_MN, float, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.d, MT), s);
     else e = run_f32<LAY_K, LAY_MN, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.d, 64), s);
     if (e != hipSuccess) return e;
   }
@@ -268,7 +272,7 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
     q.N = d.d;
     q.K = d.T;
     q.c_f32 = 1;
-    if (bf) e = run_mfma<LAY_MN, LAY_MN, float, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, 128) * cdiv(d.d, 128), s);
+    if (bf) e = run_mfma<LAY_MN, LAY_MN, float, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, MT) * cdiv(d.d, MT), s);
     else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, 64) * cdiv(d.d, 64), s);
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)d.E * d.d;

@@ -225,6 +225,65 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, const TileCtx& t,
   }
 }
 
+// Epilogue for 8 consecutive columns c .. c+7 of tile-local row r (the caller
+// has checked r < mlim and c < nlim; N is a multiple of 8, so the whole
+// vector is in range).  v / v2 hold the accumulators (v2: the DUAL partner).
+template <int GRP, int EPI>
+__device__ __forceinline__ void epi_store8(const GemmParams& p, const TileCtx& t, int r, int c,
+                                           const float (&v)[8], const float (&v2)[8]) {
+  const int64_t row = t.m0 + r;
+  const int64_t col = (int64_t)t.n0 + c;
+  if (EPI == EPI_STORE) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = v[e];
+    if (p.bias) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += p.bias[col + e];
+    }
+    int64_t crow = row;
+    void* Cb = p.C;
+    if (p.msplit && row >= p.msplit) {
+      crow = row - p.msplit;
+      Cb = p.C2;
+    }
+    int64_t off = crow * p.ldc + col;
+    if (GRP == GRP_K) off += (int64_t)t.g * p.c_gstride;
+    if (p.c_f32) {
+      float* d = reinterpret_cast<float*>(Cb) + off;
+      *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    } else {
+      Vec16<uint16_t>::store(reinterpret_cast<uint16_t*>(Cb) + off, o);
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    float h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = v[e] / (1.0f + __expf(-v[e])) * v2[e];
+    Vec16<uint16_t>::store(reinterpret_cast<uint16_t*>(p.C) + row * p.ldc + col, h);
+    if (p.gu_out) {
+      uint16_t* gu = reinterpret_cast<uint16_t*>(p.gu_out) + row * (2 * (int64_t)p.N);
+      Vec16<uint16_t>::store(gu + col, v);
+      Vec16<uint16_t>::store(gu + p.N + col, v2);
+    }
+  } else {  // EPI_SWIGLU_BWD
+    const int64_t gi = row * (2 * (int64_t)p.N) + col;
+    const uint16_t* gu = reinterpret_cast<const uint16_t*>(p.gu_in);
+    float g[8], u[8], dg[8], du[8];
+    Vec16<uint16_t>::load(gu + gi, g);
+    Vec16<uint16_t>::load(gu + gi + p.N, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = 1.0f / (1.0f + __expf(-g[e]));
+      du[e] = v[e] * g[e] * s;
+      dg[e] = v[e] * u[e] * s * (1.0f + g[e] * (1.0f - s));
+    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.C);
+    Vec16<uint16_t>::store(out + gi, dg);
+    Vec16<uint16_t>::store(out + gi + p.N, du);
+  }
+}
+
 // Pointer to operand element (mn, k) for the current k-tile, honouring the
 // group offset, the K split and the layout.  Returns the base such that
 // element (mn_local, k_local) of the tile is base[mn_local*smn + k_local*sk].
@@ -235,46 +294,71 @@ struct OpView {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel: 128 x 128 tile, BK = 64, 4 waves in 2 x 2, each wave a
-// 64 x 64 sub-tile of 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.  Operand tiles
-// are staged through LDS (double buffered) as [row][k] bf16 rows padded to 72
-// elements; M/N-contiguous operands are transposed on their way into LDS.
-// DUAL: the 128 B rows are 64 columns of B followed by the same 64 columns
-// of B2, and each wave's two n-blocks are (B, B2) at the same columns.
+// bf16 MFMA kernel.  Block tile BM x BN (256 x 256 or 128 x 128), BK = 64,
+// 4 waves in 2 x 2, each wave a (BM/2) x (BN/2) sub-tile of
+// v_mfma_f32_32x32x16_bf16 blocks (4 x 4 of them at 256 x 256, with the 256
+// float accumulators held in AccVGPRs).  Operand tiles are double buffered in
+// LDS in the layout they have in HBM, so every global load and LDS store is a
+// 16-byte vector:
+//   K-contiguous operand   -> LDS [mn][k], row pitch BK + 8; a fragment is one
+//                              ds_read_b128 (8 consecutive k of one row);
+//   M/N-contiguous operand -> LDS [k][mn], row pitch MN + 32; a fragment is two
+//                              ds_read_b64_tr_b16, the gfx950 transposing LDS
+//                              read: within each 16-lane group, lane i receives
+//                              element i%4 of the 8-byte chunk addressed by lane
+//                              i/4 + 4j (j = 0..3), so 16 lanes pointing at a
+//                              4 x 16 block of [k][mn] get one mn column each,
+//                              four consecutive k deep.
+// Both pitches keep the fragment reads free of bank conflicts.
+// DUAL: the B tile's first BN/2 rows are columns n0.. of B and the last BN/2
+// the same columns of B2; n-block ni of a wave pairs with ni + NI/2.
 // ---------------------------------------------------------------------------
 namespace mf {
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8, THREADS = 256;
-}
+constexpr int BK = 64, THREADS = 256;
+template <int ROWS> struct Lds {
+  static constexpr int KPITCH = BK + 8;        // K-contiguous: [ROWS][KPITCH]
+  static constexpr int MNPITCH = ROWS + 32;    // MN-contiguous: [BK][MNPITCH]
+  static constexpr int ELEMS = (ROWS * KPITCH > BK * MNPITCH) ? ROWS * KPITCH : BK * MNPITCH;
+};
+}  // namespace mf
 
-template <int LAY, typename ST>
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int LAY, typename ST, int ROWS>
 struct MfLoader {
-  u32x4 v[4];
+  static constexpr int NV = ROWS * mf::BK / 8 / mf::THREADS;  // 16-byte vectors per thread
+  u32x4 v[NV];
 
-  // Element (mn, k) of the operand for this k-tile lives at
-  //   K-contig: base[mn * ld + k],  MN-contig: base[k * ld + mn].
-  // base2 replaces base for rows mn >= 64 when dual (rows 64.. read base2 at mn - 64).
-  __device__ __forceinline__ void load(const ST* base, const ST* base2, int64_t ld, int mnlim,
-                                       int klim, bool dual) {
+  // Vector i of this thread: K-contig (mn, k) = (tid/8 + 32 i, (tid%8)*8);
+  // MN-contig (k, mn) = (tid/(ROWS/8) + (THREADS/(ROWS/8)) i, (tid%(ROWS/8))*8).
+  __device__ __forceinline__ void coords(int i, int& mn, int& k) const {
     const int tid = threadIdx.x;
+    if (LAY == LAY_K) {
+      mn = tid / 8 + 32 * i;
+      k = (tid % 8) * 8;
+    } else {
+      constexpr int VPR = ROWS / 8;  // vectors per k row
+      k = tid / VPR + (mf::THREADS / VPR) * i;
+      mn = (tid % VPR) * 8;
+    }
+  }
+
+  // Element (mn, k) of the tile lives at K-contig base[mn*ld + k], MN-contig
+  // base[k*ld + mn]; with dual, rows mn >= ROWS/2 come from base2 at mn - ROWS/2.
+  __device__ __forceinline__ void load(const ST* base, const ST* base2, int64_t ld, int mnlim, int klim,
+                                       bool dual) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NV; ++i) {
       int mn, k;
-      if (LAY == LAY_K) {
-        mn = tid / 8 + 32 * i;
-        k = (tid % 8) * 8;
-      } else {
-        k = tid / 16 + 16 * i;
-        mn = (tid % 16) * 8;
-      }
+      coords(i, mn, k);
       const ST* b = base;
       int mn_eff = mn;
-      if (dual && mn >= 64) {
+      if (dual && mn >= ROWS / 2) {
         b = base2;
-        mn_eff = mn - 64;
+        mn_eff = mn - ROWS / 2;
       }
-      const int lim = dual ? min(mnlim, 64) : mnlim;
-      const bool ok = (LAY == LAY_K) ? (mn_eff < lim && k < klim) : (k < klim && mn_eff < lim);
-      if (!ok) {
+      const int lim = dual ? min(mnlim, ROWS / 2) : mnlim;
+      if (!(mn_eff < lim && k < klim)) {
         v[i] = u32x4{0u, 0u, 0u, 0u};
         continue;
       }
@@ -291,31 +375,53 @@ struct MfLoader {
   }
 
   __device__ __forceinline__ void store(uint16_t* S) const {
-    const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (LAY == LAY_K) {
-        const int mn = tid / 8 + 32 * i;
-        const int k = (tid % 8) * 8;
-        *reinterpret_cast<u32x4*>(S + mn * mf::LDK + k) = v[i];
-      } else {
-        const int k = tid / 16 + 16 * i;
-        const int mn = (tid % 16) * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          S[(mn + 2 * e) * mf::LDK + k] = (uint16_t)(v[i][e] & 0xffffu);
-          S[(mn + 2 * e + 1) * mf::LDK + k] = (uint16_t)(v[i][e] >> 16);
-        }
-      }
+    for (int i = 0; i < NV; ++i) {
+      int mn, k;
+      coords(i, mn, k);
+      if (LAY == LAY_K) *reinterpret_cast<u32x4*>(S + mn * mf::Lds<ROWS>::KPITCH + k) = v[i];
+      else *reinterpret_cast<u32x4*>(S + k * mf::Lds<ROWS>::MNPITCH + mn) = v[i];
     }
   }
 };
 
-template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
-__global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
+// MFMA fragment: 8 consecutive k (kk*16 + (lane/32)*8 ..) of row/column
+// `row0 + lane%32` of an operand tile in LDS.
+template <int LAY, int ROWS>
+__device__ __forceinline__ bf16x8 mf_frag(const uint16_t* S, int row0, int kk, int lane) {
+  if (LAY == LAY_K) {
+    return *reinterpret_cast<const bf16x8*>(S + (row0 + (lane & 31)) * mf::Lds<ROWS>::KPITCH + kk * 16 +
+                                            (lane >> 5) * 8);
+  } else {
+    constexpr int P = mf::Lds<ROWS>::MNPITCH;
+    const int krow = kk * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+    const int col = row0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(S + krow * P + col));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(S + (krow + 4) * P + col));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// Persistent tile ids are remapped so that the workgroups of one XCD (blocks
+// b with the same b % 8 are dispatched to the same XCD) take a contiguous run
+// of logical tiles: neighbouring tiles share operand tiles in that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int it, int grid) {
+  const int b = blockIdx.x;
+  if (grid % 8) return it * grid + b;
+  return it * grid + (b % 8) * (grid / 8) + b / 8;
+}
+
+template <int BM, int BN, int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
+__global__ void __launch_bounds__(256, (BM * BN > 128 * 128) ? 1 : 2) gemm_mfma_kernel(GemmParams p) {
   using namespace mf;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+  static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
+  constexpr int MI = BM / 64, NI = BN / 64;   // 32 x 32 blocks per wave
+  constexpr int AE = Lds<BM>::ELEMS, BE = Lds<BN>::ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][AE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BE];
   __shared__ int s_pref[MAXG + 1];
   __shared__ int s_scan[256];
 
@@ -330,16 +436,15 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
   const uint16_t* Bg = reinterpret_cast<const uint16_t*>(p.B);
   const uint16_t* B2g = reinterpret_cast<const uint16_t*>(p.B2);
 
-  for (int id = blockIdx.x; id < sched.total; id += gridDim.x) {
+  for (int it = 0;; ++it) {
+    const int id = xcd_tile(it, gridDim.x);
+    if (it * (int)gridDim.x >= sched.total) break;
+    if (id >= sched.total) continue;
     const TileCtx t = sched.tile(p, s_pref, id);
     const int64_t klen = t.k1 - t.k0;
     const int nk = (int)((klen + BK - 1) / BK);
 
-    // A operand base for this tile (element (m_local, k_local) at k-tile 0).
-    const AT* a_base;
-    if (ALAY == LAY_K) a_base = Ag + t.m0 * p.lda + t.k0;
-    else a_base = Ag + t.k0 * p.lda + t.m0;
-    // B operand bases.
+    const AT* a_base = (ALAY == LAY_K) ? Ag + t.m0 * p.lda + t.k0 : Ag + t.k0 * p.lda + t.m0;
     const uint16_t* b_grp = Bg;
     const uint16_t* b2_grp = B2g;
     if (GRP == GRP_M) {
@@ -347,11 +452,11 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
       if (B2g) b2_grp += (int64_t)t.g * p.b_gstride;
     }
 
-    MfLoader<ALAY, AT> la;
-    MfLoader<BLAY, uint16_t> lb;
+    MfLoader<ALAY, AT, BM> la;
+    MfLoader<BLAY, uint16_t, BN> lb;
 
     auto b_ptrs = [&](int kt, const uint16_t*& b1, const uint16_t*& b2) {
-      const int64_t kg = t.k0 + (int64_t)kt * BK;  // global k of the k-tile start
+      const int64_t kg = t.k0 + (int64_t)kt * BK;
       if (BLAY == LAY_K) {
         b1 = b_grp + (int64_t)t.n0 * p.ldb + kg;
         b2 = DUAL ? b2_grp + (int64_t)t.n0 * p.ldb + kg : nullptr;
@@ -367,11 +472,11 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
     };
     auto klim_of = [&](int kt) -> int { return (int)min((int64_t)BK, klen - (int64_t)kt * BK); };
 
-    f32x16 acc[2][2];
+    f32x16 acc[MI][NI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -397,21 +502,20 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
       const uint16_t* bs = Bs[cur];
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[2], bf[2];
-        const int kof = kk * 16 + (lane >> 5) * 8;
+        bf16x8 af[MI], bfr[NI];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          af[mi] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + mi * 32 + (lane & 31)) * LDK + kof);
+        for (int mi = 0; mi < MI; ++mi) af[mi] = mf_frag<ALAY, BM>(as, wm * (BM / 2) + mi * 32, kk, lane);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int brow = DUAL ? (ni * 64 + wn * 32) : (wn * 64 + ni * 32);
-          bf[ni] = *reinterpret_cast<const bf16x8*>(bs + (brow + (lane & 31)) * LDK + kof);
+        for (int ni = 0; ni < NI; ++ni) {
+          const int brow = DUAL ? (ni / (NI / 2)) * (BN / 2) + wn * (BN / 4) + (ni % (NI / 2)) * 32
+                                : wn * (BN / 2) + ni * 32;
+          bfr[ni] = mf_frag<BLAY, BN>(bs, brow, kk, lane);
         }
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
       }
       if (more) {
         la.store(As[cur ^ 1]);
@@ -420,24 +524,42 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmParams p) {
       __syncthreads();
     }
 
-    // Epilogue: acc[mi][ni][r] is C[row][col] with
-    //   row = wm*64 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = lane%32 (+ n-block base).
+    // Epilogue, staged through LDS (free after the last barrier of the k loop)
+    // one 32-row block at a time: acc[mi][ni][r] is C[row][col] with
+    //   row = wm*BM/2 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4,
+    //   col = n-block base + lane%32,
+    // written to the wave's [32][WC] float staging area, then read back as
+    // 8-column vectors for the vectorized epilogue.
+    {
+      constexpr int WC = NI * 32;        // staged columns per wave
+      constexpr int SP = WC + 4;         // staging pitch (floats)
+      float* stage = reinterpret_cast<float*>(&As[0][0]) + wave * 32 * SP;
+      static_assert(4 * 32 * SP * 4 <= (int)sizeof(As), "staging fits in the A buffers");
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+      for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row >= t.mlim) continue;
-        if (DUAL) {
-          const int col = wn * 32 + (lane & 31);
-          if (col < t.nlim) epi_store<GRP, EPI>(p, t, row, col, acc[mi][0][r], acc[mi][1][r]);
-        } else {
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            const int col = wn * 64 + ni * 32 + (lane & 31);
-            if (col < t.nlim) epi_store<GRP, EPI>(p, t, row, col, acc[mi][ni][r], 0.f);
+          for (int r = 0; r < 16; ++r)
+            stage[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SP + ni * 32 + (lane & 31)] = acc[mi][ni][r];
+        __syncthreads();
+        constexpr int OC = DUAL ? WC / 2 : WC;   // output columns per wave
+        constexpr int CPR = OC / 8;              // 8-column vectors per row
+        for (int e = lane; e < 32 * CPR; e += 64) {
+          const int rl = e / CPR, cv = (e % CPR) * 8;
+          const int row = wm * (BM / 2) + mi * 32 + rl;
+          const int col = (DUAL ? wn * (BN / 4) : wn * (BN / 2)) + cv;
+          if (row < t.mlim && col < t.nlim) {
+            float v[8], v2[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              v[q] = stage[rl * SP + cv + q];
+              v2[q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+            }
+            epi_store8<GRP, EPI>(p, t, row, col, v, v2);
           }
         }
+        __syncthreads();
       }
     }
   }
