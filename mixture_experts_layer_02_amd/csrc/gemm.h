@@ -343,26 +343,29 @@ struct MfLoader {
     }
   }
 
+  int klim_;
+
   // Element (mn, k) of the tile lives at K-contig base[mn*ld + k], MN-contig
   // base[k*ld + mn]; with dual, rows mn >= ROWS/2 come from base2 at mn - ROWS/2.
+  // Vectors outside the tile's M/N range read a clamped in-range address: they
+  // only feed output rows/columns that the epilogue never stores.  Vectors past
+  // the tile's K extent are zeroed by store(), so the loads are branch-free and
+  // nothing waits on them before the LDS store.
   __device__ __forceinline__ void load(const ST* base, const ST* base2, int64_t ld, int mnlim, int klim,
                                        bool dual) {
+    klim_ = klim;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int mn, k;
       coords(i, mn, k);
-      const ST* b = base;
-      int mn_eff = mn;
-      if (dual && mn >= ROWS / 2) {
-        b = base2;
-        mn_eff = mn - ROWS / 2;
-      }
+      // K-contig rows of vector i are tid/8 + 32 i < 32 (i + 1): the DUAL half
+      // is known at compile time from i.
+      const bool second = (LAY == LAY_K) && dual && (32 * i >= ROWS / 2);
+      const ST* b = second ? base2 : base;
+      const int mn_eff = second ? mn - ROWS / 2 : mn;
       const int lim = dual ? min(mnlim, ROWS / 2) : mnlim;
-      if (!(mn_eff < lim && k < klim)) {
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-        continue;
-      }
-      const ST* ptr = (LAY == LAY_K) ? b + (int64_t)mn_eff * ld + k : b + (int64_t)k * ld + mn_eff;
+      const int mc = mn_eff < lim ? mn_eff : 0, kc = k < klim ? k : 0;
+      const ST* ptr = (LAY == LAY_K) ? b + (int64_t)mc * ld + kc : b + (int64_t)kc * ld + mc;
       if constexpr (sizeof(ST) == 2) {
         v[i] = *reinterpret_cast<const u32x4*>(ptr);
       } else {
@@ -374,7 +377,18 @@ struct MfLoader {
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* S) const {
+  // Zero the vectors past the K extent (only a partial k-tile has any).
+  __device__ __forceinline__ void zero_k_tail() {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int mn, k;
+      coords(i, mn, k);
+      if (k >= klim_) v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* S) {
+    if (__builtin_expect(klim_ < mf::BK, 0)) zero_k_tail();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int mn, k;
@@ -489,6 +503,20 @@ __global__ void __launch_bounds__(256, (BM * BN > 128 * 128) ? 1 : 2) gemm_mfma_
       lb.store(Bs[0]);
       __syncthreads();
     }
+    // Main loop.  Global loads of k-tile kt+1 are issued first; the MFMA
+    // fragments of k-step kk+1 are read from LDS while the 16 MFMAs of step kk
+    // run; the staged k-tile kt+1 is written to the other LDS buffer inside
+    // the last k-step, as late as possible after its loads were issued.
+    auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int kk, bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[mi] = mf_frag<ALAY, BM>(as, wm * (BM / 2) + mi * 32, kk, lane);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int brow = DUAL ? (ni / (NI / 2)) * (BN / 2) + wn * (BN / 4) + (ni % (NI / 2)) * 32
+                              : wn * (BN / 2) + ni * 32;
+        bfr[ni] = mf_frag<BLAY, BN>(bs, brow, kk, lane);
+      }
+    };
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       const bool more = kt + 1 < nk;
@@ -500,26 +528,21 @@ __global__ void __launch_bounds__(256, (BM * BN > 128 * 128) ? 1 : 2) gemm_mfma_
       }
       const uint16_t* as = As[cur];
       const uint16_t* bs = Bs[cur];
+      bf16x8 af[2][MI], bfr[2][NI];
+      read_frags(as, bs, 0, af[0], bfr[0]);
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[MI], bfr[NI];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) af[mi] = mf_frag<ALAY, BM>(as, wm * (BM / 2) + mi * 32, kk, lane);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int brow = DUAL ? (ni / (NI / 2)) * (BN / 2) + wn * (BN / 4) + (ni % (NI / 2)) * 32
-                                : wn * (BN / 2) + ni * 32;
-          bfr[ni] = mf_frag<BLAY, BN>(bs, brow, kk, lane);
+        if (kk + 1 < BK / 16) read_frags(as, bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+        if (kk == BK / 16 - 1 && more) {
+          la.store(As[cur ^ 1]);
+          lb.store(Bs[cur ^ 1]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead above this step's MFMAs
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-      }
-      if (more) {
-        la.store(As[cur ^ 1]);
-        lb.store(Bs[cur ^ 1]);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][mi], bfr[kk & 1][ni], acc[mi][ni], 0, 0, 0);
       }
       __syncthreads();
     }
