@@ -6,8 +6,10 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "gemm.h"
+#include "gemm_dma.h"
 #include "internal.h"
 
 namespace moe {
@@ -40,6 +42,20 @@ hipError_t run_mfma(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;  // whole XCD groups for the tile remap
   if (grid <= 0) return hipSuccess;
   gemm_mfma_kernel<MT, MT, ALAY, BLAY, AT, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// bf16 products: the LDS-DMA kernel when every K-contiguous operand has K a
+// multiple of its 32-wide k-tile, else the register-staged kernel.
+template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
+hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
+  const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) || (GRP != GRP_K && p.K % dma::BK == 0);
+  if (!std::is_same<AT, uint16_t>::value || !k_ok) return run_mfma<ALAY, BLAY, AT, GRP, EPI, DUAL>(p, ub_tiles, s);
+  int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus());
+  if (grid >= 8) grid -= grid % 8;
+  if (grid <= 0) return hipSuccess;
+  if constexpr (std::is_same<AT, uint16_t>::value)
+    gemm_dma_kernel<ALAY, BLAY, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -99,7 +115,7 @@ hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr
   p.bias = bias;
   p.c_f32 = 1;
   if (d.dtype == MOE_BF16)
-    return run_mfma<LAY_K, LAY_K, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.E, MT), s);
+    return run_bf16<LAY_K, LAY_K, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.E, MT), s);
   return run_f32<LAY_K, LAY_K, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.E, 64), s);
 }
 
@@ -121,7 +137,7 @@ hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void*
   p.N = d.f;
   p.K = d.d;
   p.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
+  if (bf) return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
   return run_f32<LAY_K, LAY_K, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
 }
 
@@ -141,7 +157,7 @@ hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h,
   q.N = d.d;
   q.K = d.f;
   q.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
+  if (bf) return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
   return run_f32<LAY_K, LAY_K, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
 }
 
@@ -163,7 +179,7 @@ hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* 
   p.N = d.f;
   p.K = d.d;
   p.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, MT) * cdiv(d.f, MT), s);
+  if (bf) return run_bf16<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
 }
 
@@ -186,7 +202,7 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
   q.N = d.d;
   q.K = 2 * d.f;
   q.c_f32 = bf ? 0 : 1;
-  if (bf) return run_mfma<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
+  if (bf) return run_bf16<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
 }
 
@@ -211,7 +227,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   p.N = d.d;
   p.c_f32 = 1;
   hipError_t e;
-  if (bf) e = run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
+  if (bf) e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
   else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
   if (e != hipSuccess) return e;
   // dW2 [d][f] = dy_perm^T h
@@ -228,7 +244,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   q.M = d.d;
   q.N = d.f;
   q.c_f32 = 1;
-  if (bf) return run_mfma<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
+  if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 64) * cdiv(d.f, 64), s);
 }
 

@@ -1,0 +1,335 @@
+// Grouped GEMM with direct global->LDS loads (gfx950 global_load_lds_dwordx4).
+//
+// Same products, grouping modes, tile order and epilogues as gemm_mfma_kernel
+// (gemm.h), but the operand tiles reach LDS through the gfx950 LDS DMA path:
+// each wave instruction moves 64 x 16 bytes from HBM/L2 straight into 1 KB of
+// contiguous LDS, without passing through VGPRs.  That frees the staging
+// registers and lets a 4-stage ring of BK = 32 k-slices keep three k-tiles in
+// flight, enough to cover L2 misses that go to MALL or HBM.
+//
+// LDS layouts (no padding: a DMA instruction writes 1 KB contiguously, so bank
+// conflicts are avoided by XOR-swizzling 16-byte chunks instead):
+//   K-contiguous tile  [256 rows][32 k]: a row is 4 chunks; chunk c of row r
+//     sits at position c ^ swz_k(r).  A fragment (8 k of one row) is one
+//     ds_read_b128.
+//   MN-contiguous tile [32 k][256 mn]: a k-row is 32 chunks; chunk c of k-row
+//     r sits at position c ^ swz_mn(r).  A fragment is two ds_read_b64_tr_b16.
+// Both swizzles make the fragment reads of a wave conflict-free whether the
+// LDS has 32 or 64 banks.
+#pragma once
+
+#include "gemm.h"
+
+namespace moe {
+
+namespace dma {
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+constexpr int TILE_ELEMS = 256 * BK;                 // one operand tile (16 KB)
+constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;          // A then B (32 KB)
+
+// K-contiguous: row r's chunk position XOR.  Rows r .. r+15 (64 banks) and
+// r .. r+7 (32 banks) read by one LDS cycle land on distinct bank groups.
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// MN-contiguous: k-row r's chunk XOR, one of {0, 6, 12, 10} by r % 4, so the
+// 4 k-rows x 2..4 chunks read by one LDS cycle use distinct banks.
+__device__ __forceinline__ int swz_mn(int r) { return (0xAC60 >> ((r & 3) * 4)) & 0xF; }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zero (range-checked per dword), which handles every tile edge: rows past a
+// segment, k-rows past a variable-K group, and the last rows of a buffer.
+// Word 3 is the gfx9 raw-buffer format word (32-bit data, no swizzle).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One LDS-DMA instruction: lane i copies the 16 bytes at rsrc + voff + soff to
+// LDS byte address lds_dst + 16 i.  Issued through inline asm so that the
+// compiler neither waits for it before unrelated LDS reads nor before
+// barriers: the kernel waits for it explicitly (wait_vm) where a ring stage
+// is consumed.  M0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint16_t* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// Workgroup barrier for LDS hand-offs: this wave's LDS reads and writes are
+// complete (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not
+// wait for outstanding global memory operations (the DMA ring in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 256 x 32 operand tile is 16 DMA instructions of 1 KB; wave w issues
+// instructions j = 4w .. 4w+3.  Per-lane byte offsets (fixed for the whole
+// output tile; the k-tile advance goes in the scalar offset):
+//   K-contig : j covers rows 16j .. 16j+15; lane i -> row 16j + i/4, LDS
+//              position i%4 holding global chunk (i%4) ^ swz_k(row); element
+//              (mn, k) at base[mn * ld + k].  With dual, rows >= 128 are rows
+//              row - 128 of the second resource.
+//   MN-contig: j covers k-rows 2j, 2j+1; lane i -> k-row 2j + i/32, position
+//              i%32 holding chunk (i%32) ^ swz_mn(krow); element (mn, k) at
+//              base[k * ld + mn].
+template <int LAY, bool DUAL_ROWS>
+__device__ __forceinline__ uint32_t dma_voff(int j, int lane, int64_t ld) {
+  if (LAY == LAY_K) {
+    const int row = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ swz_k(row);  // the swizzle follows the LDS row
+    const int src_row = DUAL_ROWS ? (row & 127) : row;
+    return (uint32_t)(src_row * ld * 2 + c * 16);
+  } else {
+    const int krow = 2 * j + (lane >> 5);
+    const int c = (lane & 31) ^ swz_mn(krow);
+    return (uint32_t)(krow * ld * 2 + c * 16);
+  }
+}
+
+// MFMA fragment: k = kk*16 + (lane/32)*8 + 0..7 of row/column row0 + lane%32.
+template <int LAY>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* S, int row0, int kk, int lane) {
+  if (LAY == LAY_K) {
+    const int r = row0 + (lane & 31);
+    const int p = (2 * kk + (lane >> 5)) ^ swz_k(r);
+    return *reinterpret_cast<const bf16x8*>(S + r * BK + p * 8);
+  } else {
+    const int krow = kk * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+    const int col = row0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    const int p = (col >> 3) ^ swz_mn(krow);  // krow and krow + 4 share the swizzle
+    const int off = p * 8 + (col & 7);
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(S + krow * 256 + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(S + (krow + 4) * 256 + off));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+}  // namespace dma
+
+// Requirements (checked by the host before choosing this kernel): bf16
+// operands, K-contiguous operands have K (or every k-tile) a multiple of 32.
+template <int ALAY, int BLAY, int GRP, int EPI, bool DUAL>
+__global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
+  using namespace dma;
+  static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
+  constexpr int MI = 4, NI = 4;  // 32 x 32 blocks per wave (128 x 128)
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][STAGE_ELEMS];
+  __shared__ int s_pref[MAXG + 1];
+  __shared__ int s_scan[256];
+
+  Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
+  sched.init(p, s_pref, s_scan);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA operands scalar
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint16_t* Ag = reinterpret_cast<const uint16_t*>(p.A);
+  const uint16_t* Bg = reinterpret_cast<const uint16_t*>(p.B);
+  const uint16_t* B2g = reinterpret_cast<const uint16_t*>(p.B2);
+
+  for (int it = 0;; ++it) {
+    const int id = xcd_tile(it, gridDim.x);
+    if (it * (int)gridDim.x >= sched.total) break;
+    if (id >= sched.total) continue;
+    const TileCtx t = sched.tile(p, s_pref, id);
+    const int64_t klen = t.k1 - t.k0;
+    const int nk = (int)((klen + BK - 1) / BK);
+
+    const uint16_t* a_base = (ALAY == LAY_K) ? Ag + t.m0 * p.lda + t.k0 : Ag + t.k0 * p.lda + t.m0;
+    const uint16_t* b_grp = Bg;
+    const uint16_t* b2_grp = B2g;
+    if (GRP == GRP_M) {
+      b_grp += (int64_t)t.g * p.b_gstride;
+      if (B2g) b2_grp += (int64_t)t.g * p.b_gstride;
+    }
+    // Buffer resources of this output tile.  K-contig: rows [0, lim) of the
+    // tile's row block; MN-contig: k-rows [0, klen) from column m0/n0 (the
+    // range ends with row k1-1, so it never runs past the allocation).
+    const int nlim_b = DUAL ? min(t.nlim, BN / 2) : t.nlim;
+    const i32x4 ra = (ALAY == LAY_K) ? make_rsrc(a_base, (uint64_t)t.mlim * p.lda * 2)
+                                     : make_rsrc(a_base, (uint64_t)(klen * p.lda - t.m0) * 2);
+    i32x4 rb, rb2;
+    if (BLAY == LAY_K) {
+      rb = make_rsrc(b_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2);
+      rb2 = DUAL ? make_rsrc(b2_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2) : rb;
+    } else if (p.ksplit) {  // k < ksplit from B, k >= ksplit from B2 (GRP_M: t.k0 = 0)
+      rb = make_rsrc(b_grp + t.n0, (uint64_t)((int64_t)p.ksplit * p.ldb - t.n0) * 2);
+      rb2 = make_rsrc(b2_grp + t.n0, (uint64_t)((klen - p.ksplit) * p.ldb - t.n0) * 2);
+    } else {
+      rb = make_rsrc(b_grp + t.k0 * p.ldb + t.n0, (uint64_t)(klen * p.ldb - t.n0) * 2);
+      rb2 = rb;
+    }
+    uint32_t va[4], vb[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      va[jj] = dma_voff<ALAY, false>(wave * 4 + jj, lane, p.lda);
+      vb[jj] = dma_voff<BLAY, DUAL>(wave * 4 + jj, lane, p.ldb);
+    }
+    // K-contig dual: instructions j >= 8 (waves 2, 3) read the second resource.
+    const bool b_second = DUAL && wave >= 2;
+    auto issue = [&](int kt) {
+      uint16_t* st = ring[kt % STAGES];
+      const uint32_t so_a = (ALAY == LAY_K) ? (uint32_t)kt * BK * 2 : (uint32_t)((int64_t)kt * BK * p.lda * 2);
+      i32x4 rbk = b_second ? rb2 : rb;
+      uint32_t so_b;
+      if (BLAY == LAY_K) {
+        so_b = (uint32_t)kt * BK * 2;
+      } else if (p.ksplit && (int64_t)kt * BK >= p.ksplit) {
+        rbk = rb2;
+        so_b = (uint32_t)(((int64_t)kt * BK - p.ksplit) * p.ldb * 2);
+      } else {
+        so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = wave * 4 + jj;
+        dma16(ra, va[jj], so_a, st + j * 512);
+        dma16(rbk, vb[jj], so_b, st + TILE_ELEMS + j * 512);
+      }
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Fragments of one k-step (16 k) from a ring stage.
+    auto read_frags = [&](const uint16_t* st, int kk, bf16x8(&a)[MI], bf16x8(&b)[NI]) {
+      const uint16_t* as = st;
+      const uint16_t* bs = st + TILE_ELEMS;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) a[mi] = frag<ALAY>(as, wm * 128 + mi * 32, kk, lane);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
+        b[ni] = frag<BLAY>(bs, brow, kk, lane);
+      }
+    };
+    // LDS read instructions per k-step (a transposed fragment takes two).
+    constexpr int NREAD = MI * (ALAY == LAY_K ? 1 : 2) + NI * (BLAY == LAY_K ? 1 : 2);
+    // Interleave the 16 MFMAs of a k-step with the NREAD LDS reads that
+    // prefetch the next k-step's fragments, one read after each MFMA.
+    auto interleave = [&]() {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // 1 MFMA
+        if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+      }
+      if (NREAD > 16) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - 16, 0);
+    };
+    auto mfma_step = [&](const bf16x8(&a)[MI], const bf16x8(&b)[NI]) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    };
+    // Wait until this wave's DMA of k-tile `kt` has landed, given how many
+    // later k-tiles (8 instructions each) may still be in flight, then make
+    // all waves' parts visible.  Partial k-tiles get their tail k-rows zeroed.
+    auto stage_ready = [&](int kt, int later) {
+      if (later >= 2) wait_vm<16>();
+      else if (later == 1) wait_vm<8>();
+      else wait_vm<0>();
+      lds_barrier();
+      (void)kt;
+    };
+
+    // Pipeline: k-tiles kt+1 .. kt+2 are in flight while k-tile kt is
+    // consumed.  Each k-tile is two k-steps: step 0's MFMAs overlap the reads
+    // of step 1; then the next stage is made ready (one barrier per k-tile)
+    // and its DMA refill issued; step 1's MFMAs overlap the reads of the next
+    // stage's step 0.  No fragment read is ever waited for right after issue.
+    bf16x8 f0a[MI], f0b[NI], f1a[MI], f1b[NI];
+    if (nk > 0) {
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s);
+      stage_ready(0, min(STAGES - 2, nk - 1));
+      read_frags(ring[0], 0, f0a, f0b);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* st = ring[kt % STAGES];
+      read_frags(st, 1, f1a, f1b);
+      mfma_step(f0a, f0b);
+      interleave();
+      if (kt + 1 < nk) {
+        stage_ready(kt + 1, min(1, nk - 2 - kt));
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      }
+      // Unconditional (the last k-tile reads a stale stage it never uses), so
+      // the compiler's LDS wait counts stay exact across the branch above.
+      read_frags(ring[(kt + 1) % STAGES], 0, f0a, f0b);
+      mfma_step(f1a, f1b);
+      interleave();
+    }
+    lds_barrier();  // every wave is done reading the ring (and no DMA is in flight) before staging
+
+    // Epilogue, staged through the ring one 32-row block at a time (as in
+    // gemm_mfma_kernel): acc[mi][ni][r] is C[row][col] with
+    //   row = wm*128 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4, col = n-block base + lane%32.
+    {
+      constexpr int WC = NI * 32;
+      constexpr int SP = WC + 4;
+      float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 32 * SP;
+      static_assert(4 * 32 * SP * 4 <= (int)sizeof(ring), "staging fits in the ring");
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            stage[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SP + ni * 32 + (lane & 31)] = acc[mi][ni][r];
+        lds_barrier();
+        constexpr int OC = DUAL ? WC / 2 : WC;
+        constexpr int CPR = OC / 8;
+        for (int e = lane; e < 32 * CPR; e += 64) {
+          const int rl = e / CPR, cv = (e % CPR) * 8;
+          const int row = wm * 128 + mi * 32 + rl;
+          const int col = (DUAL ? wn * 64 : wn * 128) + cv;
+          if (row < t.mlim && col < t.nlim) {
+            float v[8], v2[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              v[q] = stage[rl * SP + cv + q];
+              v2[q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+            }
+            epi_store8<GRP, EPI>(p, t, row, col, v, v2);
+          }
+        }
+        lds_barrier();
+      }
+    }
+  }
+}
+
+}  // namespace moe
