@@ -45,17 +45,24 @@ hipError_t run_mfma(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// k-slice width and ring depth of the LDS-DMA kernel (a 128 KB ring).
+#ifndef MOE_DMA_BK
+#define MOE_DMA_BK 64
+#endif
+constexpr int DMA_BK = MOE_DMA_BK;
+constexpr int DMA_STAGES = DMA_BK == 64 ? 2 : 4;
+
 // bf16 products: the LDS-DMA kernel when every K-contiguous operand has K a
 // multiple of its 32-wide k-tile, else the register-staged kernel.
 template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
 hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
-  const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) || (GRP != GRP_K && p.K % dma::BK == 0);
+  const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) || (GRP != GRP_K && p.K % DMA_BK == 0);
   if (!std::is_same<AT, uint16_t>::value || !k_ok) return run_mfma<ALAY, BLAY, AT, GRP, EPI, DUAL>(p, ub_tiles, s);
   int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus());
   if (grid >= 8) grid -= grid % 8;
   if (grid <= 0) return hipSuccess;
   if constexpr (std::is_same<AT, uint16_t>::value)
-    gemm_dma_kernel<ALAY, BLAY, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
+    gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

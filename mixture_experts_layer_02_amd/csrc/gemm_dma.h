@@ -3,17 +3,19 @@
 // Same products, grouping modes, tile order and epilogues as gemm_mfma_kernel
 // (gemm.h), but the operand tiles reach LDS through the gfx950 LDS DMA path:
 // each wave instruction moves 64 x 16 bytes from HBM/L2 straight into 1 KB of
-// contiguous LDS, without passing through VGPRs.  That frees the staging
-// registers and lets a 4-stage ring of BK = 32 k-slices keep three k-tiles in
-// flight, enough to cover L2 misses that go to MALL or HBM.
+// contiguous LDS, without passing through VGPRs.  The k-slice width BK and
+// the number of ring stages NST are template parameters (BK = 64 with 2
+// stages is the 128 KB LDS ring used by default; BK = 32 with 4 stages keeps
+// more, smaller k-tiles in flight).
 //
 // LDS layouts (no padding: a DMA instruction writes 1 KB contiguously, so bank
 // conflicts are avoided by XOR-swizzling 16-byte chunks instead):
-//   K-contiguous tile  [256 rows][32 k]: a row is 4 chunks; chunk c of row r
-//     sits at position c ^ swz_k(r).  A fragment (8 k of one row) is one
-//     ds_read_b128.
-//   MN-contiguous tile [32 k][256 mn]: a k-row is 32 chunks; chunk c of k-row
-//     r sits at position c ^ swz_mn(r).  A fragment is two ds_read_b64_tr_b16.
+//   K-contiguous tile  [256 rows][BK k]: a row is BK/8 chunks; chunk c of
+//     row r sits at position c ^ swz_k(r).  A fragment (8 k of one row) is
+//     one ds_read_b128.
+//   MN-contiguous tile [BK k][256 mn]: a k-row is 32 chunks; chunk c of
+//     k-row r sits at position c ^ swz_mn(r).  A fragment is two
+//     ds_read_b64_tr_b16.
 // Both swizzles make the fragment reads of a wave conflict-free whether the
 // LDS has 32 or 64 banks.
 #pragma once
@@ -23,13 +25,15 @@
 namespace moe {
 
 namespace dma {
-constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
-constexpr int TILE_ELEMS = 256 * BK;                 // one operand tile (16 KB)
-constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;          // A then B (32 KB)
+constexpr int BM = 256, BN = 256;
 
-// K-contiguous: row r's chunk position XOR.  Rows r .. r+15 (64 banks) and
-// r .. r+7 (32 banks) read by one LDS cycle land on distinct bank groups.
-__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// K-contiguous: row r's chunk position XOR.  The 16 (64 banks) or 8 (32
+// banks) consecutive rows read by one LDS cycle land on distinct bank groups.
+template <int BK>
+__device__ __forceinline__ int swz_k(int r) {
+  if (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
+  return (r ^ (r >> 3)) & 7;
+}
 // MN-contiguous: k-row r's chunk XOR, one of {0, 6, 12, 10} by r % 4, so the
 // 4 k-rows x 2..4 chunks read by one LDS cycle use distinct banks.
 __device__ __forceinline__ int swz_mn(int r) { return (0xAC60 >> ((r & 3) * 4)) & 0xF; }
@@ -78,21 +82,23 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One 256 x 32 operand tile is 16 DMA instructions of 1 KB; wave w issues
-// instructions j = 4w .. 4w+3.  Per-lane byte offsets (fixed for the whole
-// output tile; the k-tile advance goes in the scalar offset):
-//   K-contig : j covers rows 16j .. 16j+15; lane i -> row 16j + i/4, LDS
-//              position i%4 holding global chunk (i%4) ^ swz_k(row); element
-//              (mn, k) at base[mn * ld + k].  With dual, rows >= 128 are rows
+// One 256 x BK operand tile is BK/2 DMA instructions of 1 KB; wave w issues
+// instructions j = w*BK/8 .. (w+1)*BK/8 - 1.  Per-lane byte offsets (fixed for
+// the whole output tile; the k-tile advance goes in the scalar offset):
+//   K-contig : j covers rows RPI*j .. RPI*j+RPI-1 (RPI = 512/BK rows of BK/8
+//              chunks); lane i -> row RPI*j + i/(BK/8), LDS position i%(BK/8)
+//              holding global chunk (i%(BK/8)) ^ swz_k(row); element (mn, k)
+//              at base[mn * ld + k].  With dual, rows >= 128 are rows
 //              row - 128 of the second resource.
 //   MN-contig: j covers k-rows 2j, 2j+1; lane i -> k-row 2j + i/32, position
 //              i%32 holding chunk (i%32) ^ swz_mn(krow); element (mn, k) at
 //              base[k * ld + mn].
-template <int LAY, bool DUAL_ROWS>
+template <int BK, int LAY, bool DUAL_ROWS>
 __device__ __forceinline__ uint32_t dma_voff(int j, int lane, int64_t ld) {
   if (LAY == LAY_K) {
-    const int row = 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ swz_k(row);  // the swizzle follows the LDS row
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;  // chunks per row, rows per instruction
+    const int row = RPI * j + lane / CPR;
+    const int c = (lane % CPR) ^ swz_k<BK>(row);  // the swizzle follows the LDS row
     const int src_row = DUAL_ROWS ? (row & 127) : row;
     return (uint32_t)(src_row * ld * 2 + c * 16);
   } else {
@@ -103,11 +109,11 @@ __device__ __forceinline__ uint32_t dma_voff(int j, int lane, int64_t ld) {
 }
 
 // MFMA fragment: k = kk*16 + (lane/32)*8 + 0..7 of row/column row0 + lane%32.
-template <int LAY>
+template <int BK, int LAY>
 __device__ __forceinline__ bf16x8 frag(const uint16_t* S, int row0, int kk, int lane) {
   if (LAY == LAY_K) {
     const int r = row0 + (lane & 31);
-    const int p = (2 * kk + (lane >> 5)) ^ swz_k(r);
+    const int p = (2 * kk + (lane >> 5)) ^ swz_k<BK>(r);
     return *reinterpret_cast<const bf16x8*>(S + r * BK + p * 8);
   } else {
     const int krow = kk * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
@@ -129,15 +135,29 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// Wait until at most `later` stages of PER instructions each are outstanding.
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_stages(int later) {
+  if (MAXL >= 3 && later >= 3) wait_vm<(MAXL >= 3 ? 3 * PER : 0)>();
+  else if (MAXL >= 2 && later >= 2) wait_vm<(MAXL >= 2 ? 2 * PER : 0)>();
+  else if (MAXL >= 1 && later >= 1) wait_vm<PER>();
+  else wait_vm<0>();
+}
 }  // namespace dma
 
 // Requirements (checked by the host before choosing this kernel): bf16
 // operands, K-contiguous operands have K (or every k-tile) a multiple of 32.
-template <int ALAY, int BLAY, int GRP, int EPI, bool DUAL>
+template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
-  constexpr int MI = 4, NI = 4;  // 32 x 32 blocks per wave (128 x 128)
+  static_assert((BK == 32 && STAGES == 4) || (BK == 64 && STAGES == 2), "ring shapes of 128 KB");
+  constexpr int MI = 4, NI = 4;          // 32 x 32 blocks per wave (128 x 128)
+  constexpr int TILE_ELEMS = 256 * BK;   // one operand tile
+  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
+  constexpr int NJ = BK / 8;             // DMA instructions per wave per operand tile
+  constexpr int KS = BK / 16;            // MFMA k-steps per k-tile
   __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][STAGE_ELEMS];
   __shared__ int s_pref[MAXG + 1];
   __shared__ int s_scan[256];
@@ -185,13 +205,13 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       rb = make_rsrc(b_grp + t.k0 * p.ldb + t.n0, (uint64_t)(klen * p.ldb - t.n0) * 2);
       rb2 = rb;
     }
-    uint32_t va[4], vb[4];
+    uint32_t va[NJ], vb[NJ];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      va[jj] = dma_voff<ALAY, false>(wave * 4 + jj, lane, p.lda);
-      vb[jj] = dma_voff<BLAY, DUAL>(wave * 4 + jj, lane, p.ldb);
+    for (int jj = 0; jj < NJ; ++jj) {
+      va[jj] = dma_voff<BK, ALAY, false>(wave * NJ + jj, lane, p.lda);
+      vb[jj] = dma_voff<BK, BLAY, DUAL>(wave * NJ + jj, lane, p.ldb);
     }
-    // K-contig dual: instructions j >= 8 (waves 2, 3) read the second resource.
+    // K-contig dual: instructions j >= BK/4 (waves 2, 3) read the second resource.
     const bool b_second = DUAL && wave >= 2;
     auto issue = [&](int kt) {
       uint16_t* st = ring[kt % STAGES];
@@ -207,8 +227,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = wave * 4 + jj;
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int j = wave * NJ + jj;
         dma16(ra, va[jj], so_a, st + j * 512);
         dma16(rbk, vb[jj], so_b, st + TILE_ELEMS + j * 512);
       }
@@ -227,11 +247,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       const uint16_t* as = st;
       const uint16_t* bs = st + TILE_ELEMS;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) a[mi] = frag<ALAY>(as, wm * 128 + mi * 32, kk, lane);
+      for (int mi = 0; mi < MI; ++mi) a[mi] = frag<BK, ALAY>(as, wm * 128 + mi * 32, kk, lane);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
-        b[ni] = frag<BLAY>(bs, brow, kk, lane);
+        b[ni] = frag<BK, BLAY>(bs, brow, kk, lane);
       }
     };
     // LDS read instructions per k-step (a transposed fragment takes two).
@@ -253,43 +273,45 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     };
-    // Wait until this wave's DMA of k-tile `kt` has landed, given how many
-    // later k-tiles (8 instructions each) may still be in flight, then make
-    // all waves' parts visible.  Partial k-tiles get their tail k-rows zeroed.
-    auto stage_ready = [&](int kt, int later) {
-      if (later >= 2) wait_vm<16>();
-      else if (later == 1) wait_vm<8>();
-      else wait_vm<0>();
+    // Wait until this wave's DMA of the next needed k-tile has landed, given
+    // how many later k-tiles (2*NJ instructions each) may still be in
+    // flight, then make all waves' parts visible.
+    auto stage_ready = [&](int later) {
+      wait_stages<2 * NJ, STAGES - 1>(later);
       lds_barrier();
-      (void)kt;
     };
 
-    // Pipeline: k-tiles kt+1 .. kt+2 are in flight while k-tile kt is
-    // consumed.  Each k-tile is two k-steps: step 0's MFMAs overlap the reads
-    // of step 1; then the next stage is made ready (one barrier per k-tile)
-    // and its DMA refill issued; step 1's MFMAs overlap the reads of the next
-    // stage's step 0.  No fragment read is ever waited for right after issue.
-    bf16x8 f0a[MI], f0b[NI], f1a[MI], f1b[NI];
+    // Pipeline.  All ring stages are filled up front; while k-tile kt is
+    // consumed, k-tiles kt+1 .. kt+STAGES-1 are in flight.  A k-tile is KS
+    // k-steps; the MFMAs of each step overlap the LDS reads of the next.
+    // Before the last step, k-tile kt+1 is waited for (one barrier per
+    // k-tile), the stage of k-tile kt, now fully read, is refilled with
+    // k-tile kt+STAGES, and the last step's MFMAs overlap the reads of
+    // k-tile kt+1's first step.
+    bf16x8 fa[2][MI], fb[2][NI];
     if (nk > 0) {
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
+      for (int s = 0; s < STAGES; ++s)
         if (s < nk) issue(s);
-      stage_ready(0, min(STAGES - 2, nk - 1));
-      read_frags(ring[0], 0, f0a, f0b);
+      stage_ready(min(STAGES - 1, nk - 1));
+      read_frags(ring[0], 0, fa[0], fb[0]);
     }
     for (int kt = 0; kt < nk; ++kt) {
       const uint16_t* st = ring[kt % STAGES];
-      read_frags(st, 1, f1a, f1b);
-      mfma_step(f0a, f0b);
-      interleave();
+#pragma unroll
+      for (int s = 0; s < KS - 1; ++s) {
+        read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        mfma_step(fa[s & 1], fb[s & 1]);
+        interleave();
+      }
       if (kt + 1 < nk) {
-        stage_ready(kt + 1, min(1, nk - 2 - kt));
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+        stage_ready(min(STAGES - 2, nk - 2 - kt));
+        if (kt + STAGES < nk) issue(kt + STAGES);
       }
       // Unconditional (the last k-tile reads a stale stage it never uses), so
       // the compiler's LDS wait counts stay exact across the branch above.
-      read_frags(ring[(kt + 1) % STAGES], 0, f0a, f0b);
-      mfma_step(f1a, f1b);
+      read_frags(ring[(kt + 1) % STAGES], 0, fa[0], fb[0]);
+      mfma_step(fa[1], fb[1]);
       interleave();
     }
     lds_barrier();  // every wave is done reading the ring (and no DMA is in flight) before staging
