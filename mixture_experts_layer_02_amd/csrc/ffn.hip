@@ -92,6 +92,19 @@ int router_splits(const moe_desc& d) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
 }
 
+// float32 -> bfloat16 (round to nearest even), 8 elements per thread; n % 8 == 0.
+__global__ void __launch_bounds__(256) to_bf16_kernel(const float* __restrict__ in, int64_t n,
+                                                      uint16_t* __restrict__ out) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+    float v[8];
+    const f32x4 a = *reinterpret_cast<const f32x4*>(in + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(in + i + 4);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    Vec16<uint16_t>::store(out + i, v);
+  }
+}
+
 __global__ void __launch_bounds__(256) sum_splits_kernel(const float* __restrict__ part, int S, int64_t n,
                                                          float* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
@@ -103,8 +116,16 @@ __global__ void __launch_bounds__(256) sum_splits_kernel(const float* __restrict
 
 }  // namespace
 
+// Router backward workspace: split-K partials of dWr, then (bf16 path) a
+// bfloat16 copy of dlogits for the matrix cores.
+size_t router_bwd_partials_bytes(const moe_desc& d) {
+  return (((size_t)router_splits(d) * (size_t)d.E * (size_t)d.d * sizeof(float)) + 255) & ~(size_t)255;
+}
+
 size_t router_bwd_workspace(const moe_desc& d) {
-  return (size_t)router_splits(d) * (size_t)d.E * (size_t)d.d * sizeof(float);
+  size_t b = router_bwd_partials_bytes(d);
+  if (d.dtype == MOE_BF16) b += (size_t)d.T * (size_t)d.E * sizeof(uint16_t);
+  return b;
 }
 
 hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
@@ -259,10 +280,21 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
                              float* dx_router, float* dWr, void* ws, hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
   hipError_t e = hipSuccess;
+  float* part = reinterpret_cast<float*>(ws);
+  // bf16 path: dlogits rounded once to bf16 (the matrix-core operand).
+  const void* dl = dlogits;
+  if (bf) {
+    uint16_t* dl16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + router_bwd_partials_bytes(d));
+    const int64_t n = (int64_t)d.T * d.E;
+    const int64_t blocks = std::min<int64_t>(cdiv(n, 256 * 8), (int64_t)num_cus() * 8);
+    to_bf16_kernel<<<(unsigned)blocks, 256, 0, s>>>(dlogits, n, dl16);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dl = dl16;
+  }
   if (dx_router) {
     // dx_router [T][d] = dlogits [T][E] Wr [E][d]
     GemmParams p = blank();
-    p.A = dlogits;
+    p.A = dl;
     p.lda = d.E;
     p.B = Wr;
     p.ldb = d.d;
@@ -272,16 +304,15 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
     p.N = d.d;
     p.K = d.E;
     p.c_f32 = 1;
-    if (bf) e = run_mfma<LAY_K, LAY_MN, float, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.d, MT), s);
+    if (bf) e = run_bf16<LAY_K, LAY_MN, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.d, MT), s);
     else e = run_f32<LAY_K, LAY_MN, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.d, 64), s);
     if (e != hipSuccess) return e;
   }
   if (dWr) {
     // dWr [E][d] = dlogits^T x, split over T into S chunks, then summed in chunk order
     const int S = router_splits(d);
-    float* part = reinterpret_cast<float*>(ws);
     GemmParams q = blank();
-    q.A = dlogits;
+    q.A = dl;
     q.lda = d.E;
     q.B = x;
     q.ldb = d.d;
@@ -295,7 +326,7 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
     q.N = d.d;
     q.K = d.T;
     q.c_f32 = 1;
-    if (bf) e = run_mfma<LAY_MN, LAY_MN, float, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, MT) * cdiv(d.d, MT), s);
+    if (bf) e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, MT) * cdiv(d.d, MT), s);
     else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.E, 64) * cdiv(d.d, 64), s);
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)d.E * d.d;

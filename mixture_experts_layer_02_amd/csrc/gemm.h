@@ -152,7 +152,7 @@ struct Scheduler {
           t.k1 = p.offsets[g + 1];
         } else {
           t.k0 = (int64_t)g * p.kchunk;
-          t.k1 = min((int64_t)p.K, t.k0 + p.kchunk);
+          t.k1 = max(t.k0, min((int64_t)p.K, t.k0 + p.kchunk));  // chunks past K are empty
         }
       } else {
         t.k0 = 0;
