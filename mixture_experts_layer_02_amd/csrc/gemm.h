@@ -60,6 +60,8 @@ struct TileCtx {
   int nlim;     // valid columns in the tile
   int64_t k0, k1;  // K range of the tile
   int mtile;    // m-tile index within the group (GRP_K: within M)
+  int mtiles;   // m-tiles of the group
+  int ntile;    // n-tile index
 };
 
 // ---------------------------------------------------------------------------
@@ -129,6 +131,8 @@ struct Scheduler {
       const int mt = local % mt_g, nt = local / mt_g;
       t.g = g;
       t.mtile = mt;
+      t.mtiles = mt_g;
+      t.ntile = nt;
       t.m0 = (int64_t)r0 + (int64_t)mt * BM;
       t.mlim = min(BM, r1 - (int)t.m0);
       t.n0 = nt * BN;
@@ -142,6 +146,8 @@ struct Scheduler {
       const int mt = local % MT, nt = local / MT;
       t.g = g;
       t.mtile = mt;
+      t.mtiles = MT;
+      t.ntile = nt;
       t.m0 = (int64_t)mt * BM;
       t.mlim = min(BM, p.M - (int)t.m0);
       t.n0 = nt * BN;

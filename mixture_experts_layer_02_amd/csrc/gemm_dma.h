@@ -20,6 +20,8 @@
 // LDS has 32 or 64 banks.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace moe {
@@ -66,6 +68,23 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// L2 prefetch: lane i reads the 4 bytes at rsrc + voff + soff into the LDS
+// word lds_junk + 4 i (a scratch area nobody reads).  Its only purpose is to
+// start the L2 fill of that 64-byte sector well before the tile DMA needs
+// it; an offset outside the resource reads nothing.
+__device__ __forceinline__ void touch4(i32x4 rsrc, uint32_t voff, uint32_t soff, const uint32_t* lds_junk) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_junk);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
@@ -161,6 +180,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][STAGE_ELEMS];
   __shared__ int s_pref[MAXG + 1];
   __shared__ int s_scan[256];
+  __shared__ __attribute__((aligned(256))) uint32_t lds_junk[64];
 
   Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
   sched.init(p, s_pref, s_scan);
@@ -213,24 +233,71 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
     // K-contig dual: instructions j >= BK/4 (waves 2, 3) read the second resource.
     const bool b_second = DUAL && wave >= 2;
-    auto issue = [&](int kt) {
+    // DMA instruction q (0 .. 2*NJ-1) of k-tile kt: even q are A tiles, odd q B tiles.
+    auto dma_one = [&](int kt, int q) {
       uint16_t* st = ring[kt % STAGES];
-      const uint32_t so_a = (ALAY == LAY_K) ? (uint32_t)kt * BK * 2 : (uint32_t)((int64_t)kt * BK * p.lda * 2);
-      i32x4 rbk = b_second ? rb2 : rb;
-      uint32_t so_b;
-      if (BLAY == LAY_K) {
-        so_b = (uint32_t)kt * BK * 2;
-      } else if (p.ksplit && (int64_t)kt * BK >= p.ksplit) {
-        rbk = rb2;
-        so_b = (uint32_t)(((int64_t)kt * BK - p.ksplit) * p.ldb * 2);
-      } else {
-        so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
-      }
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        const int j = wave * NJ + jj;
+      const int jj = q >> 1;
+      const int j = wave * NJ + jj;
+      if ((q & 1) == 0) {
+        const uint32_t so_a = (ALAY == LAY_K) ? (uint32_t)kt * BK * 2 : (uint32_t)((int64_t)kt * BK * p.lda * 2);
         dma16(ra, va[jj], so_a, st + j * 512);
+      } else {
+        i32x4 rbk = b_second ? rb2 : rb;
+        uint32_t so_b;
+        if (BLAY == LAY_K) {
+          so_b = (uint32_t)kt * BK * 2;
+        } else if (p.ksplit && (int64_t)kt * BK >= p.ksplit) {
+          rbk = rb2;
+          so_b = (uint32_t)(((int64_t)kt * BK - p.ksplit) * p.ldb * 2);
+        } else {
+          so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
+        }
         dma16(rbk, vb[jj], so_b, st + TILE_ELEMS + j * 512);
+      }
+    };
+
+    // L2 prefetch of k-tile pkt, one instruction per wave per operand, each
+    // lane touching one 64-byte sector.  A tile is also loaded by the tiles
+    // of the same XCD that run at the same time and share it: the tiles of
+    // one n-tile and consecutive m-tiles share B, those of one m-tile and
+    // consecutive n-tiles share A (tiles are ordered m-fastest and an XCD
+    // takes RUN consecutive tiles per round).  The sectors of a shared tile
+    // are dealt round-robin over its C sharers, so that each is prefetched
+    // once per XCD: this tile takes sectors e = c + C*j, c = its own index
+    // modulo C.  Unassigned lanes get an offset outside every resource.
+    constexpr int NPF = 2;
+    constexpr int ITEMS = 8 * BK;  // 64-byte sectors of a 256 x BK operand tile
+    const int run = (gridDim.x % 8) ? 1 : (int)gridDim.x / 8;
+    const int cB = max(1, min(t.mtiles, run));
+    const int cA = max(1, min(sched.NT, run / max(t.mtiles, 1)));
+    auto pf_voff = [&](int C, int c, int64_t ld, int lay, int parts) -> uint32_t {
+      const int wl = wave % (4 / parts);
+      const int e = c + C * (wl * 64 + lane);
+      if (e >= ITEMS / parts) return 0x7FFFFFF0u;
+      if (lay == LAY_K) {
+        constexpr int SPR = BK / 32;  // sectors per row
+        return (uint32_t)((e / SPR) * ld * 2 + (e % SPR) * 64);
+      }
+      return (uint32_t)((e >> 3) * ld * 2 + (e & 7) * 64);
+    };
+    const uint32_t pa = pf_voff(cA, t.ntile % cA, p.lda, ALAY, 1);
+    const uint32_t pb = pf_voff(cB, t.mtile % cB, p.ldb, BLAY, DUAL ? 2 : 1);
+    auto pf_one = [&](int kt, int o) {
+      if (o == 0) {
+        const uint32_t so_a = (ALAY == LAY_K) ? (uint32_t)kt * BK * 2 : (uint32_t)((int64_t)kt * BK * p.lda * 2);
+        touch4(ra, pa, so_a, lds_junk);
+      } else {
+        i32x4 rbk = b_second ? rb2 : rb;
+        uint32_t so_b;
+        if (BLAY == LAY_K) {
+          so_b = (uint32_t)kt * BK * 2;
+        } else if (p.ksplit && (int64_t)kt * BK >= p.ksplit) {
+          rbk = rb2;
+          so_b = (uint32_t)(((int64_t)kt * BK - p.ksplit) * p.ldb * 2);
+        } else {
+          so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
+        }
+        touch4(rbk, pb, so_b, lds_junk);
       }
     };
 
@@ -242,78 +309,112 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Fragments of one k-step (16 k) from a ring stage.
-    auto read_frags = [&](const uint16_t* st, int kk, bf16x8(&a)[MI], bf16x8(&b)[NI]) {
-      const uint16_t* as = st;
-      const uint16_t* bs = st + TILE_ELEMS;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) a[mi] = frag<BK, ALAY>(as, wm * 128 + mi * 32, kk, lane);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
+    // Fragment f (0 .. MI+NI-1) of k-step kk of a ring stage, in the order the
+    // MFMAs (mi-major) first use them: A0, B0 .. B3, A1 .. A3.
+    auto read_frag = [&](const uint16_t* st, int kk, int f, bf16x8(&a)[MI], bf16x8(&b)[NI]) {
+      static_assert(MI == 4 && NI == 4, "fragment order");
+      if (f == 0 || f > NI) {
+        const int mi = f == 0 ? 0 : f - NI;
+        a[mi] = frag<BK, ALAY>(st, wm * 128 + mi * 32, kk, lane);
+      } else {
+        const int ni = f - 1;
         const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
-        b[ni] = frag<BK, BLAY>(bs, brow, kk, lane);
+        b[ni] = frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
       }
-    };
-    // LDS read instructions per k-step (a transposed fragment takes two).
-    constexpr int NREAD = MI * (ALAY == LAY_K ? 1 : 2) + NI * (BLAY == LAY_K ? 1 : 2);
-    // Interleave the 16 MFMAs of a k-step with the NREAD LDS reads that
-    // prefetch the next k-step's fragments, one read after each MFMA.
-    auto interleave = [&]() {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // 1 MFMA
-        if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-      }
-      if (NREAD > 16) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - 16, 0);
-    };
-    auto mfma_step = [&](const bf16x8(&a)[MI], const bf16x8(&b)[NI]) {
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-    };
-    // Wait until this wave's DMA of the next needed k-tile has landed, given
-    // how many later k-tiles (2*NJ instructions each) may still be in
-    // flight, then make all waves' parts visible.
-    auto stage_ready = [&](int later) {
-      wait_stages<2 * NJ, STAGES - 1>(later);
-      lds_barrier();
     };
 
-    // Pipeline.  All ring stages are filled up front; while k-tile kt is
-    // consumed, k-tiles kt+1 .. kt+STAGES-1 are in flight.  A k-tile is KS
-    // k-steps; the MFMAs of each step overlap the LDS reads of the next.
-    // Before the last step, k-tile kt+1 is waited for (one barrier per
-    // k-tile), the stage of k-tile kt, now fully read, is refilled with
-    // k-tile kt+STAGES, and the last step's MFMAs overlap the reads of
-    // k-tile kt+1's first step.
+    // One k-step: the 16 MFMAs of fragments (a, b), with, in between, the
+    // reads of the next k-step's fragments (stage rst, step rkk), ND DMA
+    // instructions q0 .. q0+ND-1 of k-tile dkt and then NP L2 prefetches of
+    // k-tile pkt, spread evenly.  The scheduling barriers pin this order, so
+    // that the DMA issue never comes as a burst that would stall the wave's
+    // MFMAs behind a full address queue.
+    auto kstep = [&](auto nd_c, auto np_c, const bf16x8(&a)[MI], const bf16x8(&b)[NI], bf16x8(&na)[MI],
+                     bf16x8(&nb)[NI], const uint16_t* rst, int rkk, int dkt, int q0, int pkt) {
+      constexpr int ND = decltype(nd_c)::value;
+      constexpr int NO = ND + decltype(np_c)::value;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int mi = i / NI, ni = i % NI;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
+#pragma unroll
+        for (int o = (i * NO) / 16; o < ((i + 1) * NO) / 16; ++o) {
+          if (o < ND) dma_one(dkt, q0 + o);
+          else pf_one(pkt, o - ND);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Pipeline.  While k-tile kt is consumed, k-tiles kt+1 .. kt+STAGES-1
+    // are in flight.  A k-tile is KS k-steps; each step's MFMAs overlap the
+    // LDS reads of the next step.  Before the last step of k-tile kt,
+    // k-tile kt+1 is waited for (one barrier per k-tile); the stage of
+    // k-tile kt, now fully read, is then refilled with k-tile kt+STAGES,
+    // whose PER DMA instructions per wave are spread over the last step of
+    // kt and the first SPREAD-1 steps of kt+1 (all before the next barrier).
+    // Right after the last of them, NPF prefetches start the L2 fill of
+    // k-tile kt+STAGES+PFD, so that its DMA, PFD k-tiles later, hits in L2;
+    // a barrier's wait leaves these prefetches in flight (they are the only
+    // loads issued after the awaited k-tile), and they have until the next
+    // barrier to land.
+    // The schedule is the same for every k-tile: k-tiles past the end
+    // (kt >= nk) are loaded too, as zero fills of a stage that is never read
+    // again (their offsets lie outside the buffer resources, so they touch
+    // no memory), which keeps the loop body free of branches.
+    constexpr int PER = 2 * NJ;
+    constexpr int SPREAD = KS >= 2 ? 2 : 1;
+    constexpr int PART = PER / SPREAD;
+    constexpr int PFD = 2;
+    static_assert(PER % SPREAD == 0 && SPREAD <= KS, "a stage's DMA is issued before the next barrier");
+    using N0 = std::integral_constant<int, 0>;
+    using NDP = std::integral_constant<int, PART>;
+    using NPP = std::integral_constant<int, NPF>;
     bf16x8 fa[2][MI], fb[2][NI];
     if (nk > 0) {
+      // The same issue pattern as the loop: each stage's DMAs, then the
+      // prefetches of the k-tile PFD further on.
 #pragma unroll
-      for (int s = 0; s < STAGES; ++s)
-        if (s < nk) issue(s);
-      stage_ready(min(STAGES - 1, nk - 1));
-      read_frags(ring[0], 0, fa[0], fb[0]);
+      for (int s = 0; s < STAGES - 1; ++s) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) dma_one(s, q);
+#pragma unroll
+        for (int o = 0; o < NPF; ++o) pf_one(s + PFD, o);
+      }
+#pragma unroll
+      for (int q = 0; q < PART; ++q) dma_one(STAGES - 1, q);
+      wait_vm<NPF + (STAGES - 2) * (PER + NPF) + PART>();  // k-tile 0 has landed
+      lds_barrier();
+#pragma unroll
+      for (int f = 0; f < MI + NI; ++f) read_frag(ring[0], 0, f, fa[0], fb[0]);
     }
     for (int kt = 0; kt < nk; ++kt) {
       const uint16_t* st = ring[kt % STAGES];
 #pragma unroll
       for (int s = 0; s < KS - 1; ++s) {
-        read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-        mfma_step(fa[s & 1], fb[s & 1]);
-        interleave();
+        if (s + 2 < SPREAD)
+          kstep(NDP(), N0(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, kt - 1 + STAGES,
+                (s + 1) * PART, 0);
+        else if (s + 2 == SPREAD)
+          kstep(NDP(), NPP(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1,
+                kt - 1 + STAGES, (s + 1) * PART, kt - 1 + STAGES + PFD);
+        else
+          kstep(N0(), N0(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
       }
-      if (kt + 1 < nk) {
-        stage_ready(min(STAGES - 2, nk - 2 - kt));
-        if (kt + STAGES < nk) issue(kt + STAGES);
-      }
-      // Unconditional (the last k-tile reads a stale stage it never uses), so
-      // the compiler's LDS wait counts stay exact across the branch above.
-      read_frags(ring[(kt + 1) % STAGES], 0, fa[0], fb[0]);
-      mfma_step(fa[1], fb[1]);
-      interleave();
+      // k-tile kt+1 has landed: after its last DMA come only its prefetches
+      // and the later stages (each PER DMAs and NPF prefetches).
+      wait_vm<(STAGES - 2) * (PER + NPF) + NPF>();
+      lds_barrier();
+      // The last step also reads k-tile kt+1's first fragments (for the
+      // last k-tile, from a stage it never uses).
+      if (SPREAD == 1)
+        kstep(NDP(), NPP(), fa[1], fb[1], fa[0], fb[0], ring[(kt + 1) % STAGES], 0, kt + STAGES, 0,
+              kt + STAGES + PFD);
+      else
+        kstep(NDP(), N0(), fa[1], fb[1], fa[0], fb[0], ring[(kt + 1) % STAGES], 0, kt + STAGES, 0, 0);
     }
+    wait_vm<0>();  // the zero fills past the end have landed before the ring is reused
     lds_barrier();  // every wave is done reading the ring (and no DMA is in flight) before staging
 
     // Epilogue, staged through the ring one 32-row block at a time (as in
