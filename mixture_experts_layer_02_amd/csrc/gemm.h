@@ -218,7 +218,7 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, const TileCtx& t,
       g = bf2f(reinterpret_cast<const uint16_t*>(p.gu_in)[gi]);
       u = bf2f(reinterpret_cast<const uint16_t*>(p.gu_in)[gi + p.N]);
     }
-    const float s = 1.0f / (1.0f + __expf(-g));
+    const float s = sigmoidf_(g);
     const float du = v * g * s;
     const float dg = v * u * s * (1.0f + g * (1.0f - s));
     if (p.c_f32) {
@@ -265,7 +265,7 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, const TileCtx& t
   } else if (EPI == EPI_SWIGLU) {
     float h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = v[e] / (1.0f + __expf(-v[e])) * v2[e];
+    for (int e = 0; e < 8; ++e) h[e] = v[e] * sigmoidf_(v[e]) * v2[e];
     Vec16<uint16_t>::store(reinterpret_cast<uint16_t*>(p.C) + row * p.ldc + col, h);
     if (p.gu_out) {
       uint16_t* gu = reinterpret_cast<uint16_t*>(p.gu_out) + row * (2 * (int64_t)p.N);
@@ -280,7 +280,7 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, const TileCtx& t
     Vec16<uint16_t>::load(gu + gi + p.N, u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float s = 1.0f / (1.0f + __expf(-g[e]));
+      const float s = sigmoidf_(g[e]);
       du[e] = v[e] * g[e] * s;
       dg[e] = v[e] * u[e] * s * (1.0f + g[e] * (1.0f - s));
     }

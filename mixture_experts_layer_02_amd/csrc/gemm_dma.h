@@ -67,6 +67,10 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      // Wait states: one for the LDS DMA reading M0 after its SALU write, five
+      // for a buffer instruction reading SGPRs a VALU op (readfirstlane,
+      // readlane) may have written just before this block.
+      "s_nop 3\n\t"
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -84,6 +88,7 @@ __device__ __forceinline__ void touch4(i32x4 rsrc, uint32_t voff, uint32_t soff,
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 3\n\t"  // as in dma16
       "buffer_load_dword %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -417,14 +422,22 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     wait_vm<0>();  // the zero fills past the end have landed before the ring is reused
     lds_barrier();  // every wave is done reading the ring (and no DMA is in flight) before staging
 
-    // Epilogue, staged through the ring one 32-row block at a time (as in
-    // gemm_mfma_kernel): acc[mi][ni][r] is C[row][col] with
+    // Epilogue, staged through the ring one 32-row block at a time: each
+    // wave writes its 32 x 128 block of acc[mi] to its own staging area and
+    // reads it back as row vectors of 8 columns.  The areas of the waves are
+    // disjoint and a wave's LDS accesses complete in order, so only the ring
+    // hand-offs need barriers (above, and after the last block).
+    //   acc[mi][ni][r] is C[row][col] with
     //   row = wm*128 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4, col = n-block base + lane%32.
     {
       constexpr int WC = NI * 32;
       constexpr int SP = WC + 4;
       float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 32 * SP;
       static_assert(4 * 32 * SP * 4 <= (int)sizeof(ring), "staging fits in the ring");
+      constexpr int OC = DUAL ? WC / 2 : WC;
+      constexpr int CPR = OC / 8;                 // 8-column vectors per row
+      constexpr int ITER = 32 * CPR / 64;         // vectors per lane per block
+      static_assert(32 * CPR % 64 == 0, "whole vectors per lane");
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -432,25 +445,27 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             stage[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SP + ni * 32 + (lane & 31)] = acc[mi][ni][r];
-        lds_barrier();
-        constexpr int OC = DUAL ? WC / 2 : WC;
-        constexpr int CPR = OC / 8;
-        for (int e = lane; e < 32 * CPR; e += 64) {
+        float v[ITER][8], v2[ITER][8];
+#pragma unroll
+        for (int it2 = 0; it2 < ITER; ++it2) {
+          const int e = lane + it2 * 64;
+          const int rl = e / CPR, cv = (e % CPR) * 8;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            v[it2][q] = stage[rl * SP + cv + q];
+            v2[it2][q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int it2 = 0; it2 < ITER; ++it2) {
+          const int e = lane + it2 * 64;
           const int rl = e / CPR, cv = (e % CPR) * 8;
           const int row = wm * 128 + mi * 32 + rl;
           const int col = (DUAL ? wn * 64 : wn * 128) + cv;
-          if (row < t.mlim && col < t.nlim) {
-            float v[8], v2[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              v[q] = stage[rl * SP + cv + q];
-              v2[q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
-            }
-            epi_store8<GRP, EPI>(p, t, row, col, v, v2);
-          }
+          if (row < t.mlim && col < t.nlim) epi_store8<GRP, EPI>(p, t, row, col, v[it2], v2[it2]);
         }
-        lds_barrier();
       }
+      lds_barrier();  // all staging reads are done before the next tile's DMA refills the ring
     }
   }
 }
