@@ -61,8 +61,12 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus());
   if (grid >= 8) grid -= grid % 8;
   if (grid <= 0) return hipSuccess;
-  if constexpr (std::is_same<AT, uint16_t>::value)
-    gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL><<<(unsigned)grid, 256, 0, s>>>(p);
+  if constexpr (std::is_same<AT, uint16_t>::value) {
+    if (EPI == EPI_STORE && p.c_f32)
+      gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true><<<(unsigned)grid, 256, 0, s>>>(p);
+    else
+      gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false><<<(unsigned)grid, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

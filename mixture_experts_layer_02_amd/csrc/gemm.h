@@ -290,6 +290,28 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, const TileCtx& t
   }
 }
 
+// Plain float store of 4 columns (EPI_STORE with a float C).
+template <int GRP>
+__device__ __forceinline__ void epi_store4f(const GemmParams& p, const TileCtx& t, int r, int c,
+                                            const float (&v)[4]) {
+  const int64_t row = t.m0 + r;
+  const int64_t col = (int64_t)t.n0 + c;
+  f32x4 o = {v[0], v[1], v[2], v[3]};
+  if (p.bias) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += p.bias[col + e];
+  }
+  int64_t crow = row;
+  void* Cb = p.C;
+  if (p.msplit && row >= p.msplit) {
+    crow = row - p.msplit;
+    Cb = p.C2;
+  }
+  int64_t off = crow * p.ldc + col;
+  if (GRP == GRP_K) off += (int64_t)t.g * p.c_gstride;
+  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Cb) + off) = o;
+}
+
 // Pointer to operand element (mn, k) for the current k-tile, honouring the
 // group offset, the K split and the layout.  Returns the base such that
 // element (mn_local, k_local) of the tile is base[mn_local*smn + k_local*sk].

@@ -171,20 +171,34 @@ __device__ __forceinline__ void wait_stages(int later) {
 }  // namespace dma
 
 // Requirements (checked by the host before choosing this kernel): bf16
-// operands, K-contiguous operands have K (or every k-tile) a multiple of 32.
-template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL>
+// operands, K-contiguous operands have K (or every k-tile) a multiple of 32,
+// msplit (if set) a multiple of 32.  CF32: C is float (EPI_STORE with
+// p.c_f32 set); a compile-time choice, so that one kernel holds one epilogue.
+//
+// Tiles are pipelined across tile boundaries: the last k-tiles of a tile
+// load the first k-tiles of the next one (positions past the end of a tile
+// continue in the next), so that the next tile's operands are in flight
+// while this tile's epilogue runs.  The epilogue stages through an LDS area
+// of its own and writes C with unconditional buffer stores (rows and columns
+// outside the tile fall outside the store resources), so that the number of
+// memory instructions it issues is a compile-time constant and the next
+// tile's first wait can let them stay in flight.
+template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
-  static_assert((BK == 32 && STAGES == 4) || (BK == 64 && STAGES == 2), "ring shapes of 128 KB");
+  static_assert(BK == 64 && STAGES == 2, "ring of two 64-wide k-tiles");
   constexpr int MI = 4, NI = 4;          // 32 x 32 blocks per wave (128 x 128)
   constexpr int TILE_ELEMS = 256 * BK;   // one operand tile
   constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
   constexpr int NJ = BK / 8;             // DMA instructions per wave per operand tile
   constexpr int KS = BK / 16;            // MFMA k-steps per k-tile
+  constexpr int WC = NI * 32;            // columns of a wave's block
+  constexpr int SP = WC + 4;             // staging row pitch (floats)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][STAGE_ELEMS];
   __shared__ int s_pref[MAXG + 1];
   __shared__ int s_scan[256];
+  __shared__ __attribute__((aligned(16))) float s_stage[4][8 * SP];
   __shared__ __attribute__((aligned(256))) uint32_t lds_junk[64];
 
   Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
@@ -197,15 +211,50 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   const uint16_t* Ag = reinterpret_cast<const uint16_t*>(p.A);
   const uint16_t* Bg = reinterpret_cast<const uint16_t*>(p.B);
   const uint16_t* B2g = reinterpret_cast<const uint16_t*>(p.B2);
+  const int run = (gridDim.x % 8) ? 1 : (int)gridDim.x / 8;
 
-  for (int it = 0;; ++it) {
-    const int id = xcd_tile(it, gridDim.x);
-    if (it * (int)gridDim.x >= sched.total) break;
-    if (id >= sched.total) continue;
-    const TileCtx t = sched.tile(p, s_pref, id);
+  // Per-lane DMA offsets (the same for every tile: the tile moves the
+  // resource bases) and the wave's B resource for dual K-contiguous B.
+  uint32_t va[NJ], vb[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    va[jj] = dma_voff<BK, ALAY, false>(wave * NJ + jj, lane, p.lda);
+    vb[jj] = dma_voff<BK, BLAY, DUAL>(wave * NJ + jj, lane, p.ldb);
+  }
+  const bool b_second = DUAL && wave >= 2;  // instructions j >= BK/4 read the second resource
+
+  // Load state of one output tile: buffer resources over its operand tiles,
+  // its k-tile count, and its L2 prefetch lane offsets.
+  struct Ld {
+    i32x4 ra, rb, rb2;
+    int nk;
+    uint32_t pa, pb;
+  };
+  // L2 prefetch: one instruction per wave per operand, each lane touching one
+  // 64-byte sector.  A tile is also loaded by the tiles of the same XCD that
+  // run at the same time and share it: the tiles of one n-tile and
+  // consecutive m-tiles share B, those of one m-tile and consecutive n-tiles
+  // share A (tiles are ordered m-fastest and an XCD takes RUN consecutive
+  // tiles per round).  The sectors of a shared tile are dealt round-robin
+  // over its C sharers, so that each is prefetched once per XCD: this tile
+  // takes sectors e = c + C*j, c = its own index modulo C.  Unassigned lanes
+  // get an offset outside every resource.
+  constexpr int NPF = 2;
+  constexpr int ITEMS = 8 * BK;  // 64-byte sectors of a 256 x BK operand tile
+  auto pf_voff = [&](int C, int c, int64_t ld, int lay, int parts) -> uint32_t {
+    const int wl = wave % (4 / parts);
+    const int e = c + C * (wl * 64 + lane);
+    if (e >= ITEMS / parts) return 0x7FFFFFF0u;
+    if (lay == LAY_K) {
+      constexpr int SPR = BK / 32;  // sectors per row
+      return (uint32_t)((e / SPR) * ld * 2 + (e % SPR) * 64);
+    }
+    return (uint32_t)((e >> 3) * ld * 2 + (e & 7) * 64);
+  };
+  auto setup = [&](const TileCtx& t) -> Ld {
+    Ld L;
     const int64_t klen = t.k1 - t.k0;
-    const int nk = (int)((klen + BK - 1) / BK);
-
+    L.nk = (int)((klen + BK - 1) / BK);
     const uint16_t* a_base = (ALAY == LAY_K) ? Ag + t.m0 * p.lda + t.k0 : Ag + t.k0 * p.lda + t.m0;
     const uint16_t* b_grp = Bg;
     const uint16_t* b2_grp = B2g;
@@ -213,100 +262,210 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       b_grp += (int64_t)t.g * p.b_gstride;
       if (B2g) b2_grp += (int64_t)t.g * p.b_gstride;
     }
-    // Buffer resources of this output tile.  K-contig: rows [0, lim) of the
-    // tile's row block; MN-contig: k-rows [0, klen) from column m0/n0 (the
-    // range ends with row k1-1, so it never runs past the allocation).
+    // K-contig: rows [0, lim) of the tile's row block; MN-contig: k-rows
+    // [0, klen) from column m0/n0 (the range ends with row k1-1, so it never
+    // runs past the allocation).
     const int nlim_b = DUAL ? min(t.nlim, BN / 2) : t.nlim;
-    const i32x4 ra = (ALAY == LAY_K) ? make_rsrc(a_base, (uint64_t)t.mlim * p.lda * 2)
-                                     : make_rsrc(a_base, (uint64_t)(klen * p.lda - t.m0) * 2);
-    i32x4 rb, rb2;
+    L.ra = (ALAY == LAY_K) ? make_rsrc(a_base, (uint64_t)t.mlim * p.lda * 2)
+                           : make_rsrc(a_base, (uint64_t)(klen * p.lda - t.m0) * 2);
     if (BLAY == LAY_K) {
-      rb = make_rsrc(b_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2);
-      rb2 = DUAL ? make_rsrc(b2_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2) : rb;
+      L.rb = make_rsrc(b_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2);
+      L.rb2 = DUAL ? make_rsrc(b2_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2) : L.rb;
     } else if (p.ksplit) {  // k < ksplit from B, k >= ksplit from B2 (GRP_M: t.k0 = 0)
-      rb = make_rsrc(b_grp + t.n0, (uint64_t)((int64_t)p.ksplit * p.ldb - t.n0) * 2);
-      rb2 = make_rsrc(b2_grp + t.n0, (uint64_t)((klen - p.ksplit) * p.ldb - t.n0) * 2);
+      L.rb = make_rsrc(b_grp + t.n0, (uint64_t)((int64_t)p.ksplit * p.ldb - t.n0) * 2);
+      L.rb2 = make_rsrc(b2_grp + t.n0, (uint64_t)((klen - p.ksplit) * p.ldb - t.n0) * 2);
     } else {
-      rb = make_rsrc(b_grp + t.k0 * p.ldb + t.n0, (uint64_t)(klen * p.ldb - t.n0) * 2);
-      rb2 = rb;
+      L.rb = make_rsrc(b_grp + t.k0 * p.ldb + t.n0, (uint64_t)(klen * p.ldb - t.n0) * 2);
+      L.rb2 = L.rb;
     }
-    uint32_t va[NJ], vb[NJ];
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      va[jj] = dma_voff<BK, ALAY, false>(wave * NJ + jj, lane, p.lda);
-      vb[jj] = dma_voff<BK, BLAY, DUAL>(wave * NJ + jj, lane, p.ldb);
-    }
-    // K-contig dual: instructions j >= BK/4 (waves 2, 3) read the second resource.
-    const bool b_second = DUAL && wave >= 2;
-    // DMA instruction q (0 .. 2*NJ-1) of k-tile kt: even q are A tiles, odd q B tiles.
-    auto dma_one = [&](int kt, int q) {
-      uint16_t* st = ring[kt % STAGES];
-      const int jj = q >> 1;
-      const int j = wave * NJ + jj;
-      if ((q & 1) == 0) {
-        const uint32_t so_a = (ALAY == LAY_K) ? (uint32_t)kt * BK * 2 : (uint32_t)((int64_t)kt * BK * p.lda * 2);
-        dma16(ra, va[jj], so_a, st + j * 512);
-      } else {
-        i32x4 rbk = b_second ? rb2 : rb;
-        uint32_t so_b;
-        if (BLAY == LAY_K) {
-          so_b = (uint32_t)kt * BK * 2;
-        } else if (p.ksplit && (int64_t)kt * BK >= p.ksplit) {
-          rbk = rb2;
-          so_b = (uint32_t)(((int64_t)kt * BK - p.ksplit) * p.ldb * 2);
-        } else {
-          so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
-        }
-        dma16(rbk, vb[jj], so_b, st + TILE_ELEMS + j * 512);
-      }
-    };
-
-    // L2 prefetch of k-tile pkt, one instruction per wave per operand, each
-    // lane touching one 64-byte sector.  A tile is also loaded by the tiles
-    // of the same XCD that run at the same time and share it: the tiles of
-    // one n-tile and consecutive m-tiles share B, those of one m-tile and
-    // consecutive n-tiles share A (tiles are ordered m-fastest and an XCD
-    // takes RUN consecutive tiles per round).  The sectors of a shared tile
-    // are dealt round-robin over its C sharers, so that each is prefetched
-    // once per XCD: this tile takes sectors e = c + C*j, c = its own index
-    // modulo C.  Unassigned lanes get an offset outside every resource.
-    constexpr int NPF = 2;
-    constexpr int ITEMS = 8 * BK;  // 64-byte sectors of a 256 x BK operand tile
-    const int run = (gridDim.x % 8) ? 1 : (int)gridDim.x / 8;
     const int cB = max(1, min(t.mtiles, run));
     const int cA = max(1, min(sched.NT, run / max(t.mtiles, 1)));
-    auto pf_voff = [&](int C, int c, int64_t ld, int lay, int parts) -> uint32_t {
-      const int wl = wave % (4 / parts);
-      const int e = c + C * (wl * 64 + lane);
-      if (e >= ITEMS / parts) return 0x7FFFFFF0u;
-      if (lay == LAY_K) {
-        constexpr int SPR = BK / 32;  // sectors per row
-        return (uint32_t)((e / SPR) * ld * 2 + (e % SPR) * 64);
-      }
-      return (uint32_t)((e >> 3) * ld * 2 + (e & 7) * 64);
-    };
-    const uint32_t pa = pf_voff(cA, t.ntile % cA, p.lda, ALAY, 1);
-    const uint32_t pb = pf_voff(cB, t.mtile % cB, p.ldb, BLAY, DUAL ? 2 : 1);
-    auto pf_one = [&](int kt, int o) {
-      if (o == 0) {
-        const uint32_t so_a = (ALAY == LAY_K) ? (uint32_t)kt * BK * 2 : (uint32_t)((int64_t)kt * BK * p.lda * 2);
-        touch4(ra, pa, so_a, lds_junk);
-      } else {
-        i32x4 rbk = b_second ? rb2 : rb;
-        uint32_t so_b;
-        if (BLAY == LAY_K) {
-          so_b = (uint32_t)kt * BK * 2;
-        } else if (p.ksplit && (int64_t)kt * BK >= p.ksplit) {
-          rbk = rb2;
-          so_b = (uint32_t)(((int64_t)kt * BK - p.ksplit) * p.ldb * 2);
-        } else {
-          so_b = (uint32_t)((int64_t)kt * BK * p.ldb * 2);
-        }
-        touch4(rbk, pb, so_b, lds_junk);
-      }
-    };
+    L.pa = pf_voff(cA, t.ntile % cA, p.lda, ALAY, 1);
+    L.pb = pf_voff(cB, t.mtile % cB, p.ldb, BLAY, DUAL ? 2 : 1);
+    return L;
+  };
+  Ld null_ld;  // loads nothing: every offset is outside its resources
+  null_ld.ra = null_ld.rb = null_ld.rb2 = make_rsrc(Ag, 0);
+  null_ld.nk = 0;
+  null_ld.pa = null_ld.pb = 0x7FFFFFF0u;
 
-    f32x16 acc[MI][NI];
+  // B resource and scalar offset of k-tile k of a tile.
+  auto b_src = [&](const Ld& L, int k, i32x4& rbk, uint32_t& so_b) {
+    rbk = b_second ? L.rb2 : L.rb;
+    if (BLAY == LAY_K) {
+      so_b = (uint32_t)k * BK * 2;
+    } else if (p.ksplit && (int64_t)k * BK >= p.ksplit) {
+      rbk = L.rb2;
+      so_b = (uint32_t)(((int64_t)k * BK - p.ksplit) * p.ldb * 2);
+    } else {
+      so_b = (uint32_t)((int64_t)k * BK * p.ldb * 2);
+    }
+  };
+  auto a_so = [&](int k) -> uint32_t {
+    return (ALAY == LAY_K) ? (uint32_t)k * BK * 2 : (uint32_t)((int64_t)k * BK * p.lda * 2);
+  };
+
+  // Current and next tile.  A ring position is a k-tile of the current tile
+  // (pos < cur.nk) or of the next one (pos - cur.nk); positions past both are
+  // loads of nothing.  Ring stage of a position: (gbase + pos) % STAGES.
+  int it = 0;
+  int id = xcd_tile(0, gridDim.x);
+  if ((int)gridDim.x * 0 >= sched.total || id >= sched.total) return;
+  TileCtx t = sched.tile(p, s_pref, id);
+  Ld cur = setup(t);
+  Ld nxt = null_ld;
+  int gbase = 0;
+  bool primed = false;  // cur's k-tiles 0 and 1 are issued, k-tile 0 has landed and its first fragments are read
+
+  auto pick = [&](int pos, int& k) -> Ld {
+    const bool c = pos < cur.nk;
+    k = c ? pos : pos - cur.nk;
+    Ld L;
+    L.ra = c ? cur.ra : nxt.ra;
+    L.rb = c ? cur.rb : nxt.rb;
+    L.rb2 = c ? cur.rb2 : nxt.rb2;
+    L.pa = c ? cur.pa : nxt.pa;
+    L.pb = c ? cur.pb : nxt.pb;
+    L.nk = 0;
+    return L;
+  };
+  // DMA instruction q (0 .. 2*NJ-1) of ring position pos: even q are A, odd q B.
+  auto dma_one = [&](int pos, int q) {
+    int k;
+    const Ld L = pick(pos, k);
+    uint16_t* st = ring[(gbase + pos) % STAGES];
+    const int jj = q >> 1;
+    const int j = wave * NJ + jj;
+    if ((q & 1) == 0) {
+      dma16(L.ra, va[jj], a_so(k), st + j * 512);
+    } else {
+      i32x4 rbk;
+      uint32_t so_b;
+      b_src(L, k, rbk, so_b);
+      dma16(rbk, vb[jj], so_b, st + TILE_ELEMS + j * 512);
+    }
+  };
+  // L2 prefetch instruction o (0: A, 1: B) of ring position pos.
+  auto pf_one = [&](int pos, int o) {
+    int k;
+    const Ld L = pick(pos, k);
+    if (o == 0) {
+      touch4(L.ra, L.pa, a_so(k), lds_junk);
+    } else {
+      i32x4 rbk;
+      uint32_t so_b;
+      b_src(L, k, rbk, so_b);
+      touch4(rbk, L.pb, so_b, lds_junk);
+    }
+  };
+
+  f32x16 acc[MI][NI];
+  // Fragment f (0 .. MI+NI-1) of k-step kk of a ring stage, in the order the
+  // MFMAs (mi-major) first use them: A0, B0 .. B3, A1 .. A3.
+  auto read_frag = [&](const uint16_t* st, int kk, int f, bf16x8(&a)[MI], bf16x8(&b)[NI]) {
+    static_assert(MI == 4 && NI == 4, "fragment order");
+    if (f == 0 || f > NI) {
+      const int mi = f == 0 ? 0 : f - NI;
+      a[mi] = frag<BK, ALAY>(st, wm * 128 + mi * 32, kk, lane);
+    } else {
+      const int ni = f - 1;
+      const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
+      b[ni] = frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
+    }
+  };
+  // One k-step: the 16 MFMAs of fragments (a, b), with, in between, the
+  // reads of the next k-step's fragments (stage rst, step rkk), ND DMA
+  // instructions q0 .. q0+ND-1 of position dpos and then NP L2 prefetches of
+  // position ppos, spread evenly.  The scheduling barriers pin this order, so
+  // that the DMA issue never comes as a burst that would stall the wave's
+  // MFMAs behind a full address queue.
+  auto kstep = [&](auto nd_c, auto np_c, const bf16x8(&a)[MI], const bf16x8(&b)[NI], bf16x8(&na)[MI],
+                   bf16x8(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos) {
+    constexpr int ND = decltype(nd_c)::value;
+    constexpr int NO = ND + decltype(np_c)::value;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mi = i / NI, ni = i % NI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+      if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
+#pragma unroll
+      for (int o = (i * NO) / 16; o < ((i + 1) * NO) / 16; ++o) {
+        if (o < ND) dma_one(dpos, q0 + o);
+        else pf_one(ppos, o - ND);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Per k-tile kt: step 0 issues the second half of position kt+1 (except
+  // for the first k-tile, whose position 1 is issued whole beforehand) and
+  // the prefetch of position kt+1+PFD; steps 1 .. KS-2 only compute; then
+  // position kt+1 is waited for (one barrier per k-tile); the last step reads
+  // position kt+1's first fragments and issues the first half of position
+  // kt+2 (the last k-tile issues it whole, before the epilogue).
+  constexpr int PER = 2 * NJ;
+  constexpr int PART = PER / 2;
+  constexpr int PFD = 2;
+  // Memory instructions per lane of one epilogue (the buffer stores and
+  // loads below, all unconditional).
+  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? 128 : (CF32 ? 64 : 32);
+  constexpr int FIRST_N_PRIMED = EPI_OPS + NPF > 63 ? 63 : EPI_OPS + NPF;
+  using N0 = std::integral_constant<int, 0>;
+  using NDP = std::integral_constant<int, PART>;
+  using NDF = std::integral_constant<int, PER>;
+  using NPP = std::integral_constant<int, NPF>;
+  bf16x8 fa[2][MI], fb[2][NI];
+
+  auto ktile = [&](int kt, auto first_c, auto last_c) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    const uint16_t* st = ring[(gbase + kt) % STAGES];
+#pragma unroll
+    for (int s = 0; s < KS - 1; ++s) {
+      if (s == 0) {
+        if (FIRST)
+          kstep(N0(), NPP(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD);
+        else
+          kstep(NDP(), NPP(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
+      } else {
+        kstep(N0(), N0(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
+      }
+    }
+    // Position kt+1 has landed: after its last DMA come only its prefetches,
+    // or, for a first k-tile primed by the previous tile, that tile's
+    // epilogue and then the prefetches.
+    if (FIRST && primed) wait_vm<FIRST_N_PRIMED>();
+    else wait_vm<NPF>();
+    lds_barrier();
+    const uint16_t* nst = ring[(gbase + kt + 1) % STAGES];
+    if (LAST)
+      kstep(NDF(), N0(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
+    else
+      kstep(NDP(), N0(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
+  };
+
+  // Epilogue resources: C (or C2 for rows past msplit) from the tile's
+  // corner, with rows [0, mlim) in range; per-lane offsets of columns past
+  // nlim lie outside.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  auto c_rsrc = [&](const void* base, int64_t ld_elems, int esz) -> __amdgpu_buffer_rsrc_t {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)((int64_t)t.mlim * ld_elems * esz), 0x00020000);
+  };
+
+  for (;;) {
+    // The next tile of this workgroup, loaded ahead if it is long enough.
+    const int idn = xcd_tile(it + 1, gridDim.x);
+    const bool has_next = (it + 1) * (int)gridDim.x < sched.total && idn < sched.total;
+    TileCtx tn = t;
+    Ld lnext = null_ld;
+    if (has_next) {
+      tn = sched.tile(p, s_pref, idn);
+      lnext = setup(tn);
+    }
+    const bool pipe = has_next && lnext.nk >= STAGES && cur.nk >= 1;
+    nxt = pipe ? lnext : null_ld;
+
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -314,160 +473,173 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Fragment f (0 .. MI+NI-1) of k-step kk of a ring stage, in the order the
-    // MFMAs (mi-major) first use them: A0, B0 .. B3, A1 .. A3.
-    auto read_frag = [&](const uint16_t* st, int kk, int f, bf16x8(&a)[MI], bf16x8(&b)[NI]) {
-      static_assert(MI == 4 && NI == 4, "fragment order");
-      if (f == 0 || f > NI) {
-        const int mi = f == 0 ? 0 : f - NI;
-        a[mi] = frag<BK, ALAY>(st, wm * 128 + mi * 32, kk, lane);
+    if (cur.nk > 0) {
+      if (!primed) {
+        // Positions 0 and 1 whole, with position 0's prefetch in between.
+#pragma unroll
+        for (int q = 0; q < PER; ++q) dma_one(0, q);
+#pragma unroll
+        for (int o = 0; o < NPF; ++o) pf_one(PFD, o);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) dma_one(1, q);
+        wait_vm<PER + NPF>();  // position 0 has landed (then come its prefetch and position 1)
+        lds_barrier();
+#pragma unroll
+        for (int f = 0; f < MI + NI; ++f) read_frag(ring[gbase % STAGES], 0, f, fa[0], fb[0]);
+      }
+      if (cur.nk == 1) {
+        ktile(0, std::true_type(), std::true_type());
       } else {
-        const int ni = f - 1;
-        const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
-        b[ni] = frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
+        ktile(0, std::true_type(), std::false_type());
+        for (int kt = 1; kt < cur.nk - 1; ++kt) ktile(kt, std::false_type(), std::false_type());
+        ktile(cur.nk - 1, std::false_type(), std::true_type());
       }
-    };
-
-    // One k-step: the 16 MFMAs of fragments (a, b), with, in between, the
-    // reads of the next k-step's fragments (stage rst, step rkk), ND DMA
-    // instructions q0 .. q0+ND-1 of k-tile dkt and then NP L2 prefetches of
-    // k-tile pkt, spread evenly.  The scheduling barriers pin this order, so
-    // that the DMA issue never comes as a burst that would stall the wave's
-    // MFMAs behind a full address queue.
-    auto kstep = [&](auto nd_c, auto np_c, const bf16x8(&a)[MI], const bf16x8(&b)[NI], bf16x8(&na)[MI],
-                     bf16x8(&nb)[NI], const uint16_t* rst, int rkk, int dkt, int q0, int pkt) {
-      constexpr int ND = decltype(nd_c)::value;
-      constexpr int NO = ND + decltype(np_c)::value;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int mi = i / NI, ni = i % NI;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-        if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
-#pragma unroll
-        for (int o = (i * NO) / 16; o < ((i + 1) * NO) / 16; ++o) {
-          if (o < ND) dma_one(dkt, q0 + o);
-          else pf_one(pkt, o - ND);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    // Pipeline.  While k-tile kt is consumed, k-tiles kt+1 .. kt+STAGES-1
-    // are in flight.  A k-tile is KS k-steps; each step's MFMAs overlap the
-    // LDS reads of the next step.  Before the last step of k-tile kt,
-    // k-tile kt+1 is waited for (one barrier per k-tile); the stage of
-    // k-tile kt, now fully read, is then refilled with k-tile kt+STAGES,
-    // whose PER DMA instructions per wave are spread over the last step of
-    // kt and the first SPREAD-1 steps of kt+1 (all before the next barrier).
-    // Right after the last of them, NPF prefetches start the L2 fill of
-    // k-tile kt+STAGES+PFD, so that its DMA, PFD k-tiles later, hits in L2;
-    // a barrier's wait leaves these prefetches in flight (they are the only
-    // loads issued after the awaited k-tile), and they have until the next
-    // barrier to land.
-    // The schedule is the same for every k-tile: k-tiles past the end
-    // (kt >= nk) are loaded too, as zero fills of a stage that is never read
-    // again (their offsets lie outside the buffer resources, so they touch
-    // no memory), which keeps the loop body free of branches.
-    constexpr int PER = 2 * NJ;
-    constexpr int SPREAD = KS >= 2 ? 2 : 1;
-    constexpr int PART = PER / SPREAD;
-    constexpr int PFD = 2;
-    static_assert(PER % SPREAD == 0 && SPREAD <= KS, "a stage's DMA is issued before the next barrier");
-    using N0 = std::integral_constant<int, 0>;
-    using NDP = std::integral_constant<int, PART>;
-    using NPP = std::integral_constant<int, NPF>;
-    bf16x8 fa[2][MI], fb[2][NI];
-    if (nk > 0) {
-      // The same issue pattern as the loop: each stage's DMAs, then the
-      // prefetches of the k-tile PFD further on.
-#pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) dma_one(s, q);
-#pragma unroll
-        for (int o = 0; o < NPF; ++o) pf_one(s + PFD, o);
-      }
-#pragma unroll
-      for (int q = 0; q < PART; ++q) dma_one(STAGES - 1, q);
-      wait_vm<NPF + (STAGES - 2) * (PER + NPF) + PART>();  // k-tile 0 has landed
-      lds_barrier();
-#pragma unroll
-      for (int f = 0; f < MI + NI; ++f) read_frag(ring[0], 0, f, fa[0], fb[0]);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* st = ring[kt % STAGES];
-#pragma unroll
-      for (int s = 0; s < KS - 1; ++s) {
-        if (s + 2 < SPREAD)
-          kstep(NDP(), N0(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, kt - 1 + STAGES,
-                (s + 1) * PART, 0);
-        else if (s + 2 == SPREAD)
-          kstep(NDP(), NPP(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1,
-                kt - 1 + STAGES, (s + 1) * PART, kt - 1 + STAGES + PFD);
-        else
-          kstep(N0(), N0(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
-      }
-      // k-tile kt+1 has landed: after its last DMA come only its prefetches
-      // and the later stages (each PER DMAs and NPF prefetches).
-      wait_vm<(STAGES - 2) * (PER + NPF) + NPF>();
-      lds_barrier();
-      // The last step also reads k-tile kt+1's first fragments (for the
-      // last k-tile, from a stage it never uses).
-      if (SPREAD == 1)
-        kstep(NDP(), NPP(), fa[1], fb[1], fa[0], fb[0], ring[(kt + 1) % STAGES], 0, kt + STAGES, 0,
-              kt + STAGES + PFD);
-      else
-        kstep(NDP(), N0(), fa[1], fb[1], fa[0], fb[0], ring[(kt + 1) % STAGES], 0, kt + STAGES, 0, 0);
-    }
-    wait_vm<0>();  // the zero fills past the end have landed before the ring is reused
-    lds_barrier();  // every wave is done reading the ring (and no DMA is in flight) before staging
 
-    // Epilogue, staged through the ring one 32-row block at a time: each
-    // wave writes its 32 x 128 block of acc[mi] to its own staging area and
-    // reads it back as row vectors of 8 columns.  The areas of the waves are
-    // disjoint and a wave's LDS accesses complete in order, so only the ring
-    // hand-offs need barriers (above, and after the last block).
+    // Epilogue.  Each wave stages its 32 x 128 block acc[mi] eight rows at a
+    // time (rows s*8 .. s*8+7 hold acc[mi][ni][4s .. 4s+3]) in its own LDS
+    // area and reads them back as row vectors of W columns (16 bytes of
+    // output: 8 bf16 or 4 float), so that consecutive lanes store
+    // consecutive 16-byte pieces of a row.  A wave's LDS accesses complete
+    // in order and the areas are disjoint, so no barrier is needed.
     //   acc[mi][ni][r] is C[row][col] with
     //   row = wm*128 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4, col = n-block base + lane%32.
     {
-      constexpr int WC = NI * 32;
-      constexpr int SP = WC + 4;
-      float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 32 * SP;
-      static_assert(4 * 32 * SP * 4 <= (int)sizeof(ring), "staging fits in the ring");
+      float* stage = s_stage[wave];
       constexpr int OC = DUAL ? WC / 2 : WC;
-      constexpr int CPR = OC / 8;                 // 8-column vectors per row
-      constexpr int ITER = 32 * CPR / 64;         // vectors per lane per block
-      static_assert(32 * CPR % 64 == 0, "whole vectors per lane");
+      constexpr int W = (EPI == EPI_STORE && CF32) ? 4 : 8;
+      constexpr int CPR = OC / W;               // vectors per row
+      constexpr int VPL = 8 * CPR / 64;          // vectors per lane per slab
+      static_assert(8 * CPR % 64 == 0, "whole vectors per lane");
+      const int col_base = (DUAL ? wn * 64 : wn * 128);
+      // Resources (row 0 = the tile's first row, element 0 = its first column).
+      const int64_t m0g = t.m0;
+      __amdgpu_buffer_rsrc_t r0, r1, r2;
+      int64_t ldo = p.ldc;
+      if (EPI == EPI_STORE) {
+        const int esz = CF32 ? 4 : 2;
+        char* cb = reinterpret_cast<char*>(p.C);
+        char* cb2 = reinterpret_cast<char*>(p.C2);
+        const int64_t gof = (GRP == GRP_K) ? (int64_t)t.g * p.c_gstride : 0;
+        r0 = c_rsrc(cb + ((m0g * p.ldc + t.n0 + gof) * esz), p.ldc, esz);
+        // C2 rows start at msplit: row r of the tile is C2 row m0 + r - msplit.
+        r1 = p.msplit ? c_rsrc(cb2 + (((m0g - p.msplit) * p.ldc + t.n0 + gof) * esz), p.ldc, esz) : r0;
+        r2 = r0;
+      } else if (EPI == EPI_SWIGLU) {
+        // h [rows][N] in C; G | U [rows][2N] in gu_out (if saved).
+        r0 = c_rsrc(reinterpret_cast<char*>(p.C) + (m0g * p.ldc + t.n0) * 2, p.ldc, 2);
+        char* gub = reinterpret_cast<char*>(p.gu_out);
+        const int64_t ld2 = 2 * (int64_t)p.N;
+        r1 = gub ? c_rsrc(gub + (m0g * ld2 + t.n0) * 2, ld2, 2)
+                 : __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(p.C), (short)0, 0, 0x00020000);
+        r2 = r1;
+        ldo = ld2;
+      } else {
+        // dG | dU [rows][2N] in C, from dH and G | U [rows][2N] in gu_in.
+        const int64_t ld2 = 2 * (int64_t)p.N;
+        r0 = c_rsrc(reinterpret_cast<char*>(p.C) + (m0g * ld2 + t.n0) * 2, ld2, 2);
+        r1 = c_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.gu_in)) + (m0g * ld2 + t.n0) * 2, ld2, 2);
+        r2 = r0;
+        ldo = ld2;
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
+        const int rowb = wm * 128 + mi * 32;  // the block's first row in the tile
+        // Rows of this block lie on one side of msplit (a multiple of 32).
+        const bool side2 = EPI == EPI_STORE && p.msplit && m0g + rowb >= p.msplit;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
+        for (int sl = 0; sl < 4; ++sl) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            stage[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SP + ni * 32 + (lane & 31)] = acc[mi][ni][r];
-        float v[ITER][8], v2[ITER][8];
+          for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int it2 = 0; it2 < ITER; ++it2) {
-          const int e = lane + it2 * 64;
-          const int rl = e / CPR, cv = (e % CPR) * 8;
+            for (int r4 = 0; r4 < 4; ++r4)
+              stage[((lane >> 5) * 4 + r4) * SP + ni * 32 + (lane & 31)] = acc[mi][ni][sl * 4 + r4];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            v[it2][q] = stage[rl * SP + cv + q];
-            v2[it2][q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+          for (int vi = 0; vi < VPL; ++vi) {
+            const int e = lane + vi * 64;
+            const int rl = e / CPR, cv = (e % CPR) * W;
+            float v[W], v2[W];
+#pragma unroll
+            for (int q = 0; q < W; ++q) {
+              v[q] = stage[rl * SP + cv + q];
+              v2[q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+            }
+            const int row = rowb + sl * 8 + rl;  // row in the tile
+            const int col = col_base + cv;       // column in the tile
+            const bool ok = col < t.nlim;
+            const int64_t eo = (int64_t)row * ldo + col;  // element offset from the corner
+            if (EPI == EPI_STORE) {
+              if (CF32) {
+                float o[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = v[q];
+                if (p.bias) {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
+                }
+                const u32x4_t d = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                   __float_as_uint(o[3])};
+                __builtin_amdgcn_raw_buffer_store_b128(d, side2 ? r1 : r0, ok ? (uint32_t)(eo * 4) : 0x80000000u, 0, 0);
+              } else {
+                float o[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) o[q] = v[q];
+                if (p.bias) {
+#pragma unroll
+                  for (int q = 0; q < 8; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
+                }
+                const u32x4_t d = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]),
+                                   pack_bf2(o[6], o[7])};
+                __builtin_amdgcn_raw_buffer_store_b128(d, side2 ? r1 : r0, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+              }
+            } else if (EPI == EPI_SWIGLU) {
+              float h[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) h[q] = v[q] * sigmoidf_(v[q]) * v2[q];
+              const u32x4_t dh = {pack_bf2(h[0], h[1]), pack_bf2(h[2], h[3]), pack_bf2(h[4], h[5]), pack_bf2(h[6], h[7])};
+              const u32x4_t dg = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+              const u32x4_t du = {pack_bf2(v2[0], v2[1]), pack_bf2(v2[2], v2[3]), pack_bf2(v2[4], v2[5]),
+                                  pack_bf2(v2[6], v2[7])};
+              const int64_t eh = (int64_t)row * p.ldc + col;
+              __builtin_amdgcn_raw_buffer_store_b128(dh, r0, ok ? (uint32_t)(eh * 2) : 0x80000000u, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(dg, r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(du, r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
+            } else {  // EPI_SWIGLU_BWD: v = dH
+              const uint32_t og = ok ? (uint32_t)(eo * 2) : 0x80000000u;
+              const uint32_t ou = ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u;
+              const u32x4_t gq = __builtin_amdgcn_raw_buffer_load_b128(r1, og, 0, 0);
+              const u32x4_t uq = __builtin_amdgcn_raw_buffer_load_b128(r1, ou, 0, 0);
+              float dg[8], du[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const uint32_t gw = gq[q >> 1], uw = uq[q >> 1];
+                const float g = __uint_as_float((q & 1) ? (gw & 0xffff0000u) : (gw << 16));
+                const float u = __uint_as_float((q & 1) ? (uw & 0xffff0000u) : (uw << 16));
+                const float sg = sigmoidf_(g);
+                du[q] = v[q] * g * sg;
+                dg[q] = v[q] * u * sg * (1.0f + g * (1.0f - sg));
+              }
+              const u32x4_t ddg = {pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]), pack_bf2(dg[4], dg[5]),
+                                   pack_bf2(dg[6], dg[7])};
+              const u32x4_t ddu = {pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]), pack_bf2(du[4], du[5]),
+                                   pack_bf2(du[6], du[7])};
+              __builtin_amdgcn_raw_buffer_store_b128(ddg, r0, og, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(ddu, r0, ou, 0, 0);
+            }
           }
         }
-#pragma unroll
-        for (int it2 = 0; it2 < ITER; ++it2) {
-          const int e = lane + it2 * 64;
-          const int rl = e / CPR, cv = (e % CPR) * 8;
-          const int row = wm * 128 + mi * 32 + rl;
-          const int col = (DUAL ? wn * 64 : wn * 128) + cv;
-          if (row < t.mlim && col < t.nlim) epi_store8<GRP, EPI>(p, t, row, col, v[it2], v2[it2]);
-        }
       }
-      lds_barrier();  // all staging reads are done before the next tile's DMA refills the ring
     }
+
+    // Advance to the next tile.
+    gbase += cur.nk;
+    ++it;
+    if (!has_next) break;
+    t = tn;
+    cur = pipe ? nxt : lnext;
+    primed = pipe;
   }
+  wait_vm<0>();  // no LDS DMA may land after the workgroup ends
 }
 
 }  // namespace moe
