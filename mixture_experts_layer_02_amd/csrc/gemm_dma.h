@@ -60,21 +60,17 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
 // LDS byte address lds_dst + 16 i.  Issued through inline asm so that the
 // compiler neither waits for it before unrelated LDS reads nor before
 // barriers: the kernel waits for it explicitly (wait_vm) where a ring stage
-// is consumed.  M0 (the LDS base of the copy) is saved and restored around it.
+// is consumed.  M0 (the LDS base of the copy) is an operand of the asm.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint16_t* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
       // Wait states: one for the LDS DMA reading M0 after its SALU write, five
       // for a buffer instruction reading SGPRs a VALU op (readfirstlane,
       // readlane) may have written just before this block.
-      "s_nop 3\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
       : "memory");
 }
 
@@ -84,15 +80,11 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
 // it; an offset outside the resource reads nothing.
 __device__ __forceinline__ void touch4(i32x4 rsrc, uint32_t voff, uint32_t soff, const uint32_t* lds_junk) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_junk);
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 3\n\t"  // as in dma16
-      "buffer_load_dword %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      "s_nop 4\n\t"  // as in dma16
+      "buffer_load_dword %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
       : "memory");
 }
 
@@ -317,7 +309,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   int gbase = 0;
   bool primed = false;  // cur's k-tiles 0 and 1 are issued, k-tile 0 has landed and its first fragments are read
 
-  auto pick = [&](int pos, int& k) -> Ld {
+  // PURE: the position is known to be one of the current tile's.
+  auto pick = [&](int pos, int& k, auto pure_c) -> Ld {
+    if (decltype(pure_c)::value) {
+      k = pos;
+      return cur;
+    }
     const bool c = pos < cur.nk;
     k = c ? pos : pos - cur.nk;
     Ld L;
@@ -330,9 +327,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     return L;
   };
   // DMA instruction q (0 .. 2*NJ-1) of ring position pos: even q are A, odd q B.
-  auto dma_one = [&](int pos, int q) {
+  auto dma_one = [&](int pos, int q, auto pure_c) {
     int k;
-    const Ld L = pick(pos, k);
+    const Ld L = pick(pos, k, pure_c);
     uint16_t* st = ring[(gbase + pos) % STAGES];
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
@@ -346,9 +343,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
   };
   // L2 prefetch instruction o (0: A, 1: B) of ring position pos.
-  auto pf_one = [&](int pos, int o) {
+  auto pf_one = [&](int pos, int o, auto pure_c) {
     int k;
-    const Ld L = pick(pos, k);
+    const Ld L = pick(pos, k, pure_c);
     if (o == 0) {
       touch4(L.ra, L.pa, a_so(k), lds_junk);
     } else {
@@ -379,8 +376,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // position ppos, spread evenly.  The scheduling barriers pin this order, so
   // that the DMA issue never comes as a burst that would stall the wave's
   // MFMAs behind a full address queue.
-  auto kstep = [&](auto nd_c, auto np_c, const bf16x8(&a)[MI], const bf16x8(&b)[NI], bf16x8(&na)[MI],
-                   bf16x8(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos) {
+  auto kstep = [&](auto nd_c, auto np_c, auto pure_c, const bf16x8(&a)[MI], const bf16x8(&b)[NI],
+                   bf16x8(&na)[MI], bf16x8(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos) {
     constexpr int ND = decltype(nd_c)::value;
     constexpr int NO = ND + decltype(np_c)::value;
 #pragma unroll
@@ -390,8 +387,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
 #pragma unroll
       for (int o = (i * NO) / 16; o < ((i + 1) * NO) / 16; ++o) {
-        if (o < ND) dma_one(dpos, q0 + o);
-        else pf_one(ppos, o - ND);
+        if (o < ND) dma_one(dpos, q0 + o, pure_c);
+        else pf_one(ppos, o - ND, pure_c);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -416,19 +413,21 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using NPP = std::integral_constant<int, NPF>;
   bf16x8 fa[2][MI], fb[2][NI];
 
-  auto ktile = [&](int kt, auto first_c, auto last_c) {
+  // PURE: every position the k-tile loads (kt+1 .. kt+1+PFD) is the current tile's.
+  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
+    using PU = decltype(pure_c);
     const uint16_t* st = ring[(gbase + kt) % STAGES];
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
       if (s == 0) {
         if (FIRST)
-          kstep(N0(), NPP(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD);
+          kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD);
         else
-          kstep(NDP(), NPP(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
+          kstep(NDP(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
       } else {
-        kstep(N0(), N0(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
+        kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
       }
     }
     // Position kt+1 has landed: after its last DMA come only its prefetches,
@@ -439,9 +438,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     lds_barrier();
     const uint16_t* nst = ring[(gbase + kt + 1) % STAGES];
     if (LAST)
-      kstep(NDF(), N0(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
+      kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
     else
-      kstep(NDP(), N0(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
+      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
   };
 
   // Epilogue resources: C (or C2 for rows past msplit) from the tile's
@@ -477,22 +476,27 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       if (!primed) {
         // Positions 0 and 1 whole, with position 0's prefetch in between.
 #pragma unroll
-        for (int q = 0; q < PER; ++q) dma_one(0, q);
+        for (int q = 0; q < PER; ++q) dma_one(0, q, std::false_type());
 #pragma unroll
-        for (int o = 0; o < NPF; ++o) pf_one(PFD, o);
+        for (int o = 0; o < NPF; ++o) pf_one(PFD, o, std::false_type());
 #pragma unroll
-        for (int q = 0; q < PER; ++q) dma_one(1, q);
+        for (int q = 0; q < PER; ++q) dma_one(1, q, std::false_type());
         wait_vm<PER + NPF>();  // position 0 has landed (then come its prefetch and position 1)
         lds_barrier();
 #pragma unroll
         for (int f = 0; f < MI + NI; ++f) read_frag(ring[gbase % STAGES], 0, f, fa[0], fb[0]);
       }
+      using T_ = std::true_type;
+      using F_ = std::false_type;
       if (cur.nk == 1) {
-        ktile(0, std::true_type(), std::true_type());
+        ktile(0, T_(), T_(), F_());
       } else {
-        ktile(0, std::true_type(), std::false_type());
-        for (int kt = 1; kt < cur.nk - 1; ++kt) ktile(kt, std::false_type(), std::false_type());
-        ktile(cur.nk - 1, std::false_type(), std::true_type());
+        ktile(0, T_(), F_(), F_());
+        // k-tiles whose positions kt+1 .. kt+1+PFD are all the current tile's
+        const int pure_end = max(1, cur.nk - 1 - PFD);
+        for (int kt = 1; kt < pure_end; ++kt) ktile(kt, F_(), F_(), T_());
+        for (int kt = pure_end; kt < cur.nk - 1; ++kt) ktile(kt, F_(), F_(), F_());
+        ktile(cur.nk - 1, F_(), T_(), F_());
       }
     }
 
