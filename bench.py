@@ -13,6 +13,7 @@ duration gives the roofline fraction.  Rank 0 prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,51 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwdbwd_1t_hbm_traffic.txt")
+
+
+def _kernel_source_sha():
+    """Digest of the HIP sources the GEMM and data-movement kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _measured_traffic(row):
+    """HBM bytes per launch of `row` from the committed counter summary, or None.
+
+    The summary holds FETCH_SIZE + WRITE_SIZE per launch (scaled by a copy
+    kernel's reading, see the file) and the digest of the sources it was
+    measured on; a different digest means the kernel changed since, and the
+    figure no longer applies.
+    """
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    sha = _kernel_source_sha()
+    for ln in lines:
+        f = ln.split()
+        if len(f) >= 5 and f[0] == "traffic" and f[1] == row and f[2] == f"sha={sha}":
+            kv = dict(x.split("=", 1) for x in f[3:])
+            return int(float(kv["fetch"]) + float(kv["write"]))
+    return None
+
+
+def _copy_calibration(nbytes):
+    """A plain device copy of nbytes, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def _cpu_baseline(cfg, inp, sample_tokens):
@@ -64,11 +110,16 @@ def main():
     ap.add_argument("--workload", default="fwdbwd_1t")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        _copy_calibration(args.copy_calibration)
+        return
 
     import torch
 
@@ -185,11 +236,11 @@ def main():
     if dom in flops:
         ach = flops[dom] / avg_ms[dom] / 1e9
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": _measured_traffic(dom)}
     else:
         ach = hbm_bytes[dom] / avg_ms[dom] / 1e6
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": _measured_traffic(dom)}
 
     note(f"timed region: {ms_step:.3f} ms/step")
     cpu = None
