@@ -304,39 +304,275 @@ hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, 
   return hipGetLastError();
 }
 
+// Batched forms of the three slot loops above for k <= KB: per chunk of the
+// row, every live slot's loads are issued before any of them is used, so a
+// wave keeps up to KB row pieces in flight instead of one.  The sums run in
+// the same slot order as above, so the results are bitwise the same.
+namespace batched {
+template <typename T> struct Raw;  // 16 bytes of a row, widened to float
+template <> struct Raw<uint16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void widen(const u32x4& q, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void widen(const u32x4& q, float (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(q[i]);
+  }
+};
+template <typename T>
+__device__ __forceinline__ u32x4 ld16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
+}  // namespace batched
+
+template <typename T, int KB>
+__global__ void __launch_bounds__(256) combine_kernel_b(const int32_t* __restrict__ slot_row,
+                                                        const float* __restrict__ w, const T* __restrict__ y_perm,
+                                                        int Tn, int k, int d, T* __restrict__ y) {
+  using R = batched::Raw<T>;
+  constexpr int VN = R::N, U = 1;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const float wl = lane < k ? w[(int64_t)t * k + lane] : 0.f;
+  const uint64_t live = __ballot(r >= 0);
+  int64_t rows[KB];
+  float wj[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    rows[j] = (int64_t)__shfl(r, j, 64) * d;
+    wj[j] = __shfl(wl, j, 64);
+  }
+  for (int c0 = 0; c0 < d; c0 += 64 * VN * U) {
+    u32x4 q[KB][U];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + (u * 64 + lane) * VN;
+          if (c < d) q[j][u] = batched::ld16(y_perm + rows[j] + c);
+        }
+    float acc[U][VN];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[u][e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float v[VN];
+          R::widen(q[j][u], v);
+#pragma unroll
+          for (int e = 0; e < VN; ++e) acc[u][e] = fmaf(wj[j], v[e], acc[u][e]);
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + (u * 64 + lane) * VN;
+      if (c < d) Vec16<T>::store(y + (int64_t)t * d + c, acc[u]);
+    }
+  }
+}
+
+template <typename T, int KB>
+__global__ void __launch_bounds__(256) combine_bwd_kernel_b(const int32_t* __restrict__ slot_row,
+                                                            const float* __restrict__ w,
+                                                            const T* __restrict__ y_perm,
+                                                            const T* __restrict__ dy, int Tn, int k, int d,
+                                                            T* __restrict__ dy_perm, float* __restrict__ dw) {
+  using R = batched::Raw<T>;
+  constexpr int VN = R::N, U = 2;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const float wl = lane < k ? w[(int64_t)t * k + lane] : 0.f;
+  const uint64_t live = __ballot(r >= 0);
+  int64_t rows[KB];
+  float wj[KB], part[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    rows[j] = (int64_t)__shfl(r, j, 64) * d;
+    wj[j] = __shfl(wl, j, 64);
+    part[j] = 0.f;
+  }
+  const T* g = dy + (int64_t)t * d;
+  for (int c0 = 0; c0 < d; c0 += 64 * VN * U) {
+    u32x4 gq[U], q[KB][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + (u * 64 + lane) * VN;
+      if (c < d) gq[u] = batched::ld16(g + c);
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + (u * 64 + lane) * VN;
+          if (c < d) q[j][u] = batched::ld16(y_perm + rows[j] + c);
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + (u * 64 + lane) * VN;
+      if (c >= d) continue;
+      float gv[VN];
+      R::widen(gq[u], gv);
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if ((live >> j) & 1) {
+          float yv[VN], ov[VN];
+          R::widen(q[j][u], yv);
+#pragma unroll
+          for (int e = 0; e < VN; ++e) {
+            part[j] = fmaf(yv[e], gv[e], part[j]);
+            ov[e] = wj[j] * gv[e];
+          }
+          Vec16<T>::store(dy_perm + rows[j] + c, ov);
+        }
+    }
+  }
+  float mydot = 0.f;  // lane j ends with slot j's dot product
+#pragma unroll
+  for (int j = 0; j < KB; ++j)
+    if ((live >> j) & 1) {
+      const float sj = wave_sum(part[j]);
+      if (lane == j) mydot = sj;
+    }
+  if (lane < k) dw[(int64_t)t * k + lane] = mydot;
+}
+
+template <typename T, int KB>
+__global__ void __launch_bounds__(256) unpermute_bwd_kernel_b(const int32_t* __restrict__ slot_row,
+                                                              const T* __restrict__ dx_perm,
+                                                              const float* __restrict__ dx_add, int Tn, int k,
+                                                              int d, T* __restrict__ dx) {
+  using R = batched::Raw<T>;
+  constexpr int VN = R::N, U = 2;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const uint64_t live = __ballot(r >= 0);
+  int64_t rows[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) rows[j] = (int64_t)__shfl(r, j, 64) * d;
+  for (int c0 = 0; c0 < d; c0 += 64 * VN * U) {
+    float acc[U][VN];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + (u * 64 + lane) * VN;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[u][e] = 0.f;
+      if (dx_add && c < d) {
+#pragma unroll
+        for (int e4 = 0; e4 < VN; e4 += 4) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(dx_add + (int64_t)t * d + c + e4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u][e4 + e] = a[e];
+        }
+      }
+    }
+    u32x4 q[KB][U];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + (u * 64 + lane) * VN;
+          if (c < d) q[j][u] = batched::ld16(dx_perm + rows[j] + c);
+        }
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float v[VN];
+          R::widen(q[j][u], v);
+#pragma unroll
+          for (int e = 0; e < VN; ++e) acc[u][e] += v[e];
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + (u * 64 + lane) * VN;
+      if (c < d) Vec16<T>::store(dx + (int64_t)t * d + c, acc[u]);
+    }
+  }
+}
+
 hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
                           void* y, hipStream_t s) {
   const dim3 grid((d.T + 3) / 4), block(256);
-  if (d.dtype == MOE_BF16)
-    combine_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm, d.T, d.k, d.d,
-                                                    (uint16_t*)y);
-  else
-    combine_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, d.T, d.k, d.d, (float*)y);
+  const bool b8 = d.k <= 8;
+  if (d.dtype == MOE_BF16) {
+    if (b8)
+      combine_kernel_b<uint16_t, 8><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm, d.T, d.k, d.d,
+                                                           (uint16_t*)y);
+    else
+      combine_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm, d.T, d.k, d.d,
+                                                      (uint16_t*)y);
+  } else {
+    if (b8)
+      combine_kernel_b<float, 8><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, d.T, d.k, d.d,
+                                                        (float*)y);
+    else
+      combine_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, d.T, d.k, d.d, (float*)y);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
                               const void* dy, void* dy_perm, float* dw, hipStream_t s) {
   const dim3 grid((d.T + 3) / 4), block(256);
-  if (d.dtype == MOE_BF16)
-    combine_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm,
-                                                        (const uint16_t*)dy, d.T, d.k, d.d,
-                                                        (uint16_t*)dy_perm, dw);
-  else
-    combine_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, (const float*)dy, d.T,
-                                                     d.k, d.d, (float*)dy_perm, dw);
+  const bool b8 = d.k <= 8;
+  if (d.dtype == MOE_BF16) {
+    if (b8)
+      combine_bwd_kernel_b<uint16_t, 8><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm,
+                                                               (const uint16_t*)dy, d.T, d.k, d.d,
+                                                               (uint16_t*)dy_perm, dw);
+    else
+      combine_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm,
+                                                          (const uint16_t*)dy, d.T, d.k, d.d,
+                                                          (uint16_t*)dy_perm, dw);
+  } else {
+    if (b8)
+      combine_bwd_kernel_b<float, 8><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, (const float*)dy,
+                                                            d.T, d.k, d.d, (float*)dy_perm, dw);
+    else
+      combine_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, (const float*)dy, d.T,
+                                                       d.k, d.d, (float*)dy_perm, dw);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
                                 const float* dx_add, void* dx, hipStream_t s) {
   const dim3 grid((d.T + 3) / 4), block(256);
-  if (d.dtype == MOE_BF16)
-    unpermute_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, (const uint16_t*)dx_perm, dx_add, d.T,
-                                                          d.k, d.d, (uint16_t*)dx);
-  else
-    unpermute_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, dx_add, d.T, d.k, d.d,
-                                                       (float*)dx);
+  const bool b8 = d.k <= 8;
+  if (d.dtype == MOE_BF16) {
+    if (b8)
+      unpermute_bwd_kernel_b<uint16_t, 8><<<grid, block, 0, s>>>(slot_row, (const uint16_t*)dx_perm, dx_add, d.T,
+                                                                 d.k, d.d, (uint16_t*)dx);
+    else
+      unpermute_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, (const uint16_t*)dx_perm, dx_add, d.T,
+                                                            d.k, d.d, (uint16_t*)dx);
+  } else {
+    if (b8)
+      unpermute_bwd_kernel_b<float, 8><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, dx_add, d.T, d.k,
+                                                              d.d, (float*)dx);
+    else
+      unpermute_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, dx_add, d.T, d.k, d.d,
+                                                         (float*)dx);
+  }
   return hipGetLastError();
 }
 
