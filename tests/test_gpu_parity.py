@@ -262,3 +262,52 @@ def test_forward_backward_is_deterministic(gpu):
         a, c = getattr(b1, n), getattr(b2, n)
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                            c.view(torch.uint8) if c.dtype == torch.bfloat16 else c), n
+
+
+# ---------------------------------------------------------------------------
+# Ragged expert segments through the whole expert path: every grouped GEMM
+# sees segments of 0, 1, 63, 64, 65, ... rows, so the weight gradients get
+# k-tile counts 0, 1, 2, 3, ... and consecutive output tiles alternate
+# between loading their successor ahead and starting cold.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,f", [(192, 128), (320, 192)])
+def test_expert_path_ragged_segments(gpu, d, f):
+    counts = [0, 1, 63, 64, 65, 128, 129, 200, 0, 300, 2, 511, 512, 513, 0, 70]  # E a multiple of 8
+    E = NL = len(counts)
+    T, k = sum(counts), 1
+    rng = np.random.default_rng(d + f)
+    idx = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+    w = np.ones((T, 1), np.float32)
+    cfg = synth.Config("ragged", 21, T, d, E, k, f, 0, NL, "bf16", 1.0, "router", True)
+    inp = synth.make_inputs(cfg)
+    D = _desc(T, d, f, E, k, 0, NL, "bf16")
+    b = moe.Buffers(D, backward=True)
+    dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
+    r = (to_dev(idx), to_dev(w))
+    moe.forward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], routing=r)
+    moe.backward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], dev["dy"], routing=r)
+    torch.cuda.synchronize()
+    x, wr = f64(inp["x"], "bf16"), f64(inp["wr"], "bf16")
+    w1, w3, w2 = f64(inp["w1"], "bf16"), f64(inp["w3"], "bf16"), f64(inp["w2"], "bf16")
+    ref = oracle.layer_forward(x, wr, w1, w3, w2, k, 0, NL, 1, routing=(idx, w))
+    g = oracle.layer_backward(ref, x, wr, w1, w3, w2, f64(inp["dy"], "bf16"), 1)
+    np.testing.assert_array_equal(to_host(b.offsets), ref["offsets"])
+    R = int(ref["offsets"][-1])
+    tol = TOL["bf16"]
+    gu = to_host(b.gu)[:R]
+    assert max_row_rel_err(gu[:, :f], ref["G"]) <= tol
+    assert max_row_rel_err(gu[:, f:], ref["U"]) <= tol
+    assert max_row_rel_err(to_host(b.h)[:R], ref["H"]) <= tol
+    assert max_row_rel_err(to_host(b.y)[:T], ref["y"]) <= tol
+    dgu = to_host(b.dgu)[:R]
+    assert max_row_rel_err(dgu[:, :f], g["dG"]) <= tol
+    assert max_row_rel_err(dgu[:, f:], g["dU"]) <= tol
+    assert max_row_rel_err(to_host(b.dx_perm)[:R], g["dx_perm"]) <= tol
+    assert max_row_rel_err(to_host(b.dx), g["dx"]) <= tol
+    for n in range(NL):
+        for name in ("dW1", "dW3", "dW2"):
+            got = to_host(getattr(b, name))[n]
+            if counts[n] == 0:
+                assert (got == 0).all(), (name, n)
+            else:
+                assert whole_rel_err(got, g[name][n]) <= tol, (name, n, counts[n])
