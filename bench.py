@@ -153,7 +153,7 @@ def main():
 
     rows = ["A1_router_logits", "A2_route", "A34_permute", "A5_gate_up", "A6_down", "A7_combine"]
     if cfg.backward:
-        rows += ["B1_combine_bwd", "B2_dh", "B3_dx", "B4_dw", "B5_route_bwd", "B5_router_bwd", "B5_unpermute"]
+        rows += ["B1_combine_bwd", "B2_dh", "B3_dx", "B4_dw", "B5_route_bwd", "B5_unpermute", "B5_router_bwd"]
     ev = {r: [] for r in rows}
 
     def timed(name, fn, rec):
@@ -187,9 +187,9 @@ def main():
         timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1,
                                                       b.dW3, b.dW2), rec)
         timed("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), rec)
-        timed("B5_router_bwd", lambda: moe.router_bwd(D, g["x"], g["wr"], b.dlogits, b.dx_router, b.dWr,
-                                                      b.ws_router_bwd), rec)
-        timed("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, b.dx_router, b.dx), rec)
+        timed("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx), rec)
+        timed("B5_router_bwd", lambda: moe.router_bwd_acc(D, g["x"], g["wr"], b.dlogits, b.dx, b.dWr,
+                                                          b.ws_router_bwd), rec)
 
     note("inputs resident in HBM; warming up")
     for _ in range(args.warmup):
@@ -216,7 +216,7 @@ def main():
                  "A7_combine": R * d * bb + T * d * bb + T * cfg.k * 8,
                  "B1_combine_bwd": T * d * bb + 2 * R * d * bb + T * cfg.k * 12,
                  "B5_route_bwd": T * E * 4 + T * cfg.k * 12,
-                 "B5_unpermute": R * d * bb + T * d * (4 + bb) + T * cfg.k * 4}
+                 "B5_unpermute": R * d * bb + T * d * bb + T * cfg.k * 4}
     per_row = {}
     for r, ms in avg_ms.items():
         ent = {"ms": round(ms, 4)}

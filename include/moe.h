@@ -208,6 +208,18 @@ int moe_route_bwd(const moe_desc* desc, const float* logits, const int32_t* topk
 int moe_router_bwd(const moe_desc* desc, const void* x, const void* Wr, const float* dlogits,
                    float* dx_router, float* dWr, void* ws, size_t ws_bytes, void* stream);
 
+/* B5c with the router path added into the token gradient in place:
+ *   dx += dlogits Wr  (dx [T][d] in the descriptor's dtype, in and out; on
+ *                      the bf16 path the sum is rounded once to bf16),
+ *   dWr = dlogits^T x ([E][d] float32 out, overwritten).
+ * Either output may be NULL.  The layer's token gradient is the unpermute
+ * sum of its expert rows plus this router term (Aurora page, Algorithm 1,
+ * stage 1, differentiated); called after moe_unpermute_bwd with dx_add NULL,
+ * it needs no float [T][d] intermediate.  Workspace and errors as for
+ * moe_router_bwd. */
+int moe_router_bwd_acc(const moe_desc* desc, const void* x, const void* Wr, const float* dlogits, void* dx,
+                       float* dWr, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_str(int status);
 

@@ -19,7 +19,7 @@ import torch  # imported before libmoe.so so that the process holds one HIP runt
 __all__ = [
     "MoeError", "MoeDesc", "lib", "make_desc", "workspace_size", "router_logits", "route", "permute",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
-    "unpermute_bwd", "route_bwd", "router_bwd", "Buffers", "forward", "backward",
+    "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
 ]
 
@@ -83,6 +83,7 @@ _SIGS = {
     "moe_unpermute_bwd": [_vp, _vp, _vp, _vp, _vp],
     "moe_route_bwd": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_router_bwd_acc": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
 }
 EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error"])
 
@@ -215,6 +216,11 @@ def router_bwd(desc, x, wr, dlogits, dx_router, dwr, ws):
     _call("moe_router_bwd", desc, x, wr, dlogits, dx_router, dwr, w, n, _stream())
 
 
+def router_bwd_acc(desc, x, wr, dlogits, dx, dwr, ws):
+    w, n = _ws(ws)
+    _call("moe_router_bwd_acc", desc, x, wr, dlogits, dx, dwr, w, n, _stream())
+
+
 class Buffers:
     """Every device tensor of one forward (+ backward) pass of a layer, allocated once."""
 
@@ -246,7 +252,6 @@ class Buffers:
             self.dW3 = torch.empty(NL, f, d, dtype=torch.float32, **z)
             self.dW2 = torch.empty(NL, d, f, dtype=torch.float32, **z)
             self.dlogits = torch.empty(T, E, dtype=torch.float32, **z)
-            self.dx_router = torch.empty(T, d, dtype=torch.float32, **z)
             self.dWr = torch.empty(E, d, dtype=torch.float32, **z)
             self.dx = torch.empty(T, d, dtype=dt, **z)
             self.ws_router_bwd = torch.empty(max(16, workspace_size(desc, OP_ROUTER_BWD)), dtype=torch.uint8, **z)
@@ -274,10 +279,8 @@ def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None):
     combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
     grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
     grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
+    unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx)
     if routing is None:
         route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits)
-        router_bwd(D, x, wr, b.dlogits, b.dx_router, b.dWr, b.ws_router_bwd)
-        unpermute_bwd(D, b.slot_row, b.dx_perm, b.dx_router, b.dx)
-    else:
-        unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx)
+        router_bwd_acc(D, x, wr, b.dlogits, b.dx, b.dWr, b.ws_router_bwd)
     return b.dx

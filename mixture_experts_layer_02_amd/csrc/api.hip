@@ -198,7 +198,17 @@ int moe_router_bwd(const moe_desc* desc, const void* x, const void* Wr, const fl
   if (!need(x) || !need(Wr) || !need(dlogits) || !opt(dx_router) || !opt(dWr)) return MOE_ERR_INVALID_ARG;
   if (dWr && (!need(ws) || ws_bytes < moe::router_bwd_workspace(*desc)))
     return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
-  return finish(moe::launch_router_bwd(*desc, x, Wr, dlogits, dx_router, dWr, ws, S(stream)));
+  return finish(moe::launch_router_bwd(*desc, x, Wr, dlogits, dx_router, nullptr, dWr, ws, S(stream)));
+}
+
+int moe_router_bwd_acc(const moe_desc* desc, const void* x, const void* Wr, const float* dlogits, void* dx,
+                       float* dWr, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(x) || !need(Wr) || !need(dlogits) || !opt(dx) || !opt(dWr)) return MOE_ERR_INVALID_ARG;
+  if (dWr && (!need(ws) || ws_bytes < moe::router_bwd_workspace(*desc)))
+    return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_router_bwd(*desc, x, Wr, dlogits, nullptr, dx, dWr, ws, S(stream)));
 }
 
 const char* moe_status_str(int status) {

@@ -62,7 +62,7 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;
   if (grid <= 0) return hipSuccess;
   if constexpr (std::is_same<AT, uint16_t>::value) {
-    if (EPI == EPI_STORE && p.c_f32)
+    if ((EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32)
       gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true><<<(unsigned)grid, 256, 0, s>>>(p);
     else
       gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false><<<(unsigned)grid, 256, 0, s>>>(p);
@@ -281,7 +281,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
 }
 
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
-                             float* dx_router, float* dWr, void* ws, hipStream_t s) {
+                             float* dx_router, void* dx_acc, float* dWr, void* ws, hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
   hipError_t e = hipSuccess;
   float* part = reinterpret_cast<float*>(ws);
@@ -295,21 +295,28 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dl = dl16;
   }
-  if (dx_router) {
-    // dx_router [T][d] = dlogits [T][E] Wr [E][d]
+  if (dx_router || dx_acc) {
+    // dx_router [T][d] = dlogits [T][E] Wr [E][d] (float), or dx += dlogits Wr
+    // in the layer's dtype
     GemmParams p = blank();
     p.A = dl;
     p.lda = d.E;
     p.B = Wr;
     p.ldb = d.d;
-    p.C = dx_router;
+    p.C = dx_router ? static_cast<void*>(dx_router) : dx_acc;
     p.ldc = d.d;
     p.M = d.T;
     p.N = d.d;
     p.K = d.E;
-    p.c_f32 = 1;
-    if (bf) e = run_bf16<LAY_K, LAY_MN, uint16_t, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, MT) * cdiv(d.d, MT), s);
-    else e = run_f32<LAY_K, LAY_MN, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.d, 64), s);
+    p.c_f32 = dx_router ? 1 : !bf;
+    const int64_t tb = cdiv(d.T, MT) * cdiv(d.d, MT), tf = cdiv(d.T, 64) * cdiv(d.d, 64);
+    if (dx_router) {
+      if (bf) e = run_bf16<LAY_K, LAY_MN, uint16_t, GRP_NONE, EPI_STORE, false>(p, tb, s);
+      else e = run_f32<LAY_K, LAY_MN, GRP_NONE, EPI_STORE, false>(p, tf, s);
+    } else {
+      if (bf) e = run_bf16<LAY_K, LAY_MN, uint16_t, GRP_NONE, EPI_ADD, false>(p, tb, s);
+      else e = run_f32<LAY_K, LAY_MN, GRP_NONE, EPI_ADD, false>(p, tf, s);
+    }
     if (e != hipSuccess) return e;
   }
   if (dWr) {

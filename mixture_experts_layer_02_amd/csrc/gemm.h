@@ -25,7 +25,7 @@ namespace moe {
 
 enum { LAY_K = 0, LAY_MN = 1 };
 enum { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_ADD = 3 };  // EPI_ADD: C += product
 
 constexpr int MAXG = 1024;
 
@@ -178,7 +178,7 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, const TileCtx& t,
                                           float v, float v2) {
   const int64_t row = t.m0 + r;
   const int64_t col = (int64_t)t.n0 + c;
-  if (EPI == EPI_STORE) {
+  if (EPI == EPI_STORE || EPI == EPI_ADD) {
     if (p.bias) v += p.bias[col];
     int64_t crow = row;
     void* Cb = p.C;
@@ -188,6 +188,7 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, const TileCtx& t,
     }
     int64_t off = crow * p.ldc + col;
     if (GRP == GRP_K) off += (int64_t)t.g * p.c_gstride;
+    if (EPI == EPI_ADD) v += p.c_f32 ? reinterpret_cast<const float*>(Cb)[off] : bf2f(reinterpret_cast<const uint16_t*>(Cb)[off]);
     if (p.c_f32) reinterpret_cast<float*>(Cb)[off] = v;
     else reinterpret_cast<uint16_t*>(Cb)[off] = f2bf(v);
   } else if (EPI == EPI_SWIGLU) {
@@ -239,7 +240,7 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, const TileCtx& t
                                            const float (&v)[8], const float (&v2)[8]) {
   const int64_t row = t.m0 + r;
   const int64_t col = (int64_t)t.n0 + c;
-  if (EPI == EPI_STORE) {
+  if (EPI == EPI_STORE || EPI == EPI_ADD) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = v[e];
@@ -255,6 +256,17 @@ __device__ __forceinline__ void epi_store8(const GemmParams& p, const TileCtx& t
     }
     int64_t off = crow * p.ldc + col;
     if (GRP == GRP_K) off += (int64_t)t.g * p.c_gstride;
+    if (EPI == EPI_ADD) {
+      float old[8];
+      if (p.c_f32) {
+        Vec16<float>::load(reinterpret_cast<const float*>(Cb) + off, *reinterpret_cast<float(*)[4]>(&old[0]));
+        Vec16<float>::load(reinterpret_cast<const float*>(Cb) + off + 4, *reinterpret_cast<float(*)[4]>(&old[4]));
+      } else {
+        Vec16<uint16_t>::load(reinterpret_cast<const uint16_t*>(Cb) + off, old);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += old[e];
+    }
     if (p.c_f32) {
       float* d = reinterpret_cast<float*>(Cb) + off;
       *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};

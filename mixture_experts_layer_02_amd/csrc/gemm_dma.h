@@ -164,8 +164,9 @@ __device__ __forceinline__ void wait_stages(int later) {
 
 // Requirements (checked by the host before choosing this kernel): bf16
 // operands, K-contiguous operands have K (or every k-tile) a multiple of 32,
-// msplit (if set) a multiple of 32.  CF32: C is float (EPI_STORE with
-// p.c_f32 set); a compile-time choice, so that one kernel holds one epilogue.
+// msplit (if set) a multiple of 32.  CF32: C is float (EPI_STORE or EPI_ADD
+// with p.c_f32 set); a compile-time choice, so that one kernel holds one
+// epilogue.
 //
 // Tiles are pipelined across tile boundaries: the last k-tiles of a tile
 // load the first k-tiles of the next one (positions past the end of a tile
@@ -405,7 +406,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   constexpr int PFD = 2;
   // Memory instructions per lane of one epilogue (the buffer stores and
   // loads below, all unconditional).
-  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? 128 : (CF32 ? 64 : 32);
+  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? 128
+                          : (EPI == EPI_ADD ? 2 : 1) * (CF32 ? 64 : 32);
   constexpr int FIRST_N_PRIMED = EPI_OPS + NPF > 63 ? 63 : EPI_OPS + NPF;
   using N0 = std::integral_constant<int, 0>;
   using NDP = std::integral_constant<int, PART>;
@@ -511,7 +513,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     {
       float* stage = s_stage[wave];
       constexpr int OC = DUAL ? WC / 2 : WC;
-      constexpr int W = (EPI == EPI_STORE && CF32) ? 4 : 8;
+      constexpr bool PLAIN = EPI == EPI_STORE || EPI == EPI_ADD;
+      constexpr int W = (PLAIN && CF32) ? 4 : 8;
       constexpr int CPR = OC / W;               // vectors per row
       constexpr int VPL = 8 * CPR / 64;          // vectors per lane per slab
       static_assert(8 * CPR % 64 == 0, "whole vectors per lane");
@@ -520,7 +523,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       const int64_t m0g = t.m0;
       __amdgpu_buffer_rsrc_t r0, r1, r2;
       int64_t ldo = p.ldc;
-      if (EPI == EPI_STORE) {
+      if (PLAIN) {
         const int esz = CF32 ? 4 : 2;
         char* cb = reinterpret_cast<char*>(p.C);
         char* cb2 = reinterpret_cast<char*>(p.C2);
@@ -550,9 +553,41 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       for (int mi = 0; mi < MI; ++mi) {
         const int rowb = wm * 128 + mi * 32;  // the block's first row in the tile
         // Rows of this block lie on one side of msplit (a multiple of 32).
-        const bool side2 = EPI == EPI_STORE && p.msplit && m0g + rowb >= p.msplit;
+        const bool side2 = PLAIN && p.msplit && m0g + rowb >= p.msplit;
+        // EPI_ADD: the block's old C values, all loaded before any of its
+        // stores (a load waits for every memory instruction issued before it).
+        u32x4_t oldc[4][VPL];
+        if (EPI == EPI_ADD) {
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+            for (int vi = 0; vi < VPL; ++vi) {
+              const int e = lane + vi * 64;
+              const int rl = e / CPR, cv = (e % CPR) * W;
+              const int row = rowb + sl * 8 + rl, col = col_base + cv;
+              const int64_t eo = (int64_t)row * ldo + col;
+              oldc[sl][vi] = __builtin_amdgcn_raw_buffer_load_b128(
+                  side2 ? r1 : r0, col < t.nlim ? (uint32_t)(eo * (CF32 ? 4 : 2)) : 0x80000000u, 0, 0);
+            }
+        }
+        u32x4_t gup[2][VPL][2];  // EPI_SWIGLU_BWD: G and U of two slabs, loaded ahead of their stores
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
+          if (EPI == EPI_SWIGLU_BWD && (sl & 1) == 0) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+              for (int vi = 0; vi < VPL; ++vi) {
+                const int e = lane + vi * 64;
+                const int rl = e / CPR, cv = (e % CPR) * W;
+                const int row = rowb + (sl + s2) * 8 + rl, col = col_base + cv;
+                const int64_t eo = (int64_t)row * ldo + col;
+                const bool ok = col < t.nlim;
+                gup[s2][vi][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+                gup[s2][vi][1] =
+                    __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
+              }
+          }
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -572,7 +607,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             const int col = col_base + cv;       // column in the tile
             const bool ok = col < t.nlim;
             const int64_t eo = (int64_t)row * ldo + col;  // element offset from the corner
-            if (EPI == EPI_STORE) {
+            if (PLAIN) {
+              const __amdgpu_buffer_rsrc_t rc = side2 ? r1 : r0;
               if (CF32) {
                 float o[4];
 #pragma unroll
@@ -581,9 +617,13 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 #pragma unroll
                   for (int q = 0; q < 4; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
                 }
+                if (EPI == EPI_ADD) {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) o[q] += __uint_as_float(oldc[sl][vi][q]);
+                }
                 const u32x4_t d = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                    __float_as_uint(o[3])};
-                __builtin_amdgcn_raw_buffer_store_b128(d, side2 ? r1 : r0, ok ? (uint32_t)(eo * 4) : 0x80000000u, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(d, rc, ok ? (uint32_t)(eo * 4) : 0x80000000u, 0, 0);
               } else {
                 float o[8];
 #pragma unroll
@@ -592,9 +632,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 #pragma unroll
                   for (int q = 0; q < 8; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
                 }
+                if (EPI == EPI_ADD) {
+                  const u32x4_t old = oldc[sl][vi];
+#pragma unroll
+                  for (int q = 0; q < 8; ++q)
+                    o[q] += __uint_as_float((q & 1) ? (old[q >> 1] & 0xffff0000u) : (old[q >> 1] << 16));
+                }
                 const u32x4_t d = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]),
                                    pack_bf2(o[6], o[7])};
-                __builtin_amdgcn_raw_buffer_store_b128(d, side2 ? r1 : r0, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(d, rc, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
               }
             } else if (EPI == EPI_SWIGLU) {
               float h[8];
@@ -611,8 +657,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             } else {  // EPI_SWIGLU_BWD: v = dH
               const uint32_t og = ok ? (uint32_t)(eo * 2) : 0x80000000u;
               const uint32_t ou = ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u;
-              const u32x4_t gq = __builtin_amdgcn_raw_buffer_load_b128(r1, og, 0, 0);
-              const u32x4_t uq = __builtin_amdgcn_raw_buffer_load_b128(r1, ou, 0, 0);
+              const u32x4_t gq = gup[sl & 1][vi][0];
+              const u32x4_t uq = gup[sl & 1][vi][1];
               float dg[8], du[8];
 #pragma unroll
               for (int q = 0; q < 8; ++q) {

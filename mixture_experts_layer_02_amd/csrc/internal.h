@@ -36,6 +36,6 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
                              const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
                              hipStream_t s);
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
-                             float* dx_router, float* dWr, void* ws, hipStream_t s);
+                             float* dx_router, void* dx_acc, float* dWr, void* ws, hipStream_t s);
 
 }  // namespace moe
