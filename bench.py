@@ -74,7 +74,7 @@ def _copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def _cpu_baseline(cfg, inp, sample_tokens):
+def _cpu_baseline(cfg, inp, sample_tokens, n_groups=1):
     """The oracle, as it stands, on the first `sample_tokens` tokens of the workload."""
     import oracle
     import synth
@@ -92,7 +92,8 @@ def _cpu_baseline(cfg, inp, sample_tokens):
     w3 = synth.as_f32(inp["w3"], dt)
     w2 = synth.as_f32(inp["w2"], dt)
     t0 = time.perf_counter()
-    fwd = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize)
+    fwd = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize,
+                               n_groups=n_groups)
     if cfg.backward:
         oracle.layer_backward(fwd, x, wr, w1, w3, w2, dy, cfg.renormalize)
     dt_s = time.perf_counter() - t0
@@ -108,6 +109,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fwdbwd_1t")
+    ap.add_argument("--n-groups", type=int, default=1,
+                    help="group-limited routing: take k/n_groups experts from each of n_groups expert groups")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -169,7 +172,10 @@ def main():
     def step(rec):
         if routing is None:
             timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits), rec)
-            timed("A2_route", lambda: moe.route(D, b.logits, b.topk_idx, b.topk_w), rec)
+            if args.n_groups > 1:
+                timed("A2_route", lambda: moe.route_grouped(D, b.logits, args.n_groups, b.topk_idx, b.topk_w), rec)
+            else:
+                timed("A2_route", lambda: moe.route(D, b.logits, b.topk_idx, b.topk_w), rec)
             idx, w = b.topk_idx, b.topk_w
         else:
             idx, w = routing
@@ -248,7 +254,7 @@ def main():
         note(f"cpu baseline: oracle on {min(args.cpu_sample_tokens, cfg.T)} tokens")
         del g, b
         torch.cuda.empty_cache()
-        cpu = _cpu_baseline(cfg, inp, min(args.cpu_sample_tokens, cfg.T))
+        cpu = _cpu_baseline(cfg, inp, min(args.cpu_sample_tokens, cfg.T), args.n_groups)
 
     out = {
         "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -256,7 +262,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} ({cfg.num_local} local from {cfg.expert_begin}) "
                                f"top-{cfg.k} f={f} {'fwd+bwd' if cfg.backward else 'fwd'}",
-                   "routed_rows": R, "global_batch": T, "parallelism": "single GPU"},
+                   "routed_rows": R, "global_batch": T, "parallelism": "single GPU",
+                   "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k"},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_mfma": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,

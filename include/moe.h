@@ -100,6 +100,20 @@ int moe_router_logits(const moe_desc* desc, const void* x, const void* Wr, const
 int moe_route(const moe_desc* desc, const float* logits, int32_t* topk_idx, float* topk_w,
               void* stream);
 
+/* A2 with group-limited selection (Domyn page, section "Group-limited expert
+ * routing": the experts form groups of consecutive experts, one per
+ * expert-parallel rank, and the router takes the same number from each).
+ *   Group g is experts [g*E/n_groups, (g+1)*E/n_groups); every token takes
+ *   its k/n_groups best experts of every group, by the same order as
+ *   moe_route (logit descending, lower index on ties), so every group
+ *   receives exactly T*k/n_groups selections.  Slots hold the k taken
+ *   experts in that order; weights as in moe_route (renormalize applies).
+ *   n_groups = 1 is moe_route.  Errors: MOE_ERR_INVALID_ARG unless
+ *   1 <= n_groups <= 64 divides both E and k.  Layouts and ownership as in
+ *   moe_route. */
+int moe_route_grouped(const moe_desc* desc, const float* logits, int n_groups, int32_t* topk_idx,
+                      float* topk_w, void* stream);
+
 /* A3 + A4, token counting, prefix sum, index generation and gather
  * (Algorithm 1 stages 2, 3 and the stage-4 gather).
  *   topk_idx [T][k] int32 (values in [0, E)), x [T][d] dtype (may be NULL:

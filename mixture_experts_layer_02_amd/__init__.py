@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "workspace_size", "router_logits", "route", "permute",
+    "MoeError", "MoeDesc", "lib", "make_desc", "workspace_size", "router_logits", "route", "route_grouped", "permute",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -70,6 +70,7 @@ class MoeError(RuntimeError):
 _SIGS = {
     "moe_router_logits": [_vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_route": [_vp, _vp, _vp, _vp],
+    "moe_route_grouped": [_vp, ctypes.c_int, _vp, _vp, _vp],
     "moe_permute": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_expert_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -157,6 +158,10 @@ def router_logits(desc, x, wr, bias, logits, ws=None):
 
 def route(desc, logits, topk_idx, topk_w):
     _call("moe_route", desc, logits, topk_idx, topk_w, _stream())
+
+
+def route_grouped(desc, logits, n_groups, topk_idx, topk_w):
+    _call("moe_route_grouped", desc, logits, int(n_groups), topk_idx, topk_w, _stream())
 
 
 def permute(desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws):
@@ -257,12 +262,16 @@ class Buffers:
             self.ws_router_bwd = torch.empty(max(16, workspace_size(desc, OP_ROUTER_BWD)), dtype=torch.uint8, **z)
 
 
-def forward(b: Buffers, x, wr, w1, w3, w2, bias=None, routing=None):
-    """Stages A1-A7.  ``routing=(topk_idx, topk_w)`` device tensors skip A1-A2."""
+def forward(b: Buffers, x, wr, w1, w3, w2, bias=None, routing=None, n_groups=1):
+    """Stages A1-A7.  ``routing=(topk_idx, topk_w)`` device tensors skip A1-A2;
+    ``n_groups`` > 1 routes with the group-limited rule (route_grouped)."""
     D = b.desc
     if routing is None:
         router_logits(D, x, wr, bias, b.logits)
-        route(D, b.logits, b.topk_idx, b.topk_w)
+        if n_groups > 1:
+            route_grouped(D, b.logits, n_groups, b.topk_idx, b.topk_w)
+        else:
+            route(D, b.logits, b.topk_idx, b.topk_w)
         idx, w = b.topk_idx, b.topk_w
     else:
         idx, w = routing

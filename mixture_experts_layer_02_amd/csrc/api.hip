@@ -67,7 +67,16 @@ int moe_route(const moe_desc* desc, const float* logits, int32_t* topk_idx, floa
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(logits) || !need(topk_idx) || !need(topk_w)) return MOE_ERR_INVALID_ARG;
-  return finish(moe::launch_route(*desc, logits, topk_idx, topk_w, S(stream)));
+  return finish(moe::launch_route(*desc, logits, 1, topk_idx, topk_w, S(stream)));
+}
+
+int moe_route_grouped(const moe_desc* desc, const float* logits, int n_groups, int32_t* topk_idx, float* topk_w,
+                      void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(logits) || !need(topk_idx) || !need(topk_w)) return MOE_ERR_INVALID_ARG;
+  if (n_groups < 1 || n_groups > 64 || desc->E % n_groups || desc->k % n_groups) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_route(*desc, logits, n_groups, topk_idx, topk_w, S(stream)));
 }
 
 int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,

@@ -12,7 +12,8 @@ size_t router_bwd_workspace(const moe_desc& d);
 
 hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
                                 float* logits, hipStream_t s);
-hipError_t launch_route(const moe_desc& d, const float* logits, int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_route(const moe_desc& d, const float* logits, int n_groups, int32_t* idx, float* w,
+                        hipStream_t s);
 hipError_t launch_route_bwd(const moe_desc& d, const float* logits, const int32_t* idx, const float* w,
                             const float* dw, float* dlogits, hipStream_t s);
 hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, int32_t* counts,

@@ -12,9 +12,17 @@
 
 namespace moe {
 
-template <int MAXV>
+// Group-limited selection (Domyn page, section "Group-limited expert
+// routing"): with G > 1 groups of Eg = E/G consecutive experts, each group
+// may give at most k/G experts.  The rounds still take the best remaining
+// eligible expert, and once a group has given its quota its other experts
+// leave the race, so the k picks are the union of every group's k/G best, in
+// descending order (the eligible set only shrinks).  Lane g counts group g's
+// picks.
+template <int MAXV, bool GROUPED>
 __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict__ logits, int T, int E,
-                                                         int k, int renorm, int32_t* __restrict__ idx_out,
+                                                         int k, int renorm, int G,
+                                                         int32_t* __restrict__ idx_out,
                                                          float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -33,6 +41,8 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
   }
   float my_v = 0.f, v0 = 0.f;
   int my_i = 0;
+  const int Eg = GROUPED ? E / G : E, kg = GROUPED ? k / G : k;
+  int group_picks = 0;  // lane g: experts taken from group g so far
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
@@ -54,6 +64,15 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
       }
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (GROUPED) {
+      const int g = bi / Eg;
+      if (lane == g) ++group_picks;
+      if (__shfl(group_picks, g, 64) == kg) {  // the group is full: its other experts leave
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i)
+          if ((i * 64 + lane) / Eg == g) taken |= 1u << i;
+      }
+    }
     if (lane == j) {
       my_v = bv;
       my_i = bi;
@@ -143,15 +162,21 @@ __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_route(const moe_desc& d, const float* logits, int32_t* idx, float* w,
-                        hipStream_t s) {
+template <bool GROUPED>
+static void route_dispatch(const moe_desc& d, const float* logits, int G, int32_t* idx, float* w, hipStream_t s) {
   const dim3 grid((d.T + 3) / 4), block(256);
   const int nv = (d.E + 63) / 64;
-  if (nv <= 1) topk_route_kernel<1><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
-  else if (nv <= 2) topk_route_kernel<2><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
-  else if (nv <= 4) topk_route_kernel<4><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
-  else if (nv <= 8) topk_route_kernel<8><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
-  else topk_route_kernel<16><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, idx, w);
+  if (nv <= 1) topk_route_kernel<1, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
+  else if (nv <= 2) topk_route_kernel<2, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
+  else if (nv <= 4) topk_route_kernel<4, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
+  else if (nv <= 8) topk_route_kernel<8, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
+  else topk_route_kernel<16, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
+}
+
+hipError_t launch_route(const moe_desc& d, const float* logits, int n_groups, int32_t* idx, float* w,
+                        hipStream_t s) {
+  if (n_groups > 1) route_dispatch<true>(d, logits, n_groups, idx, w, s);
+  else route_dispatch<false>(d, logits, 1, idx, w, s);
   return hipGetLastError();
 }
 

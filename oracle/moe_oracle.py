@@ -10,7 +10,8 @@ Sources ("the pages"):
            Aurora Super Computer": section 3.1 (FastSparseMoE), its Algorithm 1
            (FastSparseMoEBlock with expert parallelism, stages 1-5) and Figure 5.
   [Domyn]  "Training a 1T-Params MoE on EU public infrastructure": the model
-           table (hidden 6144, 384 routed experts, top-8, expert hidden 1792).
+           table (hidden 6144, 384 routed experts, top-8, expert hidden 1792)
+           and the section on group-limited expert routing.
 
 Arithmetic: every input is widened to float64 and every step runs in float64
 with no intermediate rounding.  Matrix products use numpy's matmul as a
@@ -42,7 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "router_logits", "topk_route", "count_tokens", "generate_indices", "permute",
+    "router_logits", "topk_route", "topk_route_grouped", "count_tokens", "generate_indices", "permute",
     "silu", "silu_grad", "expert_ffn_rows", "expert_ffn", "combine",
     "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd", "unpermute_bwd",
     "route_bwd", "router_bwd", "layer_forward", "layer_backward",
@@ -88,6 +89,44 @@ def topk_route(logits, k, renormalize=1):
     order = np.argsort(-L, axis=1, kind="stable")
     idx = order[:, :k].astype(np.int32)
     # Softmax over all experts, written out.
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    probs = z / z.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+def topk_route_grouped(logits, k, n_groups, renormalize=1):
+    """Group-limited top-k: the same number of experts from every group.
+
+    [Domyn] section "Group-limited expert routing": the E experts form
+    n_groups groups of E/n_groups consecutive experts (one group per
+    expert-parallel rank; 384 = 4 x 96 there), and the router takes k/n_groups
+    experts from each group (2 per group at top-8), so that every group, and
+    so every rank, receives exactly T*k/n_groups rows.  Within a group the
+    experts taken are the group's best by the same order as topk_route (logit
+    descending, lower index first on ties); the slots then hold all k taken
+    experts in that order, and the weights are computed from the selection
+    exactly as in topk_route (softmax probabilities of the selected experts,
+    divided by their sum when ``renormalize`` is 1).
+    """
+    L = _f64(logits)
+    if not np.isfinite(L).all():
+        raise ValueError("oracle: logits must be finite")
+    T, E = L.shape
+    G = int(n_groups)
+    if G < 1 or E % G or k % G or not 1 <= k <= E:
+        raise ValueError("oracle: need n_groups dividing both E and k")
+    Eg, kg = E // G, k // G
+    chosen = []
+    for g in range(G):
+        block = L[:, g * Eg:(g + 1) * Eg]
+        best = np.argsort(-block, axis=1, kind="stable")[:, :kg]
+        chosen.append(best + g * Eg)
+    sel = np.sort(np.concatenate(chosen, axis=1), axis=1)          # ascending expert index
+    vals = np.take_along_axis(L, sel, axis=1)
+    idx = np.take_along_axis(sel, np.argsort(-vals, axis=1, kind="stable"), axis=1).astype(np.int32)
     z = np.exp(L - L.max(axis=1, keepdims=True))
     probs = z / z.sum(axis=1, keepdims=True)
     w = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
@@ -361,12 +400,13 @@ def router_bwd(x, wr, dlogits):
 # --------------------------------------------------------------------------
 
 def layer_forward(x, wr, w1, w3, w2, k, e0, NL, renormalize=1, bias=None,
-                  logits=None, routing=None):
+                  logits=None, routing=None, n_groups=1):
     """Stages 1-5 on one GPU's share.  Returns a dict of every intermediate.
 
     ``logits`` (optional) replaces stage 1's matmul, so that routing can be
     taken from a given logit tensor; ``routing=(idx, w)`` (optional) replaces
-    stage 1 altogether (forced routing).
+    stage 1 altogether (forced routing); ``n_groups`` > 1 selects with the
+    group-limited rule (topk_route_grouped).
     """
     out = {}
     E = np.asarray(wr).shape[0]
@@ -377,7 +417,10 @@ def layer_forward(x, wr, w1, w3, w2, k, e0, NL, renormalize=1, bias=None,
     else:
         L = router_logits(x, wr, bias) if logits is None else _f64(logits)
         out["logits"] = L
-        idx, w = topk_route(L, k, renormalize)
+        if n_groups > 1:
+            idx, w = topk_route_grouped(L, k, n_groups, renormalize)
+        else:
+            idx, w = topk_route(L, k, renormalize)
     out["idx"], out["w"] = idx, w
     counts, offsets = count_tokens(idx, E, e0, NL)
     row_token, slot_row = generate_indices(idx, e0, NL, offsets)

@@ -35,7 +35,7 @@ def _routing_agreement(idx_g, L_ref, idx_ref):
     return same
 
 
-def _run_layer(cfg, backward, gpu):
+def _run_layer(cfg, backward, gpu, n_groups=1):
     inp = synth.make_inputs(cfg)
     dt = cfg.dtype
     D = _desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, dt, cfg.renormalize)
@@ -43,7 +43,8 @@ def _run_layer(cfg, backward, gpu):
     dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
     bias = to_dev(inp["bias"]) if "bias" in inp else None
     routing = (to_dev(inp["idx"]), to_dev(inp["w"])) if cfg.routing == "roundrobin" else None
-    moe.forward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], bias=bias, routing=routing)
+    moe.forward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], bias=bias, routing=routing,
+                n_groups=n_groups)
     if backward:
         moe.backward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], dev["dy"], routing=routing)
     torch.cuda.synchronize()

@@ -55,6 +55,70 @@ def test_route(gpu, T, E, k, renorm):
     np.testing.assert_allclose(to_host(w), rw, rtol=W_RTOL, atol=W_ATOL)
 
 
+# Group-limited selection (Domyn page, group-limited expert routing)
+@pytest.mark.parametrize("T,E,k,G,renorm", [(1000, 384, 8, 4, 1), (513, 384, 8, 4, 0), (300, 64, 8, 8, 1),
+                                             (257, 1024, 32, 16, 1), (100, 96, 6, 3, 1), (64, 8, 2, 2, 0),
+                                             (77, 48, 8, 2, 1), (130, 384, 8, 1, 1), (33, 64, 32, 32, 1)])
+def test_route_grouped(gpu, T, E, k, G, renorm):
+    rng = np.random.default_rng(T * 5 + E + k + G)
+    L = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    L[: T // 3] = np.round(L[: T // 3] * 4) / 4                       # many exact ties
+    z = rng.random((T, E)) < 0.05
+    L[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+    L[T // 2:] += np.linspace(4, -4, E, dtype=np.float32)[None, :]    # a skewed preference
+    if T > 2:
+        L[1] = 0.0
+    D = _desc(T, 64, 64, E, k, 0, E, "f32", renorm)
+    idx = torch.full((T, k), -5, dtype=torch.int32, device=gpu)
+    w = torch.empty((T, k), dtype=torch.float32, device=gpu)
+    moe.route_grouped(D, to_dev(L), G, idx, w)
+    ridx, rw = oracle.topk_route_grouped(L, k, G, renorm)
+    got = to_host(idx)
+    np.testing.assert_array_equal(got, ridx)
+    np.testing.assert_allclose(to_host(w), rw, rtol=W_RTOL, atol=W_ATOL)
+    assert (np.bincount(got.ravel() // (E // G), minlength=G) == T * k // G).all()
+
+
+def test_route_grouped_rejects_bad_groups(gpu):
+    D = _desc(16, 64, 64, 48, 8, 0, 48, "f32")
+    L = torch.zeros((16, 48), dtype=torch.float32, device=gpu)
+    idx = torch.empty((16, 8), dtype=torch.int32, device=gpu)
+    w = torch.empty((16, 8), dtype=torch.float32, device=gpu)
+    for G in (0, 3, 5, 96):
+        with pytest.raises(moe.MoeError):
+            moe.route_grouped(D, L, G, idx, w)
+
+
+@pytest.mark.parametrize("backward", [False, True])
+def test_layer_grouped_routing(gpu, backward):
+    # The 1T expert-parallel share with group-limited routing, reduced: 4 groups
+    # of E/4 experts, 2 per group at top-8; the local block is group 1, which
+    # receives exactly T*2 rows.
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], T=384, d=256, f=128, E=64, num_local=16, expert_begin=16)
+    inp, b = _run_layer(cfg, backward, gpu, n_groups=4)
+    dt, tol = cfg.dtype, TOL[cfg.dtype]
+    x, wr = f64(inp["x"], dt), f64(inp["wr"], dt)
+    w1, w3, w2 = f64(inp["w1"], dt), f64(inp["w3"], dt), f64(inp["w2"], dt)
+    ref = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize,
+                               n_groups=4)
+    assert max_row_rel_err(to_host(b.logits), ref["logits"]) <= LOGIT_TOL
+    gi = to_host(b.topk_idx)
+    ri, _ = oracle.topk_route_grouped(to_host(b.logits), cfg.k, 4, cfg.renormalize)
+    np.testing.assert_array_equal(gi, ri)                 # exact on the GPU's own logits
+    assert int(to_host(b.offsets)[-1]) == cfg.T * 2
+    assert (gi == ref["idx"]).all(), "a routing near-tie flipped"
+    np.testing.assert_array_equal(to_host(b.slot_row), ref["slot_row"])
+    assert max_row_rel_err(to_host(b.y), ref["y"]) <= tol
+    if backward:
+        g = oracle.layer_backward(ref, x, wr, w1, w3, w2, f64(inp["dy"], dt), cfg.renormalize)
+        assert max_row_rel_err(to_host(b.dx), g["dx"]) <= tol
+        assert whole_rel_err(to_host(b.dlogits), g["dlogits"]) <= tol
+        for n in range(cfg.num_local):
+            assert whole_rel_err(to_host(b.dW1)[n], g["dW1"][n]) <= tol, n
+            assert whole_rel_err(to_host(b.dW2)[n], g["dW2"][n]) <= tol, n
+        assert whole_rel_err(to_host(b.dWr), g["dWr"]) <= tol
+
+
 # ---------------------------------------------------------------------------
 # A3 + A4: counting, prefix sum, index generation, gather
 # ---------------------------------------------------------------------------
