@@ -111,6 +111,11 @@ def main():
     ap.add_argument("--workload", default="fwdbwd_1t")
     ap.add_argument("--n-groups", type=int, default=1,
                     help="group-limited routing: take k/n_groups experts from each of n_groups expert groups")
+    ap.add_argument("--schedule", choices=["static", "dynamic"], default="static",
+                    help="tile order of the grouped GEMMs")
+    ap.add_argument("--hold-cus", type=int, default=0,
+                    help="before each grouped GEMM, occupy this many CUs with another kernel (contention)")
+    ap.add_argument("--hold-us", type=int, default=2000, help="how long each --hold-cus kernel runs")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -149,10 +154,13 @@ def main():
     g = {n: up(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
     bias = up(inp["bias"]) if "bias" in inp else None
     routing = (up(inp["idx"]), up(inp["w"])) if cfg.routing == "roundrobin" else None
+    counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
     D = moe.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype,
-                      cfg.renormalize)
+                      cfg.renormalize, tile_counters=counters)
     b = moe.Buffers(D, backward=cfg.backward)
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev)
+    gemm_rows = {"A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw"}
 
     rows = ["A1_router_logits", "A2_route", "A34_permute", "A5_gate_up", "A6_down", "A7_combine"]
     if cfg.backward:
@@ -160,6 +168,12 @@ def main():
     ev = {r: [] for r in rows}
 
     def timed(name, fn, rec):
+        if args.hold_cus and name in gemm_rows:
+            # Another kernel takes hold_cus CUs as the product starts (the main
+            # stream waits 20 us so that the holder's workgroups are resident).
+            side.wait_stream(stream)
+            moe.hold_cus(args.hold_cus, args.hold_us, stream=side)
+            moe.hold_cus(1, 20, lds_bytes=64, stream=stream)
         if rec:
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record(stream)
@@ -263,7 +277,10 @@ def main():
         "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} ({cfg.num_local} local from {cfg.expert_begin}) "
                                f"top-{cfg.k} f={f} {'fwd+bwd' if cfg.backward else 'fwd'}",
                    "routed_rows": R, "global_batch": T, "parallelism": "single GPU",
-                   "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k"},
+                   "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k",
+                   "tile_schedule": args.schedule,
+                   "contention": (f"{args.hold_cus} CUs held for {args.hold_us} us at each grouped GEMM"
+                                  if args.hold_cus else None)},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_mfma": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,

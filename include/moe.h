@@ -57,6 +57,15 @@ enum moe_status {
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 
+/* Order in which the persistent bf16 GEMM workgroups take output tiles
+ * (Domyn page, section "Dynamic tile scheduling in SonicMoE").  STATIC: each
+ * workgroup's list of tiles is fixed at launch.  DYNAMIC: workgroups take
+ * the next tile from shared atomic counters when they are free (per-XCD
+ * queues, then each other's), so workgroups that start late - their CUs
+ * held by another kernel - do not delay the end of the product.  Outputs are
+ * bitwise identical under both. */
+enum moe_tile_schedule { MOE_SCHEDULE_STATIC = 0, MOE_SCHEDULE_DYNAMIC = 1 };
+
 /* Which call a workspace size is asked for. */
 enum moe_op {
   MOE_OP_ROUTER_LOGITS = 0,
@@ -78,6 +87,11 @@ typedef struct moe_desc {
   int32_t num_local;        /* local experts (the page's NR) */
   int32_t dtype;            /* enum moe_dtype */
   int32_t renormalize;      /* 1: top-k probabilities divided by their sum; 0: raw softmax probabilities */
+  int32_t tile_schedule;    /* enum moe_tile_schedule: order of the grouped GEMMs' output tiles */
+  int32_t* tile_counters;   /* MOE_SCHEDULE_DYNAMIC: device int32[16], all zero before the first call;
+                               every GEMM launch leaves them zero again.  Calls that share one array
+                               must not run concurrently (same stream, or ordered by events).  Ignored
+                               (may be NULL) for MOE_SCHEDULE_STATIC. */
 } moe_desc;
 
 /* Host-only query: bytes of device workspace that call `op` needs for desc
@@ -239,6 +253,16 @@ const char* moe_status_str(int status);
 
 /* Text of the last HIP error seen by a failing call on this thread. */
 const char* moe_last_error(void);
+
+/* Measurement aid (Domyn page, section "Dynamic tile scheduling in
+ * SonicMoE": the two tile orders are compared with and without a dummy
+ * kernel that occupies part of the GPU).  Launches `workgroups` one-wave
+ * workgroups on `stream`, each reserving lds_bytes of LDS - so that a
+ * grouped-GEMM workgroup cannot share its compute unit - and returning after
+ * `microseconds` of the device's real-time clock.  No memory is touched.
+ * MOE_ERR_INVALID_ARG unless 1 <= workgroups <= 4096,
+ * 4 <= lds_bytes <= 163840 and 0 <= microseconds <= 1000000. */
+int moe_hold_cus(int workgroups, int lds_bytes, int microseconds, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "workspace_size", "router_logits", "route", "route_grouped", "permute",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "permute",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -30,6 +30,7 @@ OP_ROUTER_LOGITS, OP_PERMUTE, OP_GROUPED_FFN, OP_FFN_BWD_DX, OP_FFN_BWD_DW, OP_R
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 _vp = ctypes.c_void_p
+SCHEDULE_STATIC, SCHEDULE_DYNAMIC = 0, 1
 _sz = ctypes.c_size_t
 
 
@@ -45,6 +46,8 @@ class MoeDesc(ctypes.Structure):
         ("num_local", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("renormalize", ctypes.c_int32),
+        ("tile_schedule", ctypes.c_int32),
+        ("tile_counters", ctypes.c_void_p),
     ]
 
     @property
@@ -86,7 +89,7 @@ _SIGS = {
     "moe_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_router_bwd_acc": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
 }
-EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error"])
+EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error", "moe_hold_cus"])
 
 _lib = None
 
@@ -106,17 +109,35 @@ def lib():
         l.moe_workspace_size.restype = ctypes.c_int
         l.moe_status_str.argtypes = [ctypes.c_int]
         l.moe_status_str.restype = ctypes.c_char_p
+        l.moe_hold_cus.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
+        l.moe_hold_cus.restype = ctypes.c_int
         l.moe_last_error.argtypes = []
         l.moe_last_error.restype = ctypes.c_char_p
         _lib = l
     return _lib
 
 
-def make_desc(T, d, f, E, k, expert_begin=0, num_local=None, dtype=MOE_BF16, renormalize=1) -> MoeDesc:
+def make_desc(T, d, f, E, k, expert_begin=0, num_local=None, dtype=MOE_BF16, renormalize=1,
+              tile_counters=None) -> MoeDesc:
+    """The layer descriptor.  ``tile_counters`` (a zeroed int32 device tensor of
+    16 elements, see new_tile_counters) selects the dynamic tile order of the
+    grouped GEMMs; the descriptor keeps a reference to it."""
     if isinstance(dtype, str):
         dtype = MOE_BF16 if dtype == "bf16" else MOE_F32
-    return MoeDesc(ctypes.sizeof(MoeDesc), T, d, f, E, k, expert_begin, E if num_local is None else num_local,
-                   dtype, renormalize)
+    D = MoeDesc(ctypes.sizeof(MoeDesc), T, d, f, E, k, expert_begin, E if num_local is None else num_local,
+                dtype, renormalize, SCHEDULE_STATIC, None)
+    if tile_counters is not None:
+        if tile_counters.dtype != torch.int32 or tile_counters.numel() < 16 or not tile_counters.is_cuda:
+            raise ValueError("tile_counters must be an int32 device tensor of 16 elements")
+        D.tile_schedule = SCHEDULE_DYNAMIC
+        D.tile_counters = tile_counters.data_ptr()
+        D._tile_counters = tile_counters
+    return D
+
+
+def new_tile_counters(device="cuda"):
+    """Zeroed counters for the dynamic tile order (every GEMM leaves them zero)."""
+    return torch.zeros(16, dtype=torch.int32, device=device)
 
 
 def _p(t):
@@ -158,6 +179,16 @@ def router_logits(desc, x, wr, bias, logits, ws=None):
 
 def route(desc, logits, topk_idx, topk_w):
     _call("moe_route", desc, logits, topk_idx, topk_w, _stream())
+
+
+def hold_cus(workgroups, microseconds, lds_bytes=96 * 1024, stream=None):
+    """Occupy `workgroups` compute units for `microseconds` (measurement aid:
+    a stand-in for another kernel, such as a collective, holding part of the
+    GPU while a grouped GEMM runs)."""
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = lib().moe_hold_cus(int(workgroups), int(lds_bytes), int(microseconds), s)
+    if rc != MOE_OK:
+        raise MoeError("moe_hold_cus", rc)
 
 
 def route_grouped(desc, logits, n_groups, topk_idx, topk_w):

@@ -27,6 +27,9 @@ int check_desc(const moe_desc* d) {
   if (d->k > d->E || (int64_t)d->expert_begin + d->num_local > d->E) return MOE_ERR_INVALID_ARG;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (d->tile_schedule != MOE_SCHEDULE_STATIC && d->tile_schedule != MOE_SCHEDULE_DYNAMIC)
+    return MOE_ERR_INVALID_ARG;
+  if (d->tile_schedule == MOE_SCHEDULE_DYNAMIC && !need(d->tile_counters)) return MOE_ERR_INVALID_ARG;
   if (d->d % 64 || d->f % 64 || d->E % 8 || d->E > 1024 || d->k > 32) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->T * d->k >= (1ll << 31) || (int64_t)d->T * d->E >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -232,5 +235,12 @@ const char* moe_status_str(int status) {
 }
 
 const char* moe_last_error(void) { return g_last_error; }
+
+int moe_hold_cus(int workgroups, int lds_bytes, int microseconds, void* stream) {
+  if (workgroups < 1 || workgroups > 4096 || lds_bytes < 4 || lds_bytes > 160 * 1024 || microseconds < 0 ||
+      microseconds > 1000000)
+    return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_hold(workgroups, lds_bytes, microseconds, S(stream)));
+}
 
 }  // extern "C"

@@ -28,8 +28,9 @@ int num_cus() {
 
 namespace {
 
-GemmParams blank() {
+GemmParams blank(const moe_desc& d) {
   GemmParams p{};
+  p.dyn = d.tile_schedule == MOE_SCHEDULE_DYNAMIC ? d.tile_counters : nullptr;
   return p;
 }
 
@@ -134,7 +135,7 @@ size_t router_bwd_workspace(const moe_desc& d) {
 
 hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
                                 float* logits, hipStream_t s) {
-  GemmParams p = blank();
+  GemmParams p = blank(d);
   p.A = x;
   p.lda = d.d;
   p.B = Wr;
@@ -154,7 +155,7 @@ hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr
 hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,
                           const void* W3, void* gu, void* h, hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
-  GemmParams p = blank();
+  GemmParams p = blank(d);
   p.A = x_perm;
   p.lda = d.d;
   p.B = W1;
@@ -176,7 +177,7 @@ hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void*
 hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h, const void* W2, void* y_perm,
                        hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
-  GemmParams q = blank();
+  GemmParams q = blank(d);
   q.A = h;
   q.lda = d.f;
   q.B = W2;
@@ -197,7 +198,7 @@ hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* 
                          const void* dy_perm, void* dgu, hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
   // dH = dY W2 (W2 stored [d][f]: N-contiguous in k = d), SwiGLU backward epilogue -> dgu
-  GemmParams p = blank();
+  GemmParams p = blank(d);
   p.A = dy_perm;
   p.lda = d.d;
   p.B = W2;
@@ -219,7 +220,7 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
                           const void* dgu, void* dx_perm, hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
   // dX = [dG | dU] [W1 ; W3]  (K = 2f; rows k < f of W1, k >= f of W3, both [f][d])
-  GemmParams q = blank();
+  GemmParams q = blank(d);
   q.A = dgu;
   q.lda = 2 * (int64_t)d.f;
   q.B = W1;
@@ -243,7 +244,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
                              hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
   // dW1 | dW3 [f][d] = [dG | dU]^T x_perm over each expert's rows (M = 2f split at f)
-  GemmParams p = blank();
+  GemmParams p = blank(d);
   p.A = dgu;
   p.lda = 2 * (int64_t)d.f;
   p.B = x_perm;
@@ -263,7 +264,7 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
   if (e != hipSuccess) return e;
   // dW2 [d][f] = dy_perm^T h
-  GemmParams q = blank();
+  GemmParams q = blank(d);
   q.A = dy_perm;
   q.lda = d.d;
   q.B = h;
@@ -298,7 +299,7 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
   if (dx_router || dx_acc) {
     // dx_router [T][d] = dlogits [T][E] Wr [E][d] (float), or dx += dlogits Wr
     // in the layer's dtype
-    GemmParams p = blank();
+    GemmParams p = blank(d);
     p.A = dl;
     p.lda = d.E;
     p.B = Wr;
@@ -322,7 +323,7 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, c
   if (dWr) {
     // dWr [E][d] = dlogits^T x, split over T into S chunks, then summed in chunk order
     const int S = router_splits(d);
-    GemmParams q = blank();
+    GemmParams q = blank(d);
     q.A = dl;
     q.lda = d.E;
     q.B = x;

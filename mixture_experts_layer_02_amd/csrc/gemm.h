@@ -50,6 +50,7 @@ struct GemmParams {
   const void* gu_in;    // EPI_SWIGLU_BWD: [rows][2N], G | U
   void* gu_out;         // EPI_SWIGLU: [rows][2N], G | U (NULL = not saved)
   int c_f32;            // 1: C is float, 0: C is bf16
+  int* dyn;             // dynamic tile queues (int[16], zero on entry and on exit), NULL = static order
 };
 
 struct TileCtx {

@@ -301,9 +301,92 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // Current and next tile.  A ring position is a k-tile of the current tile
   // (pos < cur.nk) or of the next one (pos - cur.nk); positions past both are
   // loads of nothing.  Ring stage of a position: (gbase + pos) % STAGES.
+  // Tile order.  Static (p.dyn == NULL): workgroup b takes the ids
+  // xcd_tile(0, grid), xcd_tile(1, grid), ... fixed at launch.  Dynamic
+  // (the Domyn page's "Dynamic tile scheduling in SonicMoE": idle workgroups
+  // take the next tile from a shared atomic counter, so that running ones
+  // also take the tiles of workgroups that start late): the same per-XCD
+  // sequences become eight queues, p.dyn[x] counting the tiles taken from
+  // XCD x's sequence; a workgroup takes from its own XCD's queue and, once
+  // that is empty, from the others.  Every tile is computed exactly as in
+  // the static order, so the outputs are bitwise identical.  A workgroup
+  // claims two tiles ahead (the next tile's operands load during this one);
+  // a claim is issued at the top of a tile and its result published to LDS
+  // after the wait of k-tile 1, when the atomic has long returned.  The last
+  // workgroup to finish (p.dyn[8] counts them) zeroes the counters.
+  __shared__ int s_q[2];
+  const bool dyn = p.dyn != nullptr;
+  const bool w0 = wave == 0;  // wave 0 runs the claims, all its lanes alike
+  const int nq = (gridDim.x % 8) ? 1 : 8;
+  const int x0 = (int)blockIdx.x % nq;
+  // Wave 0 state (the same in all its lanes).  Every lane of wave 0 adds 1
+  // to a counter, so a claim advances it by 64 and each lane's old value
+  // shifted right by 6 is the claim's index in its queue.
+  int exhausted = 0;  // bit x: queue x is known to be empty
+  int pend = 0;       // raw result of the own-queue claim in flight
+  bool pend_ok = false;
+  auto q_tile = [&](int x, int n) -> int {
+    return nq == 1 ? n : (n / run) * (int)gridDim.x + x * run + (n % run);
+  };
+  // The tile of the own-queue claim (pend, if pend_ok), else of the other
+  // queues in turn; sched.total when every queue is empty.  Unrolled with no
+  // early exit, and all of wave 0 runs it, so that the control flow stays
+  // uniform and the compiler keeps the tile state in scalar registers.
+  auto resolve = [&]() -> int {
+    int found = sched.total;
+    if (pend_ok) {
+      const int c = q_tile(x0, __builtin_amdgcn_readfirstlane(pend) >> 6);
+      if (c < sched.total) found = c;
+      else exhausted |= 1 << x0;
+    }
+#pragma unroll
+    for (int s = 1; s < 8; ++s) {
+      const int x = (x0 + s) & 7;
+      if (s < nq && found >= sched.total && !((exhausted >> x) & 1)) {
+        const int c = q_tile(x, __builtin_amdgcn_readfirstlane(atomicAdd(p.dyn + x, 1)) >> 6);
+        if (c < sched.total) found = c;
+        else exhausted |= 1 << x;
+      }
+    }
+    return found;
+  };
+  auto claim_own = [&]() {
+    pend_ok = !((exhausted >> x0) & 1);
+    if (pend_ok) pend = atomicAdd(p.dyn + x0, 1);
+  };
+  auto dyn_finish = [&]() {
+    if (dyn && w0) {
+      const int done = __builtin_amdgcn_readfirstlane(atomicAdd(p.dyn + 8, 1)) >> 6;
+      if (done == (int)gridDim.x - 1) {  // the last workgroup: every claim is over
+#pragma unroll
+        for (int x = 0; x < 9; ++x) atomicExch(p.dyn + x, 0);
+      }
+    }
+  };
+
   int it = 0;
-  int id = xcd_tile(0, gridDim.x);
-  if ((int)gridDim.x * 0 >= sched.total || id >= sched.total) return;
+  int id;
+  if (dyn) {
+    if (w0) {
+      claim_own();
+      const int i0 = resolve();
+      int i1 = sched.total;
+      if (i0 < sched.total) {
+        claim_own();
+        i1 = resolve();
+      }
+      s_q[0] = i0;
+      s_q[1] = i1;
+    }
+    __syncthreads();
+    id = __builtin_amdgcn_readfirstlane(s_q[0]);  // uniform: keeps the tile's resources scalar
+  } else {
+    id = xcd_tile(0, gridDim.x);
+  }
+  if (id >= sched.total) {
+    dyn_finish();
+    return;
+  }
   TileCtx t = sched.tile(p, s_pref, id);
   Ld cur = setup(t);
   Ld nxt = null_ld;
@@ -415,6 +498,31 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using NPP = std::integral_constant<int, NPF>;
   bf16x8 fa[2][MI], fb[2][NI];
 
+  // Dynamic order: the claim issued at the top of tile it resolves to tile
+  // it+2's id, stored where the top of tile it+1 reads it.
+  bool claimed = false;
+  // k-tile after whose wait the own-queue claim is published (opaque to the
+  // compiler, which would otherwise peel that k-tile into a copy of its own).
+  const int pub_kt = dyn ? __builtin_amdgcn_readfirstlane(p.ngroups >= 0 ? 1 : 2) : -1;
+  auto publish_own = [&]() {
+    if (w0 && claimed && pend_ok) {
+      const int c = q_tile(x0, __builtin_amdgcn_readfirstlane(pend) >> 6);
+      if (c < sched.total) {
+        s_q[it & 1] = c;
+        claimed = false;
+      } else {
+        exhausted |= 1 << x0;  // the tail: the tile's end takes from the other queues
+        pend_ok = false;
+      }
+    }
+  };
+  auto publish = [&]() {
+    if (w0 && claimed) {
+      s_q[it & 1] = resolve();
+      claimed = false;
+    }
+  };
+
   // PURE: every position the k-tile loads (kt+1 .. kt+1+PFD) is the current tile's.
   auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c) {
     constexpr bool FIRST = decltype(first_c)::value;
@@ -437,6 +545,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // epilogue and then the prefetches.
     if (FIRST && primed) wait_vm<FIRST_N_PRIMED>();
     else wait_vm<NPF>();
+    if (!FIRST && kt == pub_kt) publish_own();
     lds_barrier();
     const uint16_t* nst = ring[(gbase + kt + 1) % STAGES];
     if (LAST)
@@ -456,8 +565,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 
   for (;;) {
     // The next tile of this workgroup, loaded ahead if it is long enough.
-    const int idn = xcd_tile(it + 1, gridDim.x);
-    const bool has_next = (it + 1) * (int)gridDim.x < sched.total && idn < sched.total;
+    int idn;
+    bool has_next;
+    if (dyn) {
+      lds_barrier();  // s_q[(it+1)&1] was published before it; s_q[it&1] has been read by every wave
+      idn = __builtin_amdgcn_readfirstlane(s_q[(it + 1) & 1]);
+      has_next = idn < sched.total;
+      if (w0 && has_next) {  // tile it+2, published into s_q[it&1]
+        claim_own();
+        claimed = true;
+      }
+    } else {
+      idn = xcd_tile(it + 1, gridDim.x);
+      has_next = (it + 1) * (int)gridDim.x < sched.total && idn < sched.total;
+    }
     TileCtx tn = t;
     Ld lnext = null_ld;
     if (has_next) {
@@ -681,6 +802,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       }
     }
 
+    if (dyn) publish();  // a tile without a k-tile 1 publishes here
     // Advance to the next tile.
     gbase += cur.nk;
     ++it;
@@ -690,6 +812,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     primed = pipe;
   }
   wait_vm<0>();  // no LDS DMA may land after the workgroup ends
+  dyn_finish();
 }
 
 }  // namespace moe

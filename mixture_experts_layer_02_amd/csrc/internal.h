@@ -6,6 +6,7 @@
 namespace moe {
 
 int num_cus();
+hipError_t launch_hold(int workgroups, int lds_bytes, int microseconds, hipStream_t s);
 
 size_t permute_workspace(const moe_desc& d);
 size_t router_bwd_workspace(const moe_desc& d);

@@ -20,21 +20,26 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n
 
 
 def test_desc_struct_matches_header_size():
-    # 10 x 4-byte fields, no padding
-    assert ctypes.sizeof(moe.MoeDesc) == 40
+    # 11 x 4-byte fields, 4 bytes of padding, one 8-byte pointer
+    assert ctypes.sizeof(moe.MoeDesc) == 56
+    assert moe.MoeDesc.tile_counters.offset == 48
 
 
 def _d(**kw):
     base = dict(T=64, d=128, f=64, E=8, k=2, expert_begin=0, num_local=8, dtype=moe.MOE_BF16)
+    extra = {n: kw.pop(n) for n in ("tile_schedule", "tile_counters") if n in kw}
     base.update(kw)
-    return moe.make_desc(**base)
+    d = moe.make_desc(**base)
+    for n, v in extra.items():
+        setattr(d, n, v)
+    return d
 
 
 @pytest.mark.parametrize("kw,rc", [
@@ -49,6 +54,9 @@ def _d(**kw):
     (dict(E=2048, num_local=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=64, k=33, num_local=64), moe.MOE_ERR_UNSUPPORTED),
     (dict(dtype=7), moe.MOE_ERR_UNSUPPORTED),
+    (dict(tile_schedule=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(tile_schedule=1), moe.MOE_ERR_INVALID_ARG),    # dynamic order without counters
+    (dict(tile_schedule=1, tile_counters=8), moe.MOE_ERR_INVALID_ARG),  # misaligned counters
 ])
 def test_invalid_descriptors_are_rejected(kw, rc):
     n = ctypes.c_size_t(0)
@@ -57,7 +65,7 @@ def test_invalid_descriptors_are_rejected(kw, rc):
 
 def test_wrong_struct_size_and_null_desc():
     d = _d()
-    d.struct_size = 36
+    d.struct_size = 40                                  # the descriptor before the tile-order fields
     n = ctypes.c_size_t(0)
     assert moe.lib().moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_route(None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
@@ -101,3 +109,10 @@ def test_status_strings():
     l = moe.lib()
     for rc in (0, -1, -2, -3, -4, 5):
         assert isinstance(l.moe_status_str(rc), bytes)
+
+
+def test_hold_cus_rejects_bad_arguments():
+    l = moe.lib()
+    for wg, lds, us in [(0, 1024, 10), (5000, 1024, 10), (4, 2, 10), (4, 200 * 1024, 10), (4, 1024, -1),
+                        (4, 1024, 2000000)]:
+        assert l.moe_hold_cus(wg, lds, us, None) == moe.MOE_ERR_INVALID_ARG
