@@ -22,6 +22,10 @@ ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "hold.hip"]
+# ffn.hip: the GEMMs' dynamic tile claims are one lane's atomic whose result is
+# used a k-tile later; LLVM's atomic optimizer would rewrite them into a form
+# that waits for the result at once (and for every load in flight before it).
+EXTRA = {"ffn.hip": ["-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _run(cmd):
@@ -39,7 +43,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

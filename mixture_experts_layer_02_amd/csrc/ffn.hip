@@ -63,10 +63,14 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;
   if (grid <= 0) return hipSuccess;
   if constexpr (std::is_same<AT, uint16_t>::value) {
-    if ((EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32)
-      gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true><<<(unsigned)grid, 256, 0, s>>>(p);
-    else
-      gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false><<<(unsigned)grid, 256, 0, s>>>(p);
+    const bool cf = (EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32;
+    if (p.dyn) {
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true><<<(unsigned)grid, 256, 0, s>>>(p);
+      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true><<<(unsigned)grid, 256, 0, s>>>(p);
+    } else {
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false><<<(unsigned)grid, 256, 0, s>>>(p);
+      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false><<<(unsigned)grid, 256, 0, s>>>(p);
+    }
   }
   return hipGetLastError();
 }

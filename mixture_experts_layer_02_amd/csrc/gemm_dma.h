@@ -176,7 +176,7 @@ __device__ __forceinline__ void wait_stages(int later) {
 // outside the tile fall outside the store resources), so that the number of
 // memory instructions it issues is a compile-time constant and the next
 // tile's first wait can let them stay in flight.
-template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32>
+template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
@@ -315,27 +315,42 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // after the wait of k-tile 1, when the atomic has long returned.  The last
   // workgroup to finish (p.dyn[8] counts them) zeroes the counters.
   __shared__ int s_q[2];
-  const bool dyn = p.dyn != nullptr;
+  constexpr bool dyn = DYN;  // a separate instantiation: the static one carries none of this
   const bool w0 = wave == 0;  // wave 0 runs the claims, all its lanes alike
   const int nq = (gridDim.x % 8) ? 1 : 8;
   const int x0 = (int)blockIdx.x % nq;
-  // Wave 0 state (the same in all its lanes).  Every lane of wave 0 adds 1
-  // to a counter, so a claim advances it by 64 and each lane's old value
-  // shifted right by 6 is the claim's index in its queue.
+  // Wave 0 state (the same in all its lanes).  pend: the raw result of the
+  // own-queue claim in flight (its lane 0 holds the claim's index), or
+  // PEND_STEAL (the own queue is empty: take from the others).
+  constexpr int PEND_NONE = -1, PEND_STEAL = -2;
   int exhausted = 0;  // bit x: queue x is known to be empty
-  int pend = 0;       // raw result of the own-queue claim in flight
-  bool pend_ok = false;
-  auto q_tile = [&](int x, int n) -> int {
+  int pend = PEND_NONE;
+  // What the tile's claim still needs: 0 nothing, 1 publishing the own-queue
+  // claim in pend, 2 taking from the other queues.  Kept apart from pend so
+  // that pend is not rewritten inside the k-loop: a rewrite there would
+  // make the compiler copy it, and wait for the atomic, where the loop starts.
+  int pstate = 0;
+  auto q_tile = [&](int x, int n) __attribute__((always_inline)) -> int {
     return nq == 1 ? n : (n / run) * (int)gridDim.x + x * run + (n % run);
   };
-  // The tile of the own-queue claim (pend, if pend_ok), else of the other
-  // queues in turn; sched.total when every queue is empty.  Unrolled with no
-  // early exit, and all of wave 0 runs it, so that the control flow stays
-  // uniform and the compiler keeps the tile state in scalar registers.
-  auto resolve = [&]() -> int {
+  // A claim on counter x: lane 0 adds 1; its result is the claim's index.  The result is waited for only where it is
+  // used (this file is built with LLVM's atomic optimizer off, which would
+  // otherwise combine the wave's atomic into one lane's and wait for it at
+  // once, stalling wave 0 behind every load in flight).
+  auto claim = [&](int x) __attribute__((always_inline)) -> int {
+    typedef __attribute__((address_space(1))) int gint;  // global: a flat atomic would also count on lgkmcnt
+    int r = 0;
+    if (lane == 0) r = __hip_atomic_fetch_add((gint*)(p.dyn + x), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return r;
+  };
+  // The tile of claim state n (see pend), taking from the other queues in
+  // turn when the own one is empty; sched.total when every queue is.
+  // Unrolled with no early exit, and all of wave 0 runs it, so that the
+  // control flow stays uniform and the tile state stays in scalar registers.
+  auto resolve = [&](int n) __attribute__((always_inline)) -> int {
     int found = sched.total;
-    if (pend_ok) {
-      const int c = q_tile(x0, __builtin_amdgcn_readfirstlane(pend) >> 6);
+    if (n >= 0) {
+      const int c = q_tile(x0, n);
       if (c < sched.total) found = c;
       else exhausted |= 1 << x0;
     }
@@ -343,20 +358,19 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     for (int s = 1; s < 8; ++s) {
       const int x = (x0 + s) & 7;
       if (s < nq && found >= sched.total && !((exhausted >> x) & 1)) {
-        const int c = q_tile(x, __builtin_amdgcn_readfirstlane(atomicAdd(p.dyn + x, 1)) >> 6);
+        const int c = q_tile(x, __builtin_amdgcn_readfirstlane(claim(x)));
         if (c < sched.total) found = c;
         else exhausted |= 1 << x;
       }
     }
     return found;
   };
-  auto claim_own = [&]() {
-    pend_ok = !((exhausted >> x0) & 1);
-    if (pend_ok) pend = atomicAdd(p.dyn + x0, 1);
+  auto claim_own = [&]() __attribute__((always_inline)) -> int {
+    return ((exhausted >> x0) & 1) ? PEND_STEAL : claim(x0);
   };
-  auto dyn_finish = [&]() {
+  auto dyn_finish = [&]() __attribute__((always_inline)) {
     if (dyn && w0) {
-      const int done = __builtin_amdgcn_readfirstlane(atomicAdd(p.dyn + 8, 1)) >> 6;
+      const int done = __builtin_amdgcn_readfirstlane(claim(8));
       if (done == (int)gridDim.x - 1) {  // the last workgroup: every claim is over
 #pragma unroll
         for (int x = 0; x < 9; ++x) atomicExch(p.dyn + x, 0);
@@ -368,13 +382,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   int id;
   if (dyn) {
     if (w0) {
-      claim_own();
-      const int i0 = resolve();
-      int i1 = sched.total;
-      if (i0 < sched.total) {
-        claim_own();
-        i1 = resolve();
-      }
+      const int i0 = resolve(__builtin_amdgcn_readfirstlane(claim_own()));
+      const int i1 = i0 < sched.total ? resolve(__builtin_amdgcn_readfirstlane(claim_own())) : sched.total;
       s_q[0] = i0;
       s_q[1] = i1;
     }
@@ -499,27 +508,28 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   bf16x8 fa[2][MI], fb[2][NI];
 
   // Dynamic order: the claim issued at the top of tile it resolves to tile
-  // it+2's id, stored where the top of tile it+1 reads it.
-  bool claimed = false;
-  // k-tile after whose wait the own-queue claim is published (opaque to the
-  // compiler, which would otherwise peel that k-tile into a copy of its own).
+  // it+2's id, stored where the top of tile it+1 reads it.  k-tile pub_kt
+  // publishes an own-queue claim once its wait has passed (the atomic has long
+  // returned by then); the tile's end publishes whatever is left (the tail,
+  // or a tile without that k-tile).  pub_kt is opaque to the compiler, which
+  // would otherwise peel that k-tile into a copy of its own.
   const int pub_kt = dyn ? __builtin_amdgcn_readfirstlane(p.ngroups >= 0 ? 1 : 2) : -1;
-  auto publish_own = [&]() {
-    if (w0 && claimed && pend_ok) {
-      const int c = q_tile(x0, __builtin_amdgcn_readfirstlane(pend) >> 6);
+  auto publish_own = [&]() __attribute__((always_inline)) {
+    if (w0 && pstate == 1) {
+      const int c = q_tile(x0, __builtin_amdgcn_readfirstlane(pend));
       if (c < sched.total) {
         s_q[it & 1] = c;
-        claimed = false;
+        pstate = 0;
       } else {
-        exhausted |= 1 << x0;  // the tail: the tile's end takes from the other queues
-        pend_ok = false;
+        exhausted |= 1 << x0;
+        pstate = 2;
       }
     }
   };
-  auto publish = [&]() {
-    if (w0 && claimed) {
-      s_q[it & 1] = resolve();
-      claimed = false;
+  auto publish = [&]() __attribute__((always_inline)) {
+    if (w0 && pstate != 0) {
+      s_q[it & 1] = resolve(pstate == 1 ? __builtin_amdgcn_readfirstlane(pend) : PEND_NONE);
+      pstate = 0;
     }
   };
 
@@ -572,8 +582,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       idn = __builtin_amdgcn_readfirstlane(s_q[(it + 1) & 1]);
       has_next = idn < sched.total;
       if (w0 && has_next) {  // tile it+2, published into s_q[it&1]
-        claim_own();
-        claimed = true;
+        pend = claim_own();
+        pstate = ((exhausted >> x0) & 1) ? 2 : 1;
       }
     } else {
       idn = xcd_tile(it + 1, gridDim.x);
