@@ -163,6 +163,19 @@ int moe_grouped_ffn(const moe_desc* desc, const int32_t* offsets, const void* x_
 int moe_expert_gate_up(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* W1,
                        const void* W3, void* gu, void* h, void* stream);
 
+/* A4 + A5 fused (Domyn page, section "Dynamic tile scheduling in SonicMoE":
+ * SonicMoE runs the expert GEMMs straight on the token-dispatch layout,
+ * without a permuted copy of the tokens): moe_expert_gate_up with
+ * x_perm[r] read as x[row_token[r]] inside the GEMM's operand loads, so that
+ * x_perm is never written (moe_permute may then be called with x = NULL).
+ *   row_token [R_cap] int32 from moe_permute; x [T][d] bf16.  Results are
+ *   bitwise those of moe_expert_gate_up on x_perm.  MOE_ERR_UNSUPPORTED
+ *   unless dtype is MOE_BF16 and T*d*2 < 2^31 (x is addressed with 32-bit
+ *   offsets). */
+int moe_expert_gate_up_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                              const void* x, const void* W1, const void* W3, void* gu, void* h,
+                              void* stream);
+
 /* A6 alone: the down grouped GEMM, y_perm[r] = h[r] W2[n]^T (second half of
  * moe_grouped_ffn). */
 int moe_expert_down(const moe_desc* desc, const int32_t* offsets, const void* h, const void* W2,
@@ -212,6 +225,14 @@ int moe_expert_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* 
 int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const void* x_perm,
                            const void* h, const void* dgu, const void* dy_perm, float* dW1,
                            float* dW3, float* dW2, void* ws, size_t ws_bytes, void* stream);
+
+/* B4 with the gather fused (as moe_expert_gate_up_gather): dW1 and dW3 read
+ * the rows of x_perm as x[row_token[r]] inside the GEMM's operand loads.
+ *   Results are bitwise those of moe_grouped_ffn_bwd_dw on x_perm; same
+ *   conditions as moe_expert_gate_up_gather. */
+int moe_grouped_ffn_bwd_dw_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                                  const void* x, const void* h, const void* dgu, const void* dy_perm,
+                                  float* dW1, float* dW3, float* dW2, void* stream);
 
 /* B5a, backward of the gather: dx[t] = dx_add[t] + sum over local slots j of
  *   dx_perm[slot_row[t][j]], summed in float32; dx [T][d] dtype out;

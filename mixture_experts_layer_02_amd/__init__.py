@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "permute",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -77,6 +77,8 @@ _SIGS = {
     "moe_permute": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_expert_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_gate_up_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_grouped_ffn_bwd_dw_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dh": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp],
@@ -209,6 +211,15 @@ def expert_gate_up(desc, offsets, x_perm, w1, w3, gu, h):
     _call("moe_expert_gate_up", desc, offsets, x_perm, w1, w3, gu, h, _stream())
 
 
+def expert_gate_up_gather(desc, offsets, row_token, x, w1, w3, gu, h):
+    _call("moe_expert_gate_up_gather", desc, offsets, row_token, x, w1, w3, gu, h, _stream())
+
+
+def grouped_ffn_bwd_dw_gather(desc, offsets, row_token, x, h, dgu, dy_perm, dw1, dw3, dw2):
+    _call("moe_grouped_ffn_bwd_dw_gather", desc, offsets, row_token, x, h, dgu, dy_perm, dw1, dw3, dw2,
+          _stream())
+
+
 def expert_down(desc, offsets, h, w2, y_perm):
     _call("moe_expert_down", desc, offsets, h, w2, y_perm, _stream())
 
@@ -260,7 +271,8 @@ def router_bwd_acc(desc, x, wr, dlogits, dx, dwr, ws):
 class Buffers:
     """Every device tensor of one forward (+ backward) pass of a layer, allocated once."""
 
-    def __init__(self, desc: MoeDesc, device="cuda", backward=False):
+    def __init__(self, desc: MoeDesc, device="cuda", backward=False, gather=False):
+        """gather=True: the expert GEMMs read x through row_token (no x_perm)."""
         dt = desc.torch_dtype
         T, d, f, E, k, NL, Rc = desc.T, desc.d, desc.f, desc.E, desc.k, desc.num_local, desc.R_cap
         z = dict(device=device)
@@ -273,7 +285,8 @@ class Buffers:
         self.offsets = torch.empty(NL + 1, dtype=i32, **z)
         self.row_token = torch.empty(Rc, dtype=i32, **z)
         self.slot_row = torch.empty(T, k, dtype=i32, **z)
-        self.x_perm = torch.empty(Rc, d, dtype=dt, **z)
+        self.gather = gather
+        self.x_perm = None if gather else torch.empty(Rc, d, dtype=dt, **z)
         self.gu = torch.empty(Rc, 2 * f, dtype=dt, **z) if backward else None
         self.h = torch.empty(Rc, f, dtype=dt, **z)
         self.y_perm = torch.empty(Rc, d, dtype=dt, **z)
@@ -306,8 +319,13 @@ def forward(b: Buffers, x, wr, w1, w3, w2, bias=None, routing=None, n_groups=1):
         idx, w = b.topk_idx, b.topk_w
     else:
         idx, w = routing
-    permute(D, idx, x, b.counts, b.offsets, b.row_token, b.slot_row, b.x_perm, b.ws_permute)
-    grouped_ffn(D, b.offsets, b.x_perm, w1, w3, w2, b.gu, b.h, b.y_perm)
+    if b.gather:
+        permute(D, idx, None, b.counts, b.offsets, b.row_token, b.slot_row, None, b.ws_permute)
+        expert_gate_up_gather(D, b.offsets, b.row_token, x, w1, w3, b.gu, b.h)
+        expert_down(D, b.offsets, b.h, w2, b.y_perm)
+    else:
+        permute(D, idx, x, b.counts, b.offsets, b.row_token, b.slot_row, b.x_perm, b.ws_permute)
+        grouped_ffn(D, b.offsets, b.x_perm, w1, w3, w2, b.gu, b.h, b.y_perm)
     combine(D, b.slot_row, w, b.y_perm, b.y)
     return b.y
 
@@ -318,7 +336,10 @@ def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None):
     idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
     combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
     grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
-    grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
+    if b.gather:
+        grouped_ffn_bwd_dw_gather(D, b.offsets, b.row_token, x, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
+    else:
+        grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
     unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx)
     if routing is None:
         route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits)

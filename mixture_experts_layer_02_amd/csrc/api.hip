@@ -173,6 +173,33 @@ int moe_expert_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* 
   return finish(moe::launch_bwd_dxp(*desc, offsets, W1, W3, dgu, dx_perm, S(stream)));
 }
 
+// The gathered operand x is addressed with 32-bit offsets.
+static bool gather_ok(const moe_desc* d) {
+  return d->dtype == MOE_BF16 && (int64_t)d->T * d->d * 2 < (1ll << 31);
+}
+
+int moe_expert_gate_up_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token, const void* x,
+                              const void* W1, const void* W3, void* gu, void* h, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(row_token) || !need(x) || !need(W1) || !need(W3) || !opt(gu) || !need(h))
+    return MOE_ERR_INVALID_ARG;
+  if (!gather_ok(desc)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_gate_up(*desc, offsets, x, W1, W3, gu, h, S(stream), row_token));
+}
+
+int moe_grouped_ffn_bwd_dw_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                                  const void* x, const void* h, const void* dgu, const void* dy_perm, float* dW1,
+                                  float* dW3, float* dW2, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(row_token) || !need(x) || !need(h) || !need(dgu) || !need(dy_perm) || !need(dW1) ||
+      !need(dW3) || !need(dW2))
+    return MOE_ERR_INVALID_ARG;
+  if (!gather_ok(desc)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_ffn_bwd_dw(*desc, offsets, x, h, dgu, dy_perm, dW1, dW3, dW2, S(stream), row_token));
+}
+
 int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* h,
                            const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2, void* ws,
                            size_t ws_bytes, void* stream) {

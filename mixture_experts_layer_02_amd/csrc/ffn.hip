@@ -55,7 +55,7 @@ constexpr int DMA_STAGES = DMA_BK == 64 ? 2 : 4;
 
 // bf16 products: the LDS-DMA kernel when every K-contiguous operand has K a
 // multiple of its 32-wide k-tile, else the register-staged kernel.
-template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL>
+template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE>
 hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) || (GRP != GRP_K && p.K % DMA_BK == 0);
   if (!std::is_same<AT, uint16_t>::value || !k_ok) return run_mfma<ALAY, BLAY, AT, GRP, EPI, DUAL>(p, ub_tiles, s);
@@ -65,11 +65,11 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if constexpr (std::is_same<AT, uint16_t>::value) {
     const bool cf = (EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32;
     if (p.dyn) {
-      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true><<<(unsigned)grid, 256, 0, s>>>(p);
-      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true><<<(unsigned)grid, 256, 0, s>>>(p);
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
+      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
     } else {
-      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false><<<(unsigned)grid, 256, 0, s>>>(p);
-      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false><<<(unsigned)grid, 256, 0, s>>>(p);
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
+      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
     }
   }
   return hipGetLastError();
@@ -156,11 +156,15 @@ hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr
   return run_f32<LAY_K, LAY_K, GRP_NONE, EPI_STORE, false>(p, cdiv(d.T, 64) * cdiv(d.E, 64), s);
 }
 
+// row_token != NULL: x_perm is x itself and row r of the product reads
+// x[row_token[r]] (the gather fused into the A operand; bf16 only).
 hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,
-                          const void* W3, void* gu, void* h, hipStream_t s) {
+                          const void* W3, void* gu, void* h, hipStream_t s, const int32_t* row_token) {
   const bool bf = d.dtype == MOE_BF16;
   GemmParams p = blank(d);
   p.A = x_perm;
+  p.gather = row_token;
+  p.gather_rows = d.T;
   p.lda = d.d;
   p.B = W1;
   p.B2 = W3;
@@ -174,6 +178,9 @@ hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void*
   p.N = d.f;
   p.K = d.d;
   p.c_f32 = bf ? 0 : 1;
+  if (bf && row_token)
+    return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true, GATH_A>(p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
+  if (row_token) return hipErrorNotSupported;
   if (bf) return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
   return run_f32<LAY_K, LAY_K, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
 }
@@ -243,9 +250,11 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
 }
 
+// row_token != NULL: x_perm is x itself and k-row r of the dW1|dW3 product
+// reads x[row_token[r]] (the gather fused into the B operand; bf16 only).
 hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
                              const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
-                             hipStream_t s) {
+                             hipStream_t s, const int32_t* row_token) {
   const bool bf = d.dtype == MOE_BF16;
   // dW1 | dW3 [f][d] = [dG | dU]^T x_perm over each expert's rows (M = 2f split at f)
   GemmParams p = blank(d);
@@ -253,6 +262,8 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   p.lda = 2 * (int64_t)d.f;
   p.B = x_perm;
   p.ldb = d.d;
+  p.gather = row_token;
+  p.gather_rows = d.T;
   p.C = dW1;
   p.C2 = dW3;
   p.msplit = d.f;
@@ -264,7 +275,10 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   p.N = d.d;
   p.c_f32 = 1;
   hipError_t e;
-  if (bf) e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
+  if (bf && row_token)
+    e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_B>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
+  else if (row_token) e = hipErrorNotSupported;
+  else if (bf) e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
   else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
   if (e != hipSuccess) return e;
   // dW2 [d][f] = dy_perm^T h

@@ -26,6 +26,7 @@ namespace moe {
 enum { LAY_K = 0, LAY_MN = 1 };
 enum { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_ADD = 3 };  // EPI_ADD: C += product
+enum { GATH_NONE = 0, GATH_A = 1, GATH_B = 2 };  // gathered operand of the LDS-DMA kernel
 
 constexpr int MAXG = 1024;
 
@@ -51,6 +52,8 @@ struct GemmParams {
   void* gu_out;         // EPI_SWIGLU: [rows][2N], G | U (NULL = not saved)
   int c_f32;            // 1: C is float, 0: C is bf16
   int* dyn;             // dynamic tile queues (int[16], zero on entry and on exit), NULL = static order
+  const int32_t* gather;  // gathered operand (see gemm_dma_kernel's GATH): row r of it is row gather[r]
+  int gather_rows;        //   of the source matrix, which has gather_rows rows
 };
 
 struct TileCtx {

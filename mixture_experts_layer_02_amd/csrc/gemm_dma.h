@@ -176,10 +176,20 @@ __device__ __forceinline__ void wait_stages(int later) {
 // outside the tile fall outside the store resources), so that the number of
 // memory instructions it issues is a compile-time constant and the next
 // tile's first wait can let them stay in flight.
-template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN>
+//
+// GATH (the Domyn page's SonicMoE: expert GEMMs read the tokens in place,
+// with no permuted copy): 0 none; GATH_A: the K-contiguous A of a GRP_M
+// product is x[gather[r]] for row r (gate/up from x through row_token);
+// GATH_B: the MN-contiguous B of a GRP_K product has k-row k equal to row
+// gather[k] of x (dW1|dW3 from x through row_token).  The gathered matrix
+// has gather_rows rows of ldb (or lda) elements and must stay under 2 GiB.
+template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN, int GATH>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
+  static_assert(GATH == 0 || (GATH == GATH_A && ALAY == LAY_K && GRP == GRP_M) ||
+                    (GATH == GATH_B && BLAY == LAY_MN && GRP == GRP_K && !DUAL),
+                "gathered operands: K-contiguous A of GRP_M, MN-contiguous B of GRP_K");
   static_assert(BK == 64 && STAGES == 2, "ring of two 64-wide k-tiles");
   constexpr int MI = 4, NI = 4;          // 32 x 32 blocks per wave (128 x 128)
   constexpr int TILE_ELEMS = 256 * BK;   // one operand tile
@@ -193,6 +203,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   __shared__ int s_scan[256];
   __shared__ __attribute__((aligned(16))) float s_stage[4][8 * SP];
   __shared__ __attribute__((aligned(256))) uint32_t lds_junk[64];
+  // Gathered operand: the source rows of a tile (GATH_A, two tiles) or of a
+  // ring position (GATH_B, eight positions).
+  __shared__ __attribute__((aligned(256))) int32_t s_tok[GATH == GATH_A ? 2 : GATH == GATH_B ? 8 : 1]
+                                                         [GATH == GATH_A ? 256 : 64];
 
   Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
   sched.init(p, s_pref, s_scan);
@@ -222,7 +236,16 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     i32x4 ra, rb, rb2;
     int nk;
     uint32_t pa, pb;
+    // Gathered operand: the resource over the tile's tokens (the source
+    // rows of its A rows, GATH_A, or of its k-rows, GATH_B), how many are
+    // valid and the lane's L2-prefetch sector of that operand (-1: none).
+    i32x4 rt;
+    int glim;
+    int pfe;
   };
+  // GATH_A: the A offsets of the current and the next tile's rows (filled
+  // from their tokens once these are in LDS).
+  uint32_t gcur[GATH == GATH_A ? NJ : 1], gnext[GATH == GATH_A ? NJ : 1];
   // L2 prefetch: one instruction per wave per operand, each lane touching one
   // 64-byte sector.  A tile is also loaded by the tiles of the same XCD that
   // run at the same time and share it: the tiles of one n-tile and
@@ -261,7 +284,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int nlim_b = DUAL ? min(t.nlim, BN / 2) : t.nlim;
     L.ra = (ALAY == LAY_K) ? make_rsrc(a_base, (uint64_t)t.mlim * p.lda * 2)
                            : make_rsrc(a_base, (uint64_t)(klen * p.lda - t.m0) * 2);
-    if (BLAY == LAY_K) {
+    if (GATH == GATH_A) {  // rows come from anywhere in the source; row validity is in gv
+      L.ra = make_rsrc(Ag, (uint64_t)p.gather_rows * p.lda * 2);
+      L.rt = make_rsrc(p.gather + t.m0, (uint64_t)t.mlim * 4);
+    }
+    if (GATH == GATH_B) {  // k-rows come from anywhere in the source; k-row validity is in the offsets
+      L.rb = L.rb2 = make_rsrc(Bg + t.n0, (uint64_t)((int64_t)p.gather_rows * p.ldb - t.n0) * 2);
+      L.rt = make_rsrc(p.gather + t.k0, (uint64_t)klen * 4);
+    } else if (BLAY == LAY_K) {
       L.rb = make_rsrc(b_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2);
       L.rb2 = DUAL ? make_rsrc(b2_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2) : L.rb;
     } else if (p.ksplit) {  // k < ksplit from B, k >= ksplit from B2 (GRP_M: t.k0 = 0)
@@ -275,12 +305,25 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int cA = max(1, min(sched.NT, run / max(t.mtiles, 1)));
     L.pa = pf_voff(cA, t.ntile % cA, p.lda, ALAY, 1);
     L.pb = pf_voff(cB, t.mtile % cB, p.ldb, BLAY, DUAL ? 2 : 1);
+    if (GATH == GATH_A) {
+      const int e = t.ntile % cA + cA * (wave * 64 + lane);
+      L.glim = t.mlim;
+      L.pfe = e < ITEMS ? e : -1;
+      L.pa = 0x7FFFFFF0u;
+    }
+    if (GATH == GATH_B) {
+      const int e = t.mtile % cB + cB * (wave * 64 + lane);
+      L.glim = (int)klen;
+      L.pfe = e < ITEMS ? e : -1;
+    }
     return L;
   };
   Ld null_ld;  // loads nothing: every offset is outside its resources
-  null_ld.ra = null_ld.rb = null_ld.rb2 = make_rsrc(Ag, 0);
+  null_ld.ra = null_ld.rb = null_ld.rb2 = null_ld.rt = make_rsrc(Ag, 0);
   null_ld.nk = 0;
   null_ld.pa = null_ld.pb = 0x7FFFFFF0u;
+  null_ld.glim = 0;
+  null_ld.pfe = -1;
 
   // B resource and scalar offset of k-tile k of a tile.
   auto b_src = [&](const Ld& L, int k, i32x4& rbk, uint32_t& so_b) {
@@ -408,8 +451,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       k = pos;
       return cur;
     }
-    const bool c = pos < cur.nk;
-    k = c ? pos : pos - cur.nk;
+    // (cur.nk is uniform; with a gathered operand the compiler may hold a
+    // copy in a VGPR, so it is restated to keep k and the selects scalar.)
+    const int cnk = GATH != 0 ? __builtin_amdgcn_readfirstlane(cur.nk) : cur.nk;
+    const bool c = pos < cnk;
+    k = c ? pos : pos - cnk;
     Ld L;
     L.ra = c ? cur.ra : nxt.ra;
     L.rb = c ? cur.rb : nxt.rb;
@@ -417,8 +463,26 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     L.pa = c ? cur.pa : nxt.pa;
     L.pb = c ? cur.pb : nxt.pb;
     L.nk = 0;
+    if (GATH != 0) {
+      L.rt = c ? cur.rt : nxt.rt;
+      L.glim = c ? cur.glim : nxt.glim;
+      L.pfe = c ? cur.pfe : nxt.pfe;
+    }
     return L;
   };
+  // GATH_A: A offset jj of ring position pos (the current or the next tile's rows).
+  // (A position past the current tile reads the next tile's rows; when the
+  // next tile is not loaded ahead, its resource is empty and nothing loads.)
+  auto a_gv = [&](int pos, int jj, auto pure_c) __attribute__((always_inline)) -> uint32_t {
+    if (decltype(pure_c)::value) return gcur[GATH == GATH_A ? jj : 0];
+    return pos < cur.nk ? gcur[GATH == GATH_A ? jj : 0] : gnext[GATH == GATH_A ? jj : 0];
+  };
+  // GATH_B: the B offsets of the position whose DMA is being issued, and the
+  // L2-prefetch offset held for position kt+3 (see ktile).
+  uint32_t gvb[GATH == GATH_B ? NJ : 1];
+  uint32_t gpb = 0x7FFFFFF0u;
+#pragma unroll
+  for (int jj = 0; jj < (GATH == GATH_B ? NJ : 1); ++jj) gvb[jj] = 0x80000000u;
   // DMA instruction q (0 .. 2*NJ-1) of ring position pos: even q are A, odd q B.
   auto dma_one = [&](int pos, int q, auto pure_c) {
     int k;
@@ -427,7 +491,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
     if ((q & 1) == 0) {
-      dma16(L.ra, va[jj], a_so(k), st + j * 512);
+      dma16(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), st + j * 512);
+    } else if (GATH == GATH_B) {
+      dma16(L.rb, gvb[GATH == GATH_B ? jj : 0], 0u, st + TILE_ELEMS + j * 512);
     } else {
       i32x4 rbk;
       uint32_t so_b;
@@ -441,12 +507,68 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const Ld L = pick(pos, k, pure_c);
     if (o == 0) {
       touch4(L.ra, L.pa, a_so(k), lds_junk);
+    } else if (GATH == GATH_B) {
+      touch4(L.rb, gpb, __builtin_amdgcn_readfirstlane(0u), lds_junk);
     } else {
       i32x4 rbk;
       uint32_t so_b;
       b_src(L, k, rbk, so_b);
       touch4(rbk, L.pb, so_b, lds_junk);
     }
+  };
+
+  // ---- Gathered operands: token staging -------------------------------
+  const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+  // GATH_A: tile it's tokens go to s_tok[it & 1]; wave w copies rows
+  // 64w .. 64w+63 (rows past mlim read as 0 and are masked by glim).
+  auto tok_dma_tile = [&](const Ld& L, int slot) __attribute__((always_inline)) {
+    touch4(L.rt, (uint32_t)(wave * 64 + lane) * 4u, __builtin_amdgcn_readfirstlane(0u),
+           reinterpret_cast<const uint32_t*>(&s_tok[slot & (GATH == GATH_A ? 1 : 0)][wave * 64]));
+  };
+  // GATH_A: the tile's A offsets and A prefetch offset from its tokens
+  // (lane's rows 64w + 8jj + lane/8, and the prefetch sector's row pfe/2).
+  auto tok_fill_tile = [&](Ld& L, int slot, uint32_t (&gv)[GATH == GATH_A ? NJ : 1]) __attribute__((always_inline)) {
+    const int32_t* tk = s_tok[slot & (GATH == GATH_A ? 1 : 0)];
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;
+#pragma unroll
+    for (int jj = 0; jj < (GATH == GATH_A ? NJ : 1); ++jj) {
+      const int row = RPI * (wave * NJ + jj) + lane / CPR;
+      const int c = (lane % CPR) ^ swz_k<BK>(row);
+      // An invalid row gets bit 31 set, which puts it outside the resource
+      // (the source is under 2 GiB); a select on the value instead would
+      // make the compiler branch around the token read.
+      gv[jj] = ((uint32_t)tk[row] * lda2 + c * 16) | (row < L.glim ? 0u : 0x80000000u);
+    }
+    constexpr int SPR = BK / 32;
+    const int prow = L.pfe >= 0 ? L.pfe / SPR : 0;
+    L.pa = ((uint32_t)tk[prow] * lda2 + (L.pfe % SPR) * 64) | (L.pfe >= 0 && prow < L.glim ? 0u : 0x80000000u);
+  };
+  // GATH_B: ring position pos's 64 tokens go to s_tok[(gbase + pos) & 7];
+  // every wave issues the copy (so that every wave counts the same memory
+  // instructions) but only wave 0's lands in the ring.
+  auto tok_dma_pos = [&](int pos) __attribute__((always_inline)) {
+    int k;
+    const Ld L = pick(pos, k, std::false_type());
+    const uint32_t* dst = wave == 0 ? reinterpret_cast<const uint32_t*>(&s_tok[(gbase + pos) & 7][0]) : lds_junk;
+    touch4(L.rt, (uint32_t)(k * BK + lane) * 4u, __builtin_amdgcn_readfirstlane(0u), dst);
+  };
+  // GATH_B: the B offsets of position pos into gvb, and the prefetch offset
+  // of position ppos into gpb, from their tokens.
+  auto tok_fill_pos = [&](int pos, int ppos) __attribute__((always_inline)) {
+    int k;
+    const Ld L = pick(pos, k, std::false_type());
+    const int32_t* tk = s_tok[(gbase + pos) & 7];
+#pragma unroll
+    for (int jj = 0; jj < (GATH == GATH_B ? NJ : 1); ++jj) {
+      const int krow = 2 * (wave * NJ + jj) + (lane >> 5);
+      const int c = (lane & 31) ^ swz_mn(krow);
+      gvb[jj] = ((uint32_t)tk[krow] * ldb2 + c * 16) | (k * BK + krow < L.glim ? 0u : 0x80000000u);
+    }
+    int kp;
+    const Ld P = pick(ppos, kp, std::false_type());
+    const int32_t* tp = s_tok[(gbase + ppos) & 7];
+    const int pr = P.pfe >= 0 ? (P.pfe >> 3) : 0;
+    gpb = ((uint32_t)tp[pr] * ldb2 + (P.pfe & 7) * 64) | (P.pfe >= 0 && kp * BK + pr < P.glim ? 0u : 0x80000000u);
   };
 
   f32x16 acc[MI][NI];
@@ -500,7 +622,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // loads below, all unconditional).
   constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? 128
                           : (EPI == EPI_ADD ? 2 : 1) * (CF32 ? 64 : 32);
-  constexpr int FIRST_N_PRIMED = EPI_OPS + NPF > 63 ? 63 : EPI_OPS + NPF;
+  // (+1: a gathered operand's token copy is issued between the epilogue and
+  // the prefetches.)
+  constexpr int FIRST_OPS = EPI_OPS + NPF + (GATH != 0 ? 1 : 0);
+  constexpr int FIRST_N_PRIMED = FIRST_OPS > 63 ? 63 : FIRST_OPS;
   using N0 = std::integral_constant<int, 0>;
   using NDP = std::integral_constant<int, PART>;
   using NDF = std::integral_constant<int, PER>;
@@ -533,12 +658,29 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
   };
 
+  // GATH_A: the next tile's load state (its A offsets are filled from its
+  // tokens at k-tile gat_kt, opaque to the compiler for the reason above),
+  // and whether that has happened.
+  Ld lnext = null_ld;
+  bool pipe = false, gat_done = true;
+  const int gat_kt = GATH == GATH_A ? __builtin_amdgcn_readfirstlane(p.ngroups >= 0 ? 1 : 2) : -1;
+  auto gat_fill_next = [&]() __attribute__((always_inline)) {
+    if (!gat_done) {
+      tok_fill_tile(lnext, it + 1, gnext);
+      if (pipe) nxt.pa = lnext.pa;
+      gat_done = true;
+    }
+  };
+
   // PURE: every position the k-tile loads (kt+1 .. kt+1+PFD) is the current tile's.
   auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     using PU = decltype(pure_c);
     const uint16_t* st = ring[(gbase + kt) % STAGES];
+    // GATH_B: the tokens of position kt+5 (read two k-tiles later, after the
+    // barriers that follow their wait).
+    if (GATH == GATH_B) tok_dma_pos(kt + 5);
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
       if (s == 0) {
@@ -546,6 +688,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
           kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD);
         else
           kstep(NDP(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
+        // GATH_B: position kt+1 is issued whole; its offsets make way for
+        // those of kt+2 (issued at this k-tile's end and the next's start),
+        // and the prefetch offset for kt+4 (next k-tile's prefetch).
+        if (GATH == GATH_B) tok_fill_pos(kt + 2, kt + 4);
       } else {
         kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
       }
@@ -557,6 +703,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     else wait_vm<NPF>();
     if (!FIRST && kt == pub_kt) publish_own();
     lds_barrier();
+    // GATH_A: the next tile's tokens (copied at this tile's top, waited for
+    // by now in every wave) give its A offsets.
+    if (GATH == GATH_A && !FIRST && kt == gat_kt) gat_fill_next();
     const uint16_t* nst = ring[(gbase + kt + 1) % STAGES];
     if (LAST)
       kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
@@ -573,6 +722,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                                              (int)((int64_t)t.mlim * ld_elems * esz), 0x00020000);
   };
 
+  if (GATH == GATH_A) {  // the first tile's A offsets, from its tokens
+    tok_dma_tile(cur, 0);
+    wait_vm<0>();
+    lds_barrier();
+    tok_fill_tile(cur, 0, gcur);
+  }
   for (;;) {
     // The next tile of this workgroup, loaded ahead if it is long enough.
     int idn;
@@ -590,12 +745,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       has_next = (it + 1) * (int)gridDim.x < sched.total && idn < sched.total;
     }
     TileCtx tn = t;
-    Ld lnext = null_ld;
+    lnext = null_ld;
     if (has_next) {
       tn = sched.tile(p, s_pref, idn);
       lnext = setup(tn);
+      if (GATH == GATH_A) {
+        tok_dma_tile(lnext, it + 1);
+        gat_done = false;
+      }
     }
-    const bool pipe = has_next && lnext.nk >= STAGES && cur.nk >= 1;
+    // (A gathered operand: the next tile's A offsets are ready at k-tile 1
+    // (GATH_A), and token copies run five positions ahead (GATH_B), which
+    // must not reach past the next tile; so only a tile of five k-tiles or
+    // more hands over early.)
+    pipe = has_next && lnext.nk >= STAGES && cur.nk >= (GATH != 0 ? 5 : 1);
     nxt = pipe ? lnext : null_ld;
 
 #pragma unroll
@@ -607,11 +770,19 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 
     if (cur.nk > 0) {
       if (!primed) {
+        if (GATH == GATH_B) {  // tokens of positions 0 .. 4
+#pragma unroll
+          for (int q = 0; q < 5; ++q) tok_dma_pos(q);
+          wait_vm<0>();
+          lds_barrier();
+          tok_fill_pos(0, PFD);
+        }
         // Positions 0 and 1 whole, with position 0's prefetch in between.
 #pragma unroll
         for (int q = 0; q < PER; ++q) dma_one(0, q, std::false_type());
 #pragma unroll
         for (int o = 0; o < NPF; ++o) pf_one(PFD, o, std::false_type());
+        if (GATH == GATH_B) tok_fill_pos(1, PFD + 1);
 #pragma unroll
         for (int q = 0; q < PER; ++q) dma_one(1, q, std::false_type());
         wait_vm<PER + NPF>();  // position 0 has landed (then come its prefetch and position 1)
@@ -813,12 +984,21 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
 
     if (dyn) publish();  // a tile without a k-tile 1 publishes here
+    if (GATH == GATH_A && !gat_done) {  // a tile without a k-tile 1: wait for the next tile's tokens here
+      wait_vm<0>();
+      lds_barrier();
+      gat_fill_next();
+    }
     // Advance to the next tile.
     gbase += cur.nk;
     ++it;
     if (!has_next) break;
     t = tn;
     cur = pipe ? nxt : lnext;
+    if (GATH == GATH_A) {
+#pragma unroll
+      for (int jj = 0; jj < (GATH == GATH_A ? NJ : 1); ++jj) gcur[jj] = gnext[jj];
+    }
     primed = pipe;
   }
   wait_vm<0>();  // no LDS DMA may land after the workgroup ends

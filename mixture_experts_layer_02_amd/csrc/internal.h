@@ -27,7 +27,8 @@ hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const 
 hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
                                 const float* dx_add, void* dx, hipStream_t s);
 hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,
-                          const void* W3, void* gu, void* h, hipStream_t s);
+                          const void* W3, void* gu, void* h, hipStream_t s,
+                          const int32_t* row_token = nullptr);
 hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h, const void* W2, void* y_perm,
                        hipStream_t s);
 hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* W2, const void* gu,
@@ -36,7 +37,8 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
                           const void* dgu, void* dx_perm, hipStream_t s);
 hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
                              const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
-                             hipStream_t s);
+                             hipStream_t s,
+                             const int32_t* row_token = nullptr);
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
                              float* dx_router, void* dx_acc, float* dWr, void* ws, hipStream_t s);
 
