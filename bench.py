@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--hold-cus", type=int, default=0,
                     help="before each grouped GEMM, occupy this many CUs with another kernel (contention)")
     ap.add_argument("--hold-us", type=int, default=2000, help="how long each --hold-cus kernel runs")
+    ap.add_argument("--gather", action="store_true",
+                    help="gather fused into gate/up and dW1|dW3: no x_perm (A4 is index generation only)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -157,7 +159,7 @@ def main():
     counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
     D = moe.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype,
                       cfg.renormalize, tile_counters=counters)
-    b = moe.Buffers(D, backward=cfg.backward)
+    b = moe.Buffers(D, backward=cfg.backward, gather=args.gather)
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream(device=dev)
     gemm_rows = {"A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw"}
@@ -193,9 +195,16 @@ def main():
             idx, w = b.topk_idx, b.topk_w
         else:
             idx, w = routing
-        timed("A34_permute", lambda: moe.permute(D, idx, g["x"], b.counts, b.offsets, b.row_token, b.slot_row,
-                                                 b.x_perm, b.ws_permute), rec)
-        timed("A5_gate_up", lambda: moe.expert_gate_up(D, b.offsets, b.x_perm, g["w1"], g["w3"], b.gu, b.h), rec)
+        if args.gather:
+            timed("A34_permute", lambda: moe.permute(D, idx, None, b.counts, b.offsets, b.row_token, b.slot_row,
+                                                     None, b.ws_permute), rec)
+            timed("A5_gate_up", lambda: moe.expert_gate_up_gather(D, b.offsets, b.row_token, g["x"], g["w1"],
+                                                                  g["w3"], b.gu, b.h), rec)
+        else:
+            timed("A34_permute", lambda: moe.permute(D, idx, g["x"], b.counts, b.offsets, b.row_token,
+                                                     b.slot_row, b.x_perm, b.ws_permute), rec)
+            timed("A5_gate_up", lambda: moe.expert_gate_up(D, b.offsets, b.x_perm, g["w1"], g["w3"], b.gu, b.h),
+                  rec)
         timed("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), rec)
         timed("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), rec)
         if not cfg.backward:
@@ -204,8 +213,12 @@ def main():
                                                         b.dtopk_w), rec)
         timed("B2_dh", lambda: moe.expert_bwd_dh(D, b.offsets, g["w2"], b.gu, b.dy_perm, b.dgu), rec)
         timed("B3_dx", lambda: moe.expert_bwd_dx(D, b.offsets, g["w1"], g["w3"], b.dgu, b.dx_perm), rec)
-        timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1,
-                                                      b.dW3, b.dW2), rec)
+        if args.gather:
+            timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw_gather(D, b.offsets, b.row_token, g["x"], b.h, b.dgu,
+                                                                 b.dy_perm, b.dW1, b.dW3, b.dW2), rec)
+        else:
+            timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1,
+                                                          b.dW3, b.dW2), rec)
         timed("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), rec)
         timed("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx), rec)
         timed("B5_router_bwd", lambda: moe.router_bwd_acc(D, g["x"], g["wr"], b.dlogits, b.dx, b.dWr,
@@ -223,6 +236,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
+    peak_mem = torch.cuda.max_memory_allocated()
     R = int(b.offsets[-1].item())
     T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
     bb = 2 if cfg.dtype == "bf16" else 4
@@ -232,7 +246,7 @@ def main():
              "B5_router_bwd": 4.0 * T * d * E}
     ntok_local = int((b.slot_row >= 0).any(dim=1).sum().item())
     hbm_bytes = {"A2_route": T * E * 4 + T * cfg.k * 8,
-                 "A34_permute": ntok_local * d * bb + R * d * bb + T * cfg.k * 12 + R * 4,
+                 "A34_permute": (0 if args.gather else ntok_local * d * bb + R * d * bb) + T * cfg.k * 12 + R * 4,
                  "A7_combine": R * d * bb + T * d * bb + T * cfg.k * 8,
                  "B1_combine_bwd": T * d * bb + 2 * R * d * bb + T * cfg.k * 12,
                  "B5_route_bwd": T * E * 4 + T * cfg.k * 12,
@@ -279,8 +293,10 @@ def main():
                    "routed_rows": R, "global_batch": T, "parallelism": "single GPU",
                    "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k",
                    "tile_schedule": args.schedule,
+                   "gather_fused": bool(args.gather),
                    "contention": (f"{args.hold_cus} CUs held for {args.hold_us} us at each grouped GEMM"
                                   if args.hold_cus else None)},
+        "device_mem_peak_gb": round(peak_mem / 1e9, 2),
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_mfma": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
