@@ -11,7 +11,8 @@ Sources ("the pages"):
            (FastSparseMoEBlock with expert parallelism, stages 1-5) and Figure 5.
   [Domyn]  "Training a 1T-Params MoE on EU public infrastructure": the model
            table (hidden 6144, 384 routed experts, top-8, expert hidden 1792)
-           and the section on group-limited expert routing.
+           and the sections on group-limited expert routing and on the FP8
+           expert weight all-gather.
 
 Arithmetic: every input is widened to float64 and every step runs in float64
 with no intermediate rounding.  Matrix products use numpy's matmul as a
@@ -43,7 +44,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "router_logits", "topk_route", "topk_route_grouped", "count_tokens", "generate_indices", "permute",
+    "router_logits", "topk_route", "topk_route_grouped", "fp8_e4m3_decode", "fp8_e4m3_encode",
+    "fp8_quantize_blocks", "fp8_dequantize_blocks", "bf16_round", "count_tokens", "generate_indices", "permute",
     "silu", "silu_grad", "expert_ffn_rows", "expert_ffn", "combine",
     "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd", "unpermute_bwd",
     "route_bwd", "router_bwd", "layer_forward", "layer_backward",
@@ -133,6 +135,90 @@ def topk_route_grouped(logits, k, n_groups, renormalize=1):
     if renormalize:
         w = w / w.sum(axis=1, keepdims=True)
     return idx, w
+
+
+# --------------------------------------------------------------------------
+# FP8 expert weights [Domyn] ("FP8 expert weight all-gather"): blocks of 128
+# consecutive values, each scaled to the E4M3 range and cast, with one
+# float32 scale per block; dequantised to bf16 before the expert GEMMs.
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes):
+    """Value of every E4M3 code (1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 is subnormal, m/8 * 2^-6; the code with
+    all exponent and mantissa bits set is NaN; there is no infinity)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(x):
+    """The E4M3 code nearest to each x (|x| <= 448), ties to an even mantissa.
+
+    Positive codes are ordered like their values, and on each binade
+    [2^e, 2^(e+1)) (e >= -6) the codes step by 2^(e-3); below 2^-6 they step by
+    2^-9 (subnormals).  So the code is the binade's first code plus the
+    rounded number of steps, and a carry into the next binade falls out of the
+    contiguous numbering.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX) or not np.isfinite(x).all():
+        raise ValueError("oracle: E4M3 input out of range")
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                                  # subnormals share the step of binade -6
+    step = 2.0 ** (e - 3.0)
+    steps = np.rint(a / step)                                # round half to even
+    first = np.where(a < 2.0 ** -6, 0.0, (e + 7.0) * 8.0)    # code of 2^e (binade e >= -6)
+    base = np.where(a < 2.0 ** -6, 0.0, 2.0 ** e)
+    code = np.where(a < 2.0 ** -6, steps, first + (steps - base / step))
+    code = code.astype(np.int64)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)      # -0 and tiny negatives keep the sign
+
+
+def fp8_quantize_blocks(w, block=128):
+    """codes [n] uint8 and scales [n/block] float32 of w [n] (any shape, flattened).
+
+    Per block: amax = max |w| (float32); scale = amax / 448 and inv = 448 / amax,
+    both rounded to float32; each value is w * inv in float32, clamped to
+    [-448, 448] (the product may exceed 448 by a rounding) and encoded to the
+    nearest E4M3 code.  An all-zero block has scale 0 and all-zero codes.
+    """
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    if w.size % block:
+        raise ValueError("oracle: size must be a multiple of the block")
+    wb = w.reshape(-1, block)
+    amax = np.abs(wb).max(axis=1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1))
+    scale = np.where(nz, safe / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+    inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
+    xs = (wb * inv[:, None]).astype(np.float32)
+    xs = np.clip(xs, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    codes = np.where(nz[:, None], fp8_e4m3_encode(xs), 0).astype(np.uint8)
+    return codes.reshape(-1), scale
+
+
+def bf16_round(v):
+    """float32 values rounded to the nearest bfloat16 (ties to even), as float32."""
+    b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16 << 16
+    return b.astype(np.uint32).view(np.float32)
+
+
+def fp8_dequantize_blocks(codes, scales, block=128):
+    """bf16 weights (as float32 values) from codes and per-block scales:
+    decode(code) * scale in float32, rounded to bf16."""
+    dec = fp8_e4m3_decode(codes).astype(np.float32).reshape(-1, block)
+    v = (dec * np.asarray(scales, np.float32)[:, None]).astype(np.float32)
+    return bf16_round(v).reshape(-1)
 
 
 # --------------------------------------------------------------------------
