@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--hold-us", type=int, default=2000, help="how long each --hold-cus kernel runs")
     ap.add_argument("--gather", action="store_true",
                     help="gather fused into gate/up and dW1|dW3: no x_perm (A4 is index generation only)")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="expert weights held as blockwise-128 E4M3 codes + scales, dequantised to bf16 each step")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -164,7 +166,24 @@ def main():
     side = torch.cuda.Stream(device=dev)
     gemm_rows = {"A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw"}
 
+    fp8 = {}
+    if args.fp8_weights:
+        for n in ("w1", "w3", "w2"):
+            q = torch.empty(g[n].numel(), dtype=torch.uint8, device=dev)
+            sc = torch.empty(g[n].numel() // 128, dtype=torch.float32, device=dev)
+            moe.fp8_quantize(g[n], q, sc)
+            fp8[n] = (q, sc)
+        torch.cuda.synchronize()
+        qs, qe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        qs.record()
+        for n in ("w1", "w3", "w2"):
+            moe.fp8_quantize(g[n], fp8[n][0], fp8[n][1])
+        qe.record()
+        torch.cuda.synchronize()
+        fp8_quant_ms = qs.elapsed_time(qe)
     rows = ["A1_router_logits", "A2_route", "A34_permute", "A5_gate_up", "A6_down", "A7_combine"]
+    if args.fp8_weights:
+        rows = ["A0_fp8_dequant"] + rows
     if cfg.backward:
         rows += ["B1_combine_bwd", "B2_dh", "B3_dx", "B4_dw", "B5_route_bwd", "B5_unpermute", "B5_router_bwd"]
     ev = {r: [] for r in rows}
@@ -185,7 +204,13 @@ def main():
         else:
             fn()
 
+    def dequant_all():
+        for n in ("w1", "w3", "w2"):
+            moe.fp8_dequantize(fp8[n][0], fp8[n][1], g[n])
+
     def step(rec):
+        if args.fp8_weights:
+            timed("A0_fp8_dequant", dequant_all, rec)
         if routing is None:
             timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits), rec)
             if args.n_groups > 1:
@@ -245,7 +270,9 @@ def main():
              "B2_dh": 2.0 * R * d * f, "B3_dx": 4.0 * R * d * f, "B4_dw": 6.0 * R * d * f,
              "B5_router_bwd": 4.0 * T * d * E}
     ntok_local = int((b.slot_row >= 0).any(dim=1).sum().item())
-    hbm_bytes = {"A2_route": T * E * 4 + T * cfg.k * 8,
+    nw = 3 * cfg.num_local * d * f
+    hbm_bytes = {"A0_fp8_dequant": nw * (1 + 2) + nw // 128 * 4,
+                 "A2_route": T * E * 4 + T * cfg.k * 8,
                  "A34_permute": (0 if args.gather else ntok_local * d * bb + R * d * bb) + T * cfg.k * 12 + R * 4,
                  "A7_combine": R * d * bb + T * d * bb + T * cfg.k * 8,
                  "B1_combine_bwd": T * d * bb + 2 * R * d * bb + T * cfg.k * 12,
@@ -294,9 +321,13 @@ def main():
                    "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k",
                    "tile_schedule": args.schedule,
                    "gather_fused": bool(args.gather),
+                   "expert_weights": "fp8 e4m3 blocks of 128, dequantised each step" if args.fp8_weights else "bf16",
                    "contention": (f"{args.hold_cus} CUs held for {args.hold_us} us at each grouped GEMM"
                                   if args.hold_cus else None)},
         "device_mem_peak_gb": round(peak_mem / 1e9, 2),
+        "fp8_quantize": ({"ms": round(fp8_quant_ms, 4),
+                          "GB/s": round((nw * (2 + 1) + nw // 128 * 4) / fp8_quant_ms / 1e6, 1)}
+                         if args.fp8_weights else None),
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_mfma": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,

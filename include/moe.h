@@ -275,6 +275,25 @@ const char* moe_status_str(int status);
 /* Text of the last HIP error seen by a failing call on this thread. */
 const char* moe_last_error(void);
 
+/* FP8 expert weights (Domyn page, section "FP8 expert weight all-gather":
+ * the weights are cut into blocks of 128 values, each block is scaled to the
+ * E4M3 range and cast, with one float32 scale per block, and the receivers
+ * dequantise to bf16 before the expert GEMMs; the error is up to about 6% of
+ * the block maximum per value).
+ *   w [n] (MOE_BF16 or MOE_F32 as `dtype`), blocks of 128 consecutive values
+ *   in memory order (the rows of W1/W3 [NL][f][d] and W2 [NL][d][f] when d
+ *   and f are multiples of 128); q [n] uint8 E4M3 codes (OCP, no infinity,
+ *   448 the largest); scales [n/128] float32.  Per block: amax = max |w|,
+ *   scale = amax / 448, each code = the E4M3 value nearest to w * (448 / amax)
+ *   (ties to even, after clamping to +-448); a block of zeros has scale 0 and
+ *   codes 0.  Errors: MOE_ERR_INVALID_ARG if n is not a multiple of 128 or a
+ *   pointer is NULL or not 16-byte aligned. */
+int moe_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* scales, void* stream);
+
+/* The inverse: w [n] bf16 = decode(q) * scale, in float32 rounded to nearest
+ * even.  Same layouts and errors as moe_fp8_quantize. */
+int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, void* stream);
+
 /* Measurement aid (Domyn page, section "Dynamic tile scheduling in
  * SonicMoE": the two tile orders are compared with and without a dummy
  * kernel that occupies part of the GPU).  Launches `workgroups` one-wave

@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -91,7 +91,8 @@ _SIGS = {
     "moe_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_router_bwd_acc": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
 }
-EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error", "moe_hold_cus"])
+EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error", "moe_hold_cus",
+                                 "moe_fp8_quantize", "moe_fp8_dequantize"])
 
 _lib = None
 
@@ -111,6 +112,10 @@ def lib():
         l.moe_workspace_size.restype = ctypes.c_int
         l.moe_status_str.argtypes = [ctypes.c_int]
         l.moe_status_str.restype = ctypes.c_char_p
+        l.moe_fp8_quantize.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp]
+        l.moe_fp8_quantize.restype = ctypes.c_int
+        l.moe_fp8_dequantize.argtypes = [_vp, _vp, ctypes.c_int64, _vp, _vp]
+        l.moe_fp8_dequantize.restype = ctypes.c_int
         l.moe_hold_cus.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
         l.moe_hold_cus.restype = ctypes.c_int
         l.moe_last_error.argtypes = []
@@ -181,6 +186,27 @@ def router_logits(desc, x, wr, bias, logits, ws=None):
 
 def route(desc, logits, topk_idx, topk_w):
     _call("moe_route", desc, logits, topk_idx, topk_w, _stream())
+
+
+def fp8_quantize(w, q, scales):
+    """Blockwise-128 E4M3 codes q (uint8, w's size) and float32 scales (size/128) of w (bf16 or fp32)."""
+    dt = MOE_BF16 if w.dtype == torch.bfloat16 else MOE_F32
+    for t in (w, q, scales):
+        if not t.is_contiguous():
+            raise ValueError("libmoe needs contiguous tensors")
+    rc = lib().moe_fp8_quantize(w.data_ptr(), dt, w.numel(), q.data_ptr(), scales.data_ptr(), _stream())
+    if rc != MOE_OK:
+        raise MoeError("moe_fp8_quantize", rc)
+
+
+def fp8_dequantize(q, scales, w):
+    """bf16 weights w (q's size) = decode(q) * scale of each 128-value block."""
+    for t in (w, q, scales):
+        if not t.is_contiguous():
+            raise ValueError("libmoe needs contiguous tensors")
+    rc = lib().moe_fp8_dequantize(q.data_ptr(), scales.data_ptr(), q.numel(), w.data_ptr(), _stream())
+    if rc != MOE_OK:
+        raise MoeError("moe_fp8_dequantize", rc)
 
 
 def hold_cus(workgroups, microseconds, lds_bytes=96 * 1024, stream=None):

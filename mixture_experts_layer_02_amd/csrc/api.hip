@@ -263,6 +263,17 @@ const char* moe_status_str(int status) {
 
 const char* moe_last_error(void) { return g_last_error; }
 
+int moe_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* scales, void* stream) {
+  if (!need(w) || !need(q) || !need(scales) || n < 0 || n % 128) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_fp8_quantize(w, dtype, n, q, scales, S(stream)));
+}
+
+int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, void* stream) {
+  if (!need(w) || !need(q) || !need(scales) || n < 0 || n % 128) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_fp8_dequantize(q, scales, n, w, S(stream)));
+}
+
 int moe_hold_cus(int workgroups, int lds_bytes, int microseconds, void* stream) {
   if (workgroups < 1 || workgroups > 4096 || lds_bytes < 4 || lds_bytes > 160 * 1024 || microseconds < 0 ||
       microseconds > 1000000)

@@ -7,6 +7,8 @@ namespace moe {
 
 int num_cus();
 hipError_t launch_hold(int workgroups, int lds_bytes, int microseconds, hipStream_t s);
+hipError_t launch_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* scales, hipStream_t s);
+hipError_t launch_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, hipStream_t s);
 
 size_t permute_workspace(const moe_desc& d);
 size_t router_bwd_workspace(const moe_desc& d);

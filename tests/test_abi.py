@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 25
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n
@@ -116,3 +116,12 @@ def test_hold_cus_rejects_bad_arguments():
     for wg, lds, us in [(0, 1024, 10), (5000, 1024, 10), (4, 2, 10), (4, 200 * 1024, 10), (4, 1024, -1),
                         (4, 1024, 2000000)]:
         assert l.moe_hold_cus(wg, lds, us, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    l = moe.lib()
+    good = 1 << 20
+    assert l.moe_fp8_quantize(good, moe.MOE_BF16, 100, good, good, None) == moe.MOE_ERR_INVALID_ARG   # not 128k
+    assert l.moe_fp8_quantize(None, moe.MOE_BF16, 128, good, good, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_fp8_quantize(good, 7, 128, good, good, None) == moe.MOE_ERR_UNSUPPORTED
+    assert l.moe_fp8_dequantize(good, good + 4, 128, good, None) == moe.MOE_ERR_INVALID_ARG     # misaligned
