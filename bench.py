@@ -120,6 +120,8 @@ def main():
                     help="gather fused into gate/up and dW1|dW3: no x_perm (A4 is index generation only)")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights held as blockwise-128 E4M3 codes + scales, dequantised to bf16 each step")
+    ap.add_argument("--fp8-gemm", action="store_true",
+                    help="with --fp8-weights: the forward expert GEMMs read the FP8 weights directly")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -182,8 +184,10 @@ def main():
         torch.cuda.synchronize()
         fp8_quant_ms = qs.elapsed_time(qe)
     rows = ["A1_router_logits", "A2_route", "A34_permute", "A5_gate_up", "A6_down", "A7_combine"]
-    if args.fp8_weights:
-        rows = ["A0_fp8_dequant"] + rows
+    if args.fp8_gemm and not args.fp8_weights:
+        raise SystemExit("--fp8-gemm needs --fp8-weights")
+    if args.fp8_weights and not (args.fp8_gemm and not cfg.backward):
+        rows = ["A0_fp8_dequant"] + rows      # bf16 weights for the GEMMs (or for the backward)
     if cfg.backward:
         rows += ["B1_combine_bwd", "B2_dh", "B3_dx", "B4_dw", "B5_route_bwd", "B5_unpermute", "B5_router_bwd"]
     ev = {r: [] for r in rows}
@@ -209,7 +213,7 @@ def main():
             moe.fp8_dequantize(fp8[n][0], fp8[n][1], g[n])
 
     def step(rec):
-        if args.fp8_weights:
+        if args.fp8_weights and "A0_fp8_dequant" in rows:
             timed("A0_fp8_dequant", dequant_all, rec)
         if routing is None:
             timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits), rec)
@@ -220,7 +224,17 @@ def main():
             idx, w = b.topk_idx, b.topk_w
         else:
             idx, w = routing
-        if args.gather:
+        if args.fp8_gemm:
+            if args.gather:
+                timed("A34_permute", lambda: moe.permute(D, idx, None, b.counts, b.offsets, b.row_token,
+                                                         b.slot_row, None, b.ws_permute), rec)
+            else:
+                timed("A34_permute", lambda: moe.permute(D, idx, g["x"], b.counts, b.offsets, b.row_token,
+                                                         b.slot_row, b.x_perm, b.ws_permute), rec)
+            timed("A5_gate_up", lambda: moe.expert_gate_up_fp8(
+                D, b.offsets, b.row_token if args.gather else None, g["x"] if args.gather else b.x_perm,
+                fp8["w1"][0], fp8["w1"][1], fp8["w3"][0], fp8["w3"][1], b.gu, b.h), rec)
+        elif args.gather:
             timed("A34_permute", lambda: moe.permute(D, idx, None, b.counts, b.offsets, b.row_token, b.slot_row,
                                                      None, b.ws_permute), rec)
             timed("A5_gate_up", lambda: moe.expert_gate_up_gather(D, b.offsets, b.row_token, g["x"], g["w1"],
@@ -230,7 +244,11 @@ def main():
                                                      b.slot_row, b.x_perm, b.ws_permute), rec)
             timed("A5_gate_up", lambda: moe.expert_gate_up(D, b.offsets, b.x_perm, g["w1"], g["w3"], b.gu, b.h),
                   rec)
-        timed("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), rec)
+        if args.fp8_gemm:
+            timed("A6_down", lambda: moe.expert_down_fp8(D, b.offsets, b.h, fp8["w2"][0], fp8["w2"][1], b.y_perm),
+                  rec)
+        else:
+            timed("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), rec)
         timed("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), rec)
         if not cfg.backward:
             return
@@ -321,7 +339,9 @@ def main():
                    "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k",
                    "tile_schedule": args.schedule,
                    "gather_fused": bool(args.gather),
-                   "expert_weights": "fp8 e4m3 blocks of 128, dequantised each step" if args.fp8_weights else "bf16",
+                   "expert_weights": ("bf16" if not args.fp8_weights else
+                                      "fp8 e4m3 blocks of 128, read by the forward GEMMs" if args.fp8_gemm else
+                                      "fp8 e4m3 blocks of 128, dequantised each step"),
                    "contention": (f"{args.hold_cus} CUs held for {args.hold_us} us at each grouped GEMM"
                                   if args.hold_cus else None)},
         "device_mem_peak_gb": round(peak_mem / 1e9, 2),

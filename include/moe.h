@@ -294,6 +294,24 @@ int moe_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* sca
  * even.  Same layouts and errors as moe_fp8_quantize. */
 int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, void* stream);
 
+/* A5 and A6 on FP8 weights (the page's further step: the expert GEMMs take
+ * the FP8 weights directly).  The weight tiles move as E4M3 codes - half the
+ * bytes of bf16 - and are decoded to bf16 in the kernel where the MFMA
+ * operands are read (decode * scale in float32, rounded to nearest even),
+ * so the results are bitwise those of moe_expert_gate_up / moe_expert_down
+ * on the weights moe_fp8_dequantize returns.
+ *   W1q, W3q [NL][f][d] and W2q [NL][d][f] E4M3 codes with scales W1s, W3s
+ *   [NL][f][d/128] and W2s [NL][d][f/128] as moe_fp8_quantize writes them;
+ *   activations as in the bf16 calls; row_token NULL: `a` is x_perm, else `a`
+ *   is x read through row_token (as moe_expert_gate_up_gather).
+ *   MOE_ERR_UNSUPPORTED unless dtype is MOE_BF16 and d and f are multiples
+ *   of 128 (and, with row_token, T*d*2 < 2^31). */
+int moe_expert_gate_up_fp8(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                           const void* a, const uint8_t* W1q, const float* W1s, const uint8_t* W3q,
+                           const float* W3s, void* gu, void* h, void* stream);
+int moe_expert_down_fp8(const moe_desc* desc, const int32_t* offsets, const void* h, const uint8_t* W2q,
+                        const float* W2s, void* y_perm, void* stream);
+
 /* Measurement aid (Domyn page, section "Dynamic tile scheduling in
  * SonicMoE": the two tile orders are compared with and without a dummy
  * kernel that occupies part of the GPU).  Launches `workgroups` one-wave

@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -78,6 +78,8 @@ _SIGS = {
     "moe_grouped_ffn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_expert_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_gate_up_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_gate_up_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_down_fp8": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_ffn_bwd_dw_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dh": [_vp, _vp, _vp, _vp, _vp, _vp],
@@ -244,6 +246,15 @@ def expert_gate_up_gather(desc, offsets, row_token, x, w1, w3, gu, h):
 def grouped_ffn_bwd_dw_gather(desc, offsets, row_token, x, h, dgu, dy_perm, dw1, dw3, dw2):
     _call("moe_grouped_ffn_bwd_dw_gather", desc, offsets, row_token, x, h, dgu, dy_perm, dw1, dw3, dw2,
           _stream())
+
+
+def expert_gate_up_fp8(desc, offsets, row_token, a, w1q, w1s, w3q, w3s, gu, h):
+    """gate/up on FP8 weights (codes + block scales); row_token None: `a` is x_perm, else x."""
+    _call("moe_expert_gate_up_fp8", desc, offsets, row_token, a, w1q, w1s, w3q, w3s, gu, h, _stream())
+
+
+def expert_down_fp8(desc, offsets, h, w2q, w2s, y_perm):
+    _call("moe_expert_down_fp8", desc, offsets, h, w2q, w2s, y_perm, _stream())
 
 
 def expert_down(desc, offsets, h, w2, y_perm):

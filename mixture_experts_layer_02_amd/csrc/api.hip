@@ -274,6 +274,31 @@ int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w
   return finish(moe::launch_fp8_dequantize(q, scales, n, w, S(stream)));
 }
 
+// FP8 weights in the GEMMs: bf16 activations, and K (d for gate/up, f for
+// down) in whole 128-value scale blocks.
+static bool q8_ok(const moe_desc* d) { return d->dtype == MOE_BF16 && d->d % 128 == 0 && d->f % 128 == 0; }
+
+int moe_expert_gate_up_fp8(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token, const void* a,
+                           const uint8_t* W1q, const float* W1s, const uint8_t* W3q, const float* W3s, void* gu,
+                           void* h, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !opt(row_token) || !need(a) || !need(W1q) || !need(W1s) || !need(W3q) || !need(W3s) ||
+      !opt(gu) || !need(h))
+    return MOE_ERR_INVALID_ARG;
+  if (!q8_ok(desc) || (row_token && !gather_ok(desc))) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_gate_up_q8(*desc, offsets, a, row_token, W1q, W1s, W3q, W3s, gu, h, S(stream)));
+}
+
+int moe_expert_down_fp8(const moe_desc* desc, const int32_t* offsets, const void* h, const uint8_t* W2q,
+                        const float* W2s, void* y_perm, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(h) || !need(W2q) || !need(W2s) || !need(y_perm)) return MOE_ERR_INVALID_ARG;
+  if (!q8_ok(desc)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_down_q8(*desc, offsets, h, W2q, W2s, y_perm, S(stream)));
+}
+
 int moe_hold_cus(int workgroups, int lds_bytes, int microseconds, void* stream) {
   if (workgroups < 1 || workgroups > 4096 || lds_bytes < 4 || lds_bytes > 160 * 1024 || microseconds < 0 ||
       microseconds > 1000000)

@@ -55,7 +55,7 @@ constexpr int DMA_STAGES = DMA_BK == 64 ? 2 : 4;
 
 // bf16 products: the LDS-DMA kernel when every K-contiguous operand has K a
 // multiple of its 32-wide k-tile, else the register-staged kernel.
-template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE>
+template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE, bool BQ8 = false>
 hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) || (GRP != GRP_K && p.K % DMA_BK == 0);
   if (!std::is_same<AT, uint16_t>::value || !k_ok) return run_mfma<ALAY, BLAY, AT, GRP, EPI, DUAL>(p, ub_tiles, s);
@@ -65,11 +65,11 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if constexpr (std::is_same<AT, uint16_t>::value) {
     const bool cf = (EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32;
     if (p.dyn) {
-      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
-      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
     } else {
-      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
-      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH><<<(unsigned)grid, 256, 0, s>>>(p);
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
     }
   }
   return hipGetLastError();
@@ -183,6 +183,53 @@ hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void*
   if (row_token) return hipErrorNotSupported;
   if (bf) return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
   return run_f32<LAY_K, LAY_K, GRP_M, EPI_SWIGLU, true>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
+}
+
+// FP8 expert weights in the GEMMs (bf16 only): W1q/W3q [NL][f][d] and W2q
+// [NL][d][f] E4M3 codes, s1/s3 [NL][f][d/128] and s2 [NL][d][f/128] block
+// scales.  row_token != NULL: a is x, read through it (as launch_gate_up).
+hipError_t launch_gate_up_q8(const moe_desc& d, const int32_t* offsets, const void* a, const int32_t* row_token,
+                             const uint8_t* W1q, const float* s1, const uint8_t* W3q, const float* s3, void* gu,
+                             void* h, hipStream_t s) {
+  GemmParams p = blank(d);
+  p.A = a;
+  p.lda = d.d;
+  p.gather = row_token;
+  p.gather_rows = d.T;
+  p.B = W1q;
+  p.B2 = W3q;
+  p.ldb = d.d;
+  p.bs = s1;
+  p.bs2 = s3;
+  p.b_gstride = (int64_t)d.f * d.d;
+  p.C = h;
+  p.ldc = d.f;
+  p.gu_out = gu;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.N = d.f;
+  p.K = d.d;
+  const int64_t ub = mtiles_ub(d, MT) * cdiv(d.f, MT / 2);
+  if (row_token) return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true, GATH_A, true>(p, ub, s);
+  return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true, GATH_NONE, true>(p, ub, s);
+}
+
+hipError_t launch_down_q8(const moe_desc& d, const int32_t* offsets, const void* h, const uint8_t* W2q,
+                          const float* s2, void* y_perm, hipStream_t s) {
+  GemmParams q = blank(d);
+  q.A = h;
+  q.lda = d.f;
+  q.B = W2q;
+  q.ldb = d.f;
+  q.bs = s2;
+  q.b_gstride = (int64_t)d.d * d.f;
+  q.C = y_perm;
+  q.ldc = d.d;
+  q.offsets = offsets;
+  q.ngroups = d.num_local;
+  q.N = d.d;
+  q.K = d.f;
+  return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false, GATH_NONE, true>(q, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
 }
 
 hipError_t launch_down(const moe_desc& d, const int32_t* offsets, const void* h, const void* W2, void* y_perm,

@@ -54,6 +54,8 @@ struct GemmParams {
   int* dyn;             // dynamic tile queues (int[16], zero on entry and on exit), NULL = static order
   const int32_t* gather;  // gathered operand (see gemm_dma_kernel's GATH): row r of it is row gather[r]
   int gather_rows;        //   of the source matrix, which has gather_rows rows
+  const float* bs;        // BQ8: float32 scale of each 128-value block of B's rows (B2's in bs2)
+  const float* bs2;
 };
 
 struct TileCtx {

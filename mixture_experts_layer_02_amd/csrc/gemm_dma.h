@@ -39,6 +39,8 @@ __device__ __forceinline__ int swz_k(int r) {
 // MN-contiguous: k-row r's chunk XOR, one of {0, 6, 12, 10} by r % 4, so the
 // 4 k-rows x 2..4 chunks read by one LDS cycle use distinct banks.
 __device__ __forceinline__ int swz_mn(int r) { return (0xAC60 >> ((r & 3) * 4)) & 0xF; }
+// FP8 K-contiguous rows of 64 bytes (four 16-byte chunks per k-tile).
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 3; }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -145,6 +147,25 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* S, int row0, int kk, int 
   }
 }
 
+// FP8 B fragment (k = kk*16 + (lane/32)*8 + 0..7 of row row0 + lane%32) as
+// bf16: the 8 codes are one 8-byte read, decoded to float32, multiplied by
+// the row's block scale (16 KB past the codes) and rounded to nearest even.
+typedef float f32x2_q8 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 frag_q8(const uint16_t* S, int row0, int kk, int lane) {
+  const int r = row0 + (lane & 31);
+  const uint8_t* Sb = reinterpret_cast<const uint8_t*>(S);
+  const uint2 c = *reinterpret_cast<const uint2*>(Sb + r * 64 + ((kk ^ swz8(r)) << 4) + ((lane >> 5) << 3));
+  const float sc = reinterpret_cast<const float*>(Sb + 16384)[r];
+  const f32x2_q8 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+  const f32x2_q8 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+  const f32x2_q8 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+  const f32x2_q8 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+  typedef uint32_t u32x4q __attribute__((ext_vector_type(4)));
+  const u32x4q w = {pack_bf2(v0[0] * sc, v0[1] * sc), pack_bf2(v1[0] * sc, v1[1] * sc),
+                    pack_bf2(v2[0] * sc, v2[1] * sc), pack_bf2(v3[0] * sc, v3[1] * sc)};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -183,18 +204,30 @@ __device__ __forceinline__ void wait_stages(int later) {
 // GATH_B: the MN-contiguous B of a GRP_K product has k-row k equal to row
 // gather[k] of x (dW1|dW3 from x through row_token).  The gathered matrix
 // has gather_rows rows of ldb (or lda) elements and must stay under 2 GiB.
-template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN, int GATH>
+//
+// BQ8 (FP8 expert weights, Domyn page section "FP8 expert weight
+// all-gather"): the K-contiguous B of a GRP_M product holds E4M3 codes, one
+// float32 scale per 128 consecutive values of a row (bs, bs2 for the second
+// B).  The tiles move as bytes (half the traffic and LDS of bf16) and are
+// decoded to bf16 when the MFMA fragments are read: decode * scale in
+// float32, rounded to nearest even, which is exactly what moe_fp8_dequantize
+// writes, so the product equals the bf16 product on dequantised weights.
+template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN, int GATH,
+          bool BQ8>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
   static_assert(GATH == 0 || (GATH == GATH_A && ALAY == LAY_K && GRP == GRP_M) ||
                     (GATH == GATH_B && BLAY == LAY_MN && GRP == GRP_K && !DUAL),
                 "gathered operands: K-contiguous A of GRP_M, MN-contiguous B of GRP_K");
+  static_assert(!BQ8 || (BLAY == LAY_K && GRP == GRP_M && GATH != GATH_B && BK == 64),
+                "FP8 B: K-contiguous B of GRP_M, 64-wide k-tiles (half a scale block)");
   static_assert(BK == 64 && STAGES == 2, "ring of two 64-wide k-tiles");
   constexpr int MI = 4, NI = 4;          // 32 x 32 blocks per wave (128 x 128)
   constexpr int TILE_ELEMS = 256 * BK;   // one operand tile
   constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
   constexpr int NJ = BK / 8;             // DMA instructions per wave per operand tile
+  constexpr int NJB = BQ8 ? NJ / 2 : NJ;  // ... for B (FP8 B is half the bytes)
   constexpr int KS = BK / 16;            // MFMA k-steps per k-tile
   constexpr int WC = NI * 32;            // columns of a wave's block
   constexpr int SP = WC + 4;             // staging row pitch (floats)
@@ -228,6 +261,22 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     va[jj] = dma_voff<BK, ALAY, false>(wave * NJ + jj, lane, p.lda);
     vb[jj] = dma_voff<BK, BLAY, DUAL>(wave * NJ + jj, lane, p.ldb);
   }
+  // FP8 B: a k-tile row is 64 bytes, four 16-byte chunks; instruction j
+  // covers rows 16j .. 16j+15, lane i row 16j + i/4 at LDS chunk i%4, which
+  // holds global chunk (i%4) ^ swz8(row) (the swizzle spreads the 8-byte
+  // fragment reads of consecutive rows over the banks).  The scale of a
+  // lane's row (wave w copies rows 64w .. 64w+63) sits 16 KB into the stage.
+  uint32_t vs = 0;
+  if (BQ8) {
+#pragma unroll
+    for (int jj = 0; jj < NJB; ++jj) {
+      const int row = 16 * (wave * NJB + jj) + lane / 4;
+      const int src_row = DUAL ? (row & 127) : row;
+      vb[jj] = (uint32_t)(src_row * p.K + (((lane & 3) ^ swz8(row)) << 4));
+    }
+    const int srow = DUAL ? ((wave * 64 + lane) & 127) : wave * 64 + lane;
+    vs = (uint32_t)(srow * (p.K / 128) * 4);
+  }
   const bool b_second = DUAL && wave >= 2;  // instructions j >= BK/4 read the second resource
 
   // Load state of one output tile: buffer resources over its operand tiles,
@@ -242,6 +291,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     i32x4 rt;
     int glim;
     int pfe;
+    i32x4 rs;  // BQ8: the scales of the tile's B rows (of the second B for waves 2 and 3 with dual B)
   };
   // GATH_A: the A offsets of the current and the next tile's rows (filled
   // from their tokens once these are in LDS).
@@ -305,6 +355,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int cA = max(1, min(sched.NT, run / max(t.mtiles, 1)));
     L.pa = pf_voff(cA, t.ntile % cA, p.lda, ALAY, 1);
     L.pb = pf_voff(cB, t.mtile % cB, p.ldb, BLAY, DUAL ? 2 : 1);
+    if (BQ8) {
+      // FP8 B: bytes, and a k-tile row is one 64-byte sector.
+      const uint8_t* q_grp = reinterpret_cast<const uint8_t*>(p.B) + (int64_t)t.g * p.b_gstride;
+      const uint8_t* q2_grp = reinterpret_cast<const uint8_t*>(p.B2) + (int64_t)t.g * p.b_gstride;
+      L.rb = make_rsrc(q_grp + (int64_t)t.n0 * p.K, (uint64_t)nlim_b * p.K);
+      L.rb2 = DUAL ? make_rsrc(q2_grp + (int64_t)t.n0 * p.K, (uint64_t)nlim_b * p.K) : L.rb;
+      const int kbl = p.K / 128;
+      const int64_t srow0 = (int64_t)t.g * (p.b_gstride / p.K) + t.n0;
+      const float* s_base = (DUAL && wave >= 2 ? p.bs2 : p.bs) + srow0 * kbl;
+      L.rs = make_rsrc(s_base, (uint64_t)nlim_b * kbl * 4);
+      const int parts = DUAL ? 2 : 1;
+      const int e = t.mtile % cB + cB * ((wave % (4 / parts)) * 64 + lane);
+      L.pb = e < 256 / parts ? (uint32_t)(e * p.K) : 0x7FFFFFF0u;
+    }
     if (GATH == GATH_A) {
       const int e = t.ntile % cA + cA * (wave * 64 + lane);
       L.glim = t.mlim;
@@ -319,7 +383,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     return L;
   };
   Ld null_ld;  // loads nothing: every offset is outside its resources
-  null_ld.ra = null_ld.rb = null_ld.rb2 = null_ld.rt = make_rsrc(Ag, 0);
+  null_ld.ra = null_ld.rb = null_ld.rb2 = null_ld.rt = null_ld.rs = make_rsrc(Ag, 0);
   null_ld.nk = 0;
   null_ld.pa = null_ld.pb = 0x7FFFFFF0u;
   null_ld.glim = 0;
@@ -328,7 +392,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // B resource and scalar offset of k-tile k of a tile.
   auto b_src = [&](const Ld& L, int k, i32x4& rbk, uint32_t& so_b) {
     rbk = b_second ? L.rb2 : L.rb;
-    if (BLAY == LAY_K) {
+    if (BQ8) {
+      so_b = (uint32_t)k * BK;
+    } else if (BLAY == LAY_K) {
       so_b = (uint32_t)k * BK * 2;
     } else if (p.ksplit && (int64_t)k * BK >= p.ksplit) {
       rbk = L.rb2;
@@ -453,7 +519,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
     // (cur.nk is uniform; with a gathered operand the compiler may hold a
     // copy in a VGPR, so it is restated to keep k and the selects scalar.)
-    const int cnk = GATH != 0 ? __builtin_amdgcn_readfirstlane(cur.nk) : cur.nk;
+    const int cnk = (GATH != 0 || BQ8) ? __builtin_amdgcn_readfirstlane(cur.nk) : cur.nk;
     const bool c = pos < cnk;
     k = c ? pos : pos - cnk;
     Ld L;
@@ -463,6 +529,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     L.pa = c ? cur.pa : nxt.pa;
     L.pb = c ? cur.pb : nxt.pb;
     L.nk = 0;
+    if (BQ8) L.rs = c ? cur.rs : nxt.rs;
     if (GATH != 0) {
       L.rt = c ? cur.rt : nxt.rt;
       L.glim = c ? cur.glim : nxt.glim;
@@ -488,6 +555,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     int k;
     const Ld L = pick(pos, k, pure_c);
     uint16_t* st = ring[(gbase + pos) % STAGES];
+    if (BQ8) {  // q < NJ: A; then NJB FP8 B instructions; then the B rows' scales
+      if (q < NJ) {
+        dma16(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), st + (wave * NJ + q) * 512);
+      } else if (q < NJ + NJB) {
+        i32x4 rbk;
+        uint32_t so_b;
+        b_src(L, k, rbk, so_b);
+        dma16(rbk, vb[q - NJ], so_b, st + TILE_ELEMS + (wave * NJB + q - NJ) * 512);
+      } else {
+        touch4(L.rs, vs, (uint32_t)(k >> 1) * 4u,
+               reinterpret_cast<const uint32_t*>(st + TILE_ELEMS + 8192 + wave * 128));
+      }
+      return;
+    }
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
     if ((q & 1) == 0) {
@@ -582,7 +663,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     } else {
       const int ni = f - 1;
       const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
-      b[ni] = frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
+      b[ni] = BQ8 ? frag_q8(st + TILE_ELEMS, brow, kk, lane) : frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
     }
   };
   // One k-step: the 16 MFMAs of fragments (a, b), with, in between, the
@@ -615,8 +696,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // position kt+1 is waited for (one barrier per k-tile); the last step reads
   // position kt+1's first fragments and issues the first half of position
   // kt+2 (the last k-tile issues it whole, before the epilogue).
-  constexpr int PER = 2 * NJ;
-  constexpr int PART = PER / 2;
+  constexpr int PER = BQ8 ? NJ + NJB + 1 : 2 * NJ;  // DMA instructions per wave per ring position
+  constexpr int PART = PER / 2;                      // first part; the second has PER - PART
   constexpr int PFD = 2;
   // Memory instructions per lane of one epilogue (the buffer stores and
   // loads below, all unconditional).
@@ -628,6 +709,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   constexpr int FIRST_N_PRIMED = FIRST_OPS > 63 ? 63 : FIRST_OPS;
   using N0 = std::integral_constant<int, 0>;
   using NDP = std::integral_constant<int, PART>;
+  using NDP1 = std::integral_constant<int, PER - PART>;
   using NDF = std::integral_constant<int, PER>;
   using NPP = std::integral_constant<int, NPF>;
   bf16x8 fa[2][MI], fb[2][NI];
@@ -687,7 +769,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         if (FIRST)
           kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD);
         else
-          kstep(NDP(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
+          kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
         // GATH_B: position kt+1 is issued whole; its offsets make way for
         // those of kt+2 (issued at this k-tile's end and the next's start),
         // and the prefetch offset for kt+4 (next k-tile's prefetch).

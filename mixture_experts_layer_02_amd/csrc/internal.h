@@ -7,6 +7,11 @@ namespace moe {
 
 int num_cus();
 hipError_t launch_hold(int workgroups, int lds_bytes, int microseconds, hipStream_t s);
+hipError_t launch_gate_up_q8(const moe_desc& d, const int32_t* offsets, const void* a, const int32_t* row_token,
+                             const uint8_t* W1q, const float* s1, const uint8_t* W3q, const float* s3, void* gu,
+                             void* h, hipStream_t s);
+hipError_t launch_down_q8(const moe_desc& d, const int32_t* offsets, const void* h, const uint8_t* W2q,
+                          const float* s2, void* y_perm, hipStream_t s);
 hipError_t launch_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, hipStream_t s);
 

@@ -117,3 +117,51 @@ def test_layer_on_fp8_weights(gpu):
                                cfg.num_local, cfg.renormalize)
     assert (to_host(b.topk_idx) == ref["idx"]).all()
     assert max_row_rel_err(to_host(b.y), ref["y"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("gather,dyn", [(False, False), (True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("scale", [
+    dict(T=2048, d=512, f=256, E=32, num_local=16, expert_begin=8),
+    dict(T=1500, d=384, f=256, E=64, num_local=24, expert_begin=40, k=6),    # ragged, empty experts
+    dict(T=300, d=128, f=128, E=8, num_local=8, expert_begin=0, k=2),        # K of 2 k-tiles
+])
+def test_fp8_gemms_equal_bf16_on_dequantised_weights(gpu, scale, gather, dyn):
+    # The FP8-weight GEMMs decode the codes in the kernel exactly as
+    # moe_fp8_dequantize does, so they must equal the bf16 GEMMs run on the
+    # dequantised weights bit for bit.
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[fp8 gemm] {scale} gather={gather} dynamic={dyn}", flush=True)
+    inp = synth.make_inputs(cfg, want=("x", "wr", "w1", "w3", "w2"))
+    dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2")}
+    q, deq = {}, {}
+    for n in ("w1", "w3", "w2"):
+        c = torch.empty(dev[n].numel(), dtype=torch.uint8, device=gpu)
+        sc = torch.empty(dev[n].numel() // 128, dtype=torch.float32, device=gpu)
+        moe.fp8_quantize(dev[n], c, sc)
+        q[n] = (c, sc)
+        deq[n] = torch.empty_like(dev[n])
+        moe.fp8_dequantize(c, sc, deq[n])
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype, cfg.renormalize)
+    D = moe.make_desc(*args, tile_counters=moe.new_tile_counters(gpu) if dyn else None)
+    b = moe.Buffers(D, backward=True)
+    moe.forward(b, dev["x"], dev["wr"], deq["w1"], deq["w3"], deq["w2"])     # reference: bf16 on dequantised
+    R = int(b.offsets[-1].item())
+    gu8 = torch.empty_like(b.gu)
+    h8 = torch.empty_like(b.h)
+    y8 = torch.empty_like(b.y_perm)
+    a = dev["x"] if gather else b.x_perm
+    moe.expert_gate_up_fp8(D, b.offsets, b.row_token if gather else None, a, q["w1"][0], q["w1"][1],
+                           q["w3"][0], q["w3"][1], gu8, h8)
+    moe.expert_down_fp8(D, b.offsets, h8, q["w2"][0], q["w2"][1], y8)
+    torch.cuda.synchronize()
+    for name, got, ref in (("gu", gu8, b.gu), ("h", h8, b.h), ("y_perm", y8, b.y_perm)):
+        assert torch.equal(got[:R].view(torch.int16), ref[:R].view(torch.int16)), name
+
+
+def test_fp8_gemms_reject_unsupported_shapes(gpu):
+    D = _desc(64, 192, 128, 8, 2, 0, 8, "bf16")                 # d not a multiple of 128
+    z = torch.zeros(1 << 16, dtype=torch.float32, device=gpu)
+    with pytest.raises(moe.MoeError):
+        moe.expert_gate_up_fp8(D, z, None, z, z, z, z, z, z, z)
+    with pytest.raises(moe.MoeError):
+        moe.expert_down_fp8(D, z, z, z, z, z)
