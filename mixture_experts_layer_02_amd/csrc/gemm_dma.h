@@ -698,7 +698,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // kt+2 (the last k-tile issues it whole, before the epilogue).
   constexpr int PER = BQ8 ? NJ + NJB + 1 : 2 * NJ;  // DMA instructions per wave per ring position
   constexpr int PART = PER / 2;                      // first part; the second has PER - PART
-  constexpr int PFD = 2;
+  constexpr int PFD = 1;  // (measured: 1 beats 2 and 3 by 1-2% on the 1T shapes)
   // Memory instructions per lane of one epilogue (the buffer stores and
   // loads below, all unconditional).
   constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? 128
@@ -760,9 +760,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     constexpr bool LAST = decltype(last_c)::value;
     using PU = decltype(pure_c);
     const uint16_t* st = ring[(gbase + kt) % STAGES];
-    // GATH_B: the tokens of position kt+5 (read two k-tiles later, after the
+    // GATH_B: the tokens of position kt+3+PFD (read two k-tiles later, after the
     // barriers that follow their wait).
-    if (GATH == GATH_B) tok_dma_pos(kt + 5);
+    if (GATH == GATH_B) tok_dma_pos(kt + 3 + PFD);
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
       if (s == 0) {
@@ -772,8 +772,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
           kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
         // GATH_B: position kt+1 is issued whole; its offsets make way for
         // those of kt+2 (issued at this k-tile's end and the next's start),
-        // and the prefetch offset for kt+4 (next k-tile's prefetch).
-        if (GATH == GATH_B) tok_fill_pos(kt + 2, kt + 4);
+        // and the prefetch offset for kt+2+PFD (next k-tile's prefetch).
+        if (GATH == GATH_B) tok_fill_pos(kt + 2, kt + 2 + PFD);
       } else {
         kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
       }
@@ -852,9 +852,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 
     if (cur.nk > 0) {
       if (!primed) {
-        if (GATH == GATH_B) {  // tokens of positions 0 .. 4
+        if (GATH == GATH_B) {  // tokens of positions 0 .. 2+PFD
 #pragma unroll
-          for (int q = 0; q < 5; ++q) tok_dma_pos(q);
+          for (int q = 0; q < 3 + PFD; ++q) tok_dma_pos(q);
           wait_vm<0>();
           lds_barrier();
           tok_fill_pos(0, PFD);
