@@ -67,6 +67,7 @@ struct TileCtx {
   int64_t k0, k1;  // K range of the tile
   int mtile;    // m-tile index within the group (GRP_K: within M)
   int mtiles;   // m-tiles of the group
+  bool nfast;   // tiles ordered n-tile fastest (else m-tile fastest)
   int ntile;    // n-tile index
 };
 
@@ -135,6 +136,7 @@ struct Scheduler {
       const int mt_g = (r1 - r0 + BM - 1) / BM;
       const int local = id - s_pref[g];
       const int mt = local % mt_g, nt = local / mt_g;
+      t.nfast = false;
       t.g = g;
       t.mtile = mt;
       t.mtiles = mt_g;
@@ -149,7 +151,12 @@ struct Scheduler {
       const int per = MT * NT;
       const int g = GRP == GRP_K ? id / per : 0;
       const int local = id - g * per;
-      const int mt = local % MT, nt = local / MT;
+      // One plain product with fewer n-tiles than m-tiles (the router's, N =
+      // E): n-tile fastest, so that the tiles sharing an A row block run
+      // together and A (T x d) streams from memory once, not once per n-tile.
+      const bool nf = GRP == GRP_NONE && MT >= NT;
+      const int mt = nf ? local / NT : local % MT, nt = nf ? local % NT : local / MT;
+      t.nfast = nf;
       t.g = g;
       t.mtile = mt;
       t.mtiles = MT;

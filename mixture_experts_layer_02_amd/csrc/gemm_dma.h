@@ -351,8 +351,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       L.rb = make_rsrc(b_grp + t.k0 * p.ldb + t.n0, (uint64_t)(klen * p.ldb - t.n0) * 2);
       L.rb2 = L.rb;
     }
-    const int cB = max(1, min(t.mtiles, run));
-    const int cA = max(1, min(sched.NT, run / max(t.mtiles, 1)));
+    // Sharers within an XCD's run of consecutive tiles: m-tile fastest, the
+    // run's m-tiles share B and, when a group has fewer m-tiles than the run,
+    // its n-tiles share A; n-tile fastest, the other way round.
+    const int cB = t.nfast ? max(1, min(t.mtiles, run / max(sched.NT, 1))) : max(1, min(t.mtiles, run));
+    const int cA = t.nfast ? max(1, min(sched.NT, run)) : max(1, min(sched.NT, run / max(t.mtiles, 1)));
     L.pa = pf_voff(cA, t.ntile % cA, p.lda, ALAY, 1);
     L.pb = pf_voff(cB, t.mtile % cB, p.ldb, BLAY, DUAL ? 2 : 1);
     if (BQ8) {
