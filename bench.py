@@ -128,7 +128,7 @@ def main():
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
