@@ -63,8 +63,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
 // compiler neither waits for it before unrelated LDS reads nor before
 // barriers: the kernel waits for it explicitly (wait_vm) where a ring stage
 // is consumed.  M0 (the LDS base of the copy) is an operand of the asm.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint16_t* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+// lds: the destination's LDS byte address, already wave-uniform (the kernel
+// derives it with scalar arithmetic from the ring's base, so that no vector
+// instruction sits between the address and the copy).
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile(
       // Wait states: one for the LDS DMA reading M0 after its SALU write, five
       // for a buffer instruction reading SGPRs a VALU op (readfirstlane,
@@ -80,14 +82,16 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
 // word lds_junk + 4 i (a scratch area nobody reads).  Its only purpose is to
 // start the L2 fill of that 64-byte sector well before the tile DMA needs
 // it; an offset outside the resource reads nothing.
-__device__ __forceinline__ void touch4(i32x4 rsrc, uint32_t voff, uint32_t soff, const uint32_t* lds_junk) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_junk);
+__device__ __forceinline__ void touch4u(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile(
       "s_nop 4\n\t"  // as in dma16
       "buffer_load_dword %0, %1, %2 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
       : "memory");
+}
+__device__ __forceinline__ void touch4(i32x4 rsrc, uint32_t voff, uint32_t soff, const uint32_t* lds_dst) {
+  touch4u(rsrc, voff, soff, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst));
 }
 
 // Workgroup barrier for LDS hand-offs: this wave's LDS reads and writes are
@@ -243,6 +247,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 
   Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
   sched.init(p, s_pref, s_scan);
+  // LDS byte address of the ring (the low half of its generic address).
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&ring[0][0]);
+  const uint32_t junk_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&lds_junk[0]);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -558,14 +565,16 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     int k;
     const Ld L = pick(pos, k, pure_c);
     uint16_t* st = ring[(gbase + pos) % STAGES];
+    // the stage's LDS byte address in scalar arithmetic; element offsets x2
+    const uint32_t stb = ring_lds + (uint32_t)(((gbase + pos) % STAGES) * STAGE_ELEMS * 2);
     if (BQ8) {  // q < NJ: A; then NJB FP8 B instructions; then the B rows' scales
       if (q < NJ) {
-        dma16(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), st + (wave * NJ + q) * 512);
+        dma16(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), stb + (wave * NJ + q) * 1024);
       } else if (q < NJ + NJB) {
         i32x4 rbk;
         uint32_t so_b;
         b_src(L, k, rbk, so_b);
-        dma16(rbk, vb[q - NJ], so_b, st + TILE_ELEMS + (wave * NJB + q - NJ) * 512);
+        dma16(rbk, vb[q - NJ], so_b, stb + TILE_ELEMS * 2 + (wave * NJB + q - NJ) * 1024);
       } else {
         touch4(L.rs, vs, (uint32_t)(k >> 1) * 4u,
                reinterpret_cast<const uint32_t*>(st + TILE_ELEMS + 8192 + wave * 128));
@@ -575,14 +584,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
     if ((q & 1) == 0) {
-      dma16(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), st + j * 512);
+      dma16(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), stb + j * 1024);
     } else if (GATH == GATH_B) {
-      dma16(L.rb, gvb[GATH == GATH_B ? jj : 0], 0u, st + TILE_ELEMS + j * 512);
+      dma16(L.rb, gvb[GATH == GATH_B ? jj : 0], 0u, stb + TILE_ELEMS * 2 + j * 1024);
     } else {
       i32x4 rbk;
       uint32_t so_b;
       b_src(L, k, rbk, so_b);
-      dma16(rbk, vb[jj], so_b, st + TILE_ELEMS + j * 512);
+      dma16(rbk, vb[jj], so_b, stb + TILE_ELEMS * 2 + j * 1024);
     }
   };
   // L2 prefetch instruction o (0: A, 1: B) of ring position pos.
@@ -590,14 +599,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     int k;
     const Ld L = pick(pos, k, pure_c);
     if (o == 0) {
-      touch4(L.ra, L.pa, a_so(k), lds_junk);
+      touch4u(L.ra, L.pa, a_so(k), junk_lds);
     } else if (GATH == GATH_B) {
-      touch4(L.rb, gpb, __builtin_amdgcn_readfirstlane(0u), lds_junk);
+      touch4u(L.rb, gpb, __builtin_amdgcn_readfirstlane(0u), junk_lds);
     } else {
       i32x4 rbk;
       uint32_t so_b;
       b_src(L, k, rbk, so_b);
-      touch4(rbk, L.pb, so_b, lds_junk);
+      touch4u(rbk, L.pb, so_b, junk_lds);
     }
   };
 
