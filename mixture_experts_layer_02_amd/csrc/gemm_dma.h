@@ -907,13 +907,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     //   acc[mi][ni][r] is C[row][col] with
     //   row = wm*128 + mi*32 + (r/4)*8 + (lane/32)*4 + r%4, col = n-block base + lane%32.
     {
+      // The epilogue's lane-dependent offsets are recomputed here from an
+      // opaque copy of the lane index: hoisted out of the tile loop they
+      // would stay live across the k-loop and be spilled.
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
       float* stage = s_stage[wave];
       constexpr int OC = DUAL ? WC / 2 : WC;
       constexpr bool PLAIN = EPI == EPI_STORE || EPI == EPI_ADD;
+      // A bias is only taken by plain ungrouped products (the router's logits).
+      constexpr bool HAS_BIAS = GRP == GRP_NONE && EPI == EPI_STORE;
       constexpr int W = (PLAIN && CF32) ? 4 : 8;
       constexpr int CPR = OC / W;               // vectors per row
-      constexpr int VPL = 8 * CPR / 64;          // vectors per lane per slab
-      static_assert(8 * CPR % 64 == 0, "whole vectors per lane");
+      constexpr int VPL = 8 * CPR / 64;          // vectors per lane_e per slab
+      static_assert(8 * CPR % 64 == 0, "whole vectors per lane_e");
       const int col_base = (DUAL ? wn * 64 : wn * 128);
       // Resources (row 0 = the tile's first row, element 0 = its first column).
       const int64_t m0g = t.m0;
@@ -958,7 +965,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
           for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
             for (int vi = 0; vi < VPL; ++vi) {
-              const int e = lane + vi * 64;
+              const int e = lane_e + vi * 64;
               const int rl = e / CPR, cv = (e % CPR) * W;
               const int row = rowb + sl * 8 + rl, col = col_base + cv;
               const int64_t eo = (int64_t)row * ldo + col;
@@ -974,7 +981,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
               for (int vi = 0; vi < VPL; ++vi) {
-                const int e = lane + vi * 64;
+                const int e = lane_e + vi * 64;
                 const int rl = e / CPR, cv = (e % CPR) * W;
                 const int row = rowb + (sl + s2) * 8 + rl, col = col_base + cv;
                 const int64_t eo = (int64_t)row * ldo + col;
@@ -988,10 +995,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
           for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
-              stage[((lane >> 5) * 4 + r4) * SP + ni * 32 + (lane & 31)] = acc[mi][ni][sl * 4 + r4];
+              stage[((lane_e >> 5) * 4 + r4) * SP + ni * 32 + (lane_e & 31)] = acc[mi][ni][sl * 4 + r4];
 #pragma unroll
           for (int vi = 0; vi < VPL; ++vi) {
-            const int e = lane + vi * 64;
+            const int e = lane_e + vi * 64;
             const int rl = e / CPR, cv = (e % CPR) * W;
             float v[W], v2[W];
 #pragma unroll
@@ -1009,7 +1016,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 float o[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = v[q];
-                if (p.bias) {
+                if (HAS_BIAS && p.bias) {
 #pragma unroll
                   for (int q = 0; q < 4; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
                 }
@@ -1024,7 +1031,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 float o[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) o[q] = v[q];
-                if (p.bias) {
+                if (HAS_BIAS && p.bias) {
 #pragma unroll
                   for (int q = 0; q < 8; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
                 }
