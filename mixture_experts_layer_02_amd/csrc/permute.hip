@@ -48,25 +48,48 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
 // One workgroup of 1024 threads: counts[e] for every expert, and the exclusive
 // prefix sum of the local experts' block counts in expert-major order
 // (the page's partial_cum_token_counts); offsets[n] = base of expert n's
-// first block, offsets[NL] = R.
+// first block, offsets[NL] = R.  A single workgroup is latency-bound, so every
+// loop issues its loads in batches (four experts per wave pass, eight block
+// counts per thread) rather than one dependent load at a time.
 __global__ void __launch_bounds__(1024) scan_kernel(const int32_t* __restrict__ blk_counts, int E, int nblk,
                                                     int e0, int NL, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ base) {
   __shared__ int sh[1024];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = wv; e < E; e += 16) {
-    int s = 0;
-    for (int b = lane; b < nblk; b += 64) s += blk_counts[(int64_t)e * nblk + b];
+  constexpr int EU = 4;  // experts per wave pass
+  for (int eb = wv; eb < E; eb += 16 * EU) {
+    int sum[EU] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int b = lane; b < nblk; b += 64) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) counts[e] = s;
+      for (int u = 0; u < EU; ++u) {
+        const int e = eb + 16 * u;
+        if (e < E) sum[u] += blk_counts[(int64_t)e * nblk + b];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      int v = sum[u];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0 && eb + 16 * u < E) counts[eb + 16 * u] = v;
+    }
   }
   const int64_t n_loc = (int64_t)NL * nblk;
   const int32_t* src = blk_counts + (int64_t)e0 * nblk;
   const int64_t per = (n_loc + 1023) / 1024;
   const int64_t lo = min(n_loc, (int64_t)tid * per), hi = min(n_loc, lo + per);
+  constexpr int CH = 8;
   int s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += src[i];
+  int64_t i = lo;
+  for (; i + CH <= hi; i += CH) {
+    int v[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) v[u] = src[i + u];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) s += v[u];
+  }
+  for (; i < hi; ++i) s += src[i];
   sh[tid] = s;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -76,9 +99,29 @@ __global__ void __launch_bounds__(1024) scan_kernel(const int32_t* __restrict__ 
     __syncthreads();
   }
   int run = sh[tid] - s;
-  for (int64_t i = lo; i < hi; ++i) {
+  // the first expert boundary (a multiple of nblk) at or after lo
+  int64_t nb = (lo + nblk - 1) / nblk * nblk;
+  i = lo;
+  for (; i + CH <= hi; i += CH) {
+    int v[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) v[u] = src[i + u];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      base[i + u] = run;
+      if (i + u == nb) {
+        offsets[nb / nblk] = run;
+        nb += nblk;
+      }
+      run += v[u];
+    }
+  }
+  for (; i < hi; ++i) {
     base[i] = run;
-    if (i % nblk == 0) offsets[i / nblk] = run;
+    if (i == nb) {
+      offsets[nb / nblk] = run;
+      nb += nblk;
+    }
     run += src[i];
   }
   if (tid == 0) offsets[NL] = sh[1023];

@@ -99,7 +99,9 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
 
 // dlogits for one token per wave.  renorm: dL_m = w_m (dw_m - <w, dw>) on the
 // selected experts (local or not), 0 elsewhere.  raw softmax: dL_e = p_e (g_e -
-// <w, dw>) with g_e = dw_j at e = idx_j.
+// <w, dw>) with g_e = dw_j at e = idx_j.  The k selections are read once into
+// scalar registers (their lane is uniform) and scattered into the row held
+// by the lanes: expert e is element e/64 of lane e%64.
 template <int MAXV>
 __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict__ logits,
                                                         const int32_t* __restrict__ idx,
@@ -117,19 +119,25 @@ __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict_
     my_dw = dw[(int64_t)t * k + lane];
   }
   const float s = wave_sum(my_w * my_dw);
+  // g[i]: for renorm w_j (dw_j - s) at the selected experts, else dw_j
+  float g[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) g[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int ij = __builtin_amdgcn_readlane(my_i, j);
+    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+    const float dwj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dw), j));
+    const float val = renorm ? wj * (dwj - s) : dwj;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (ij == i * 64 + lane) g[i] = val;
+  }
   float* out = dlogits + (int64_t)t * E;
   if (renorm) {
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int e = i * 64 + lane;
-      float g = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int ij = __shfl(my_i, j, 64);
-        const float wj = __shfl(my_w, j, 64);
-        const float dwj = __shfl(my_dw, j, 64);
-        if (ij == e) g = wj * (dwj - s);
-      }
-      if (e < E) out[e] = g;
+      if (e < E) out[e] = g[i];
     }
   } else {
     const float* row = logits + (int64_t)t * E;
@@ -151,13 +159,7 @@ __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict_
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int e = i * 64 + lane;
-      float g = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int ij = __shfl(my_i, j, 64);
-        const float dwj = __shfl(my_dw, j, 64);
-        if (ij == e) g = dwj;
-      }
-      if (e < E) out[e] = expf(v[i] - mx) / z * (g - s);
+      if (e < E) out[e] = expf(v[i] - mx) / z * (g[i] - s);
     }
   }
 }
