@@ -216,7 +216,7 @@ def main():
         if args.fp8_weights and "A0_fp8_dequant" in rows:
             timed("A0_fp8_dequant", dequant_all, rec)
         if routing is None:
-            timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits), rec)
+            timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits, b.ws_router), rec)
             if args.n_groups > 1:
                 timed("A2_route", lambda: moe.route_grouped(D, b.logits, args.n_groups, b.topk_idx, b.topk_w), rec)
             else:

@@ -101,7 +101,14 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes);
 /* A1, router scores (Aurora page, Algorithm 1 stage 1: the router is a linear
  * layer producing one logit per token and expert).
  *   x [T][d] dtype, Wr [E][d] dtype, bias [E] float32 or NULL (added to every
- *   token's logits), logits [T][E] float32 out.  Accumulation is float32. */
+ *   token's logits), logits [T][E] float32 out.  Accumulation is float32.
+ *   ws: moe_workspace_size(MOE_OP_ROUTER_LOGITS) bytes (may be NULL when that
+ *   is 0).  For bf16 shapes with fewer 256x256 output tiles than 256, the
+ *   product is split over d into whole 64-wide chunks whose float32 partial
+ *   sums go to ws and are added in chunk order, then the bias; the split
+ *   depends on the shape only, so results are the same on every call.
+ *   Errors: MOE_ERR_WORKSPACE (ws too small), MOE_ERR_INVALID_ARG (ws NULL or
+ *   misaligned when the query is not 0). */
 int moe_router_logits(const moe_desc* desc, const void* x, const void* Wr, const float* bias,
                       float* logits, void* ws, size_t ws_bytes, void* stream);
 

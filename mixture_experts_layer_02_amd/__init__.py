@@ -182,6 +182,9 @@ def _ws(ws):
 
 
 def router_logits(desc, x, wr, bias, logits, ws=None):
+    if ws is None:  # a workspace of the queried size, when the shape needs one
+        need = workspace_size(desc, OP_ROUTER_LOGITS)
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device) if need else None
     w, n = _ws(ws)
     _call("moe_router_logits", desc, x, wr, bias, logits, w, n, _stream())
 
@@ -329,6 +332,7 @@ class Buffers:
         self.y_perm = torch.empty(Rc, d, dtype=dt, **z)
         self.y = torch.empty(T, d, dtype=dt, **z)
         self.ws_permute = torch.empty(max(16, workspace_size(desc, OP_PERMUTE)), dtype=torch.uint8, **z)
+        self.ws_router = torch.empty(max(16, workspace_size(desc, OP_ROUTER_LOGITS)), dtype=torch.uint8, **z)
         if backward:
             self.dy_perm = torch.empty(Rc, d, dtype=dt, **z)
             self.dtopk_w = torch.empty(T, k, dtype=torch.float32, **z)
@@ -348,7 +352,7 @@ def forward(b: Buffers, x, wr, w1, w3, w2, bias=None, routing=None, n_groups=1):
     ``n_groups`` > 1 routes with the group-limited rule (route_grouped)."""
     D = b.desc
     if routing is None:
-        router_logits(D, x, wr, bias, b.logits)
+        router_logits(D, x, wr, bias, b.logits, b.ws_router)
         if n_groups > 1:
             route_grouped(D, b.logits, n_groups, b.topk_idx, b.topk_w)
         else:

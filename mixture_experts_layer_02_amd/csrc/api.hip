@@ -46,7 +46,7 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
   if (rc) return rc;
   if (!bytes) return MOE_ERR_INVALID_ARG;
   switch (op) {
-    case MOE_OP_ROUTER_LOGITS:
+    case MOE_OP_ROUTER_LOGITS: *bytes = moe::router_logits_workspace(*desc); return MOE_OK;
     case MOE_OP_GROUPED_FFN:
     case MOE_OP_FFN_BWD_DX:
     case MOE_OP_FFN_BWD_DW: *bytes = 0; return MOE_OK;
@@ -58,12 +58,12 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
 
 int moe_router_logits(const moe_desc* desc, const void* x, const void* Wr, const float* bias, float* logits,
                       void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(x) || !need(Wr) || !need(logits) || !opt(bias)) return MOE_ERR_INVALID_ARG;
-  return finish(moe::launch_router_logits(*desc, x, Wr, bias, logits, S(stream)));
+  const size_t need_ws = moe::router_logits_workspace(*desc);
+  if (need_ws && (!need(ws) || ws_bytes < need_ws)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_router_logits(*desc, x, Wr, bias, logits, ws, S(stream)));
 }
 
 int moe_route(const moe_desc* desc, const float* logits, int32_t* topk_idx, float* topk_w, void* stream) {

@@ -57,7 +57,11 @@ constexpr int DMA_STAGES = DMA_BK == 64 ? 2 : 4;
 // multiple of its 32-wide k-tile, else the register-staged kernel.
 template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE, bool BQ8 = false>
 hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
-  const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) || (GRP != GRP_K && p.K % DMA_BK == 0);
+  // K-contiguous operands need whole 64-wide k-tiles: every K (GRP_M, plain)
+  // or every K chunk (GRP_K split into kchunk pieces) a multiple of 64.
+  const bool k_ok = (ALAY == LAY_MN && BLAY == LAY_MN) ||
+                    (GRP != GRP_K && p.K % DMA_BK == 0) ||
+                    (GRP == GRP_K && !p.offsets && p.kchunk % DMA_BK == 0 && p.K % DMA_BK == 0);
   if (!std::is_same<AT, uint16_t>::value || !k_ok) return run_mfma<ALAY, BLAY, AT, GRP, EPI, DUAL>(p, ub_tiles, s);
   int64_t grid = std::min<int64_t>(ub_tiles, (int64_t)num_cus());
   if (grid >= 8) grid -= grid % 8;
@@ -114,11 +118,15 @@ __global__ void __launch_bounds__(256) to_bf16_kernel(const float* __restrict__ 
   }
 }
 
+// out[i] = sum of the S partials in split order (+ bias[i % ncol] when given).
 __global__ void __launch_bounds__(256) sum_splits_kernel(const float* __restrict__ part, int S, int64_t n,
-                                                         float* __restrict__ out) {
+                                                         float* __restrict__ out,
+                                                         const float* __restrict__ bias = nullptr,
+                                                         int ncol = 1) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float acc = 0.f;
     for (int s = 0; s < S; ++s) acc += part[(int64_t)s * n + i];
+    if (bias) acc += bias[i % ncol];
     out[i] = acc;
   }
 }
@@ -137,8 +145,52 @@ size_t router_bwd_workspace(const moe_desc& d) {
   return b;
 }
 
+// Router logits (bf16): with fewer output tiles than a 256-CU part has CUs
+// (few tokens, or E small), the product is split over d into S chunks of
+// whole 64-wide k-tiles, written as float32 partials [S][T][E] into the
+// workspace and summed in chunk order (deterministic).  S depends on the
+// shape only.
+int router_logit_splits(const moe_desc& d) {
+  if (d.dtype != MOE_BF16 || d.d % 64) return 1;
+  const int64_t tiles = cdiv(d.T, MT) * cdiv(d.E, MT);
+  const int64_t s = std::min<int64_t>(std::min<int64_t>(cdiv(256, tiles), d.d / 64), 16);
+  if (s <= 1) return 1;
+  const int64_t chunk = cdiv(d.d / 64, s) * 64;
+  return (int)cdiv(d.d, chunk);
+}
+
+size_t router_logits_workspace(const moe_desc& d) {
+  const int S = router_logit_splits(d);
+  return S > 1 ? (size_t)S * (size_t)d.T * (size_t)d.E * sizeof(float) : 0;
+}
+
 hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
-                                float* logits, hipStream_t s) {
+                                float* logits, void* ws, hipStream_t s) {
+  const int S = router_logit_splits(d);
+  if (S > 1) {
+    float* part = reinterpret_cast<float*>(ws);
+    GemmParams q = blank(d);
+    q.A = x;
+    q.lda = d.d;
+    q.B = Wr;
+    q.ldb = d.d;
+    q.C = part;
+    q.ldc = d.E;
+    q.c_gstride = (int64_t)d.T * d.E;
+    q.offsets = nullptr;
+    q.ngroups = S;
+    q.kchunk = (int)(cdiv(d.d / 64, S) * 64);
+    q.M = d.T;
+    q.N = d.E;
+    q.K = d.d;
+    q.c_f32 = 1;
+    hipError_t e = run_bf16<LAY_K, LAY_K, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)S * cdiv(d.T, MT) * cdiv(d.E, MT), s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)d.T * d.E;
+    const int64_t blocks = std::min<int64_t>(cdiv(n, 256), (int64_t)num_cus() * 8);
+    sum_splits_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, S, n, logits, bias, d.E);
+    return hipGetLastError();
+  }
   GemmParams p = blank(d);
   p.A = x;
   p.lda = d.d;

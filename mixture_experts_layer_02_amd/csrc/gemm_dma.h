@@ -339,7 +339,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // [0, klen) from column m0/n0 (the range ends with row k1-1, so it never
     // runs past the allocation).
     const int nlim_b = DUAL ? min(t.nlim, BN / 2) : t.nlim;
-    L.ra = (ALAY == LAY_K) ? make_rsrc(a_base, (uint64_t)t.mlim * p.lda * 2)
+    L.ra = (ALAY == LAY_K) ? make_rsrc(a_base, (uint64_t)((int64_t)t.mlim * p.lda - t.k0) * 2)
                            : make_rsrc(a_base, (uint64_t)(klen * p.lda - t.m0) * 2);
     if (GATH == GATH_A) {  // rows come from anywhere in the source; row validity is in gv
       L.ra = make_rsrc(Ag, (uint64_t)p.gather_rows * p.lda * 2);
@@ -349,8 +349,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       L.rb = L.rb2 = make_rsrc(Bg + t.n0, (uint64_t)((int64_t)p.gather_rows * p.ldb - t.n0) * 2);
       L.rt = make_rsrc(p.gather + t.k0, (uint64_t)klen * 4);
     } else if (BLAY == LAY_K) {
-      L.rb = make_rsrc(b_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2);
-      L.rb2 = DUAL ? make_rsrc(b2_grp + (int64_t)t.n0 * p.ldb, (uint64_t)nlim_b * p.ldb * 2) : L.rb;
+      // (a grouped-K product, split over K, starts at its chunk's k0)
+      const int64_t bk0 = GRP == GRP_K ? t.k0 : 0;
+      L.rb = make_rsrc(b_grp + (int64_t)t.n0 * p.ldb + bk0, (uint64_t)((int64_t)nlim_b * p.ldb - bk0) * 2);
+      L.rb2 = DUAL ? make_rsrc(b2_grp + (int64_t)t.n0 * p.ldb + bk0, (uint64_t)((int64_t)nlim_b * p.ldb - bk0) * 2)
+                   : L.rb;
     } else if (p.ksplit) {  // k < ksplit from B, k >= ksplit from B2 (GRP_M: t.k0 = 0)
       L.rb = make_rsrc(b_grp + t.n0, (uint64_t)((int64_t)p.ksplit * p.ldb - t.n0) * 2);
       L.rb2 = make_rsrc(b2_grp + t.n0, (uint64_t)((klen - p.ksplit) * p.ldb - t.n0) * 2);

@@ -18,8 +18,9 @@ hipError_t launch_fp8_dequantize(const uint8_t* q, const float* scales, int64_t 
 size_t permute_workspace(const moe_desc& d);
 size_t router_bwd_workspace(const moe_desc& d);
 
+size_t router_logits_workspace(const moe_desc& d);
 hipError_t launch_router_logits(const moe_desc& d, const void* x, const void* Wr, const float* bias,
-                                float* logits, hipStream_t s);
+                                float* logits, void* ws, hipStream_t s);
 hipError_t launch_route(const moe_desc& d, const float* logits, int n_groups, int32_t* idx, float* w,
                         hipStream_t s);
 hipError_t launch_route_bwd(const moe_desc& d, const float* logits, const int32_t* idx, const float* w,

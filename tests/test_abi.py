@@ -97,12 +97,43 @@ def test_workspace_too_small_is_reported():
     assert rc == moe.MOE_ERR_WORKSPACE
 
 
+def _router_splits(T, d, E, dtype):
+    # bf16 products with fewer than 256 output tiles of 256 x 256 are split
+    # over d into whole 64-wide chunks (at most 16), one per 256 / tiles
+    if dtype != "bf16" or d % 64:
+        return 1
+    tiles = -(-T // 256) * -(-E // 256)
+    s = min(-(-256 // tiles), d // 64, 16)
+    if s <= 1:
+        return 1
+    chunk = -(-(d // 64) // s) * 64
+    return -(-d // chunk)
+
+
 def test_workspace_sizes():
     d = _d()
     assert moe.workspace_size(d, moe.OP_GROUPED_FFN) == 0
-    assert moe.workspace_size(d, moe.OP_ROUTER_LOGITS) == 0
     with pytest.raises(moe.MoeError):
         moe.workspace_size(d, 99)
+    for T, dd, E, dt in [(d.T, d.d, d.E, "bf16"), (65536, 6144, 384, "bf16"), (8192, 6144, 384, "bf16"),
+                         (16384, 6144, 96, "bf16"), (300, 256, 72, "bf16"), (256, 128, 8, "f32")]:
+        D = moe.make_desc(T, dd, 64, E, 2, 0, E, dt)
+        s = _router_splits(T, dd, E, dt)
+        assert moe.workspace_size(D, moe.OP_ROUTER_LOGITS) == (s * T * E * 4 if s > 1 else 0), (T, dd, E, dt)
+    # the 1T fwd+bwd shape needs none; the 1T share splits in 4
+    assert _router_splits(65536, 6144, 384, "bf16") == 1 and _router_splits(8192, 6144, 384, "bf16") == 4
+
+
+def test_router_logits_rejects_short_workspace():
+    l = moe.lib()
+    D = moe.make_desc(300, 256, 64, 72, 2, 0, 72, "bf16")
+    need = moe.workspace_size(D, moe.OP_ROUTER_LOGITS)
+    assert need > 0
+    g = 1 << 20
+    rc = l.moe_router_logits(ctypes.byref(D), g, g, None, g, g, need - 16, None)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    rc = l.moe_router_logits(ctypes.byref(D), g, g, None, g, None, 0, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():
