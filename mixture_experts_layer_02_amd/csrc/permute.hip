@@ -45,91 +45,65 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
   }
 }
 
-// One workgroup of 1024 threads: counts[e] for every expert, and the exclusive
-// prefix sum of the local experts' block counts in expert-major order
-// (the page's partial_cum_token_counts); offsets[n] = base of expert n's
-// first block, offsets[NL] = R.  A single workgroup is latency-bound, so every
-// loop issues its loads in batches (four experts per wave pass, eight block
-// counts per thread) rather than one dependent load at a time.
-__global__ void __launch_bounds__(1024) scan_kernel(const int32_t* __restrict__ blk_counts, int E, int nblk,
-                                                    int e0, int NL, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ base) {
+// The page's partial_cum_token_counts (an exclusive prefix sum of the block
+// counts in expert-major order) in two parallel steps.  expert_scan_kernel,
+// one workgroup per expert: counts[e] = the expert's total over all blocks,
+// and, for a local expert n, base_rel[n][b] = the exclusive prefix sum of its
+// block counts.  offsets_kernel: offsets[n] = exclusive prefix sum of the
+// local experts' counts, offsets[NL] = R.  A block's base is then
+// offsets[n] + base_rel[n][b], which is the expert-major prefix sum.
+__global__ void __launch_bounds__(256) expert_scan_kernel(const int32_t* __restrict__ blk_counts, int nblk, int e0,
+                                                          int NL, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ base_rel) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int32_t* src = blk_counts + (int64_t)e * nblk;
+  const bool local = e >= e0 && e < e0 + NL;
+  int32_t* dst = local ? base_rel + (int64_t)(e - e0) * nblk : base_rel;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + tid;
+    const int v = b < nblk ? src[b] : 0;
+    int inc = v;  // inclusive scan inside the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) wsum[wv] = inc;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wv; ++w) before += wsum[w];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();  // wsum is rewritten by the next chunk
+    if (local && b < nblk) dst[b] = before + inc - v;
+    carry += total;
+  }
+  if (tid == 0) counts[e] = carry;
+}
+
+// One workgroup of 1024 threads (NL <= 1024).
+__global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict__ counts, int e0, int NL,
+                                                       int32_t* __restrict__ offsets) {
   __shared__ int sh[1024];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  constexpr int EU = 4;  // experts per wave pass
-  for (int eb = wv; eb < E; eb += 16 * EU) {
-    int sum[EU] = {0, 0, 0, 0};
-#pragma unroll 4
-    for (int b = lane; b < nblk; b += 64) {
-#pragma unroll
-      for (int u = 0; u < EU; ++u) {
-        const int e = eb + 16 * u;
-        if (e < E) sum[u] += blk_counts[(int64_t)e * nblk + b];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < EU; ++u) {
-      int v = sum[u];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      if (lane == 0 && eb + 16 * u < E) counts[eb + 16 * u] = v;
-    }
-  }
-  const int64_t n_loc = (int64_t)NL * nblk;
-  const int32_t* src = blk_counts + (int64_t)e0 * nblk;
-  const int64_t per = (n_loc + 1023) / 1024;
-  const int64_t lo = min(n_loc, (int64_t)tid * per), hi = min(n_loc, lo + per);
-  constexpr int CH = 8;
-  int s = 0;
-  int64_t i = lo;
-  for (; i + CH <= hi; i += CH) {
-    int v[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) v[u] = src[i + u];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) s += v[u];
-  }
-  for (; i < hi; ++i) s += src[i];
-  sh[tid] = s;
+  const int tid = threadIdx.x;
+  const int v = tid < NL ? counts[e0 + tid] : 0;
+  sh[tid] = v;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? sh[tid - off] : 0;
+    const int u = tid >= off ? sh[tid - off] : 0;
     __syncthreads();
-    sh[tid] += v;
+    sh[tid] += u;
     __syncthreads();
   }
-  int run = sh[tid] - s;
-  // the first expert boundary (a multiple of nblk) at or after lo
-  int64_t nb = (lo + nblk - 1) / nblk * nblk;
-  i = lo;
-  for (; i + CH <= hi; i += CH) {
-    int v[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) v[u] = src[i + u];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      base[i + u] = run;
-      if (i + u == nb) {
-        offsets[nb / nblk] = run;
-        nb += nblk;
-      }
-      run += v[u];
-    }
-  }
-  for (; i < hi; ++i) {
-    base[i] = run;
-    if (i == nb) {
-      offsets[nb / nblk] = run;
-      nb += nblk;
-    }
-    run += src[i];
-  }
+  if (tid < NL) offsets[tid] = sh[tid] - v;
   if (tid == 0) offsets[NL] = sh[1023];
 }
 
 // row_token and slot_row from the block bases (the page's index generation).
 __global__ void __launch_bounds__(256) place_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
-                                                    int e0, int NL, const int32_t* __restrict__ base, int nblk,
+                                                    int e0, int NL, const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ base_rel, int nblk,
                                                     int32_t* __restrict__ row_token,
                                                     int32_t* __restrict__ slot_row) {
   extern __shared__ uint64_t masks[];  // [4][NL]
@@ -153,7 +127,7 @@ __global__ void __launch_bounds__(256) place_kernel(const int32_t* __restrict__ 
     if ((unsigned)n < (unsigned)NL) {
       int before = __popcll(masks[wave * NL + n] & below);
       for (int w = 0; w < wave; ++w) before += __popcll(masks[w * NL + n]);
-      row = base[(int64_t)n * nblk + blockIdx.x] + before;
+      row = offsets[n] + base_rel[(int64_t)n * nblk + blockIdx.x] + before;
       row_token[row] = t;
     }
     slot_row[(int64_t)t * k + j] = row;
@@ -335,10 +309,11 @@ hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, 
   int32_t* blk_counts = reinterpret_cast<int32_t*>(ws);
   int32_t* base = blk_counts + (int64_t)d.E * nblk;
   count_kernel<<<nblk, 256, 4 * d.E * sizeof(uint64_t), s>>>(idx, d.T, d.k, d.E, blk_counts, nblk);
-  scan_kernel<<<1, 1024, 0, s>>>(blk_counts, d.E, nblk, d.expert_begin, d.num_local, counts, offsets, base);
+  expert_scan_kernel<<<d.E, 256, 0, s>>>(blk_counts, nblk, d.expert_begin, d.num_local, counts, base);
+  offsets_kernel<<<1, 1024, 0, s>>>(counts, d.expert_begin, d.num_local, offsets);
   place_kernel<<<nblk, 256, 4 * d.num_local * sizeof(uint64_t), s>>>(idx, d.T, d.k, d.E, d.expert_begin,
-                                                                      d.num_local, base, nblk, row_token,
-                                                                      slot_row);
+                                                                      d.num_local, offsets, base, nblk,
+                                                                      row_token, slot_row);
   if (x) {
     const int64_t row_bytes = (int64_t)d.d * (d.dtype == MOE_BF16 ? 2 : 4);
     gather_kernel<<<(d.T + 3) / 4, 256, 0, s>>>(reinterpret_cast<const uint8_t*>(x), slot_row, d.T, d.k,
