@@ -95,14 +95,27 @@ int64_t r_cap(const moe_desc& d) { return (int64_t)d.T * std::min(d.k, d.num_loc
 int64_t mtiles_ub(const moe_desc& d, int bm) { return cdiv(r_cap(d), bm) + d.num_local; }
 
 // Split-K factor of the router-weight gradient (K = T is long, M x N small):
-// enough chunks for two workgroups per compute unit of a 256-CU part.  It
-// depends on the shape only, so the summation order (and the result) is the
-// same on every device and the workspace query needs no device.
+// the S that minimises a simple time model on a 256-CU part, rounds of
+// output tiles times k-tiles per tile (~1.6 us per 64-wide k-tile of a
+// 256 x 256 tile), plus writing and reading the S float32 partials at
+// ~5 TB/s.  It depends on the shape only, so the summation order (and the
+// result) is the same on every device and the workspace query needs no
+// device.  Ties go to the smaller S.
 int router_splits(const moe_desc& d) {
   const int64_t tiles = cdiv(d.E, MT) * cdiv(d.d, MT);
-  int64_t s = cdiv((int64_t)256 * 2, tiles);
-  s = std::min<int64_t>(s, cdiv(d.T, 256));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int S = 1; S <= 64; ++S) {
+    if (S > 1 && cdiv(d.T, S) < 64) break;  // chunks of at least one k-tile
+    // cost in units of 1e-13 s: k-tile time 1.6 us = 16e6 units; a byte at 5 TB/s = 2 units
+    const int64_t cost = cdiv((int64_t)S * tiles, 256) * cdiv(cdiv(d.T, S), 64) * 16000000 +
+                         (int64_t)S * d.E * d.d * 8 * 2;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
 }
 
 // float32 -> bfloat16 (round to nearest even), 8 elements per thread; n % 8 == 0.
