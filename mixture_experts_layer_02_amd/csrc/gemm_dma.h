@@ -1029,7 +1029,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 }
                 const u32x4_t d = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                    __float_as_uint(o[3])};
-                __builtin_amdgcn_raw_buffer_store_b128(d, rc, ok ? (uint32_t)(eo * 4) : 0x80000000u, 0, 0);
+                // (weight gradients, written once and not read in this pass:
+                // non-temporal stores)
+                __builtin_amdgcn_raw_buffer_store_b128(d, rc, ok ? (uint32_t)(eo * 4) : 0x80000000u, 0,
+                                                       GRP == GRP_K ? 2 : 0);
               } else {
                 float o[8];
 #pragma unroll
@@ -1058,8 +1061,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                                   pack_bf2(v2[6], v2[7])};
               const int64_t eh = (int64_t)row * p.ldc + col;
               __builtin_amdgcn_raw_buffer_store_b128(dh, r0, ok ? (uint32_t)(eh * 2) : 0x80000000u, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b128(dg, r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b128(du, r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
+              // (G | U is read back only by the backward: non-temporal stores)
+              __builtin_amdgcn_raw_buffer_store_b128(dg, r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 2);
+              __builtin_amdgcn_raw_buffer_store_b128(du, r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 2);
             } else {  // EPI_SWIGLU_BWD: v = dH
               const uint32_t og = ok ? (uint32_t)(eo * 2) : 0x80000000u;
               const uint32_t ou = ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u;
