@@ -19,26 +19,17 @@ namespace moe {
 // leave the race, so the k picks are the union of every group's k/G best, in
 // descending order (the eligible set only shrinks).  Lane g counts group g's
 // picks.
+//
+// k rounds of a lane-local arg-max and a wave butterfly over the wave's
+// token (v: the lane's logits, element i = expert i*64 + lane); writes the
+// token's k selections and weights.
 template <int MAXV, bool GROUPED>
-__global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict__ logits, int T, int E,
-                                                         int k, int renorm, int G,
-                                                         int32_t* __restrict__ idx_out,
-                                                         float* __restrict__ w_out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
-  float v[MAXV];
+__device__ __forceinline__ void topk_rounds(const float (&v)[MAXV], int lane, int t, int E, int k, int renorm,
+                                            int G, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   uint32_t taken = 0;  // bit i: element i is selected already or absent
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = i * 64 + lane;
-    if (e < E) v[i] = row[e];
-    else {
-      v[i] = 0.f;
-      taken |= 1u << i;
-    }
-  }
+  for (int i = 0; i < MAXV; ++i)
+    if (i * 64 + lane >= E) taken |= 1u << i;
   float my_v = 0.f, v0 = 0.f;
   int my_i = 0;
   const int Eg = GROUPED ? E / G : E, kg = GROUPED ? k / G : k;
@@ -94,6 +85,113 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
   if (lane < k) {
     idx_out[(int64_t)t * k + lane] = my_i;
     w_out[(int64_t)t * k + lane] = w;
+  }
+}
+
+// Order-preserving unsigned key of a float (larger float, larger key), with
+// -0.0 made equal to +0.0; 0 is below every finite float's key and marks an
+// absent element.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x + 0.0f);  // -0.0 + 0.0 = +0.0
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+template <int MAXV, bool GROUPED>
+__global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict__ logits, int T, int E,
+                                                         int k, int renorm, int G,
+                                                         int32_t* __restrict__ idx_out,
+                                                         float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  float v[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = i * 64 + lane;
+    v[i] = e < E ? row[e] : 0.f;
+  }
+  if (GROUPED) {
+    topk_rounds<MAXV, GROUPED>(v, lane, t, E, k, renorm, G, idx_out, w_out);
+    return;
+  }
+  // Threshold selection.  theta = the k-th largest of the lanes' maximum keys
+  // (a binary search over the key bits, counting lanes with ballots): at
+  // least k elements have key >= theta, so every one of the k selections
+  // does, and the candidates (key >= theta) are usually few.  They are
+  // compacted through LDS, and a candidate's slot is the number of
+  // candidates that come before it in the order (logit descending, expert
+  // ascending).  With more than 64 candidates (heavy ties) the wave takes
+  // the k rounds instead.
+  uint32_t key[MAXV];
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    key[i] = i * 64 + lane < E ? order_key(v[i]) : 0u;
+    kmax = max(kmax, key[i]);
+  }
+  uint32_t theta = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = theta | (1u << b);
+    if ((int)__popcll(__ballot(kmax >= c)) >= k) theta = c;
+  }
+  uint64_t m[MAXV];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    m[i] = __ballot(key[i] != 0u && key[i] >= theta);
+    cnt += (int)__popcll(m[i]);
+  }
+  if (cnt > 64) {  // uniform
+    topk_rounds<MAXV, false>(v, lane, t, E, k, renorm, 1, idx_out, w_out);
+    return;
+  }
+  __shared__ uint32_t s_key[4][64];
+  __shared__ int32_t s_idx[4][64];
+  __shared__ float s_val[4][64];
+  const int wv = threadIdx.x >> 6;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    if ((m[i] >> lane) & 1ull) {
+      const int pos = base + (int)__popcll(m[i] & ((1ull << lane) - 1ull));
+      s_key[wv][pos] = key[i];
+      s_idx[wv][pos] = i * 64 + lane;
+      s_val[wv][pos] = v[i];
+    }
+    base += (int)__popcll(m[i]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const bool cand = lane < cnt;
+  const uint32_t ck = cand ? s_key[wv][lane] : 0u;
+  const int ci = cand ? s_idx[wv][lane] : 0x7fffffff;
+  const float cv = cand ? s_val[wv][lane] : 0.f;
+  int rank = 0;
+  for (int j = 0; j < cnt; ++j) {
+    const uint32_t kj = __builtin_amdgcn_readlane(ck, j);
+    const int ij = __builtin_amdgcn_readlane(ci, j);
+    rank += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
+  }
+  const bool sel = cand && rank < k;
+  // the largest selected logit (slot 0)
+  const uint64_t top = __ballot(cand && rank == 0);
+  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv), (int)__builtin_ctzll(top)));
+  float w;
+  if (renorm) {
+    const float ex = sel ? expf(cv - v0) : 0.f;
+    w = ex / wave_sum(ex);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i * 64 + lane < E) s += expf(v[i] - v0);
+    s = wave_sum(s);
+    w = expf(cv - v0) / s;
+  }
+  if (sel) {
+    idx_out[(int64_t)t * k + rank] = ci;
+    w_out[(int64_t)t * k + rank] = w;
   }
 }
 
