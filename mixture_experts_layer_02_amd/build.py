@@ -36,6 +36,11 @@ def _run(cmd):
     return out
 
 
+# Sources holding the LDS-DMA GEMM kernels: their device assembly is checked
+# for the SGPR wait-state hazard of the inline-asm DMA (hazard_check.py).
+CHECKED = ["ffn.hip", "fp8.hip"]
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     objs = []
@@ -44,10 +49,33 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+    asms = []
+    for src in CHECKED:
+        asm = os.path.join(OBJ, src.replace(".hip", ".gfx950.s"))
+        asms.append(asm)
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
+                     "-o", asm])
     with cf.ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
+    sys.path.insert(0, HERE)
+    try:
+        import hazard_check
+    finally:
+        sys.path.pop(0)
+    import io
+    report = io.StringIO()
+    n_dma = n_bad = 0
+    for asm in asms:
+        t, b = hazard_check.check(asm, report)
+        n_dma += t
+        n_bad += b
+    if n_bad:
+        raise RuntimeError(f"LDS-DMA wait-state hazards in the generated code ({n_bad} of {n_dma}):\n" +
+                           report.getvalue())
+    if verbose:
+        print(f"hazard check: {n_dma} LDS-DMA instructions, none within 5 wait states of a VALU write of its SGPRs")
     tmp = OUT + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, OUT)

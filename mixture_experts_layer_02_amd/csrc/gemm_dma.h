@@ -66,29 +66,52 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
 // lds: the destination's LDS byte address, already wave-uniform (the kernel
 // derives it with scalar arithmetic from the ring's base, so that no vector
 // instruction sits between the address and the copy).
+//
+// Wait states before it: one for the LDS DMA reading M0 after its SALU write,
+// five for a buffer instruction reading SGPRs that a VALU op (readfirstlane,
+// or the readlane of an SGPR spill reload) may have just written.  LIGHT
+// issues one only; it is used in the steady k-loop alone, and the build checks
+// the generated code of every kernel for a VALU write of a DMA's SGPR operand
+// within five wait states before it (hazard_check.py), failing if there is
+// one.
+template <bool LIGHT = false>
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile(
-      // Wait states: one for the LDS DMA reading M0 after its SALU write, five
-      // for a buffer instruction reading SGPRs a VALU op (readfirstlane,
-      // readlane) may have written just before this block.
-      "s_nop 4\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
-      : "memory");
+  if (LIGHT)
+    asm volatile(
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+        : "memory");
 }
 
 // L2 prefetch: lane i reads the 4 bytes at rsrc + voff + soff into the LDS
 // word lds_junk + 4 i (a scratch area nobody reads).  Its only purpose is to
 // start the L2 fill of that 64-byte sector well before the tile DMA needs
 // it; an offset outside the resource reads nothing.
+template <bool LIGHT = false>
 __device__ __forceinline__ void touch4u(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile(
-      "s_nop 4\n\t"  // as in dma16
-      "buffer_load_dword %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
-      : "memory");
+  if (LIGHT)
+    asm volatile(
+        "s_nop 0\n\t"  // as in dma16
+        "buffer_load_dword %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_nop 4\n\t"  // as in dma16
+        "buffer_load_dword %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+        : "memory");
 }
 __device__ __forceinline__ void touch4(i32x4 rsrc, uint32_t voff, uint32_t soff, const uint32_t* lds_dst) {
   touch4u(rsrc, voff, soff, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst));
@@ -586,30 +609,32 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
+    constexpr bool LT = decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
     if ((q & 1) == 0) {
-      dma16(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), stb + j * 1024);
+      dma16<LT>(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), stb + j * 1024);
     } else if (GATH == GATH_B) {
-      dma16(L.rb, gvb[GATH == GATH_B ? jj : 0], 0u, stb + TILE_ELEMS * 2 + j * 1024);
+      dma16<LT>(L.rb, gvb[GATH == GATH_B ? jj : 0], 0u, stb + TILE_ELEMS * 2 + j * 1024);
     } else {
       i32x4 rbk;
       uint32_t so_b;
       b_src(L, k, rbk, so_b);
-      dma16(rbk, vb[jj], so_b, stb + TILE_ELEMS * 2 + j * 1024);
+      dma16<LT>(rbk, vb[jj], so_b, stb + TILE_ELEMS * 2 + j * 1024);
     }
   };
   // L2 prefetch instruction o (0: A, 1: B) of ring position pos.
   auto pf_one = [&](int pos, int o, auto pure_c) {
     int k;
     const Ld L = pick(pos, k, pure_c);
+    constexpr bool LT = decltype(pure_c)::value;  // as in dma_one
     if (o == 0) {
-      touch4u(L.ra, L.pa, a_so(k), junk_lds);
+      touch4u<LT>(L.ra, L.pa, a_so(k), junk_lds);
     } else if (GATH == GATH_B) {
-      touch4u(L.rb, gpb, __builtin_amdgcn_readfirstlane(0u), junk_lds);
+      touch4u(L.rb, gpb, __builtin_amdgcn_readfirstlane(0u), junk_lds);  // (a readfirstlane just before)
     } else {
       i32x4 rbk;
       uint32_t so_b;
       b_src(L, k, rbk, so_b);
-      touch4u(rbk, L.pb, so_b, junk_lds);
+      touch4u<LT>(rbk, L.pb, so_b, junk_lds);
     }
   };
 

@@ -1,0 +1,51 @@
+"""The build-time LDS-DMA wait-state check (mixture_experts_layer_02_amd/hazard_check.py) on
+small hand-written gfx950 assembly: it must flag a VALU write of a DMA's SGPR operand within
+five wait states on any path, and pass code whose waits are long enough or whose SGPRs come
+from scalar instructions."""
+import io
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, os.path.join(ROOT, "mixture_experts_layer_02_amd"))
+import hazard_check  # noqa: E402
+
+
+def _check(tmp_path, body):
+    p = tmp_path / "k.s"
+    p.write_text("_Z6kernelv:\n" + "\n".join("\t" + l if not l.startswith(".L") else l for l in body) + "\n")
+    return hazard_check.check(str(p), io.StringIO())
+
+
+DMA = "buffer_load_dwordx4 v4, s[0:3], s8 offen lds"
+
+
+def test_flags_readlane_into_soffset(tmp_path):
+    assert _check(tmp_path, ["v_readlane_b32 s8, v10, 3", "s_nop 0", DMA]) == (1, 1)
+
+
+def test_flags_readfirstlane_into_resource(tmp_path):
+    assert _check(tmp_path, ["v_readfirstlane_b32 s2, v1", "s_mov_b32 m0, s9", "s_nop 0", DMA]) == (1, 1)
+
+
+def test_flags_carry_out_into_resource(tmp_path):
+    assert _check(tmp_path, ["v_add_co_u32_e64 v1, s[2:3], v2, v3", "s_nop 0", DMA]) == (1, 1)
+
+
+def test_five_wait_states_clear_it(tmp_path):
+    assert _check(tmp_path, ["v_readlane_b32 s8, v10, 3", "s_nop 4", DMA]) == (1, 0)
+    assert _check(tmp_path, ["v_readlane_b32 s8, v10, 3", "s_nop 1", "s_mov_b32 m0, s9", "s_nop 1", DMA]) == (1, 0)
+
+
+def test_scalar_writes_and_unrelated_sgprs_pass(tmp_path):
+    assert _check(tmp_path, ["s_add_u32 s8, s8, 64", "v_readlane_b32 s20, v10, 3", "s_nop 0", DMA]) == (1, 0)
+    # a VALU source SGPR is not a write
+    assert _check(tmp_path, ["v_add_u32_e32 v1, s8, v2", "s_nop 0", DMA]) == (1, 0)
+
+
+def test_follows_branches_into_the_dma_block(tmp_path):
+    body = ["s_cbranch_scc1 .LBB0_2", "v_readlane_b32 s8, v10, 3", "s_branch .LBB0_3",
+            ".LBB0_2:", "s_nop 7", ".LBB0_3:", "s_nop 0", DMA]
+    assert _check(tmp_path, body) == (1, 1)   # the path through the readlane
+    body[1] = "s_mov_b32 s8, 0"
+    assert _check(tmp_path, body) == (1, 0)
