@@ -432,15 +432,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       so_b = (uint32_t)k * BK;
     } else if (BLAY == LAY_K) {
       so_b = (uint32_t)k * BK * 2;
-    } else if (p.ksplit && (int64_t)k * BK >= p.ksplit) {
-      rbk = L.rb2;
-      so_b = (uint32_t)(((int64_t)k * BK - p.ksplit) * p.ldb * 2);
+    } else if (p.ksplit && k * BK >= p.ksplit) {  // (32-bit scalar arithmetic: k * BK < K < 2^31, and the
+      rbk = L.rb2;                                 //  offset is the 32-bit scalar offset of the buffer load)
+      so_b = (uint32_t)(k * BK - p.ksplit) * (uint32_t)p.ldb * 2u;
     } else {
-      so_b = (uint32_t)((int64_t)k * BK * p.ldb * 2);
+      so_b = (uint32_t)(k * BK) * (uint32_t)p.ldb * 2u;
     }
   };
   auto a_so = [&](int k) -> uint32_t {
-    return (ALAY == LAY_K) ? (uint32_t)k * BK * 2 : (uint32_t)((int64_t)k * BK * p.lda * 2);
+    return (ALAY == LAY_K) ? (uint32_t)k * BK * 2 : (uint32_t)(k * BK) * (uint32_t)p.lda * 2u;
   };
 
   // Current and next tile.  A ring position is a k-tile of the current tile
@@ -590,9 +590,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   auto dma_one = [&](int pos, int q, auto pure_c) {
     int k;
     const Ld L = pick(pos, k, pure_c);
-    uint16_t* st = ring[(gbase + pos) % STAGES];
+    uint16_t* st = ring[(uint32_t)(gbase + pos) % STAGES];
     // the stage's LDS byte address in scalar arithmetic; element offsets x2
-    const uint32_t stb = ring_lds + (uint32_t)(((gbase + pos) % STAGES) * STAGE_ELEMS * 2);
+    const uint32_t stb = ring_lds + ((uint32_t)(gbase + pos) % STAGES) * STAGE_ELEMS * 2;
     if (BQ8) {  // q < NJ: A; then NJB FP8 B instructions; then the B rows' scales
       if (q < NJ) {
         dma16(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), stb + (wave * NJ + q) * 1024);
@@ -799,7 +799,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     using PU = decltype(pure_c);
-    const uint16_t* st = ring[(gbase + kt) % STAGES];
+    const uint16_t* st = ring[(uint32_t)(gbase + kt) % STAGES];
     // GATH_B: the tokens of position kt+3+PFD (read two k-tiles later, after the
     // barriers that follow their wait).
     if (GATH == GATH_B) tok_dma_pos(kt + 3 + PFD);
@@ -828,7 +828,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // GATH_A: the next tile's tokens (copied at this tile's top, waited for
     // by now in every wave) give its A offsets.
     if (GATH == GATH_A && !FIRST && kt == gat_kt) gat_fill_next();
-    const uint16_t* nst = ring[(gbase + kt + 1) % STAGES];
+    const uint16_t* nst = ring[(uint32_t)(gbase + kt + 1) % STAGES];
     if (LAST)
       kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
     else
@@ -910,7 +910,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         wait_vm<PER + NPF>();  // position 0 has landed (then come its prefetch and position 1)
         lds_barrier();
 #pragma unroll
-        for (int f = 0; f < MI + NI; ++f) read_frag(ring[gbase % STAGES], 0, f, fa[0], fb[0]);
+        for (int f = 0; f < MI + NI; ++f) read_frag(ring[(uint32_t)gbase % STAGES], 0, f, fa[0], fb[0]);
       }
       using T_ = std::true_type;
       using F_ = std::false_type;
