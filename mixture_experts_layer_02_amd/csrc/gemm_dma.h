@@ -594,13 +594,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // the stage's LDS byte address in scalar arithmetic; element offsets x2
     const uint32_t stb = ring_lds + ((uint32_t)(gbase + pos) % STAGES) * STAGE_ELEMS * 2;
     if (BQ8) {  // q < NJ: A; then NJB FP8 B instructions; then the B rows' scales
+      constexpr bool LTQ = decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
       if (q < NJ) {
-        dma16(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), stb + (wave * NJ + q) * 1024);
+        dma16<LTQ>(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), stb + (wave * NJ + q) * 1024);
       } else if (q < NJ + NJB) {
         i32x4 rbk;
         uint32_t so_b;
         b_src(L, k, rbk, so_b);
-        dma16(rbk, vb[q - NJ], so_b, stb + TILE_ELEMS * 2 + (wave * NJB + q - NJ) * 1024);
+        dma16<LTQ>(rbk, vb[q - NJ], so_b, stb + TILE_ELEMS * 2 + (wave * NJB + q - NJ) * 1024);
       } else {
         touch4(L.rs, vs, (uint32_t)(k >> 1) * 4u,
                reinterpret_cast<const uint32_t*>(st + TILE_ELEMS + 8192 + wave * 128));
