@@ -131,6 +131,8 @@ PERMUTE_CASES = [
     (256, 8, 1, 0, 1, 64, "f32", 0.0),
     (2000, 96, 8, 0, 96, 512, "bf16", 1.5),      # skewed: hot and empty experts
     (1500, 40, 4, 8, 24, 64, "bf16", 0.0),
+    (70000, 64, 8, 8, 40, 64, "bf16", 1.5),      # 274 token blocks: the per-expert scan runs two chunks
+    (140000, 16, 2, 0, 16, 64, "f32", 0.0),      # 547 token blocks: three chunks
 ]
 
 
@@ -167,9 +169,11 @@ def test_permute(gpu, T, E, k, e0, NL, d, dtype, skew):
 # ---------------------------------------------------------------------------
 # A1: router logits
 # ---------------------------------------------------------------------------
+# (bf16 shapes with fewer than 256 output tiles are split over d: 300 x 256 x 72 in 4 chunks,
+# 1000 x 512 x 384 in 8, 11008 x 640 x 384 in 3 of 256, 256 and 128; 1 x 64 x 8 is not split)
 @pytest.mark.parametrize("T,d,E,dtype,bias", [(1, 64, 8, "bf16", False), (300, 256, 72, "bf16", True),
-                                             (1000, 512, 384, "bf16", False), (129, 128, 8, "f32", True),
-                                             (333, 192, 96, "f32", False)])
+                                             (1000, 512, 384, "bf16", False), (11008, 640, 384, "bf16", True),
+                                             (129, 128, 8, "f32", True), (333, 192, 96, "f32", False)])
 def test_router_logits(gpu, T, d, E, dtype, bias):
     cfg = synth.Config("t", 11, T, d, E, 2, 64, 0, E, dtype, 1.0, "router", False)
     inp = synth.make_inputs(cfg, want=("wr", "x"))
