@@ -981,15 +981,39 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         r2 = r0;
         ldo = ld2;
       }
+      // Values the epilogue reads are loaded in batches ahead of the stores
+      // that use them: a load waits for every memory instruction issued
+      // before it, so each batch costs one round trip after the previous
+      // batch's stores. EPI_ADD: the old C values of two 32-row blocks (one
+      // for fp32 C, whose two would not fit in registers). EPI_SWIGLU_BWD: G
+      // and U of the four 8-row slabs of one block.
+      constexpr int AB = VPL <= 2 ? 2 : 1;
+      u32x4_t oldc[AB][4][VPL];
+      u32x4_t gup[4][VPL][2];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int rowb = wm * 128 + mi * 32;  // the block's first row in the tile
         // Rows of this block lie on one side of msplit (a multiple of 32).
         const bool side2 = PLAIN && p.msplit && m0g + rowb >= p.msplit;
-        // EPI_ADD: the block's old C values, all loaded before any of its
-        // stores (a load waits for every memory instruction issued before it).
-        u32x4_t oldc[4][VPL];
-        if (EPI == EPI_ADD) {
+        if (EPI == EPI_ADD && mi % AB == 0) {
+#pragma unroll
+          for (int m2 = 0; m2 < AB; ++m2) {
+            const int rowb2 = rowb + m2 * 32;
+            const bool side2b = p.msplit && m0g + rowb2 >= p.msplit;
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+              for (int vi = 0; vi < VPL; ++vi) {
+                const int e = lane_e + vi * 64;
+                const int rl = e / CPR, cv = (e % CPR) * W;
+                const int row = rowb2 + sl * 8 + rl, col = col_base + cv;
+                const int64_t eo = (int64_t)row * ldo + col;
+                oldc[m2][sl][vi] = __builtin_amdgcn_raw_buffer_load_b128(
+                    side2b ? r1 : r0, col < t.nlim ? (uint32_t)(eo * (CF32 ? 4 : 2)) : 0x80000000u, 0, 0);
+              }
+          }
+        }
+        if (EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
           for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -998,28 +1022,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
               const int rl = e / CPR, cv = (e % CPR) * W;
               const int row = rowb + sl * 8 + rl, col = col_base + cv;
               const int64_t eo = (int64_t)row * ldo + col;
-              oldc[sl][vi] = __builtin_amdgcn_raw_buffer_load_b128(
-                  side2 ? r1 : r0, col < t.nlim ? (uint32_t)(eo * (CF32 ? 4 : 2)) : 0x80000000u, 0, 0);
+              const bool ok = col < t.nlim;
+              gup[sl][vi][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+              gup[sl][vi][1] =
+                  __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
             }
         }
-        u32x4_t gup[2][VPL][2];  // EPI_SWIGLU_BWD: G and U of two slabs, loaded ahead of their stores
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-          if (EPI == EPI_SWIGLU_BWD && (sl & 1) == 0) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-              for (int vi = 0; vi < VPL; ++vi) {
-                const int e = lane_e + vi * 64;
-                const int rl = e / CPR, cv = (e % CPR) * W;
-                const int row = rowb + (sl + s2) * 8 + rl, col = col_base + cv;
-                const int64_t eo = (int64_t)row * ldo + col;
-                const bool ok = col < t.nlim;
-                gup[s2][vi][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
-                gup[s2][vi][1] =
-                    __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
-              }
-          }
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -1050,8 +1060,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                   for (int q = 0; q < 4; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
                 }
                 if (EPI == EPI_ADD) {
+                  u32x4_t old = oldc[mi % AB][sl][vi];
+                  asm volatile("" : "+v"(old));  // used here, not hoisted to its load
 #pragma unroll
-                  for (int q = 0; q < 4; ++q) o[q] += __uint_as_float(oldc[sl][vi][q]);
+                  for (int q = 0; q < 4; ++q) o[q] += __uint_as_float(old[q]);
                 }
                 const u32x4_t d = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                    __float_as_uint(o[3])};
@@ -1068,7 +1080,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                   for (int q = 0; q < 8; ++q) o[q] += ok ? p.bias[t.n0 + col + q] : 0.f;
                 }
                 if (EPI == EPI_ADD) {
-                  const u32x4_t old = oldc[sl][vi];
+                  u32x4_t old = oldc[mi % AB][sl][vi];
+                  asm volatile("" : "+v"(old));  // used here, not hoisted to its load
 #pragma unroll
                   for (int q = 0; q < 8; ++q)
                     o[q] += __uint_as_float((q & 1) ? (old[q >> 1] & 0xffff0000u) : (old[q >> 1] << 16));
@@ -1093,8 +1106,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             } else {  // EPI_SWIGLU_BWD: v = dH
               const uint32_t og = ok ? (uint32_t)(eo * 2) : 0x80000000u;
               const uint32_t ou = ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u;
-              const u32x4_t gq = gup[sl & 1][vi][0];
-              const u32x4_t uq = gup[sl & 1][vi][1];
+              u32x4_t gq = gup[sl][vi][0];
+              u32x4_t uq = gup[sl][vi][1];
+              asm volatile("" : "+v"(gq), "+v"(uq));  // used here, not hoisted to their loads
               float dg[8], du[8];
 #pragma unroll
               for (int q = 0; q < 8; ++q) {
