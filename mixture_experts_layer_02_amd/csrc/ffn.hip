@@ -67,13 +67,19 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;
   if (grid <= 0) return hipSuccess;
   if constexpr (std::is_same<AT, uint16_t>::value) {
+    // Grouped-K products (weight gradients, split-K partials) write fp32 only,
+    // so no bf16-output kernel is built for them.
+    constexpr bool F32_ONLY = GRP == GRP_K;
+    if (F32_ONLY && !p.c_f32) return hipErrorInvalidValue;
     const bool cf = (EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32;
     if (p.dyn) {
       if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
-      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+      else if constexpr (!F32_ONLY)
+        gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
     } else {
       if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
-      else gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+      else if constexpr (!F32_ONLY)
+        gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
     }
   }
   return hipGetLastError();

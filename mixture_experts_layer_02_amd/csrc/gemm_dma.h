@@ -990,6 +990,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       constexpr int AB = VPL <= 2 ? 2 : 1;
       u32x4_t oldc[AB][4][VPL];
       u32x4_t gup[4][VPL][2];
+      // Rows 8 sl .. 8 sl + 7 of the wave's 32-row block mi, as fp32, into the
+      // wave's staging area.
+      auto stage_slab = [&](int mi_, int sl_) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            stage[((lane_e >> 5) * 4 + r4) * SP + ni * 32 + (lane_e & 31)] = acc[mi_][ni][sl_ * 4 + r4];
+      };
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int rowb = wm * 128 + mi * 32;  // the block's first row in the tile
@@ -1030,11 +1039,25 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         }
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
+          if (mi == 0 && sl == 0) stage_slab(0, 0);  // later slabs are staged one ahead, below
+          float vv[VPL][W], vv2[VPL][W];
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
+          for (int vi = 0; vi < VPL; ++vi) {
+            const int e = lane_e + vi * 64;
+            const int rl = e / CPR, cv = (e % CPR) * W;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-              stage[((lane_e >> 5) * 4 + r4) * SP + ni * 32 + (lane_e & 31)] = acc[mi][ni][sl * 4 + r4];
+            for (int q = 0; q < W; ++q) {
+              vv[vi][q] = stage[rl * SP + cv + q];
+              vv2[vi][q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+            }
+          }
+          // Stage the next slab now: a wave's LDS operations run in order, so
+          // these writes land after the reads above, and they issue while the
+          // reads return and this slab is converted and stored.
+          if (sl < 3)
+            stage_slab(mi, sl + 1);
+          else if (mi + 1 < MI)
+            stage_slab(mi + 1, 0);
 #pragma unroll
           for (int vi = 0; vi < VPL; ++vi) {
             const int e = lane_e + vi * 64;
@@ -1042,8 +1065,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             float v[W], v2[W];
 #pragma unroll
             for (int q = 0; q < W; ++q) {
-              v[q] = stage[rl * SP + cv + q];
-              v2[q] = DUAL ? stage[rl * SP + OC + cv + q] : 0.f;
+              v[q] = vv[vi][q];
+              v2[q] = vv2[vi][q];
             }
             const int row = rowb + sl * 8 + rl;  // row in the tile
             const int col = col_base + cv;       // column in the tile
