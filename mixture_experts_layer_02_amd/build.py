@@ -1,6 +1,7 @@
 """Build libmoe.so (all HIP sources under csrc/) for gfx950 with hipcc.
 
-Usage: python -m mixture_experts_layer_02_amd.build   (or __graft_entry__.build())
+Usage: python -m mixture_experts_layer_02_amd.build [-q] [--no-light-dma]
+       (or __graft_entry__.build())
 Objects go to _build/ at the repository root; the library is written next to
 this file so that it travels with the source tree.
 """
@@ -41,24 +42,28 @@ def _run(cmd):
 CHECKED = ["ffn.hip", "fp8.hip"]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    objs = []
-    cmds = []
+def _compile(light: bool, verbose: bool):
+    """Objects of every source and device assembly of the checked ones."""
+    defs = [] if light else ["-DMOE_LIGHT_DMA=0"]
+    objs, asms, cmds = [], [], []
     for src in SOURCES:
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
-    asms = []
+        cmds.append([HIPCC, *FLAGS, *defs, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CHECKED:
         asm = os.path.join(OBJ, src.replace(".hip", ".gfx950.s"))
         asms.append(asm)
-        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
-                     "-o", asm])
+        cmds.append([HIPCC, *FLAGS, *defs, *EXTRA.get(src, []), "--cuda-device-only", "-S",
+                     os.path.join(CSRC, src), "-o", asm])
     with cf.ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
+    return objs, asms
+
+
+def _check(asms):
+    """(LDS DMAs, hazards, report) over the given device assembly files."""
     sys.path.insert(0, HERE)
     try:
         import hazard_check
@@ -71,11 +76,28 @@ def build(verbose: bool = False) -> str:
         t, b = hazard_check.check(asm, report)
         n_dma += t
         n_bad += b
+    return n_dma, n_bad, report.getvalue()
+
+
+def build(verbose: bool = False, light: bool = True) -> str:
+    """Compile and link libmoe.so. The steady-loop DMAs carry one wait state
+    (light) unless the generated code has a VALU write of a DMA's SGPR within
+    five wait states; then everything is compiled again with five everywhere."""
+    os.makedirs(OBJ, exist_ok=True)
+    objs, asms = _compile(light, verbose)
+    n_dma, n_bad, report = _check(asms)
+    if n_bad and light:
+        print(f"warning: {n_bad} of {n_dma} LDS DMAs have a VALU write of an SGPR operand within five wait "
+              "states; compiling again with five wait states before every DMA (slower steady loop)\n" + report,
+              file=sys.stderr)
+        light = False
+        objs, asms = _compile(light, verbose)
+        n_dma, n_bad, report = _check(asms)
     if n_bad:
-        raise RuntimeError(f"LDS-DMA wait-state hazards in the generated code ({n_bad} of {n_dma}):\n" +
-                           report.getvalue())
+        raise RuntimeError(f"LDS-DMA wait-state hazards in the generated code ({n_bad} of {n_dma}):\n" + report)
     if verbose:
-        print(f"hazard check: {n_dma} LDS-DMA instructions, none within 5 wait states of a VALU write of its SGPRs")
+        print(f"hazard check: {n_dma} LDS-DMA instructions, none within 5 wait states of a VALU write of its SGPRs"
+              + ("" if light else " (five wait states before every DMA)"))
     tmp = OUT + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, OUT)
@@ -85,4 +107,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    build(verbose="-q" not in sys.argv, light="--no-light-dma" not in sys.argv)

@@ -72,8 +72,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
 // or the readlane of an SGPR spill reload) may have just written.  LIGHT
 // issues one only; it is used in the steady k-loop alone, and the build checks
 // the generated code of every kernel for a VALU write of a DMA's SGPR operand
-// within five wait states before it (hazard_check.py), failing if there is
-// one.
+// within five wait states before it (hazard_check.py). If the check finds one,
+// the build compiles again with MOE_LIGHT_DMA=0, which gives every DMA five.
+#ifndef MOE_LIGHT_DMA
+#define MOE_LIGHT_DMA 1
+#endif
 template <bool LIGHT = false>
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   if (LIGHT)
@@ -594,7 +597,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // the stage's LDS byte address in scalar arithmetic; element offsets x2
     const uint32_t stb = ring_lds + ((uint32_t)(gbase + pos) % STAGES) * STAGE_ELEMS * 2;
     if (BQ8) {  // q < NJ: A; then NJB FP8 B instructions; then the B rows' scales
-      constexpr bool LTQ = decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
+      constexpr bool LTQ = MOE_LIGHT_DMA && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
       if (q < NJ) {
         dma16<LTQ>(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), stb + (wave * NJ + q) * 1024);
       } else if (q < NJ + NJB) {
@@ -610,7 +613,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
-    constexpr bool LT = decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
+    constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
     if ((q & 1) == 0) {
       dma16<LT>(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), stb + j * 1024);
     } else if (GATH == GATH_B) {
@@ -626,7 +629,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   auto pf_one = [&](int pos, int o, auto pure_c) {
     int k;
     const Ld L = pick(pos, k, pure_c);
-    constexpr bool LT = decltype(pure_c)::value;  // as in dma_one
+    constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // as in dma_one
     if (o == 0) {
       touch4u<LT>(L.ra, L.pa, a_so(k), junk_lds);
     } else if (GATH == GATH_B) {
@@ -953,7 +956,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       const int col_base = (DUAL ? wn * 64 : wn * 128);
       // Resources (row 0 = the tile's first row, element 0 = its first column).
       const int64_t m0g = t.m0;
-      __amdgpu_buffer_rsrc_t r0, r1, r2;
+      __amdgpu_buffer_rsrc_t r0, r1;
       int64_t ldo = p.ldc;
       if (PLAIN) {
         const int esz = CF32 ? 4 : 2;
@@ -963,7 +966,6 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         r0 = c_rsrc(cb + ((m0g * p.ldc + t.n0 + gof) * esz), p.ldc, esz);
         // C2 rows start at msplit: row r of the tile is C2 row m0 + r - msplit.
         r1 = p.msplit ? c_rsrc(cb2 + (((m0g - p.msplit) * p.ldc + t.n0 + gof) * esz), p.ldc, esz) : r0;
-        r2 = r0;
       } else if (EPI == EPI_SWIGLU) {
         // h [rows][N] in C; G | U [rows][2N] in gu_out (if saved).
         r0 = c_rsrc(reinterpret_cast<char*>(p.C) + (m0g * p.ldc + t.n0) * 2, p.ldc, 2);
@@ -971,14 +973,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         const int64_t ld2 = 2 * (int64_t)p.N;
         r1 = gub ? c_rsrc(gub + (m0g * ld2 + t.n0) * 2, ld2, 2)
                  : __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(p.C), (short)0, 0, 0x00020000);
-        r2 = r1;
         ldo = ld2;
       } else {
         // dG | dU [rows][2N] in C, from dH and G | U [rows][2N] in gu_in.
         const int64_t ld2 = 2 * (int64_t)p.N;
         r0 = c_rsrc(reinterpret_cast<char*>(p.C) + (m0g * ld2 + t.n0) * 2, ld2, 2);
         r1 = c_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.gu_in)) + (m0g * ld2 + t.n0) * 2, ld2, 2);
-        r2 = r0;
         ldo = ld2;
       }
       // Values the epilogue reads are loaded in batches ahead of the stores

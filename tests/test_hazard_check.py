@@ -1,7 +1,7 @@
 """The build-time LDS-DMA wait-state check (mixture_experts_layer_02_amd/hazard_check.py) on
 small hand-written gfx950 assembly: it must flag a VALU write of a DMA's SGPR operand within
 five wait states on any path, and pass code whose waits are long enough or whose SGPRs come
-from scalar instructions."""
+from scalar instructions. Also the build's fallback when the check finds something."""
 import io
 import os
 import sys
@@ -49,3 +49,50 @@ def test_follows_branches_into_the_dma_block(tmp_path):
     assert _check(tmp_path, body) == (1, 1)   # the path through the readlane
     body[1] = "s_mov_b32 s8, 0"
     assert _check(tmp_path, body) == (1, 0)
+
+
+# The build's response to a finding: compile again with five wait states before
+# every DMA (MOE_LIGHT_DMA=0), and fail only if that build has a finding too.
+# Compilation, the check and the link are stubbed; only the control flow runs.
+import mixture_experts_layer_02_amd.build as moe_build  # noqa: E402
+import pytest  # noqa: E402
+
+
+def _stub_build(monkeypatch, findings):
+    calls = []
+
+    def compile_(light, verbose):
+        calls.append(light)
+        return ["a.o"], ["a.s"]
+
+    results = iter(findings)
+    monkeypatch.setattr(moe_build, "_compile", compile_)
+    monkeypatch.setattr(moe_build, "_check", lambda asms: next(results))
+    monkeypatch.setattr(moe_build, "_run", lambda cmd: "")
+    monkeypatch.setattr(moe_build.os, "replace", lambda a, b: None)
+    monkeypatch.setattr(moe_build.os, "makedirs", lambda *a, **k: None)
+    return calls
+
+
+def test_build_keeps_light_dmas_without_findings(monkeypatch):
+    calls = _stub_build(monkeypatch, [(10, 0, "")])
+    moe_build.build()
+    assert calls == [True]
+
+
+def test_build_falls_back_to_five_wait_states(monkeypatch, capsys):
+    calls = _stub_build(monkeypatch, [(10, 2, "hazard in k"), (10, 0, "")])
+    moe_build.build()
+    assert calls == [True, False]
+    assert "compiling again with five wait states" in capsys.readouterr().err
+
+
+def test_build_fails_if_the_five_wait_state_build_has_findings(monkeypatch):
+    calls = _stub_build(monkeypatch, [(10, 2, "hazard in k"), (10, 1, "hazard in k")])
+    with pytest.raises(RuntimeError, match="hazards"):
+        moe_build.build()
+    assert calls == [True, False]
+    calls = _stub_build(monkeypatch, [(10, 1, "hazard in k")])
+    with pytest.raises(RuntimeError, match="hazards"):
+        moe_build.build(light=False)
+    assert calls == [False]
