@@ -156,3 +156,13 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert l.moe_fp8_quantize(None, moe.MOE_BF16, 128, good, good, None) == moe.MOE_ERR_INVALID_ARG
     assert l.moe_fp8_quantize(good, 7, 128, good, good, None) == moe.MOE_ERR_UNSUPPORTED
     assert l.moe_fp8_dequantize(good, good + 4, 128, good, None) == moe.MOE_ERR_INVALID_ARG     # misaligned
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    # no fallback path: without libmoe.so every entry point fails loudly
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.workspace_size(_d(), moe.OP_PERMUTE)
