@@ -227,6 +227,14 @@ def fp8_dequantize_blocks(codes, scales, block=128):
 # of the local (token, slot) selections by expert).
 # --------------------------------------------------------------------------
 
+def _check_distinct(idx):
+    """A token's k selections are k distinct experts (the top-k of stage 1
+    never repeats one); a routing that repeats an expert is rejected."""
+    for t, row in enumerate(np.asarray(idx).reshape(len(idx), -1)):
+        if len(set(int(e) for e in row)) != len(row):
+            raise ValueError(f"token {t} lists an expert more than once: {row.tolist()}")
+
+
 def count_tokens(idx, E, e0, NL):
     """counts[e] for every expert e, and the local boundaries offsets[0..NL].
 
@@ -238,6 +246,7 @@ def count_tokens(idx, E, e0, NL):
     routed rows R.
     """
     idx = np.asarray(idx)
+    _check_distinct(idx)
     counts = np.zeros(E, np.int64)
     for e in idx.reshape(-1):
         counts[int(e)] += 1
@@ -258,6 +267,7 @@ def generate_indices(idx, e0, NL, offsets):
     order, so every segment lists its tokens in ascending order.
     """
     idx = np.asarray(idx)
+    _check_distinct(idx)
     T, k = idx.shape
     R = int(offsets[NL])
     next_row = [int(offsets[n]) for n in range(NL)]

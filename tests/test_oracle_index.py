@@ -185,3 +185,14 @@ def test_empty_and_nonlocal_only():
     assert offsets.tolist() == [0, 0, 0]
     row_token, slot_row = oracle.generate_indices(idx, 2, 2, offsets)
     assert row_token.size == 0 and (slot_row == -1).all()
+
+
+def test_repeated_expert_in_a_token_is_rejected():
+    # The k selections of a token are k distinct experts (top-k over the
+    # experts); a routing that lists one twice has no row layout and is
+    # refused rather than silently counted.
+    idx = np.array([[0, 1], [2, 2], [1, 3]], np.int64)
+    with pytest.raises(ValueError):
+        oracle.count_tokens(idx, 4, 0, 4)
+    with pytest.raises(ValueError):
+        oracle.generate_indices(idx, 0, 4, np.array([0, 1, 2, 4, 5]))
