@@ -3,16 +3,28 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fwdbwd_1t]
 
 A step is one pass of the whole hot path over one batch: router logits,
-top-k routing, counting + permutation, the gate/up and down grouped GEMMs,
-the weighted combine, and the backward of each (combine, dH, dX, dW, route,
-router, unpermute).  Inputs are seeded synthetic tensors already resident in
-HBM when the timed region starts.  Every entry point is bracketed by HIP
-events on the stream it is launched on; the dominant kernel's average
-duration gives the roofline fraction.  Rank 0 prints one JSON line.
+top-k routing, counting + index generation, the gate/up and down grouped
+GEMMs (the gate/up reading the tokens in place through row_token), the
+weighted combine, and the backward of each (combine, dH, dX, dW1|dW3, dW2,
+route, unpermute, router).  Inputs are seeded synthetic tensors already
+resident in HBM.  Before each timed step a 1 GiB buffer is rewritten by a
+fill kernel, outside the timed events, so that every step starts with the
+L2 and infinity caches holding none of its data.  Every entry point is
+bracketed by HIP events on the stream it is launched on; the step time is
+the span from the first to the last event of the step.
+
+The longest single kernel launch of the step is graded against its roofline:
+its algorithmic flops (or bytes) per launch over its average event duration.
+
+After the main workload, the forward-only 1T-shape workloads (the one-GPU
+expert-parallel share, and the Zipf-skewed and forced-uniform routings of the
+96 local experts) are timed the same way and reported in a nested object.
+Rank 0 prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -27,7 +39,52 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop/B where the two roofs meet
+FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwdbwd_1t_hbm_traffic.txt")
+GEMM_ROWS = ("A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw13", "B4_dw2")
+EXTRA_WORKLOADS = ("share_1t", "zipf_1t", "uniform_1t")
+
+
+@dataclasses.dataclass
+class Row:
+    """One timed entry point of the step: its launches, algorithmic flops and bytes."""
+    name: str
+    fn: object
+    launches: int
+    flops: float = 0.0
+    nbytes: float = 0.0
+
+
+def pick_dominant(avg_ms, launches):
+    """The row holding the longest single kernel launch.
+
+    Rows that make one launch are compared by their average duration.  A row
+    of several launches is timed as a whole, so its longest launch is not
+    known; it can only be ruled out, by its whole time being shorter than the
+    chosen single launch.  If it is not, the choice is ambiguous and this
+    raises, rather than grade the wrong kernel."""
+    single = [r for r in avg_ms if launches[r] == 1]
+    if not single:
+        raise ValueError("no single-launch row to grade")
+    dom = max(single, key=lambda r: avg_ms[r])
+    for r in avg_ms:
+        if launches[r] > 1 and avg_ms[r] >= avg_ms[dom]:
+            raise ValueError(f"row {r} ({launches[r]} launches, {avg_ms[r]:.3f} ms) may hold a launch longer "
+                             f"than {dom} ({avg_ms[dom]:.3f} ms); time its launches separately")
+    return dom
+
+
+def grade(row, ms):
+    """Roofline of one launch: MFMA when its arithmetic intensity (algorithmic
+    flops per algorithmic byte) is at or above the ridge, else HBM."""
+    if row.flops and row.flops / row.nbytes >= RIDGE:
+        ach = row.flops / ms / 1e9
+        return {"kernel": row.name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    ach = row.nbytes / ms / 1e6
+    return {"kernel": row.name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
 def _kernel_source_sha():
@@ -74,33 +131,252 @@ def _copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def _cpu_baseline(cfg, inp, sample_tokens, n_groups=1):
-    """The oracle, as it stands, on the first `sample_tokens` tokens of the workload."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline(cfg, inp, sample_tokens, n_groups, extra_inputs):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of the
+    workload (every host core this process may use), plus single-thread
+    forward times on small samples of the tiny, small and 1T-share configs."""
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+
+    def f64(a, dt):
+        return synth.as_f32(a, dt).astype(np.float64)
+
+    def forward_backward(c, data, Ts, threads, groups=1):
+        dt = c.dtype
+        x = f64(data["x"][:Ts], dt)
+        w = {n: synth.as_f32(data[n], dt) for n in ("wr", "w1", "w3", "w2")}
+        with threadpool_limits(threads):
+            t0 = time.perf_counter()
+            fwd = oracle.layer_forward(x, w["wr"], w["w1"], w["w3"], w["w2"], c.k, c.expert_begin, c.num_local,
+                                       c.renormalize, bias=data.get("bias"), n_groups=groups)
+            if c.backward:
+                oracle.layer_backward(fwd, x, w["wr"], w["w1"], w["w3"], w["w2"], f64(data["dy"][:Ts], dt),
+                                      c.renormalize)
+            return time.perf_counter() - t0
+
     Ts = sample_tokens
-    dt = cfg.dtype
-    x = synth.as_f32(inp["x"][:Ts], dt).astype(np.float64)
-    dy = synth.as_f32(inp["dy"][:Ts], dt).astype(np.float64)
-    wr = synth.as_f32(inp["wr"], dt)
-    w1 = synth.as_f32(inp["w1"], dt)
-    w3 = synth.as_f32(inp["w3"], dt)
-    w2 = synth.as_f32(inp["w2"], dt)
-    t0 = time.perf_counter()
-    fwd = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize,
-                               n_groups=n_groups)
-    if cfg.backward:
-        oracle.layer_backward(fwd, x, wr, w1, w3, w2, dy, cfg.renormalize)
-    dt_s = time.perf_counter() - t0
-    return {"value": Ts / dt_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    wall = forward_backward(cfg, inp, Ts, cores, n_groups)
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    single = {}
+    for name, n in (("tiny_f32", 256), ("small_bf16", 256), ("share_1t", 64)):
+        c = dataclasses.replace(synth.CONFIGS[name], backward=False)
+        data = extra_inputs.get(name) or synth.make_inputs(c, want=("x", "wr", "w1", "w3", "w2"))
+        s = forward_backward(c, data, n, 1)
+        single[name] = {"tokens": n, "forward_s": round(s, 3), "tokens/s": round(n / s, 1)}
+    return {"value": Ts / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {Ts} of {cfg.T} tokens of {cfg.name}, all {cfg.num_local} local experts' "
-                      f"weights, {'forward+backward' if cfg.backward else 'forward'}, float64 numpy; "
-                      f"{dt_s:.1f} s wall"}
+                      f"weights, {'forward+backward' if cfg.backward else 'forward'}, float64 numpy with the "
+                      f"BLAS pool limited to the {cores} cores of the process's affinity mask; {wall:.1f} s wall",
+            "cpu_model": _cpu_model(), "blas_threads_max": int(blas),
+            "single_thread_forward": single}
+
+
+class Workload:
+    """Device tensors and the ordered rows of one workload's step."""
+
+    def __init__(self, moe, torch, cfg, inp, args, dev):
+        self.cfg = cfg
+        T, d, f, E, k, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.num_local
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        names = ("x", "wr", "w1", "w3", "w2") + (("dy",) if cfg.backward else ())
+        g = self.g = {n: up(inp[n]) for n in names}
+        bias = up(inp["bias"]) if "bias" in inp else None
+        routing = (up(inp["idx"]), up(inp["w"])) if cfg.routing == "roundrobin" else None
+        counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
+        D = self.D = moe.make_desc(T, d, f, E, k, cfg.expert_begin, NL, cfg.dtype, cfg.renormalize,
+                                   tile_counters=counters)
+        gather = not args.no_gather
+        b = self.b = moe.Buffers(D, backward=cfg.backward, gather=gather)
+        bb = 2 if cfg.dtype == "bf16" else 4
+        fp8 = self.fp8 = {}
+        if args.fp8_weights:
+            for n in ("w1", "w3", "w2"):
+                q = torch.empty(g[n].numel(), dtype=torch.uint8, device=dev)
+                sc = torch.empty(g[n].numel() // 128, dtype=torch.float32, device=dev)
+                moe.fp8_quantize(g[n], q, sc)
+                fp8[n] = (q, sc)
+        self.routing = routing
+        self.gather = gather
+        R_est = T * min(k, NL)       # replaced by the measured R after the run
+        self.R = R_est
+        wb = 1 if args.fp8_gemm else bb
+        idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
+        rows = []
+
+        def add(name, fn, launches, flops=lambda R: 0.0, nbytes=lambda R: 0.0):
+            rows.append((name, fn, launches, flops, nbytes))
+
+        nw = 3 * NL * d * f
+        if args.fp8_weights and not (args.fp8_gemm and not cfg.backward):
+            def dequant():
+                for n in ("w1", "w3", "w2"):
+                    moe.fp8_dequantize(fp8[n][0], fp8[n][1], g[n])
+            add("A0_fp8_dequant", dequant, 3, nbytes=lambda R: nw * 3 + nw // 128 * 4)
+        if routing is None:
+            add("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits, b.ws_router),
+                1 + (moe.workspace_size(D, moe.OP_ROUTER_LOGITS) > 0),
+                lambda R: 2.0 * T * d * E, lambda R: T * d * bb + E * d * bb + T * E * 4)
+            if args.n_groups > 1:
+                add("A2_route", lambda: moe.route_grouped(D, b.logits, args.n_groups, b.topk_idx, b.topk_w), 1,
+                    nbytes=lambda R: T * E * 4 + T * k * 8)
+            else:
+                add("A2_route", lambda: moe.route(D, b.logits, b.topk_idx, b.topk_w), 1,
+                    nbytes=lambda R: T * E * 4 + T * k * 8)
+        # counting (2 kernels), the expert offsets, placement, and the gather when x_perm is built
+        self.ntok_local = None
+        add("A34_permute", lambda: moe.permute(D, idx, None if gather else g["x"], b.counts, b.offsets,
+                                               b.row_token, b.slot_row, None if gather else b.x_perm,
+                                               b.ws_permute),
+            4 if gather else 5,
+            nbytes=lambda R: (0 if gather else self.ntok_local * d * bb + R * d * bb) + T * k * 12 + R * 4)
+        gu_bytes = (lambda R: R * 2 * f * bb) if cfg.backward else (lambda R: 0)
+        if args.fp8_gemm:
+            add("A5_gate_up", lambda: moe.expert_gate_up_fp8(
+                D, b.offsets, b.row_token if gather else None, g["x"] if gather else b.x_perm,
+                fp8["w1"][0], fp8["w1"][1], fp8["w3"][0], fp8["w3"][1], b.gu, b.h), 1,
+                lambda R: 4.0 * R * d * f, lambda R: R * d * bb + 2 * NL * f * d * wb + R * f * bb + gu_bytes(R))
+            add("A6_down", lambda: moe.expert_down_fp8(D, b.offsets, b.h, fp8["w2"][0], fp8["w2"][1], b.y_perm), 1,
+                lambda R: 2.0 * R * d * f, lambda R: R * f * bb + NL * f * d * wb + R * d * bb)
+        else:
+            if gather:
+                fn = lambda: moe.expert_gate_up_gather(D, b.offsets, b.row_token, g["x"], g["w1"], g["w3"], b.gu, b.h)
+            else:
+                fn = lambda: moe.expert_gate_up(D, b.offsets, b.x_perm, g["w1"], g["w3"], b.gu, b.h)
+            add("A5_gate_up", fn, 1,
+                lambda R: 4.0 * R * d * f, lambda R: R * d * bb + 2 * NL * f * d * bb + R * f * bb + gu_bytes(R))
+            add("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), 1,
+                lambda R: 2.0 * R * d * f, lambda R: R * f * bb + NL * f * d * bb + R * d * bb)
+        add("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), 1,
+            nbytes=lambda R: R * d * bb + T * d * bb + T * k * 8)
+        if cfg.backward:
+            add("B1_combine_bwd", lambda: moe.combine_bwd(D, b.slot_row, w, b.y_perm, g["dy"], b.dy_perm,
+                                                          b.dtopk_w), 1,
+                nbytes=lambda R: T * d * bb + 2 * R * d * bb + T * k * 12)
+            add("B2_dh", lambda: moe.expert_bwd_dh(D, b.offsets, g["w2"], b.gu, b.dy_perm, b.dgu), 1,
+                lambda R: 2.0 * R * d * f, lambda R: R * d * bb + NL * f * d * bb + 2 * R * 2 * f * bb)
+            add("B3_dx", lambda: moe.expert_bwd_dx(D, b.offsets, g["w1"], g["w3"], b.dgu, b.dx_perm), 1,
+                lambda R: 4.0 * R * d * f, lambda R: R * 2 * f * bb + 2 * NL * f * d * bb + R * d * bb)
+            add("B4_dw13", lambda: moe.expert_bwd_dw_gate_up(D, b.offsets, b.row_token if gather else None,
+                                                             g["x"] if gather else b.x_perm, b.dgu, b.dW1,
+                                                             b.dW3), 1,
+                lambda R: 4.0 * R * d * f, lambda R: R * d * bb + R * 2 * f * bb + 2 * NL * f * d * 4)
+            add("B4_dw2", lambda: moe.expert_bwd_dw_down(D, b.offsets, b.dy_perm, b.h, b.dW2), 1,
+                lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
+            if routing is None:
+                add("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), 1,
+                    nbytes=lambda R: T * E * 4 + T * k * 12)
+            add("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx), 1,
+                nbytes=lambda R: R * d * bb + T * d * bb + T * k * 4)
+            if routing is None:
+                # dlogits to bf16, dx += dlogits Wr, dWr split-K partials, their sum
+                add("B5_router_bwd", lambda: moe.router_bwd_acc(D, g["x"], g["wr"], b.dlogits, b.dx, b.dWr,
+                                                                b.ws_router_bwd), 4,
+                    lambda R: 4.0 * T * d * E, lambda R: 2 * T * d * bb + 2 * E * d * bb + T * E * 4 + E * d * 4)
+        self._rows = rows
+
+    def steps(self):
+        """(name, entry-point call) of each row, in step order."""
+        return [(n, fn) for n, fn, _, _, _ in self._rows]
+
+    def rows(self):
+        """Every row with its algorithmic flops and bytes at the measured R."""
+        R = self.R
+        return [Row(n, fn, l, fl(R), nb(R)) for n, fn, l, fl, nb in self._rows]
+
+
+def run(moe, torch, wl, args, steps, warmup, flush, note):
+    """Warm-up, then `steps` timed steps (each after a cache flush); per-row
+    and per-step event times in ms, and the timed loop's wall time."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=stream.device)
+    calls = wl.steps()
+    ev = {n: [] for n, _ in calls}
+    spans = []
+
+    def step(rec):
+        first = last = None
+        for name, fn in calls:
+            if args.hold_cus and name in GEMM_ROWS:
+                # Another kernel takes hold_cus CUs as the product starts (the main
+                # stream waits 20 us so that the holder's workgroups are resident).
+                side.wait_stream(stream)
+                moe.hold_cus(args.hold_cus, args.hold_us, stream=side)
+                moe.hold_cus(1, 20, lds_bytes=64, stream=stream)
+            if rec:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+                fn()
+                e.record(stream)
+                ev[name].append((s, e))
+                first = first or s
+                last = e
+            else:
+                fn()
+        if rec:
+            spans.append((first, last))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    note(f"{wl.cfg.name}: {warmup} warmup steps done; timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)          # outside the step's events
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg = {r: float(np.mean([s.elapsed_time(e) for s, e in ev[r]])) for r in ev if ev[r]}
+    step_ms = [s.elapsed_time(e) for s, e in spans]
+    return avg, step_ms, wall
+
+
+def summarize(wl, avg, step_ms, wall, steps, default_run):
+    """Per-row figures, the grouped-GEMM aggregate and the roofline of the longest launch."""
+    cfg, b = wl.cfg, wl.b
+    R = int(b.offsets[-1].item())
+    wl.R = R
+    wl.ntok_local = int((b.slot_row >= 0).any(dim=1).sum().item())
+    rows = {r.name: r for r in wl.rows()}
+    launches = {n: rows[n].launches for n in avg}
+    per_row = {}
+    for n, ms in avg.items():
+        r = rows[n]
+        ent = {"ms": round(ms, 4), "launches": r.launches}
+        if r.flops:
+            ent["TFLOP/s"] = round(r.flops / ms / 1e9, 1)
+            ent["frac_mfma"] = round(r.flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+        if r.nbytes:
+            ent["GB/s"] = round(r.nbytes / ms / 1e6, 1)
+            ent["frac_hbm"] = round(r.nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)
+        per_row[n] = ent
+    gemm = [n for n in GEMM_ROWS if n in avg]
+    gemm_tflops = sum(rows[n].flops for n in gemm) / sum(avg[n] for n in gemm) / 1e9
+    dom = pick_dominant(avg, launches)
+    roof = grade(rows[dom], avg[dom])
+    roof["traffic"] = _measured_traffic(dom) if default_run else None
+    ms_step = float(np.mean(step_ms))
+    return {"ms_per_step": ms_step, "R": R, "rows": per_row, "gemm_tflops": gemm_tflops, "roofline": roof,
+            "step_ms_min": float(np.min(step_ms)), "step_ms_max": float(np.max(step_ms)),
+            "wall_ms_per_step_incl_flush": wall * 1e3 / steps}
 
 
 def main():
@@ -109,6 +385,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fwdbwd_1t")
+    ap.add_argument("--extra-workloads", default=",".join(EXTRA_WORKLOADS),
+                    help="forward-only workloads timed after the main one (comma list, or 'none')")
+    ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--n-groups", type=int, default=1,
                     help="group-limited routing: take k/n_groups experts from each of n_groups expert groups")
     ap.add_argument("--schedule", choices=["static", "dynamic"], default="static",
@@ -116,8 +395,8 @@ def main():
     ap.add_argument("--hold-cus", type=int, default=0,
                     help="before each grouped GEMM, occupy this many CUs with another kernel (contention)")
     ap.add_argument("--hold-us", type=int, default=2000, help="how long each --hold-cus kernel runs")
-    ap.add_argument("--gather", action="store_true",
-                    help="gather fused into gate/up and dW1|dW3: no x_perm (A4 is index generation only)")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="build x_perm in the permute step instead of reading x through row_token in the GEMMs")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights held as blockwise-128 E4M3 codes + scales, dequantised to bf16 each step")
     ap.add_argument("--fp8-gemm", action="store_true",
@@ -134,242 +413,94 @@ def main():
     if args.copy_calibration:
         _copy_calibration(args.copy_calibration)
         return
+    if args.fp8_gemm and not args.fp8_weights:
+        raise SystemExit("--fp8-gemm needs --fp8-weights")
 
     import torch
 
     import mixture_experts_layer_02_amd as moe
     import synth
 
-    cfg = synth.CONFIGS[args.workload]
-
     def note(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.workload]
     t_gen = time.perf_counter()
     inp = synth.make_inputs(cfg)
     gen_s = time.perf_counter() - t_gen
     note(f"inputs of {cfg.name} drawn in {gen_s:.1f} s")
-    dev = torch.device("cuda:0")
-
-    def up(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    g = {n: up(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
-    bias = up(inp["bias"]) if "bias" in inp else None
-    routing = (up(inp["idx"]), up(inp["w"])) if cfg.routing == "roundrobin" else None
-    counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
-    D = moe.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype,
-                      cfg.renormalize, tile_counters=counters)
-    b = moe.Buffers(D, backward=cfg.backward, gather=args.gather)
-    stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream(device=dev)
-    gemm_rows = {"A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw"}
-
-    fp8 = {}
-    if args.fp8_weights:
-        for n in ("w1", "w3", "w2"):
-            q = torch.empty(g[n].numel(), dtype=torch.uint8, device=dev)
-            sc = torch.empty(g[n].numel() // 128, dtype=torch.float32, device=dev)
-            moe.fp8_quantize(g[n], q, sc)
-            fp8[n] = (q, sc)
-        torch.cuda.synchronize()
-        qs, qe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        qs.record()
-        for n in ("w1", "w3", "w2"):
-            moe.fp8_quantize(g[n], fp8[n][0], fp8[n][1])
-        qe.record()
-        torch.cuda.synchronize()
-        fp8_quant_ms = qs.elapsed_time(qe)
-    rows = ["A1_router_logits", "A2_route", "A34_permute", "A5_gate_up", "A6_down", "A7_combine"]
-    if args.fp8_gemm and not args.fp8_weights:
-        raise SystemExit("--fp8-gemm needs --fp8-weights")
-    if args.fp8_weights and not (args.fp8_gemm and not cfg.backward):
-        rows = ["A0_fp8_dequant"] + rows      # bf16 weights for the GEMMs (or for the backward)
-    if cfg.backward:
-        rows += ["B1_combine_bwd", "B2_dh", "B3_dx", "B4_dw", "B5_route_bwd", "B5_unpermute", "B5_router_bwd"]
-    ev = {r: [] for r in rows}
-
-    def timed(name, fn, rec):
-        if args.hold_cus and name in gemm_rows:
-            # Another kernel takes hold_cus CUs as the product starts (the main
-            # stream waits 20 us so that the holder's workgroups are resident).
-            side.wait_stream(stream)
-            moe.hold_cus(args.hold_cus, args.hold_us, stream=side)
-            moe.hold_cus(1, 20, lds_bytes=64, stream=stream)
-        if rec:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            fn()
-            e.record(stream)
-            ev[name].append((s, e))
-        else:
-            fn()
-
-    def dequant_all():
-        for n in ("w1", "w3", "w2"):
-            moe.fp8_dequantize(fp8[n][0], fp8[n][1], g[n])
-
-    def step(rec):
-        if args.fp8_weights and "A0_fp8_dequant" in rows:
-            timed("A0_fp8_dequant", dequant_all, rec)
-        if routing is None:
-            timed("A1_router_logits", lambda: moe.router_logits(D, g["x"], g["wr"], bias, b.logits, b.ws_router), rec)
-            if args.n_groups > 1:
-                timed("A2_route", lambda: moe.route_grouped(D, b.logits, args.n_groups, b.topk_idx, b.topk_w), rec)
-            else:
-                timed("A2_route", lambda: moe.route(D, b.logits, b.topk_idx, b.topk_w), rec)
-            idx, w = b.topk_idx, b.topk_w
-        else:
-            idx, w = routing
-        if args.fp8_gemm:
-            if args.gather:
-                timed("A34_permute", lambda: moe.permute(D, idx, None, b.counts, b.offsets, b.row_token,
-                                                         b.slot_row, None, b.ws_permute), rec)
-            else:
-                timed("A34_permute", lambda: moe.permute(D, idx, g["x"], b.counts, b.offsets, b.row_token,
-                                                         b.slot_row, b.x_perm, b.ws_permute), rec)
-            timed("A5_gate_up", lambda: moe.expert_gate_up_fp8(
-                D, b.offsets, b.row_token if args.gather else None, g["x"] if args.gather else b.x_perm,
-                fp8["w1"][0], fp8["w1"][1], fp8["w3"][0], fp8["w3"][1], b.gu, b.h), rec)
-        elif args.gather:
-            timed("A34_permute", lambda: moe.permute(D, idx, None, b.counts, b.offsets, b.row_token, b.slot_row,
-                                                     None, b.ws_permute), rec)
-            timed("A5_gate_up", lambda: moe.expert_gate_up_gather(D, b.offsets, b.row_token, g["x"], g["w1"],
-                                                                  g["w3"], b.gu, b.h), rec)
-        else:
-            timed("A34_permute", lambda: moe.permute(D, idx, g["x"], b.counts, b.offsets, b.row_token,
-                                                     b.slot_row, b.x_perm, b.ws_permute), rec)
-            timed("A5_gate_up", lambda: moe.expert_gate_up(D, b.offsets, b.x_perm, g["w1"], g["w3"], b.gu, b.h),
-                  rec)
-        if args.fp8_gemm:
-            timed("A6_down", lambda: moe.expert_down_fp8(D, b.offsets, b.h, fp8["w2"][0], fp8["w2"][1], b.y_perm),
-                  rec)
-        else:
-            timed("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), rec)
-        timed("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), rec)
-        if not cfg.backward:
-            return
-        timed("B1_combine_bwd", lambda: moe.combine_bwd(D, b.slot_row, w, b.y_perm, g["dy"], b.dy_perm,
-                                                        b.dtopk_w), rec)
-        timed("B2_dh", lambda: moe.expert_bwd_dh(D, b.offsets, g["w2"], b.gu, b.dy_perm, b.dgu), rec)
-        timed("B3_dx", lambda: moe.expert_bwd_dx(D, b.offsets, g["w1"], g["w3"], b.dgu, b.dx_perm), rec)
-        if args.gather:
-            timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw_gather(D, b.offsets, b.row_token, g["x"], b.h, b.dgu,
-                                                                 b.dy_perm, b.dW1, b.dW3, b.dW2), rec)
-        else:
-            timed("B4_dw", lambda: moe.grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1,
-                                                          b.dW3, b.dW2), rec)
-        timed("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), rec)
-        timed("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx), rec)
-        timed("B5_router_bwd", lambda: moe.router_bwd_acc(D, g["x"], g["wr"], b.dlogits, b.dx, b.dWr,
-                                                          b.ws_router_bwd), rec)
-
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    wl = Workload(moe, torch, cfg, inp, args, dev)
+    torch.cuda.synchronize()
     note("inputs resident in HBM; warming up")
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    note(f"{args.warmup} warmup steps done; timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
+    avg, step_ms, wall = run(moe, torch, wl, args, args.steps, args.warmup, flush, note)
     peak_mem = torch.cuda.max_memory_allocated()
-    R = int(b.offsets[-1].item())
-    T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
-    bb = 2 if cfg.dtype == "bf16" else 4
-    avg_ms = {r: float(np.mean([s.elapsed_time(e) for s, e in ev[r]])) for r in rows if ev[r]}
-    flops = {"A1_router_logits": 2.0 * T * d * E, "A5_gate_up": 4.0 * R * d * f, "A6_down": 2.0 * R * d * f,
-             "B2_dh": 2.0 * R * d * f, "B3_dx": 4.0 * R * d * f, "B4_dw": 6.0 * R * d * f,
-             "B5_router_bwd": 4.0 * T * d * E}
-    ntok_local = int((b.slot_row >= 0).any(dim=1).sum().item())
-    nw = 3 * cfg.num_local * d * f
-    hbm_bytes = {"A0_fp8_dequant": nw * (1 + 2) + nw // 128 * 4,
-                 "A2_route": T * E * 4 + T * cfg.k * 8,
-                 "A34_permute": (0 if args.gather else ntok_local * d * bb + R * d * bb) + T * cfg.k * 12 + R * 4,
-                 "A7_combine": R * d * bb + T * d * bb + T * cfg.k * 8,
-                 "B1_combine_bwd": T * d * bb + 2 * R * d * bb + T * cfg.k * 12,
-                 "B5_route_bwd": T * E * 4 + T * cfg.k * 12,
-                 "B5_unpermute": R * d * bb + T * d * bb + T * cfg.k * 4}
-    # GEMM rows: each operand read once and each output written once (weights in the stored type)
-    wb = 1 if args.fp8_gemm else bb
-    NL = cfg.num_local
-    gemm_bytes = {"A1_router_logits": T * d * bb + E * d * bb + T * E * 4,
-                  "A5_gate_up": R * d * bb + 2 * NL * f * d * wb + R * f * bb + (R * 2 * f * bb if cfg.backward else 0),
-                  "A6_down": R * f * bb + NL * f * d * wb + R * d * bb,
-                  "B2_dh": R * d * bb + NL * f * d * bb + 2 * R * 2 * f * bb,
-                  "B3_dx": R * 2 * f * bb + 2 * NL * f * d * bb + R * d * bb,
-                  "B4_dw": 2 * R * d * bb + R * 3 * f * bb + 3 * NL * f * d * 4}
-    per_row = {}
-    for r, ms in avg_ms.items():
-        ent = {"ms": round(ms, 4)}
-        if r in flops:
-            ent["TFLOP/s"] = round(flops[r] / ms / 1e9, 1)
-            ent["frac_mfma"] = round(flops[r] / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
-        if r in hbm_bytes or r in gemm_bytes:
-            nbytes = hbm_bytes.get(r, gemm_bytes.get(r))
-            ent["GB/s"] = round(nbytes / ms / 1e6, 1)
-            ent["frac_hbm"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)
-        per_row[r] = ent
-    gemm_rows = [r for r in ("A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw") if r in avg_ms]
-    gemm_tflops = sum(flops[r] for r in gemm_rows) / sum(avg_ms[r] for r in gemm_rows) / 1e9
-    # dominant single-kernel row: the largest time among rows that launch one kernel
-    single = [r for r in ("A1_router_logits", "A2_route", "A5_gate_up", "A6_down", "A7_combine", "B1_combine_bwd",
-                          "B2_dh", "B3_dx", "B5_route_bwd", "B5_unpermute") if r in avg_ms]
-    dom = max(single, key=lambda r: avg_ms[r])
-    # the committed traffic figures were measured on the default fwdbwd_1t step only
-    default_run = (cfg.name == "fwdbwd_1t" and not (args.gather or args.fp8_weights or args.fp8_gemm or
+    default_run = (cfg.name == "fwdbwd_1t" and not (args.no_gather or args.fp8_weights or args.fp8_gemm or
                    args.hold_cus or args.n_groups > 1 or args.schedule != "static"))
-    traffic = _measured_traffic(dom) if default_run else None
-    # a GEMM whose arithmetic intensity is under the ridge (peak flops / peak bytes) is bound by HBM
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if dom in flops and flops[dom] / gemm_bytes[dom] >= ridge:
-        ach = flops[dom] / avg_ms[dom] / 1e9
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
-    else:
-        nbytes = gemm_bytes[dom] if dom in gemm_bytes else hbm_bytes[dom]
-        ach = nbytes / avg_ms[dom] / 1e6
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
-
+    main_sum = summarize(wl, avg, step_ms, wall, args.steps, default_run)
+    ms_step = main_sum["ms_per_step"]
     note(f"timed region: {ms_step:.3f} ms/step")
+    T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
+    del wl
+    torch.cuda.empty_cache()
+
+    # forward-only 1T workloads after the main one
+    extras, extra_inputs = {}, {}
+    names = [] if args.extra_workloads == "none" else [n for n in args.extra_workloads.split(",") if n]
+    for name in names:
+        c = synth.CONFIGS[name]
+        data = synth.make_inputs(c)
+        if name == "share_1t":             # reused by the CPU baseline's single-thread sample
+            extra_inputs[name] = data
+        w2 = Workload(moe, torch, c, data, args, dev)
+        torch.cuda.synchronize()
+        a2, s2, wall2 = run(moe, torch, w2, args, args.extra_steps, args.warmup, flush, note)
+        sm = summarize(w2, a2, s2, wall2, args.extra_steps, False)
+        extras[name] = {
+            "workload": f"{name}: T={c.T} d={c.d} E={c.E} ({c.num_local} local) top-{c.k} f={c.f} fwd, "
+                        f"routing {c.routing}",
+            "steps": args.extra_steps, "ms_per_step": round(sm["ms_per_step"], 4),
+            "tokens/s": round(c.T / sm["ms_per_step"] * 1e3, 1), "routed_rows": sm["R"],
+            "grouped_gemm_tflops": round(sm["gemm_tflops"], 1),
+            "grouped_gemm_frac_mfma": round(sm["gemm_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "roofline": sm["roofline"], "rows": sm["rows"]}
+        note(f"{name}: {sm['ms_per_step']:.3f} ms/step")
+        del w2
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         note(f"cpu baseline: oracle on {min(args.cpu_sample_tokens, cfg.T)} tokens")
-        del g, b
+        del flush
         torch.cuda.empty_cache()
-        cpu = _cpu_baseline(cfg, inp, min(args.cpu_sample_tokens, cfg.T), args.n_groups)
+        cpu = _cpu_baseline(cfg, inp, min(args.cpu_sample_tokens, cfg.T), args.n_groups, extra_inputs)
 
     out = {
-        "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(T / ms_step * 1e3, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} ({cfg.num_local} local from {cfg.expert_begin}) "
                                f"top-{cfg.k} f={f} {'fwd+bwd' if cfg.backward else 'fwd'}",
-                   "routed_rows": R, "global_batch": T, "parallelism": "single GPU",
+                   "routed_rows": main_sum["R"], "global_batch": T, "parallelism": "single GPU",
                    "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k",
                    "tile_schedule": args.schedule,
-                   "gather_fused": bool(args.gather),
+                   "gather_fused": not args.no_gather,
                    "expert_weights": ("bf16" if not args.fp8_weights else
                                       "fp8 e4m3 blocks of 128, read by the forward GEMMs" if args.fp8_gemm else
                                       "fp8 e4m3 blocks of 128, dequantised each step"),
                    "contention": (f"{args.hold_cus} CUs held for {args.hold_us} us at each grouped GEMM"
-                                  if args.hold_cus else None)},
+                                  if args.hold_cus else None),
+                   "timing": "per-step span of HIP events after a 1 GiB cache flush outside the events"},
+        "step_ms_min_max": [round(main_sum["step_ms_min"], 3), round(main_sum["step_ms_max"], 3)],
+        "wall_ms_per_step_incl_flush": round(main_sum["wall_ms_per_step_incl_flush"], 3),
         "device_mem_peak_gb": round(peak_mem / 1e9, 2),
-        "fp8_quantize": ({"ms": round(fp8_quant_ms, 4),
-                          "GB/s": round((nw * (2 + 1) + nw // 128 * 4) / fp8_quant_ms / 1e6, 1)}
-                         if args.fp8_weights else None),
-        "grouped_gemm_tflops": round(gemm_tflops, 1),
-        "grouped_gemm_frac_mfma": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": roof,
+        "grouped_gemm_tflops": round(main_sum["gemm_tflops"], 1),
+        "grouped_gemm_frac_mfma": round(main_sum["gemm_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "roofline": main_sum["roofline"],
         "cpu_baseline": cpu,
-        "rows": per_row,
+        "rows": main_sum["rows"],
+        "workloads": extras,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out), flush=True)

@@ -138,7 +138,11 @@ int moe_route_grouped(const moe_desc* desc, const float* logits, int n_groups, i
 /* A3 + A4, token counting, prefix sum, index generation and gather
  * (Algorithm 1 stages 2, 3 and the stage-4 gather).
  *   topk_idx [T][k] int32 (values in [0, E)), x [T][d] dtype (may be NULL:
- *   indices only);
+ *   indices only).  A token's k experts must be distinct (moe_route and
+ *   moe_route_grouped always give distinct experts; a routing supplied by
+ *   the caller must too).  Not checked: a repeated expert is counted once
+ *   and both of its slots get the same row, so counts no longer sum to T*k
+ *   and the backward's per-row writes collide;
  *   counts [E] int32: selections of every expert, local or not;
  *   offsets [NL+1] int32: exclusive prefix sum of the local counts
  *     (offsets[NL] = R), the page's cum_token_counts;
@@ -240,6 +244,22 @@ int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const v
 int moe_grouped_ffn_bwd_dw_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
                                   const void* x, const void* h, const void* dgu, const void* dy_perm,
                                   float* dW1, float* dW3, float* dW2, void* stream);
+
+/* B4, first launch alone: dW1[n] = dG_n^T a_n and dW3[n] = dU_n^T a_n
+ * ([NL][f][d] float32, overwritten; exact zeros for an expert with no rows).
+ *   row_token NULL: a is x_perm [R_cap][d]; else a is x [T][d] and k-row r
+ *   of the product reads x[row_token[r]] (bf16 only, x under 2 GiB, else
+ *   MOE_ERR_UNSUPPORTED).  dgu [R_cap][2f] as written by the dH step.
+ *   Results are bitwise those of moe_grouped_ffn_bwd_dw's dW1 and dW3. */
+int moe_expert_bwd_dw_gate_up(const moe_desc* desc, const int32_t* offsets,
+                              const int32_t* row_token, const void* a, const void* dgu,
+                              float* dW1, float* dW3, void* stream);
+
+/* B4, second launch alone: dW2[n] = dy_perm_n^T h_n ([NL][d][f] float32,
+ * overwritten; exact zeros for an expert with no rows); bitwise
+ * moe_grouped_ffn_bwd_dw's dW2. */
+int moe_expert_bwd_dw_down(const moe_desc* desc, const int32_t* offsets, const void* dy_perm,
+                           const void* h, float* dW2, void* stream);
 
 /* B5a, backward of the gather: dx[t] = dx_add[t] + sum over local slots j of
  *   dx_perm[slot_row[t][j]], summed in float32; dx [T][d] dtype out;

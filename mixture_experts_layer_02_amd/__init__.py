@@ -18,7 +18,7 @@ import torch  # imported before libmoe.so so that the process holds one HIP runt
 
 __all__ = [
     "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8",
-    "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
+    "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
 ]
@@ -84,6 +84,8 @@ _SIGS = {
     "moe_expert_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dh": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dw_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dw_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _vp],
     "moe_combine_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_ffn_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -270,6 +272,15 @@ def expert_bwd_dh(desc, offsets, w2, gu, dy_perm, dgu):
 
 def expert_bwd_dx(desc, offsets, w1, w3, dgu, dx_perm):
     _call("moe_expert_bwd_dx", desc, offsets, w1, w3, dgu, dx_perm, _stream())
+
+
+def expert_bwd_dw_gate_up(desc, offsets, row_token, a, dgu, dw1, dw3):
+    """dW1 | dW3 alone; row_token None: `a` is x_perm, else x (read through row_token)."""
+    _call("moe_expert_bwd_dw_gate_up", desc, offsets, row_token, a, dgu, dw1, dw3, _stream())
+
+
+def expert_bwd_dw_down(desc, offsets, dy_perm, h, dw2):
+    _call("moe_expert_bwd_dw_down", desc, offsets, dy_perm, h, dw2, _stream())
 
 
 def combine(desc, slot_row, topk_w, y_perm, y):

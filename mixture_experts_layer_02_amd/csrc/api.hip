@@ -213,6 +213,24 @@ int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const v
   return finish(moe::launch_ffn_bwd_dw(*desc, offsets, x_perm, h, dgu, dy_perm, dW1, dW3, dW2, S(stream)));
 }
 
+int moe_expert_bwd_dw_gate_up(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token, const void* a,
+                              const void* dgu, float* dW1, float* dW3, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !opt(row_token) || !need(a) || !need(dgu) || !need(dW1) || !need(dW3))
+    return MOE_ERR_INVALID_ARG;
+  if (row_token && !gather_ok(desc)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_dw_gate_up(*desc, offsets, a, dgu, dW1, dW3, S(stream), row_token));
+}
+
+int moe_expert_bwd_dw_down(const moe_desc* desc, const int32_t* offsets, const void* dy_perm, const void* h,
+                           float* dW2, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(dy_perm) || !need(h) || !need(dW2)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_dw_down(*desc, offsets, dy_perm, h, dW2, S(stream)));
+}
+
 int moe_unpermute_bwd(const moe_desc* desc, const int32_t* slot_row, const void* dx_perm, const float* dx_add,
                       void* dx, void* stream) {
   int rc = check_desc(desc);

@@ -368,13 +368,12 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_STORE, false>(q, mtiles_ub(d, 64) * cdiv(d.d, 64), s);
 }
 
-// row_token != NULL: x_perm is x itself and k-row r of the dW1|dW3 product
-// reads x[row_token[r]] (the gather fused into the B operand; bf16 only).
-hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
-                             const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
-                             hipStream_t s, const int32_t* row_token) {
+// dW1 | dW3 [f][d] = [dG | dU]^T x_perm over each expert's rows (one grouped-K
+// product with M = 2f split at f).  row_token != NULL: x_perm is x itself and
+// k-row r reads x[row_token[r]] (the gather fused into the B operand; bf16 only).
+hipError_t launch_dw_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* dgu,
+                             float* dW1, float* dW3, hipStream_t s, const int32_t* row_token) {
   const bool bf = d.dtype == MOE_BF16;
-  // dW1 | dW3 [f][d] = [dG | dU]^T x_perm over each expert's rows (M = 2f split at f)
   GemmParams p = blank(d);
   p.A = dgu;
   p.lda = 2 * (int64_t)d.f;
@@ -392,14 +391,17 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   p.M = 2 * d.f;
   p.N = d.d;
   p.c_f32 = 1;
-  hipError_t e;
-  if (bf && row_token)
-    e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_B>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
-  else if (row_token) e = hipErrorNotSupported;
-  else if (bf) e = run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT), s);
-  else e = run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
-  if (e != hipSuccess) return e;
-  // dW2 [d][f] = dy_perm^T h
+  const int64_t tiles = (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT);
+  if (bf && row_token) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_B>(p, tiles, s);
+  if (row_token) return hipErrorNotSupported;
+  if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, tiles, s);
+  return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
+}
+
+// dW2 [d][f] = dy_perm^T h over each expert's rows.
+hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void* dy_perm, const void* h, float* dW2,
+                          hipStream_t s) {
+  const bool bf = d.dtype == MOE_BF16;
   GemmParams q = blank(d);
   q.A = dy_perm;
   q.lda = d.d;
@@ -415,6 +417,14 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
   q.c_f32 = 1;
   if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 64) * cdiv(d.f, 64), s);
+}
+
+hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
+                             const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
+                             hipStream_t s, const int32_t* row_token) {
+  hipError_t e = launch_dw_gate_up(d, offsets, x_perm, dgu, dW1, dW3, s, row_token);
+  if (e != hipSuccess) return e;
+  return launch_dw_down(d, offsets, dy_perm, h, dW2, s);
 }
 
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,

@@ -47,6 +47,10 @@ hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const vo
                              const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
                              hipStream_t s,
                              const int32_t* row_token = nullptr);
+hipError_t launch_dw_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* dgu,
+                             float* dW1, float* dW3, hipStream_t s, const int32_t* row_token = nullptr);
+hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void* dy_perm, const void* h, float* dW2,
+                          hipStream_t s);
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
                              float* dx_router, void* dx_acc, float* dWr, void* ws, hipStream_t s);
 

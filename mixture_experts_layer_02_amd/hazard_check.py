@@ -3,6 +3,8 @@
 A buffer instruction that reads an SGPR needs five wait states after a VALU
 instruction wrote that SGPR (readfirstlane, readlane - also as the reload of an
 SGPR spilled to a VGPR lane -, compares and carry-outs with an SGPR result).
+An LDS DMA also reads M0 (its LDS destination), so a VALU write of M0 counts.
+Long branches (s_getpc / s_setpc) are followed to the labels they name.
 The compiler cannot see that hazard through the inline-asm LDS DMA, so the
 kernels insert the wait themselves: five states in general, one (for M0) in
 the steady k-loop.  This script walks back from every `buffer_load_* ... lds`
@@ -21,7 +23,10 @@ _SDST2 = re.compile(r"v_(add|sub|subrev|addc|subb|subbrev)_co_u32|v_div_scale_|v
 
 
 def _sregs(tok):
+    """SGPRs named by an operand token; M0 counts as the register "m0"."""
     tok = tok.strip().rstrip(",")
+    if tok == "m0":
+        return {"m0"}
     m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
     if m:
         return set(range(int(m.group(1)), int(m.group(2)) + 1))
@@ -62,6 +67,22 @@ def check(path, out=sys.stdout):
             m = re.match(r"s_(cbranch_\w+|branch)\s+(\.L\w+)", v)
             if m and m.group(2) in labels:
                 preds[labels[m.group(2)]].append(i)
+            if re.match(r"s_setpc_b64\b", v):
+                # A long branch: s_getpc, the target's offset added from a label
+                # difference, s_setpc.  Its targets are the labels named since
+                # the s_getpc; without one the jump is unknown and fails.
+                targets = set()
+                for j in range(i - 1, max(-1, i - 8), -1):
+                    if ins[j][0] == "inst":
+                        targets |= {t for t in re.findall(r"\.L\w+", ins[j][1]) if t in labels}
+                        if re.match(r"s_getpc_b64\b", ins[j][1]):
+                            break
+                targets -= {t for t in targets if t.startswith(".Lpost_getpc")}
+                if not targets:
+                    bad += 1
+                    print(f"unknown jump target in {f['name']}: {v!r}", file=out)
+                for t in targets:
+                    preds[labels[t]].append(i)
         for i, (k, v) in enumerate(ins):
             if k == "label":
                 j = i - 1
@@ -73,7 +94,7 @@ def check(path, out=sys.stdout):
             if k != "inst" or not re.match(r"buffer_load_\w+\s", v) or not v.endswith(" lds"):
                 continue
             total += 1
-            need = set()
+            need = {"m0"}  # the LDS destination base is read from M0
             for o in v.split(None, 1)[1].split(",")[1:]:
                 for t in o.split():
                     need |= _sregs(t)

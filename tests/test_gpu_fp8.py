@@ -7,7 +7,9 @@ weights too (decode * scale in float32, rounded to nearest even).  At the 1T
 expert shape the codes of sampled blocks are recomputed by the oracle one
 block at a time, and the page's error bound (at most 1/16 of the block
 maximum) is checked on every value.  The layer run on dequantised weights is
-checked against the oracle layer on the oracle's dequantised weights.
+checked against the oracle layer on the oracle's dequantised weights, and
+the GEMMs that read the FP8 codes directly against the oracle's expert MLP on
+those weights.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ import mixture_experts_layer_02_amd as moe
 import oracle
 import synth
 from gpu_util import f64, to_dev, to_host
-from layer_checks import TOL, _desc
+from layer_checks import TOL, _desc, random_routing
 from metrics import max_row_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -165,3 +167,48 @@ def test_fp8_gemms_reject_unsupported_shapes(gpu):
         moe.expert_gate_up_fp8(D, z, None, z, z, z, z, z, z, z)
     with pytest.raises(moe.MoeError):
         moe.expert_down_fp8(D, z, z, z, z, z)
+
+
+@pytest.mark.parametrize("gather,dyn", [(False, False), (True, False), (True, True)])
+@pytest.mark.parametrize("scale", [
+    dict(T=1024, d=512, f=256, E=32, num_local=16, expert_begin=8, k=4),
+    dict(T=700, d=384, f=256, E=64, num_local=24, expert_begin=40, k=6),     # ragged, empty experts
+])
+def test_fp8_gemms_match_the_oracle(gpu, scale, gather, dyn):
+    # gate/up + SwiGLU and down reading E4M3 codes and block scales, against
+    # the oracle's expert MLP on the oracle's own dequantised weights.
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[fp8 gemm vs oracle] {scale} gather={gather} dynamic={dyn}", flush=True)
+    T, d, f, E, k, e0, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local
+    inp = synth.make_inputs(cfg, want=("x", "w1", "w3", "w2"))
+    idx = random_routing(np.random.default_rng(T + d), T, E, k, skew=1.0)
+    D = moe.make_desc(T, d, f, E, k, e0, NL, "bf16", 1, tile_counters=moe.new_tile_counters(gpu) if dyn else None)
+    b = moe.Buffers(D, backward=True, gather=gather)
+    x = to_dev(inp["x"])
+    moe.permute(D, to_dev(idx), None if gather else x, b.counts, b.offsets, b.row_token, b.slot_row,
+                None if gather else b.x_perm, b.ws_permute)
+    q, ref_w = {}, {}
+    for n in ("w1", "w3", "w2"):
+        wd = to_dev(inp[n])
+        c = torch.empty(wd.numel(), dtype=torch.uint8, device=gpu)
+        sc = torch.empty(wd.numel() // 128, dtype=torch.float32, device=gpu)
+        moe.fp8_quantize(wd, c, sc)
+        q[n] = (c, sc)
+        codes, scales = oracle.fp8_quantize_blocks(synth.as_f32(inp[n], "bf16"))
+        ref_w[n] = oracle.fp8_dequantize_blocks(codes, scales).reshape(inp[n].shape).astype(np.float64)
+    moe.expert_gate_up_fp8(D, b.offsets, b.row_token if gather else None, x if gather else b.x_perm,
+                           q["w1"][0], q["w1"][1], q["w3"][0], q["w3"][1], b.gu, b.h)
+    moe.expert_down_fp8(D, b.offsets, b.h, q["w2"][0], q["w2"][1], b.y_perm)
+    torch.cuda.synchronize()
+    _, off = oracle.count_tokens(idx, E, e0, NL)
+    rows, _ = oracle.generate_indices(idx, e0, NL, off)
+    np.testing.assert_array_equal(to_host(b.offsets), off)
+    R = int(off[-1])
+    xp = oracle.permute(f64(inp["x"], "bf16"), rows)
+    G, U, H, Y = oracle.expert_ffn(xp, off, ref_w["w1"], ref_w["w3"], ref_w["w2"])
+    tol = TOL["bf16"]
+    gu = to_host(b.gu)[:R]
+    assert max_row_rel_err(gu[:, :f], G) <= tol
+    assert max_row_rel_err(gu[:, f:], U) <= tol
+    assert max_row_rel_err(to_host(b.h)[:R], H) <= tol
+    assert max_row_rel_err(to_host(b.y_perm)[:R], Y) <= tol

@@ -13,13 +13,20 @@ of the benchmark); the float64 oracle then recomputes what it can afford:
   token only, so the oracle computes them by running the layer on the sample;
 * the weight gradients dW1, dW3, dW2 of two whole experts (the least and the
   most loaded local expert that no near-tie touches), from the oracle's own
-  routing of every token.
+  routing of every token;
+* the layer again with the gather fused into the GEMMs (the configuration the
+  benchmark times), whose every output must equal the x_perm path's bit for
+  bit, so that all of the above holds for it too.
 
 dWr sums dlogits over all tokens, and dlogits needs every token's expert
 outputs, which is beyond what the oracle finishes in seconds at this size.
 It is checked by the property that defines it, dWr = dlogits^T x, on sampled
-entries with the GPU's dlogits; dlogits itself is checked on the sample
-above, and dWr against the oracle at reduced size in the other GPU tests.
+entries with the GPU's dlogits (dlogits itself is checked on the sample
+above), and against the oracle on the sampled tokens: the router backward
+runs again at the full shape, with the split and launches of the layer's
+own call, on a dlogits that holds the oracle's sampled rows and zeros
+elsewhere; its dWr must equal the oracle's dWr of the sampled tokens alone,
+and its input gradient the oracle's on those tokens.
 """
 import numpy as np
 import pytest
@@ -40,6 +47,14 @@ def _sample_tokens(T, seed):
     rng = np.random.default_rng(seed)
     s = rng.choice(np.arange(1, T - 1), size=min(N_SAMPLE, T - 2), replace=False)
     return np.unique(np.concatenate([[0, T - 1], s])).astype(np.int64)
+
+
+def _rows_t(t, rows):
+    return to_host(t[torch.as_tensor(rows, device=t.device)])
+
+
+def _dev_bf16(inp, name, dev):
+    return torch.from_numpy(inp[name].view(np.int16)).to(dev).view(torch.bfloat16)
 
 
 def _rows(b, name, rows):
@@ -112,6 +127,19 @@ def test_full_size_layer_sampled(gpu, name):
     assert torch.equal(xp.view(torch.int16), x_dev[xs]), "x_perm rows differ from x[row_token]"
     del x_dev, xs
 
+    # the gather-fused layer (no x_perm) gives bitwise the same outputs
+    _, bg = _run_layer(cfg, back, gpu, gather=True, inp=inp)
+    names = ["topk_idx", "offsets", "slot_row", "row_token", "h", "y_perm", "y"] + (
+        ["gu", "dy_perm", "dtopk_w", "dgu", "dx_perm", "dW1", "dW3", "dW2", "dlogits", "dWr", "dx"] if back else [])
+    for n in names:
+        a, c = getattr(b, n), getattr(bg, n)
+        if a.shape[0] == b.desc.R_cap and n not in ("topk_idx", "slot_row"):
+            a, c = a[:R], c[:R]
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                           c.view(torch.uint8) if c.dtype != torch.int32 else c), n
+    del bg
+    torch.cuda.empty_cache()
+
     # --- per-token quantities on a sample --------------------------------
     toks = _sample_tokens(T, cfg.seed)
     toks = toks[same[toks]]
@@ -161,6 +189,22 @@ def test_full_size_layer_sampled(gpu, name):
         assert whole_rel_err(to_host(b.dW1[n]), dW1) <= tol, n
         assert whole_rel_err(to_host(b.dW3[n]), dW3) <= tol, n
         assert whole_rel_err(to_host(b.dW2[n]), dW2) <= tol, n
+
+    # --- router backward at full shape on the oracle's sampled dlogits ---------
+    import mixture_experts_layer_02_amd as moe
+    from layer_checks import _desc
+    D = _desc(T, cfg.d, f, E, k, e0, NL, dt, cfg.renormalize)
+    dl_full = torch.zeros(T, E, dtype=torch.float32, device=b.dlogits.device)
+    dl_full[torch.as_tensor(toks, device=dl_full.device)] = torch.from_numpy(
+        g["dlogits"].astype(np.float32)).to(dl_full.device)
+    dwr_sub = torch.empty(E, cfg.d, dtype=torch.float32, device=dl_full.device)
+    dx_r = torch.empty(T, cfg.d, dtype=torch.float32, device=dl_full.device)
+    moe.router_bwd(D, _dev_bf16(inp, "x", dl_full.device), _dev_bf16(inp, "wr", dl_full.device), dl_full, dx_r,
+                   dwr_sub, b.ws_router_bwd)
+    torch.cuda.synchronize()
+    assert whole_rel_err(to_host(dwr_sub), g["dWr"]) <= tol
+    assert max_row_rel_err(_rows_t(dx_r, toks), g["dx_router"]) <= tol
+    del dl_full, dx_r, dwr_sub
 
     # --- dWr = dlogits^T x on sampled entries (property) ------------------
     rng = np.random.default_rng(cfg.seed + 1)

@@ -19,16 +19,10 @@ from metrics import max_row_rel_err, whole_rel_err
 
 pytestmark = pytest.mark.gpu
 
-from layer_checks import LOGIT_TOL, TOL, W_ATOL, W_RTOL, _desc, _routing_agreement, _run_layer
+from layer_checks import LOGIT_TOL, TOL, W_ATOL, W_RTOL, _desc, _routing_agreement, _run_layer, check_layer_backward, random_routing
 
 
-def _random_routing(rng, T, E, k, skew=0.0):
-    """Distinct experts per token; skew > 0 draws experts with Zipf-like popularity."""
-    keys = rng.random((T, E))
-    if skew > 0:
-        pop = (np.arange(E) + 1.0) ** -skew
-        keys = keys ** (1.0 / pop[rng.permutation(E)])
-    return np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+_random_routing = random_routing
 
 
 # ---------------------------------------------------------------------------
@@ -302,34 +296,7 @@ def test_layer_backward(gpu, name, scale):
     if scale:
         cfg = synth.scaled(cfg, **scale)
     inp, b = _run_layer(cfg, True, gpu)
-    dt = cfg.dtype
-    tol = TOL[dt]
-    x, wr = f64(inp["x"], dt), f64(inp["wr"], dt)
-    w1, w3, w2 = f64(inp["w1"], dt), f64(inp["w3"], dt), f64(inp["w2"], dt)
-    dy = f64(inp["dy"], dt)
-    ref = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize)
-    same = _routing_agreement(to_host(b.topk_idx), ref["logits"], ref["idx"])
-    assert same.all(), "a routing near-tie flipped; the weight gradients are not comparable"
-    g = oracle.layer_backward(ref, x, wr, w1, w3, w2, dy, cfg.renormalize)
-    R = int(ref["offsets"][-1])
-    assert max_row_rel_err(to_host(b.y), ref["y"]) <= tol
-    assert max_row_rel_err(to_host(b.dy_perm)[:R], g["dy_perm"]) <= tol
-    # dw and dlogits are scored against the whole tensor's maximum:
-    # dw[t][j] = <y_perm[row], dy[t]> is a dot product over d whose rounding
-    # error scales with the norms of its operands, not with its (often
-    # cancelling) value, so a per-token row of k values is ill-conditioned.
-    assert whole_rel_err(to_host(b.dtopk_w), g["dw"]) <= tol
-    dgu = to_host(b.dgu)[:R]
-    assert max_row_rel_err(dgu[:, :cfg.f], g["dG"]) <= tol
-    assert max_row_rel_err(dgu[:, cfg.f:], g["dU"]) <= tol
-    assert max_row_rel_err(to_host(b.dx_perm)[:R], g["dx_perm"]) <= tol
-    for n in range(cfg.num_local):
-        assert whole_rel_err(to_host(b.dW1)[n], g["dW1"][n]) <= tol, n
-        assert whole_rel_err(to_host(b.dW3)[n], g["dW3"][n]) <= tol, n
-        assert whole_rel_err(to_host(b.dW2)[n], g["dW2"][n]) <= tol, n
-    assert whole_rel_err(to_host(b.dlogits), g["dlogits"]) <= tol
-    assert whole_rel_err(to_host(b.dWr), g["dWr"]) <= tol
-    assert max_row_rel_err(to_host(b.dx), g["dx"]) <= tol
+    check_layer_backward(cfg, inp, b)
 
 
 def test_zero_row_experts_get_exact_zero_gradients(gpu):

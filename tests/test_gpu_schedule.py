@@ -7,7 +7,8 @@ Every bf16 product of the layer (router, gate/up + SwiGLU, down, dH + SwiGLU
 backward, dX, dW1|dW3, dW2, router backward and dW_r) runs once under each
 order on the same inputs, alone and with another kernel holding a third of
 the compute units for part of the run, and every output must match bit for
-bit.  The counters must be zero again after each call.
+bit.  The counters must be zero again after each call.  The dynamic-order
+layer is also compared with the oracle directly, alone and under contention.
 """
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ import torch
 import mixture_experts_layer_02_amd as moe
 import synth
 from gpu_util import to_dev
-from layer_checks import _desc
+from layer_checks import _desc, check_layer_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -65,3 +66,26 @@ def test_dynamic_order_is_bitwise_identical(gpu, scale, hold):
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
                                b.view(torch.uint8) if b.dtype != torch.int32 else b), (n, rep)
         assert int(counters.abs().sum().item()) == 0, counters.tolist()
+
+
+@pytest.mark.parametrize("scale,hold", [
+    (dict(T=512, d=256, f=128, E=32, num_local=8, expert_begin=8), False),
+    (dict(T=512, d=256, f=128, E=32, num_local=8, expert_begin=8), True),
+    (dict(T=700, d=192, f=192, E=16, num_local=16, expert_begin=0), True),
+])
+def test_dynamic_order_matches_the_oracle(gpu, scale, hold):
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[schedule vs oracle] {scale} hold={hold}", flush=True)
+    inp = synth.make_inputs(cfg)
+    dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
+    counters = moe.new_tile_counters(gpu)
+    dd = moe.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype,
+                       cfg.renormalize, tile_counters=counters)
+    if hold:
+        side = torch.cuda.Stream(device=gpu)
+        side.wait_stream(torch.cuda.current_stream())
+        moe.hold_cus(max(1, torch.cuda.get_device_properties(gpu).multi_processor_count // 3), 3000, stream=side)
+    b = _layer(cfg, dd, dev, None)
+    torch.cuda.synchronize()
+    assert int(counters.abs().sum().item()) == 0, counters.tolist()
+    check_layer_backward(cfg, inp, b)

@@ -96,3 +96,22 @@ def test_build_fails_if_the_five_wait_state_build_has_findings(monkeypatch):
     with pytest.raises(RuntimeError, match="hazards"):
         moe_build.build(light=False)
     assert calls == [False]
+
+
+def test_flags_valu_write_of_m0(tmp_path):
+    # the DMA reads M0 without naming it
+    assert _check(tmp_path, ["v_readfirstlane_b32 m0, v1", "s_nop 0", DMA]) == (1, 1)
+    assert _check(tmp_path, ["v_readfirstlane_b32 m0, v1", "s_nop 4", DMA]) == (1, 0)
+    assert _check(tmp_path, ["s_mov_b32 m0, s9", "s_nop 0", DMA]) == (1, 0)
+
+
+def test_follows_long_branches(tmp_path):
+    body = ["v_readlane_b32 s8, v10, 3", "s_getpc_b64 s[20:21]", ".Lpost_getpc0:",
+            "s_add_u32 s20, s20, (.LBB0_4-.Lpost_getpc0)&4294967295",
+            "s_addc_u32 s21, s21, (.LBB0_4-.Lpost_getpc0)>>32", "s_setpc_b64 s[20:21]",
+            ".LBB0_9:", "s_nop 7", "s_nop 7", ".LBB0_4:", DMA]
+    assert _check(tmp_path, body) == (1, 1)   # reached from the readlane through the jump
+
+
+def test_unknown_long_branch_target_fails(tmp_path):
+    assert _check(tmp_path, ["s_setpc_b64 s[20:21]", "s_nop 7", DMA])[1] == 1
