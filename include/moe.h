@@ -156,6 +156,25 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* x, in
                 int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid it): the same kernels and bitwise the same outputs, with the
+ * per-block counts and bases kept in a fixed scratch array of 4 MiB that the
+ * library holds in each device's memory for the life of the process, instead
+ * of a caller workspace.  The call allocates nothing: no hipMalloc, no
+ * allocating library routine.  Arguments, layouts and ownership as in
+ * moe_permute (the caller still passes every input and output).
+ *   Limit: (E + num_local) * ceil(T / 256) * 4 bytes <= 4 MiB (e.g. E = 384,
+ *   96 local: T up to 559,104 tokens); a larger shape returns
+ *   MOE_ERR_UNSUPPORTED with the sizes in moe_last_error().
+ *   The scratch is shared by every call on one device and keeps the last
+ *   call's contents (each call rewrites all it reads): calls that may
+ *   overlap on one device (different streams, or different host threads
+ *   without ordering) race and must be serialised by the caller. */
+int moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_idx, const void* x,
+                        int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                        void* x_perm, void* stream);
+
 /* A5 + A6, the grouped SwiGLU expert MLP (Algorithm 1 stage 4: Grouped_mm of
  * gate and up, Silu(gate) * up, Grouped_mm of down, with segment boundaries
  * offsets).  For each local expert n and row r in [offsets[n], offsets[n+1]):

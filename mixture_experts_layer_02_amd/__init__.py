@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -75,6 +75,7 @@ _SIGS = {
     "moe_route": [_vp, _vp, _vp, _vp],
     "moe_route_grouped": [_vp, ctypes.c_int, _vp, _vp, _vp],
     "moe_permute": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_permute_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_ffn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_expert_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_gate_up_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -233,6 +234,11 @@ def route_grouped(desc, logits, n_groups, topk_idx, topk_w):
 def permute(desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws):
     w, n = _ws(ws)
     _call("moe_permute", desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, w, n, _stream())
+
+
+def permute_noalloc(desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm):
+    """moe_permute with the library's fixed device scratch instead of a workspace."""
+    _call("moe_permute_noalloc", desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, _stream())
 
 
 def grouped_ffn(desc, offsets, x_perm, w1, w3, w2, gu, h, y_perm, ws=None):

@@ -1,5 +1,6 @@
 // The extern "C" entry points of libmoe.so (declared in include/moe.h):
 // argument validation on the host, then the kernel launches of each step.
+#include <stdio.h>
 #include <string.h>
 
 #include "internal.h"
@@ -92,6 +93,24 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* x, in
   if (!need(ws) || ws_bytes < moe::permute_workspace(*desc)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
   return finish(moe::launch_permute(*desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws,
                                     S(stream)));
+}
+
+int moe_permute_noalloc(const moe_desc* desc, const int32_t* topk_idx, const void* x, int32_t* counts,
+                        int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(topk_idx) || !need(counts) || !need(offsets) || !need(row_token) || !need(slot_row) || !opt(x))
+    return MOE_ERR_INVALID_ARG;
+  if (x && !need(x_perm)) return MOE_ERR_INVALID_ARG;
+  const size_t want = moe::permute_workspace(*desc);
+  if (want > moe::PERMUTE_SCRATCH_BYTES) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "moe_permute_noalloc: the shape needs %zu bytes of scratch, the fixed scratch holds %zu", want,
+             moe::PERMUTE_SCRATCH_BYTES);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return finish(moe::launch_permute_noalloc(*desc, topk_idx, x, counts, offsets, row_token, slot_row, x_perm,
+                                            S(stream)));
 }
 
 int moe_grouped_ffn(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* W1,

@@ -16,6 +16,11 @@ hipError_t launch_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, 
 hipError_t launch_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, hipStream_t s);
 
 size_t permute_workspace(const moe_desc& d);
+// Size of the allocation-free permute's fixed device scratch (4 MiB per device).
+constexpr size_t PERMUTE_SCRATCH_BYTES = (size_t)4 << 20;
+hipError_t launch_permute_noalloc(const moe_desc& d, const int32_t* idx, const void* x, int32_t* counts,
+                                  int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm,
+                                  hipStream_t s);
 size_t router_bwd_workspace(const moe_desc& d);
 
 size_t router_logits_workspace(const moe_desc& d);

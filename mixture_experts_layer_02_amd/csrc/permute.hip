@@ -17,6 +17,9 @@
 // Data movement (gather, combine and the backward scatter/sum) is token
 // major: one wavefront per token reads the token's row once and writes or
 // reads its routed rows with 16-byte vector accesses.
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 namespace moe {
@@ -300,6 +303,52 @@ size_t permute_workspace(const moe_desc& d) {
   const int64_t nblk = (d.T + BLK_TOK - 1) / BLK_TOK;
   // blk_counts [E][nblk] + base [NL][nblk]
   return (size_t)((int64_t)d.E * nblk + (int64_t)d.num_local * nblk) * sizeof(int32_t);
+}
+
+// Fixed device scratch of the allocation-free permute: the per-block counts
+// and bases that moe_permute keeps in the caller's workspace.  Every kernel
+// writes each entry it later reads, so nothing needs clearing between calls.
+// Each device holds its own copy, at its own address, for the life of the
+// process; host code uses only that address (from hipGetSymbolAddress),
+// never the array's name.
+static __device__ __align__(256) int32_t scratch[PERMUTE_SCRATCH_BYTES / sizeof(int32_t)];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_addr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// The current device's scratch address, resolved on the first call on that
+// device (with it current) and kept.
+hipError_t permute_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_permute_noalloc(const moe_desc& d, const int32_t* idx, const void* x, int32_t* counts,
+                                  int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm,
+                                  hipStream_t s) {
+  if (permute_workspace(d) > PERMUTE_SCRATCH_BYTES) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = permute_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_permute(d, idx, x, counts, offsets, row_token, slot_row, x_perm, ws, s);
 }
 
 hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, int32_t* counts,

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 30
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n
@@ -166,3 +166,16 @@ def test_missing_library_raises(monkeypatch, tmp_path):
         moe.lib()
     with pytest.raises(RuntimeError, match="missing"):
         moe.workspace_size(_d(), moe.OP_PERMUTE)
+
+
+def test_permute_noalloc_rejects_shapes_beyond_its_scratch():
+    # (E + NL) * ceil(T/256) * 4 bytes must fit the fixed 4 MiB scratch; the
+    # check is on the host, before any launch.
+    l = moe.lib()
+    g = 1 << 20
+    d = moe.make_desc(600_000, 6144, 1792, 384, 8, 0, 96)         # 480 * 2344 * 4 > 4 MiB
+    assert l.moe_permute_noalloc(ctypes.byref(d), g, None, g, g, g, g, None, None) == moe.MOE_ERR_UNSUPPORTED
+    assert b"scratch" in l.moe_last_error()
+    d = _d()
+    assert l.moe_permute_noalloc(ctypes.byref(d), None, None, g, g, g, g, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_permute_noalloc(ctypes.byref(d), g, g, g, g, g, g, None, None) == moe.MOE_ERR_INVALID_ARG
