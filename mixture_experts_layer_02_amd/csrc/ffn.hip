@@ -95,6 +95,16 @@ hipError_t run_f32(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Band of the grouped-K tile order for a product of mtiles m-tiles: the
+// divisor of mtiles nearest to the square root of an XCD's run of 32 tiles
+// (6, then 5, 7, 4, 8), else 6; 0 (no bands) when M has 8 m-tiles or fewer.
+int k_band(int64_t mtiles) {
+  if (mtiles <= 8) return 0;
+  for (int b : {6, 5, 7, 4, 8})
+    if (mtiles % b == 0) return b;
+  return 6;
+}
+
 int64_t r_cap(const moe_desc& d) { return (int64_t)d.T * std::min(d.k, d.num_local); }
 
 // Upper bound on the m-tiles of a variable-M grouped product.
@@ -392,6 +402,7 @@ hipError_t launch_dw_gate_up(const moe_desc& d, const int32_t* offsets, const vo
   p.N = d.d;
   p.c_f32 = 1;
   const int64_t tiles = (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT);
+  if (bf) p.band = k_band(cdiv(2 * d.f, MT));
   if (bf && row_token) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_B>(p, tiles, s);
   if (row_token) return hipErrorNotSupported;
   if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, tiles, s);
@@ -415,6 +426,7 @@ hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void*
   q.M = d.d;
   q.N = d.f;
   q.c_f32 = 1;
+  if (bf) q.band = k_band(cdiv(d.d, MT));
   if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 64) * cdiv(d.f, 64), s);
 }

@@ -56,6 +56,7 @@ struct GemmParams {
   int gather_rows;        //   of the source matrix, which has gather_rows rows
   const float* bs;        // BQ8: float32 scale of each 128-value block of B's rows (B2's in bs2)
   const float* bs2;
+  int band;               // GRP_K: m-tiles per band of the tile order (0 = m-tile fastest over all of M)
 };
 
 struct TileCtx {
@@ -65,8 +66,8 @@ struct TileCtx {
   int n0;
   int nlim;     // valid columns in the tile
   int64_t k0, k1;  // K range of the tile
-  int mtile;    // m-tile index within the group (GRP_K: within M)
-  int mtiles;   // m-tiles of the group
+  int mtile;    // m-tile index within the group (GRP_K: within M, or within its band)
+  int mtiles;   // m-tiles of the group (or of the band)
   bool nfast;   // tiles ordered n-tile fastest (else m-tile fastest)
   int ntile;    // n-tile index
 };
@@ -123,6 +124,9 @@ struct Scheduler {
     }
   }
 
+  // BANDED = false compiles the banded order out (the dynamic-order
+  // kernels, whose scalar registers are already at their limit).
+  template <bool BANDED = true>
   __device__ TileCtx tile(const GemmParams& p, const int* s_pref, int id) const {
     TileCtx t;
     if (GRP == GRP_M) {
@@ -155,11 +159,25 @@ struct Scheduler {
       // E): n-tile fastest, so that the tiles sharing an A row block run
       // together and A (T x d) streams from memory once, not once per n-tile.
       const bool nf = GRP == GRP_NONE && MT >= NT;
-      const int mt = nf ? local / NT : local % MT, nt = nf ? local % NT : local / MT;
-      t.nfast = nf;
-      t.g = g;
+      int mt = nf ? local / NT : local % MT, nt = nf ? local % NT : local / MT;
       t.mtile = mt;
       t.mtiles = MT;
+      if (GRP == GRP_K && BANDED && p.band > 0 && p.band < MT) {
+        // Banded order: bands of `band` m-tiles, m-tile fastest inside a band,
+        // so that the consecutive tiles an XCD runs together form a block of
+        // about band x (run / band) tiles, whose A and B k-slices they share,
+        // instead of a column of all M.  (The last band may be shorter.)
+        const int G = p.band;
+        const int b = local / (G * NT);
+        const int bm = min(G, MT - b * G);
+        const int in = local - b * G * NT;
+        mt = b * G + in % bm;
+        nt = in / bm;
+        t.mtile = in % bm;  // the sharers of a B k-slice are the band's m-tiles
+        t.mtiles = bm;
+      }
+      t.nfast = nf;
+      t.g = g;
       t.ntile = nt;
       t.m0 = (int64_t)mt * BM;
       t.mlim = min(BM, p.M - (int)t.m0);

@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     dyn_finish();
     return;
   }
-  TileCtx t = sched.tile(p, s_pref, id);
+  TileCtx t = sched.template tile<!DYN>(p, s_pref, id);
   Ld cur = setup(t);
   Ld nxt = null_ld;
   int gbase = 0;
@@ -873,7 +873,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     TileCtx tn = t;
     lnext = null_ld;
     if (has_next) {
-      tn = sched.tile(p, s_pref, idn);
+      tn = sched.template tile<!DYN>(p, s_pref, idn);
       lnext = setup(tn);
       if (GATH == GATH_A) {
         tok_dma_tile(lnext, it + 1);
