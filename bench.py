@@ -3,10 +3,10 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fwdbwd_1t]
 
 A step is one pass of the whole hot path over one batch: router logits,
-top-k routing, counting + index generation, the gate/up and down grouped
-GEMMs (the gate/up reading the tokens in place through row_token), the
-weighted combine, and the backward of each (combine, dH, dX, dW1|dW3, dW2,
-route, unpermute, router).  Inputs are seeded synthetic tensors already
+top-k routing, counting + index generation + the permuted copy of x, the
+gate/up and down grouped GEMMs, the weighted combine, and the backward of
+each (combine, dH, dX, dW1|dW3, dW2, route, unpermute, router), with dH and
+dW2 reading dy in place through row_token (no permuted copy of dy).  Inputs are seeded synthetic tensors already
 resident in HBM.  Before each timed step a 1 GiB buffer is rewritten by a
 fill kernel, outside the timed events, so that every step starts with the
 L2 and infinity caches holding none of its data.  Every entry point is
@@ -204,8 +204,9 @@ class Workload:
         counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
         D = self.D = moe.make_desc(T, d, f, E, k, cfg.expert_begin, NL, cfg.dtype, cfg.renormalize,
                                    tile_counters=counters)
-        gather = not args.no_gather
-        b = self.b = moe.Buffers(D, backward=cfg.backward, gather=gather)
+        gather = args.x_path == "gather"
+        gdy = args.dy_path == "gather" and cfg.dtype == "bf16"
+        b = self.b = moe.Buffers(D, backward=cfg.backward, gather=gather, gather_dy=gdy)
         bb = 2 if cfg.dtype == "bf16" else 4
         fp8 = self.fp8 = {}
         if args.fp8_weights:
@@ -267,20 +268,36 @@ class Workload:
                 lambda R: 2.0 * R * d * f, lambda R: R * f * bb + NL * f * d * bb + R * d * bb)
         add("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), 1,
             nbytes=lambda R: R * d * bb + T * d * bb + T * k * 8)
-        if cfg.backward:
+        if cfg.backward and gdy:
+            # dy read in place: no dy_perm; the routing weight of each row is
+            # applied inside dH, which also writes hw = w silu(G) U for dW2
+            add("B1_combine_bwd", lambda: moe.combine_bwd_gather(D, b.slot_row, w, b.y_perm, g["dy"], b.row_w,
+                                                                 b.dtopk_w), 1,
+                nbytes=lambda R: T * d * bb + R * d * bb + T * k * 8 + R * 4)
+            add("B2_dh", lambda: moe.expert_bwd_dh_gather(D, b.offsets, b.row_token, b.row_w, g["dy"], g["w2"],
+                                                          b.gu, b.dgu, b.hw), 1,
+                lambda R: 2.0 * R * d * f,
+                lambda R: R * d * bb + NL * f * d * bb + 2 * R * 2 * f * bb + R * f * bb + R * 4)
+        elif cfg.backward:
             add("B1_combine_bwd", lambda: moe.combine_bwd(D, b.slot_row, w, b.y_perm, g["dy"], b.dy_perm,
                                                           b.dtopk_w), 1,
                 nbytes=lambda R: T * d * bb + 2 * R * d * bb + T * k * 12)
             add("B2_dh", lambda: moe.expert_bwd_dh(D, b.offsets, g["w2"], b.gu, b.dy_perm, b.dgu), 1,
                 lambda R: 2.0 * R * d * f, lambda R: R * d * bb + NL * f * d * bb + 2 * R * 2 * f * bb)
+        if cfg.backward:
             add("B3_dx", lambda: moe.expert_bwd_dx(D, b.offsets, g["w1"], g["w3"], b.dgu, b.dx_perm), 1,
                 lambda R: 4.0 * R * d * f, lambda R: R * 2 * f * bb + 2 * NL * f * d * bb + R * d * bb)
             add("B4_dw13", lambda: moe.expert_bwd_dw_gate_up(D, b.offsets, b.row_token if gather else None,
                                                              g["x"] if gather else b.x_perm, b.dgu, b.dW1,
                                                              b.dW3), 1,
                 lambda R: 4.0 * R * d * f, lambda R: R * d * bb + R * 2 * f * bb + 2 * NL * f * d * 4)
-            add("B4_dw2", lambda: moe.expert_bwd_dw_down(D, b.offsets, b.dy_perm, b.h, b.dW2), 1,
-                lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
+            if gdy:
+                add("B4_dw2", lambda: moe.expert_bwd_dw_down_gather(D, b.offsets, b.row_token, g["dy"], b.hw,
+                                                                    b.dW2), 1,
+                    lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
+            else:
+                add("B4_dw2", lambda: moe.expert_bwd_dw_down(D, b.offsets, b.dy_perm, b.h, b.dW2), 1,
+                    lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
             if routing is None:
                 add("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), 1,
                     nbytes=lambda R: T * E * 4 + T * k * 12)
@@ -395,8 +412,12 @@ def main():
     ap.add_argument("--hold-cus", type=int, default=0,
                     help="before each grouped GEMM, occupy this many CUs with another kernel (contention)")
     ap.add_argument("--hold-us", type=int, default=2000, help="how long each --hold-cus kernel runs")
-    ap.add_argument("--no-gather", action="store_true",
-                    help="build x_perm in the permute step instead of reading x through row_token in the GEMMs")
+    ap.add_argument("--x-path", choices=["perm", "gather"], default="perm",
+                    help="perm: the permute step copies x into x_perm for gate/up and dW1|dW3; gather: they read "
+                         "x through row_token (no x_perm)")
+    ap.add_argument("--dy-path", choices=["perm", "gather"], default="gather",
+                    help="gather: dH and dW2 read dy through row_token with the routing weight applied inside "
+                         "(no dy_perm); perm: the combine backward writes dy_perm")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights held as blockwise-128 E4M3 codes + scales, dequantised to bf16 each step")
     ap.add_argument("--fp8-gemm", action="store_true",
@@ -436,8 +457,8 @@ def main():
     note("inputs resident in HBM; warming up")
     avg, step_ms, wall = run(moe, torch, wl, args, args.steps, args.warmup, flush, note)
     peak_mem = torch.cuda.max_memory_allocated()
-    default_run = (cfg.name == "fwdbwd_1t" and not (args.no_gather or args.fp8_weights or args.fp8_gemm or
-                   args.hold_cus or args.n_groups > 1 or args.schedule != "static"))
+    default_run = (cfg.name == "fwdbwd_1t" and args.x_path == "perm" and args.dy_path == "gather" and not (
+        args.fp8_weights or args.fp8_gemm or args.hold_cus or args.n_groups > 1 or args.schedule != "static"))
     main_sum = summarize(wl, avg, step_ms, wall, args.steps, default_run)
     ms_step = main_sum["ms_per_step"]
     note(f"timed region: {ms_step:.3f} ms/step")
@@ -485,7 +506,9 @@ def main():
                    "routed_rows": main_sum["R"], "global_batch": T, "parallelism": "single GPU",
                    "routing": f"group-limited, {args.n_groups} groups" if args.n_groups > 1 else "top-k",
                    "tile_schedule": args.schedule,
-                   "gather_fused": not args.no_gather,
+                   "x_path": ("x_perm copy" if args.x_path == "perm" else "x read through row_token"),
+                   "dy_path": ("dy read through row_token, no dy_perm" if args.dy_path == "gather"
+                               else "dy_perm copy"),
                    "expert_weights": ("bf16" if not args.fp8_weights else
                                       "fp8 e4m3 blocks of 128, read by the forward GEMMs" if args.fp8_gemm else
                                       "fp8 e4m3 blocks of 128, dequantised each step"),

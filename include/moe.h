@@ -280,6 +280,35 @@ int moe_expert_bwd_dw_gate_up(const moe_desc* desc, const int32_t* offsets,
 int moe_expert_bwd_dw_down(const moe_desc* desc, const int32_t* offsets, const void* dy_perm,
                            const void* h, float* dW2, void* stream);
 
+/* The backward with dy read in place (Domyn page, section "Dynamic tile
+ * scheduling in SonicMoE": the expert GEMMs run on the dispatch layout, with
+ * no permuted copies).  dy_perm[r] = w_r dy[row_token[r]] is never stored;
+ * its routing weight w_r is applied inside the products instead.  bf16 only,
+ * x and dy under 2 GiB (else MOE_ERR_UNSUPPORTED).  In order:
+ *
+ * B1: dtopk_w [T][k] float32 as in moe_combine_bwd, and row_w [R_cap]
+ *   float32, row_w[slot_row[t][j]] = topk_w[t][j] for every local slot (the
+ *   weight row r carries).  No dy_perm is written. */
+int moe_combine_bwd_gather(const moe_desc* desc, const int32_t* slot_row, const float* topk_w,
+                           const void* y_perm, const void* dy, float* row_w, float* dtopk_w,
+                           void* stream);
+
+/* B2: dH[r] = row_w[r] * (dy[row_token[r]] W2[n]) with the SwiGLU backward
+ *   fused as in moe_expert_bwd_dh -> dgu [R_cap][2f]; and, when hw is not
+ *   NULL, hw[r] = row_w[r] * silu(G) * U [R_cap][f] bf16 from the saved
+ *   G | U (gu), the operand of the dW2 product below.  dy [T][d]. */
+int moe_expert_bwd_dh_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                             const float* row_w, const void* dy, const void* W2, const void* gu,
+                             void* dgu, void* hw, void* stream);
+
+/* B4, dW2 with dy read in place: dW2[n] = sum over rows r of expert n of
+ *   dy[row_token[r]]^T hw[r]  ([NL][d][f] float32, overwritten; exact zeros
+ *   for an expert with no rows).  dW1 | dW3 come from
+ *   moe_expert_bwd_dw_gate_up with row_token. */
+int moe_expert_bwd_dw_down_gather(const moe_desc* desc, const int32_t* offsets,
+                                  const int32_t* row_token, const void* dy, const void* hw,
+                                  float* dW2, void* stream);
+
 /* B5a, backward of the gather: dx[t] = dx_add[t] + sum over local slots j of
  *   dx_perm[slot_row[t][j]], summed in float32; dx [T][d] dtype out;
  *   dx_add [T][d] float32 or NULL (e.g. the router path's input gradient). */

@@ -18,7 +18,7 @@ import torch  # imported before libmoe.so so that the process holds one HIP runt
 
 __all__ = [
     "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8",
-    "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
+    "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine_bwd_gather", "expert_bwd_dh_gather", "expert_bwd_dw_down_gather", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
 ]
@@ -87,6 +87,9 @@ _SIGS = {
     "moe_expert_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dw_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dw_down": [_vp, _vp, _vp, _vp, _vp],
+    "moe_combine_bwd_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dh_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dw_down_gather": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _vp],
     "moe_combine_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_ffn_bwd_dx": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -289,6 +292,21 @@ def expert_bwd_dw_down(desc, offsets, dy_perm, h, dw2):
     _call("moe_expert_bwd_dw_down", desc, offsets, dy_perm, h, dw2, _stream())
 
 
+def combine_bwd_gather(desc, slot_row, topk_w, y_perm, dy, row_w, dtopk_w):
+    """dtopk_w and the per-row routing weights row_w; no dy_perm."""
+    _call("moe_combine_bwd_gather", desc, slot_row, topk_w, y_perm, dy, row_w, dtopk_w, _stream())
+
+
+def expert_bwd_dh_gather(desc, offsets, row_token, row_w, dy, w2, gu, dgu, hw):
+    """dH from dy read through row_token, scaled by row_w, SwiGLU backward -> dgu; hw = row_w silu(G) U."""
+    _call("moe_expert_bwd_dh_gather", desc, offsets, row_token, row_w, dy, w2, gu, dgu, hw, _stream())
+
+
+def expert_bwd_dw_down_gather(desc, offsets, row_token, dy, hw, dw2):
+    """dW2 from dy read through row_token and hw."""
+    _call("moe_expert_bwd_dw_down_gather", desc, offsets, row_token, dy, hw, dw2, _stream())
+
+
 def combine(desc, slot_row, topk_w, y_perm, y):
     _call("moe_combine", desc, slot_row, topk_w, y_perm, y, _stream())
 
@@ -328,8 +346,11 @@ def router_bwd_acc(desc, x, wr, dlogits, dx, dwr, ws):
 class Buffers:
     """Every device tensor of one forward (+ backward) pass of a layer, allocated once."""
 
-    def __init__(self, desc: MoeDesc, device="cuda", backward=False, gather=False):
-        """gather=True: the expert GEMMs read x through row_token (no x_perm)."""
+    def __init__(self, desc: MoeDesc, device="cuda", backward=False, gather=False, gather_dy=None):
+        """gather=True: the expert GEMMs read x through row_token (no x_perm).
+        gather_dy (default: gather) = True: the backward reads dy through
+        row_token (no dy_perm) and keeps the per-row routing weights row_w and
+        hw = row_w silu(G) U instead."""
         dt = desc.torch_dtype
         T, d, f, E, k, NL, Rc = desc.T, desc.d, desc.f, desc.E, desc.k, desc.num_local, desc.R_cap
         z = dict(device=device)
@@ -343,6 +364,8 @@ class Buffers:
         self.row_token = torch.empty(Rc, dtype=i32, **z)
         self.slot_row = torch.empty(T, k, dtype=i32, **z)
         self.gather = gather
+        self.gather_dy = gather if gather_dy is None else gather_dy
+        gdy = self.gather_dy
         self.x_perm = None if gather else torch.empty(Rc, d, dtype=dt, **z)
         self.gu = torch.empty(Rc, 2 * f, dtype=dt, **z) if backward else None
         self.h = torch.empty(Rc, f, dtype=dt, **z)
@@ -351,7 +374,9 @@ class Buffers:
         self.ws_permute = torch.empty(max(16, workspace_size(desc, OP_PERMUTE)), dtype=torch.uint8, **z)
         self.ws_router = torch.empty(max(16, workspace_size(desc, OP_ROUTER_LOGITS)), dtype=torch.uint8, **z)
         if backward:
-            self.dy_perm = torch.empty(Rc, d, dtype=dt, **z)
+            self.dy_perm = None if gdy else torch.empty(Rc, d, dtype=dt, **z)
+            self.row_w = torch.empty(Rc, dtype=torch.float32, **z) if gdy else None
+            self.hw = torch.empty(Rc, f, dtype=dt, **z) if gdy else None
             self.dtopk_w = torch.empty(T, k, dtype=torch.float32, **z)
             self.dgu = torch.empty(Rc, 2 * f, dtype=dt, **z)
             self.dx_perm = torch.empty(Rc, d, dtype=dt, **z)
@@ -392,11 +417,22 @@ def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None):
     """Stages B1-B5 for upstream gradient dy (needs Buffers(backward=True))."""
     D = b.desc
     idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
-    combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
-    grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
-    if b.gather:
+    if b.gather_dy:
+        combine_bwd_gather(D, b.slot_row, w, b.y_perm, dy, b.row_w, b.dtopk_w)
+        expert_bwd_dh_gather(D, b.offsets, b.row_token, b.row_w, dy, w2, b.gu, b.dgu, b.hw)
+        expert_bwd_dx(D, b.offsets, w1, w3, b.dgu, b.dx_perm)
+        if b.gather:
+            expert_bwd_dw_gate_up(D, b.offsets, b.row_token, x, b.dgu, b.dW1, b.dW3)
+        else:
+            expert_bwd_dw_gate_up(D, b.offsets, None, b.x_perm, b.dgu, b.dW1, b.dW3)
+        expert_bwd_dw_down_gather(D, b.offsets, b.row_token, dy, b.hw, b.dW2)
+    elif b.gather:
+        combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
+        grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
         grouped_ffn_bwd_dw_gather(D, b.offsets, b.row_token, x, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
     else:
+        combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
+        grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
         grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
     unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx)
     if routing is None:

@@ -250,6 +250,36 @@ int moe_expert_bwd_dw_down(const moe_desc* desc, const int32_t* offsets, const v
   return finish(moe::launch_dw_down(*desc, offsets, dy_perm, h, dW2, S(stream)));
 }
 
+int moe_combine_bwd_gather(const moe_desc* desc, const int32_t* slot_row, const float* topk_w, const void* y_perm,
+                           const void* dy, float* row_w, float* dtopk_w, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(topk_w) || !need(y_perm) || !need(dy) || !need(row_w) || !need(dtopk_w))
+    return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_combine_bwd(*desc, slot_row, topk_w, y_perm, dy, nullptr, dtopk_w, S(stream), row_w));
+}
+
+int moe_expert_bwd_dh_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                             const float* row_w, const void* dy, const void* W2, const void* gu, void* dgu,
+                             void* hw, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(row_token) || !need(row_w) || !need(dy) || !need(W2) || !need(gu) || !need(dgu) ||
+      !opt(hw))
+    return MOE_ERR_INVALID_ARG;
+  if (!gather_ok(desc)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_bwd_dh_gather(*desc, offsets, row_token, row_w, dy, W2, gu, dgu, hw, S(stream)));
+}
+
+int moe_expert_bwd_dw_down_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                                  const void* dy, const void* hw, float* dW2, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(row_token) || !need(dy) || !need(hw) || !need(dW2)) return MOE_ERR_INVALID_ARG;
+  if (!gather_ok(desc)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_dw_down_gather(*desc, offsets, row_token, dy, hw, dW2, S(stream)));
+}
+
 int moe_unpermute_bwd(const moe_desc* desc, const int32_t* slot_row, const void* dx_perm, const float* dx_add,
                       void* dx, void* stream) {
   int rc = check_desc(desc);

@@ -355,6 +355,58 @@ hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* 
   return run_f32<LAY_K, LAY_MN, GRP_M, EPI_SWIGLU_BWD, false>(p, mtiles_ub(d, 64) * cdiv(d.f, 64), s);
 }
 
+// dH with dy read in place (bf16): row r of the product is dy[row_token[r]],
+// scaled in the epilogue by row_w[r] (the routing weight the permuted copy
+// would carry), then the SwiGLU backward -> dgu; hw[r] = row_w[r] silu(G) U
+// (bf16) for the dW2 product.
+hipError_t launch_bwd_dh_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
+                                const float* row_w, const void* dy, const void* W2, const void* gu, void* dgu,
+                                void* hw, hipStream_t s) {
+  GemmParams p = blank(d);
+  p.A = dy;
+  p.lda = d.d;
+  p.gather = row_token;
+  p.gather_rows = d.T;
+  p.row_scale = row_w;
+  p.h_out = hw;
+  p.B = W2;
+  p.ldb = d.f;
+  p.b_gstride = (int64_t)d.d * d.f;
+  p.C = dgu;
+  p.ldc = 2 * (int64_t)d.f;
+  p.gu_in = gu;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.N = d.f;
+  p.K = d.d;
+  p.c_f32 = 0;
+  return run_bf16<LAY_K, LAY_MN, uint16_t, GRP_M, EPI_SWIGLU_BWD, false, GATH_A>(p, mtiles_ub(d, MT) * cdiv(d.f, MT), s);
+}
+
+// dW2 [d][f] = dy_perm^T hw with dy read in place: k-row r of the A operand
+// is dy[row_token[r]] (bf16); hw carries the routing weight.
+hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
+                                 const void* dy, const void* hw, float* dW2, hipStream_t s) {
+  GemmParams q = blank(d);
+  q.A = dy;
+  q.lda = d.d;
+  q.gather = row_token;
+  q.gather_rows = d.T;
+  q.B = hw;
+  q.ldb = d.f;
+  q.C = dW2;
+  q.ldc = d.f;
+  q.c_gstride = (int64_t)d.d * d.f;
+  q.offsets = offsets;
+  q.ngroups = d.num_local;
+  q.M = d.d;
+  q.N = d.f;
+  q.c_f32 = 1;
+  q.band = k_band(cdiv(d.d, MT));
+  return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_AK>(
+      q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
+}
+
 hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void* W1, const void* W3,
                           const void* dgu, void* dx_perm, hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;

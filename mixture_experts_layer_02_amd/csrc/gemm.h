@@ -26,7 +26,10 @@ namespace moe {
 enum { LAY_K = 0, LAY_MN = 1 };
 enum { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_ADD = 3 };  // EPI_ADD: C += product
-enum { GATH_NONE = 0, GATH_A = 1, GATH_B = 2 };  // gathered operand of the LDS-DMA kernel
+// Gathered operand of the LDS-DMA kernel: GATH_A the K-contiguous A of a
+// GRP_M product, GATH_B the MN-contiguous B of a GRP_K product, GATH_AK the
+// MN-contiguous A of a GRP_K product.
+enum { GATH_NONE = 0, GATH_A = 1, GATH_B = 2, GATH_AK = 3 };
 
 constexpr int MAXG = 1024;
 
@@ -57,6 +60,8 @@ struct GemmParams {
   const float* bs;        // BQ8: float32 scale of each 128-value block of B's rows (B2's in bs2)
   const float* bs2;
   int band;               // GRP_K: m-tiles per band of the tile order (0 = m-tile fastest over all of M)
+  const float* row_scale; // EPI_SWIGLU_BWD with a gathered A: dH of row r is scaled by row_scale[r]
+  void* h_out;            //   and, when set, row_scale[r] * silu(G) * U is written here ([rows][N])
 };
 
 struct TileCtx {

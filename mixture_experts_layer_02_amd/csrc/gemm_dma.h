@@ -232,8 +232,13 @@ __device__ __forceinline__ void wait_stages(int later) {
 // with no permuted copy): 0 none; GATH_A: the K-contiguous A of a GRP_M
 // product is x[gather[r]] for row r (gate/up from x through row_token);
 // GATH_B: the MN-contiguous B of a GRP_K product has k-row k equal to row
-// gather[k] of x (dW1|dW3 from x through row_token).  The gathered matrix
-// has gather_rows rows of ldb (or lda) elements and must stay under 2 GiB.
+// gather[k] of x (dW1|dW3 from x through row_token); GATH_AK the same for the
+// MN-contiguous A of a GRP_K product (dW2 from the layer's dy through
+// row_token).  The gathered matrix has gather_rows rows of ldb (or lda)
+// elements and must stay under 2 GiB.  With GATH_A and EPI_SWIGLU_BWD (dH
+// from dy through row_token), row r's dH is scaled by row_scale[r] (the
+// routing weight that the permuted copy of dy would carry), and
+// row_scale[r] * silu(G) * U is written to h_out when it is set.
 //
 // BQ8 (FP8 expert weights, Domyn page section "FP8 expert weight
 // all-gather"): the K-contiguous B of a GRP_M product holds E4M3 codes, one
@@ -248,11 +253,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
   static_assert(GATH == 0 || (GATH == GATH_A && ALAY == LAY_K && GRP == GRP_M) ||
-                    (GATH == GATH_B && BLAY == LAY_MN && GRP == GRP_K && !DUAL),
+                    (GATH == GATH_B && BLAY == LAY_MN && GRP == GRP_K && !DUAL) ||
+                    (GATH == GATH_AK && ALAY == LAY_MN && GRP == GRP_K && !DUAL),
                 "gathered operands: K-contiguous A of GRP_M, MN-contiguous B of GRP_K");
-  static_assert(!BQ8 || (BLAY == LAY_K && GRP == GRP_M && GATH != GATH_B && BK == 64),
+  static_assert(!BQ8 || (BLAY == LAY_K && GRP == GRP_M && (GATH == GATH_NONE || GATH == GATH_A) && BK == 64),
                 "FP8 B: K-contiguous B of GRP_M, 64-wide k-tiles (half a scale block)");
   static_assert(BK == 64 && STAGES == 2, "ring of two 64-wide k-tiles");
+  // GKB: the k-rows of an MN-contiguous operand of a grouped-K product are
+  // gathered (B for GATH_B, A for GATH_AK), through a ring of token copies.
+  constexpr bool GKB = GATH == GATH_B || GATH == GATH_AK;
   constexpr int MI = 4, NI = 4;          // 32 x 32 blocks per wave (128 x 128)
   constexpr int TILE_ELEMS = 256 * BK;   // one operand tile
   constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
@@ -267,8 +276,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) float s_stage[4][8 * SP];
   __shared__ __attribute__((aligned(256))) uint32_t lds_junk[64];
   // Gathered operand: the source rows of a tile (GATH_A, two tiles) or of a
-  // ring position (GATH_B, eight positions).
-  __shared__ __attribute__((aligned(256))) int32_t s_tok[GATH == GATH_A ? 2 : GATH == GATH_B ? 8 : 1]
+  // ring position (GATH_B and GATH_AK, eight positions).
+  __shared__ __attribute__((aligned(256))) int32_t s_tok[GATH == GATH_A ? 2 : GKB ? 8 : 1]
                                                          [GATH == GATH_A ? 256 : 64];
 
   Scheduler<GRP, BM, DUAL ? BN / 2 : BN> sched;
@@ -371,6 +380,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       L.ra = make_rsrc(Ag, (uint64_t)p.gather_rows * p.lda * 2);
       L.rt = make_rsrc(p.gather + t.m0, (uint64_t)t.mlim * 4);
     }
+    if (GATH == GATH_AK) {  // A's k-rows come from anywhere in the source; validity is in the offsets
+      L.ra = make_rsrc(Ag + t.m0, (uint64_t)((int64_t)p.gather_rows * p.lda - t.m0) * 2);
+      L.rt = make_rsrc(p.gather + t.k0, (uint64_t)klen * 4);
+    }
     if (GATH == GATH_B) {  // k-rows come from anywhere in the source; k-row validity is in the offsets
       L.rb = L.rb2 = make_rsrc(Bg + t.n0, (uint64_t)((int64_t)p.gather_rows * p.ldb - t.n0) * 2);
       L.rt = make_rsrc(p.gather + t.k0, (uint64_t)klen * 4);
@@ -418,6 +431,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       const int e = t.mtile % cB + cB * (wave * 64 + lane);
       L.glim = (int)klen;
       L.pfe = e < ITEMS ? e : -1;
+    }
+    if (GATH == GATH_AK) {
+      const int e = t.ntile % cA + cA * (wave * 64 + lane);
+      L.glim = (int)klen;
+      L.pfe = e < ITEMS ? e : -1;
+      L.pa = 0x7FFFFFF0u;
     }
     return L;
   };
@@ -583,12 +602,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     if (decltype(pure_c)::value) return gcur[GATH == GATH_A ? jj : 0];
     return pos < cur.nk ? gcur[GATH == GATH_A ? jj : 0] : gnext[GATH == GATH_A ? jj : 0];
   };
-  // GATH_B: the B offsets of the position whose DMA is being issued, and the
-  // L2-prefetch offset held for position kt+3 (see ktile).
-  uint32_t gvb[GATH == GATH_B ? NJ : 1];
+  // GATH_B (GATH_AK): the B (A) offsets of the position whose DMA is being
+  // issued, and the L2-prefetch offset held for position kt+3 (see ktile).
+  uint32_t gvb[GKB ? NJ : 1];
   uint32_t gpb = 0x7FFFFFF0u;
 #pragma unroll
-  for (int jj = 0; jj < (GATH == GATH_B ? NJ : 1); ++jj) gvb[jj] = 0x80000000u;
+  for (int jj = 0; jj < (GKB ? NJ : 1); ++jj) gvb[jj] = 0x80000000u;
   // DMA instruction q (0 .. 2*NJ-1) of ring position pos: even q are A, odd q B.
   auto dma_one = [&](int pos, int q, auto pure_c) {
     int k;
@@ -614,10 +633,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
     constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
-    if ((q & 1) == 0) {
+    if ((q & 1) == 0 && GATH == GATH_AK) {
+      dma16<LT>(L.ra, gvb[GKB ? jj : 0], 0u, stb + j * 1024);
+    } else if ((q & 1) == 0) {
       dma16<LT>(L.ra, GATH == GATH_A ? a_gv(pos, jj, pure_c) : va[jj], a_so(k), stb + j * 1024);
     } else if (GATH == GATH_B) {
-      dma16<LT>(L.rb, gvb[GATH == GATH_B ? jj : 0], 0u, stb + TILE_ELEMS * 2 + j * 1024);
+      dma16<LT>(L.rb, gvb[GKB ? jj : 0], 0u, stb + TILE_ELEMS * 2 + j * 1024);
     } else {
       i32x4 rbk;
       uint32_t so_b;
@@ -630,7 +651,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     int k;
     const Ld L = pick(pos, k, pure_c);
     constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // as in dma_one
-    if (o == 0) {
+    if (o == 0 && GATH == GATH_AK) {
+      touch4u(L.ra, gpb, __builtin_amdgcn_readfirstlane(0u), junk_lds);  // (a readfirstlane just before)
+    } else if (o == 0) {
       touch4u<LT>(L.ra, L.pa, a_so(k), junk_lds);
     } else if (GATH == GATH_B) {
       touch4u(L.rb, gpb, __builtin_amdgcn_readfirstlane(0u), junk_lds);  // (a readfirstlane just before)
@@ -668,7 +691,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int prow = L.pfe >= 0 ? L.pfe / SPR : 0;
     L.pa = ((uint32_t)tk[prow] * lda2 + (L.pfe % SPR) * 64) | (L.pfe >= 0 && prow < L.glim ? 0u : 0x80000000u);
   };
-  // GATH_B: ring position pos's 64 tokens go to s_tok[(gbase + pos) & 7];
+  // GATH_B, GATH_AK: ring position pos's 64 tokens go to s_tok[(gbase + pos) & 7];
   // every wave issues the copy (so that every wave counts the same memory
   // instructions) but only wave 0's lands in the ring.
   auto tok_dma_pos = [&](int pos) __attribute__((always_inline)) {
@@ -677,23 +700,25 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const uint32_t* dst = wave == 0 ? reinterpret_cast<const uint32_t*>(&s_tok[(gbase + pos) & 7][0]) : lds_junk;
     touch4(L.rt, (uint32_t)(k * BK + lane) * 4u, __builtin_amdgcn_readfirstlane(0u), dst);
   };
-  // GATH_B: the B offsets of position pos into gvb, and the prefetch offset
+  // GATH_B, GATH_AK: the gathered operand's offsets of position pos into gvb, and the prefetch offset
   // of position ppos into gpb, from their tokens.
   auto tok_fill_pos = [&](int pos, int ppos) __attribute__((always_inline)) {
     int k;
     const Ld L = pick(pos, k, std::false_type());
     const int32_t* tk = s_tok[(gbase + pos) & 7];
+    constexpr bool GA = GATH == GATH_AK;  // the gathered operand is A (its row pitch is lda)
 #pragma unroll
-    for (int jj = 0; jj < (GATH == GATH_B ? NJ : 1); ++jj) {
+    for (int jj = 0; jj < (GKB ? NJ : 1); ++jj) {
       const int krow = 2 * (wave * NJ + jj) + (lane >> 5);
       const int c = (lane & 31) ^ swz_mn(krow);
-      gvb[jj] = ((uint32_t)tk[krow] * ldb2 + c * 16) | (k * BK + krow < L.glim ? 0u : 0x80000000u);
+      gvb[jj] = ((uint32_t)tk[krow] * (GA ? lda2 : ldb2) + c * 16) | (k * BK + krow < L.glim ? 0u : 0x80000000u);
     }
     int kp;
     const Ld P = pick(ppos, kp, std::false_type());
     const int32_t* tp = s_tok[(gbase + ppos) & 7];
     const int pr = P.pfe >= 0 ? (P.pfe >> 3) : 0;
-    gpb = ((uint32_t)tp[pr] * ldb2 + (P.pfe & 7) * 64) | (P.pfe >= 0 && kp * BK + pr < P.glim ? 0u : 0x80000000u);
+    gpb = ((uint32_t)tp[pr] * (GA ? lda2 : ldb2) + (P.pfe & 7) * 64) |
+          (P.pfe >= 0 && kp * BK + pr < P.glim ? 0u : 0x80000000u);
   };
 
   f32x16 acc[MI][NI];
@@ -745,7 +770,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   constexpr int PFD = 1;  // (measured: 1 beats 2 and 3 by 1-2% on the 1T shapes)
   // Memory instructions per lane of one epilogue (the buffer stores and
   // loads below, all unconditional).
-  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? 128
+  // (ROWSC: dH scaled per row, with the scales loaded and h_out stored: 32 more of each.)
+  constexpr bool ROWSC = EPI == EPI_SWIGLU_BWD && GATH == GATH_A;
+  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? (ROWSC ? 192 : 128)
                           : (EPI == EPI_ADD ? 2 : 1) * (CF32 ? 64 : 32);
   // (+1: a gathered operand's token copy is issued between the epilogue and
   // the prefetches.)
@@ -806,7 +833,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const uint16_t* st = ring[(uint32_t)(gbase + kt) % STAGES];
     // GATH_B: the tokens of position kt+3+PFD (read two k-tiles later, after the
     // barriers that follow their wait).
-    if (GATH == GATH_B) tok_dma_pos(kt + 3 + PFD);
+    if (GKB) tok_dma_pos(kt + 3 + PFD);
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
       if (s == 0) {
@@ -817,7 +844,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         // GATH_B: position kt+1 is issued whole; its offsets make way for
         // those of kt+2 (issued at this k-tile's end and the next's start),
         // and the prefetch offset for kt+2+PFD (next k-tile's prefetch).
-        if (GATH == GATH_B) tok_fill_pos(kt + 2, kt + 2 + PFD);
+        if (GKB) tok_fill_pos(kt + 2, kt + 2 + PFD);
       } else {
         kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
       }
@@ -896,7 +923,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 
     if (cur.nk > 0) {
       if (!primed) {
-        if (GATH == GATH_B) {  // tokens of positions 0 .. 2+PFD
+        if (GKB) {  // tokens of positions 0 .. 2+PFD
 #pragma unroll
           for (int q = 0; q < 3 + PFD; ++q) tok_dma_pos(q);
           wait_vm<0>();
@@ -908,7 +935,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         for (int q = 0; q < PER; ++q) dma_one(0, q, std::false_type());
 #pragma unroll
         for (int o = 0; o < NPF; ++o) pf_one(PFD, o, std::false_type());
-        if (GATH == GATH_B) tok_fill_pos(1, PFD + 1);
+        if (GKB) tok_fill_pos(1, PFD + 1);
 #pragma unroll
         for (int q = 0; q < PER; ++q) dma_one(1, q, std::false_type());
         wait_vm<PER + NPF>();  // position 0 has landed (then come its prefetch and position 1)
@@ -981,6 +1008,13 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         r1 = c_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.gu_in)) + (m0g * ld2 + t.n0) * 2, ld2, 2);
         ldo = ld2;
       }
+      // ROWSC: the rows' scales (float) and h_out ([rows][N] bf16, or nothing).
+      __amdgpu_buffer_rsrc_t rsc = r0, rho = r0;
+      if (ROWSC) {
+        rsc = c_rsrc(const_cast<float*>(p.row_scale) + m0g, 1, 4);
+        rho = p.h_out ? c_rsrc(reinterpret_cast<char*>(p.h_out) + (m0g * p.N + t.n0) * 2, p.N, 2)
+                      : __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(p.C), (short)0, 0, 0x00020000);
+      }
       // Values the epilogue reads are loaded in batches ahead of the stores
       // that use them: a load waits for every memory instruction issued
       // before it, so each batch costs one round trip after the previous
@@ -990,6 +1024,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       constexpr int AB = VPL <= 2 ? 2 : 1;
       u32x4_t oldc[AB][4][VPL];
       u32x4_t gup[4][VPL][2];
+      uint32_t rsv[4][VPL];
       // Rows 8 sl .. 8 sl + 7 of the wave's 32-row block mi, as fp32, into the
       // wave's staging area.
       auto stage_slab = [&](int mi_, int sl_) __attribute__((always_inline)) {
@@ -1035,6 +1070,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
               gup[sl][vi][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
               gup[sl][vi][1] =
                   __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
+              if (ROWSC) rsv[sl][vi] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)row * 4u, 0, 0);
             }
         }
 #pragma unroll
@@ -1132,15 +1168,29 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
               u32x4_t gq = gup[sl][vi][0];
               u32x4_t uq = gup[sl][vi][1];
               asm volatile("" : "+v"(gq), "+v"(uq));  // used here, not hoisted to their loads
-              float dg[8], du[8];
+              float sc = 1.0f;
+              if (ROWSC) {
+                uint32_t sw = rsv[sl][vi];
+                asm volatile("" : "+v"(sw));
+                sc = __uint_as_float(sw);
+              }
+              float dg[8], du[8], hs[8];
 #pragma unroll
               for (int q = 0; q < 8; ++q) {
                 const uint32_t gw = gq[q >> 1], uw = uq[q >> 1];
                 const float g = __uint_as_float((q & 1) ? (gw & 0xffff0000u) : (gw << 16));
                 const float u = __uint_as_float((q & 1) ? (uw & 0xffff0000u) : (uw << 16));
                 const float sg = sigmoidf_(g);
-                du[q] = v[q] * g * sg;
-                dg[q] = v[q] * u * sg * (1.0f + g * (1.0f - sg));
+                const float dh = ROWSC ? v[q] * sc : v[q];
+                du[q] = dh * g * sg;
+                dg[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
+                hs[q] = g * sg * u * sc;
+              }
+              if (ROWSC) {
+                const u32x4_t dhw = {pack_bf2(hs[0], hs[1]), pack_bf2(hs[2], hs[3]), pack_bf2(hs[4], hs[5]),
+                                     pack_bf2(hs[6], hs[7])};
+                const int64_t eh = (int64_t)row * p.N + col;
+                __builtin_amdgcn_raw_buffer_store_b128(dhw, rho, ok ? (uint32_t)(eh * 2) : 0x80000000u, 0, 0);
               }
               const u32x4_t ddg = {pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]), pack_bf2(dg[4], dg[5]),
                                    pack_bf2(dg[6], dg[7])};

@@ -36,7 +36,12 @@ hipError_t launch_permute(const moe_desc& d, const int32_t* idx, const void* x, 
 hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
                           void* y, hipStream_t s);
 hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
-                              const void* dy, void* dy_perm, float* dw, hipStream_t s);
+                              const void* dy, void* dy_perm, float* dw, hipStream_t s, float* row_w = nullptr);
+hipError_t launch_bwd_dh_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
+                                const float* row_w, const void* dy, const void* W2, const void* gu, void* dgu,
+                                void* hw, hipStream_t s);
+hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
+                                 const void* dy, const void* hw, float* dW2, hipStream_t s);
 hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
                                 const float* dx_add, void* dx, hipStream_t s);
 hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,

@@ -219,13 +219,16 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
   }
 }
 
-// dy_perm[row] = w dy[t];  dw[t][j] = <y_perm[row], dy[t]> (0 for non-local slots).
+// dy_perm[row] = w dy[t] (when dy_perm is given);  dw[t][j] = <y_perm[row], dy[t]>
+// (0 for non-local slots);  row_w[row] = w (when row_w is given: the weight
+// each routed row carries, for a backward that reads dy in place).
 template <typename T>
 __global__ void __launch_bounds__(256) combine_bwd_kernel(const int32_t* __restrict__ slot_row,
                                                           const float* __restrict__ w,
                                                           const T* __restrict__ y_perm,
                                                           const T* __restrict__ dy, int Tn, int k, int d,
-                                                          T* __restrict__ dy_perm, float* __restrict__ dw) {
+                                                          T* __restrict__ dy_perm, float* __restrict__ dw,
+                                                          float* __restrict__ row_w) {
   using V = Vec16<T>;
   constexpr int VN = V::N;
   const int lane = threadIdx.x & 63;
@@ -234,6 +237,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const int32_t* __restr
   const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
   const float wl = lane < k ? w[(int64_t)t * k + lane] : 0.f;
   const uint64_t live = __ballot(r >= 0);
+  if (row_w && r >= 0) row_w[r] = wl;
   float mydot = 0.f;  // lane j ends with slot j's dot product
   uint64_t m = live;
   while (m) {
@@ -254,7 +258,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const int32_t* __restr
         part = fmaf(yv[e], gv[e], part);
         ov[e] = wj * gv[e];
       }
-      V::store(out + c, ov);
+      if (dy_perm) V::store(out + c, ov);
     }
     part = wave_sum(part);
     if (lane == j) mydot = part;
@@ -455,7 +459,8 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel_b(const int32_t* __res
                                                             const float* __restrict__ w,
                                                             const T* __restrict__ y_perm,
                                                             const T* __restrict__ dy, int Tn, int k, int d,
-                                                            T* __restrict__ dy_perm, float* __restrict__ dw) {
+                                                            T* __restrict__ dy_perm, float* __restrict__ dw,
+                                                            float* __restrict__ row_w) {
   using R = batched::Raw<T>;
   constexpr int VN = R::N, U = 2;
   const int lane = threadIdx.x & 63;
@@ -464,6 +469,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel_b(const int32_t* __res
   const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
   const float wl = lane < k ? w[(int64_t)t * k + lane] : 0.f;
   const uint64_t live = __ballot(r >= 0);
+  if (row_w && r >= 0) row_w[r] = wl;
   int64_t rows[KB];
   float wj[KB], part[KB];
 #pragma unroll
@@ -504,7 +510,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel_b(const int32_t* __res
             part[j] = fmaf(yv[e], gv[e], part[j]);
             ov[e] = wj[j] * gv[e];
           }
-          Vec16<T>::store(dy_perm + rows[j] + c, ov);
+          if (dy_perm) Vec16<T>::store(dy_perm + rows[j] + c, ov);
         }
     }
   }
@@ -598,25 +604,25 @@ hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const floa
 }
 
 hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
-                              const void* dy, void* dy_perm, float* dw, hipStream_t s) {
+                              const void* dy, void* dy_perm, float* dw, hipStream_t s, float* row_w) {
   const dim3 grid((d.T + 3) / 4), block(256);
   const bool b8 = d.k <= 8;
   if (d.dtype == MOE_BF16) {
     if (b8)
       combine_bwd_kernel_b<uint16_t, 8><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm,
                                                                (const uint16_t*)dy, d.T, d.k, d.d,
-                                                               (uint16_t*)dy_perm, dw);
+                                                               (uint16_t*)dy_perm, dw, row_w);
     else
       combine_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, w, (const uint16_t*)y_perm,
                                                           (const uint16_t*)dy, d.T, d.k, d.d,
-                                                          (uint16_t*)dy_perm, dw);
+                                                          (uint16_t*)dy_perm, dw, row_w);
   } else {
     if (b8)
       combine_bwd_kernel_b<float, 8><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, (const float*)dy,
-                                                            d.T, d.k, d.d, (float*)dy_perm, dw);
+                                                            d.T, d.k, d.d, (float*)dy_perm, dw, row_w);
     else
       combine_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, w, (const float*)y_perm, (const float*)dy, d.T,
-                                                       d.k, d.d, (float*)dy_perm, dw);
+                                                       d.k, d.d, (float*)dy_perm, dw, row_w);
   }
   return hipGetLastError();
 }

@@ -47,11 +47,11 @@ def _routing_agreement(idx_g, L_ref, idx_ref):
     return same
 
 
-def _run_layer(cfg, backward, gpu, n_groups=1, gather=False, inp=None):
+def _run_layer(cfg, backward, gpu, n_groups=1, gather=False, inp=None, gather_dy=None):
     inp = synth.make_inputs(cfg) if inp is None else inp
     dt = cfg.dtype
     D = _desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, dt, cfg.renormalize)
-    b = moe.Buffers(D, backward=backward, gather=gather)
+    b = moe.Buffers(D, backward=backward, gather=gather, gather_dy=gather_dy)
     dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
     bias = to_dev(inp["bias"]) if "bias" in inp else None
     routing = (to_dev(inp["idx"]), to_dev(inp["w"])) if cfg.routing == "roundrobin" else None

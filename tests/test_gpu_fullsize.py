@@ -14,9 +14,10 @@ of the benchmark); the float64 oracle then recomputes what it can afford:
 * the weight gradients dW1, dW3, dW2 of two whole experts (the least and the
   most loaded local expert that no near-tie touches), from the oracle's own
   routing of every token;
-* the layer again with the gather fused into the GEMMs (the configuration the
-  benchmark times), whose every output must equal the x_perm path's bit for
-  bit, so that all of the above holds for it too.
+* the forward again with the gather fused into the GEMMs, whose every output
+  must equal the x_perm path's bit for bit; and the forward + backward with
+  x and dy read in place (the configuration the benchmark times), checked
+  like the x_perm path above, plus its per-row weights and hw = w silu(G) U.
 
 dWr sums dlogits over all tokens, and dlogits needs every token's expert
 outputs, which is beyond what the oracle finishes in seconds at this size.
@@ -78,13 +79,17 @@ def _check_index_maps(cfg, idx, counts, offsets, row_token, slot_row):
     assert (r[order] == np.arange(len(r))).all()
 
 
-@pytest.mark.parametrize("name", ["share_1t", "zipf_1t", "uniform_1t", "fwdbwd_1t"])
-def test_full_size_layer_sampled(gpu, name):
+@pytest.mark.parametrize("name,gather,gather_dy", [
+    ("share_1t", False, False), ("zipf_1t", False, False), ("uniform_1t", False, False),
+    ("fwdbwd_1t", False, False),
+    ("fwdbwd_1t", False, True),    # the benchmark's configuration: x_perm, dy read in place
+    ("fwdbwd_1t", True, True)])
+def test_full_size_layer_sampled(gpu, name, gather, gather_dy):
     cfg = synth.CONFIGS[name]
     back = cfg.backward
     print(f"[fullsize] {name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} NL={cfg.num_local} k={cfg.k} "
-          f"backward={back}", flush=True)
-    inp, b = _run_layer(cfg, back, gpu)
+          f"backward={back} gather={gather} gather_dy={gather_dy}", flush=True)
+    inp, b = _run_layer(cfg, back, gpu, gather=gather, gather_dy=gather_dy)
     dt, tol = cfg.dtype, TOL[cfg.dtype]
     T, E, k, e0, NL, f = cfg.T, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.f
     x32 = synth.as_f32(inp["x"], dt)
@@ -120,26 +125,27 @@ def test_full_size_layer_sampled(gpu, name):
     else:
         _check_index_maps(cfg, idx_g, counts_g, offsets_g, to_host(b.row_token), slot_g)
 
-    # x_perm: every row bit-exact (a copy)
-    xp = b.x_perm[:R]
-    xs = torch.as_tensor(row_token_g.astype(np.int64), device=xp.device)
-    x_dev = torch.from_numpy(inp["x"].view(np.int16)).to(xp.device)
-    assert torch.equal(xp.view(torch.int16), x_dev[xs]), "x_perm rows differ from x[row_token]"
-    del x_dev, xs
+    if not gather:
+        # x_perm: every row bit-exact (a copy)
+        xp = b.x_perm[:R]
+        xs = torch.as_tensor(row_token_g.astype(np.int64), device=xp.device)
+        x_dev = torch.from_numpy(inp["x"].view(np.int16)).to(xp.device)
+        assert torch.equal(xp.view(torch.int16), x_dev[xs]), "x_perm rows differ from x[row_token]"
+        del x_dev, xs
 
-    # the gather-fused layer (no x_perm) gives bitwise the same outputs
-    _, bg = _run_layer(cfg, back, gpu, gather=True, inp=inp)
-    names = (["topk_idx"] if cfg.routing != "roundrobin" else []) + ["offsets", "slot_row", "row_token", "h",
-                                                                       "y_perm", "y"] + (
-        ["gu", "dy_perm", "dtopk_w", "dgu", "dx_perm", "dW1", "dW3", "dW2", "dlogits", "dWr", "dx"] if back else [])
-    for n in names:
-        a, c = getattr(b, n), getattr(bg, n)
-        if a.shape[0] == b.desc.R_cap and n not in ("topk_idx", "slot_row"):
-            a, c = a[:R], c[:R]
-        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
-                           c.view(torch.uint8) if c.dtype != torch.int32 else c), n
-    del bg
-    torch.cuda.empty_cache()
+    if not gather and not gather_dy:
+        # the gather-fused forward (no x_perm) gives bitwise the same outputs
+        _, bg = _run_layer(cfg, False, gpu, gather=True, inp=inp)
+        names = (["topk_idx"] if cfg.routing != "roundrobin" else []) + ["offsets", "slot_row", "row_token",
+                                                                           "h", "y_perm", "y"]
+        for n in names:
+            a, c = getattr(b, n), getattr(bg, n)
+            if a.shape[0] == b.desc.R_cap and n not in ("topk_idx", "slot_row"):
+                a, c = a[:R], c[:R]
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                               c.view(torch.uint8) if c.dtype != torch.int32 else c), n
+        del bg
+        torch.cuda.empty_cache()
 
     # --- per-token quantities on a sample --------------------------------
     toks = _sample_tokens(T, cfg.seed)
@@ -166,7 +172,13 @@ def test_full_size_layer_sampled(gpu, name):
 
     dy_s = f64(inp["dy"][toks], dt)
     g = oracle.layer_backward(ref, xs, wr, W["w1"], W["w3"], W["w2"], dy_s, cfg.renormalize)
-    assert max_row_rel_err(_rows(b, "dy_perm", r_g), g["dy_perm"][r_o]) <= tol
+    if gather_dy:
+        # the weight each row carries, and hw = w silu(G) U (dW2's operand)
+        w_rows = ref["w"][ti, tj]
+        assert np.allclose(_rows(b, "row_w", r_g), w_rows, rtol=1e-4, atol=1e-6)
+        assert max_row_rel_err(_rows(b, "hw", r_g), w_rows[:, None] * ref["H"][r_o]) <= tol
+    else:
+        assert max_row_rel_err(_rows(b, "dy_perm", r_g), g["dy_perm"][r_o]) <= tol
     assert whole_rel_err(_rows(b, "dtopk_w", toks), g["dw"]) <= tol
     dgu = _rows(b, "dgu", r_g)
     assert max_row_rel_err(dgu[:, :f], g["dG"][r_o]) <= tol

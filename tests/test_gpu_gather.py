@@ -1,12 +1,17 @@
 """The gather fused into the grouped GEMMs (Domyn page, section "Dynamic tile
 scheduling in SonicMoE": SonicMoE's expert GEMMs run on the token-dispatch
-layout with no permuted copy of the tokens).
+layout with no permuted copies).
 
-gate/up and dW1|dW3 read x through row_token instead of the materialised
+Forward: gate/up reads x through row_token instead of the materialised
 x_perm.  The operand values, the tiles and the order of every sum are the
-same, so each output must equal the x_perm path's bit for bit; the x_perm path
-is itself checked against the oracle in the other GPU tests, and the whole
-layer in gather mode is checked against the oracle here too.
+same, so each forward output must equal the x_perm path's bit for bit; so
+must dW1|dW3 read through row_token, given the same dG|dU.
+
+Backward: dy is read through row_token too (dH and dW2), with the routing
+weight applied inside the products instead of in a stored dy_perm, so the
+rounding differs from the x_perm path; the whole gathered layer, forward and
+backward, and its new intermediates (the per-row weights and hw = w silu(G) U)
+are checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -16,7 +21,7 @@ import mixture_experts_layer_02_amd as moe
 import oracle
 import synth
 from gpu_util import f64, to_dev, to_host
-from layer_checks import TOL, _desc
+from layer_checks import TOL, _desc, check_layer_backward
 from metrics import max_row_rel_err, whole_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -51,41 +56,60 @@ def _same(a, b):
 
 @pytest.mark.parametrize("dyn", [False, True])
 @pytest.mark.parametrize("scale", SHAPES)
-def test_gather_fused_is_bitwise_the_permuted_path(gpu, scale, dyn):
+def test_gather_fused_forward_is_bitwise_the_permuted_path(gpu, scale, dyn):
     cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
     print(f"[gather] {scale} dynamic={dyn}", flush=True)
     inp, (ref, got) = _pair(cfg, dyn, gpu)
-    assert got.x_perm is None
+    assert got.x_perm is None and got.dy_perm is None
     R = int(ref.offsets[-1].item())
     assert torch.equal(ref.row_token[:R], got.row_token[:R])
-    for n in ("gu", "h", "y_perm", "dgu", "dx_perm"):
+    for n in ("gu", "h", "y_perm"):
         assert _same(getattr(ref, n)[:R], getattr(got, n)[:R]), n
-    for n in ("y", "dW1", "dW3", "dW2", "dx", "dWr"):
-        assert _same(getattr(ref, n), getattr(got, n)), n
+    assert _same(ref.y, got.y)
+    # dW1 | dW3 with x read through row_token, on the permuted path's dG | dU
+    D = got.desc
+    dw1, dw3 = torch.empty_like(ref.dW1), torch.empty_like(ref.dW3)
+    moe.expert_bwd_dw_gate_up(D, got.offsets, got.row_token, to_dev(inp["x"]), ref.dgu, dw1, dw3)
+    torch.cuda.synchronize()
+    assert _same(ref.dW1, dw1) and _same(ref.dW3, dw3)
 
 
-def test_gather_layer_against_oracle(gpu):
-    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], T=512, d=256, f=128, E=32, num_local=8, expert_begin=8)
+@pytest.mark.parametrize("gather_x", [True, False])
+@pytest.mark.parametrize("dyn", [False, True])
+@pytest.mark.parametrize("scale", [
+    dict(T=512, d=256, f=128, E=32, num_local=8, expert_begin=8),
+    dict(T=700, d=192, f=192, E=16, num_local=16, expert_begin=0),
+    dict(T=1500, d=320, f=192, E=64, num_local=24, expert_begin=40, k=6),     # ragged, empty experts
+    dict(T=777, d=256, f=128, E=64, num_local=3, expert_begin=61, k=8),       # few local experts
+])
+def test_gather_layer_against_oracle(gpu, scale, dyn, gather_x):
+    # gather_x False: x through x_perm, dy read in place (the benchmark's configuration)
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[gather vs oracle] {scale} dynamic={dyn} gather_x={gather_x}", flush=True)
     inp = synth.make_inputs(cfg)
     dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
-    D = _desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype, cfg.renormalize)
-    b = moe.Buffers(D, backward=True, gather=True)
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype, cfg.renormalize)
+    D = moe.make_desc(*args, tile_counters=moe.new_tile_counters(gpu) if dyn else None)
+    b = moe.Buffers(D, backward=True, gather=gather_x, gather_dy=True)
     moe.forward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"])
     moe.backward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], dev["dy"])
     torch.cuda.synchronize()
+    assert b.dy_perm is None and (b.x_perm is None) == gather_x
+    check_layer_backward(cfg, inp, b)
+    # the per-row routing weights and hw = w silu(G) U
     dt, tol = cfg.dtype, TOL[cfg.dtype]
     x, wr = f64(inp["x"], dt), f64(inp["wr"], dt)
     w1, w3, w2 = f64(inp["w1"], dt), f64(inp["w3"], dt), f64(inp["w2"], dt)
     ref = oracle.layer_forward(x, wr, w1, w3, w2, cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize)
-    assert (to_host(b.topk_idx) == ref["idx"]).all(), "a routing near-tie flipped"
-    g = oracle.layer_backward(ref, x, wr, w1, w3, w2, f64(inp["dy"], dt), cfg.renormalize)
     R = int(ref["offsets"][-1])
-    assert max_row_rel_err(to_host(b.h)[:R], ref["H"]) <= tol
-    assert max_row_rel_err(to_host(b.y), ref["y"]) <= tol
-    assert max_row_rel_err(to_host(b.dx), g["dx"]) <= tol
-    for n in range(cfg.num_local):
-        assert whole_rel_err(to_host(b.dW1)[n], g["dW1"][n]) <= tol, n
-        assert whole_rel_err(to_host(b.dW3)[n], g["dW3"][n]) <= tol, n
+    t_of, j_of = np.nonzero(ref["slot_row"] >= 0)
+    rows = ref["slot_row"][t_of, j_of]
+    w_row = np.zeros(R)
+    w_row[rows] = ref["w"][t_of, j_of]
+    rw = to_host(b.row_w)[:R]
+    np.testing.assert_array_equal(rw[rows], to_host(b.topk_w)[t_of, j_of])    # a copy of the GPU's weights
+    np.testing.assert_allclose(rw, w_row, rtol=1e-4, atol=1e-6)
+    assert max_row_rel_err(to_host(b.hw)[:R], w_row[:, None] * ref["H"]) <= tol
 
 
 def test_gather_rejects_fp32_and_oversized_x(gpu):
@@ -93,6 +117,14 @@ def test_gather_rejects_fp32_and_oversized_x(gpu):
     z = torch.zeros(1 << 16, dtype=torch.float32, device=gpu)
     with pytest.raises(moe.MoeError):
         moe.expert_gate_up_gather(D, z, z, z, z, z, z, z)
-    D = _desc(1 << 20, 1024, 64, 8, 2, 0, 8, "bf16")          # x of 2 GiB
+    with pytest.raises(moe.MoeError):
+        moe.expert_bwd_dh_gather(D, z, z, z, z, z, z, z, z)
+    with pytest.raises(moe.MoeError):
+        moe.expert_bwd_dw_down_gather(D, z, z, z, z, z)
+    D = _desc(1 << 20, 1024, 64, 8, 2, 0, 8, "bf16")          # x (and dy) of 2 GiB
     with pytest.raises(moe.MoeError):
         moe.grouped_ffn_bwd_dw_gather(D, z, z, z, z, z, z, z, z, z)
+    with pytest.raises(moe.MoeError):
+        moe.expert_bwd_dh_gather(D, z, z, z, z, z, z, z, z)
+    with pytest.raises(moe.MoeError):
+        moe.expert_bwd_dw_down_gather(D, z, z, z, z, z)
