@@ -90,31 +90,22 @@ __device__ __forceinline__ void topk_rounds(const float (&v)[MAXV], int lane, in
 
 // Order-preserving unsigned key of a float (larger float, larger key), with
 // -0.0 made equal to +0.0; 0 is below every finite float's key and marks an
-// absent element.
+// absent element.  key_float inverts it (+0.0 for the key of zero).
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);  // -0.0 + 0.0 = +0.0
   return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
 
-template <int MAXV, bool GROUPED>
-__global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict__ logits, int T, int E,
-                                                         int k, int renorm, int G,
-                                                         int32_t* __restrict__ idx_out,
-                                                         float* __restrict__ w_out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
-  float v[MAXV];
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = i * 64 + lane;
-    v[i] = e < E ? row[e] : 0.f;
-  }
-  if (GROUPED) {
-    topk_rounds<MAXV, GROUPED>(v, lane, t, E, k, renorm, G, idx_out, w_out);
-    return;
-  }
+// The selection of one token t by one wave: v holds the token's logits,
+// element i of lane l being expert i*64 + l (absent experts -infinity);
+// s_idx / s_val are the wave's 64-entry LDS area.
+template <int MAXV>
+__device__ __forceinline__ void topk_token(const float (&v)[MAXV], int lane, int t, int E, int k, int renorm,
+                                           int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                           int32_t* s_idx, float* s_val) {
   // Threshold selection.  theta = the k-th largest of the lanes' maximum keys
   // (a binary search over the key bits, counting lanes with ballots): at
   // least k elements have key >= theta, so every one of the k selections
@@ -122,56 +113,50 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
   // compacted through LDS, and a candidate's slot is the number of
   // candidates that come before it in the order (logit descending, expert
   // ascending).  With more than 64 candidates (heavy ties) the wave takes
-  // the k rounds instead.
-  uint32_t key[MAXV];
-  uint32_t kmax = 0;
+  // the k rounds instead.  Only the lane maxima need keys: theta is one of
+  // them, the k-th largest, so key >= theta is the float comparison
+  // v >= key_float(theta), under which -0.0 and +0.0 are equal too.
+  float vmax = v[0];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    key[i] = i * 64 + lane < E ? order_key(v[i]) : 0u;
-    kmax = max(kmax, key[i]);
-  }
+  for (int i = 1; i < MAXV; ++i) vmax = fmaxf(vmax, v[i]);
+  const uint32_t kmax = lane < E ? order_key(vmax) : 0u;  // a lane holds an expert iff lane < E
   uint32_t theta = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = theta | (1u << b);
     if ((int)__popcll(__ballot(kmax >= c)) >= k) theta = c;
   }
+  const float thf = key_float(theta);
   uint64_t m[MAXV];
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    m[i] = __ballot(key[i] != 0u && key[i] >= theta);
+    m[i] = __ballot(v[i] >= thf);  // absent experts are -infinity, below every finite theta
     cnt += (int)__popcll(m[i]);
   }
   if (cnt > 64) {  // uniform
     topk_rounds<MAXV, false>(v, lane, t, E, k, renorm, 1, idx_out, w_out);
     return;
   }
-  __shared__ uint32_t s_key[4][64];
-  __shared__ int32_t s_idx[4][64];
-  __shared__ float s_val[4][64];
-  const int wv = threadIdx.x >> 6;
   int base = 0;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     if ((m[i] >> lane) & 1ull) {
       const int pos = base + (int)__popcll(m[i] & ((1ull << lane) - 1ull));
-      s_key[wv][pos] = key[i];
-      s_idx[wv][pos] = i * 64 + lane;
-      s_val[wv][pos] = v[i];
+      s_idx[pos] = i * 64 + lane;
+      s_val[pos] = v[i];
     }
     base += (int)__popcll(m[i]);
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const bool cand = lane < cnt;
-  const uint32_t ck = cand ? s_key[wv][lane] : 0u;
-  const int ci = cand ? s_idx[wv][lane] : 0x7fffffff;
-  const float cv = cand ? s_val[wv][lane] : 0.f;
+  const int ci = cand ? s_idx[lane] : 0x7fffffff;
+  const float cv = cand ? s_val[lane] : 0.f;
   int rank = 0;
   for (int j = 0; j < cnt; ++j) {
-    const uint32_t kj = __builtin_amdgcn_readlane(ck, j);
+    const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv), j));
     const int ij = __builtin_amdgcn_readlane(ci, j);
-    rank += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
+    rank += (vj > cv || (vj == cv && ij < ci)) ? 1 : 0;
   }
   const bool sel = cand && rank < k;
   // the largest selected logit (slot 0)
@@ -195,82 +180,152 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
   }
 }
 
-// dlogits for one token per wave.  renorm: dL_m = w_m (dw_m - <w, dw>) on the
-// selected experts (local or not), 0 elsewhere.  raw softmax: dL_e = p_e (g_e -
-// <w, dw>) with g_e = dw_j at e = idx_j.  The k selections are read once into
-// scalar registers (their lane is uniform) and scattered into the row held
-// by the lanes: expert e is element e/64 of lane e%64.
-template <int MAXV>
+// MAXV = ceil(E / 64): lane l holds experts l, l + 64, ... (absent ones as
+// -infinity).  Each wave selects for TPW consecutive tokens, with the loads
+// of all their rows issued first, so that a wave keeps TPW rows in flight
+// while it works through the selections.
+template <int MAXV, bool GROUPED, int TPW>
+__global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict__ logits, int T, int E,
+                                                         int k, int renorm, int G,
+                                                         int32_t* __restrict__ idx_out,
+                                                         float* __restrict__ w_out) {
+  __shared__ int32_t s_idx[4][64];
+  __shared__ float s_val[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int t0 = (blockIdx.x * 4 + wv) * TPW;
+  if (t0 >= T) return;
+  float v[TPW][MAXV];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = min(t0 + u, T - 1);  // (a token past T re-reads the last row, unused)
+    const float* row = logits + (int64_t)t * E;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      v[u][i] = e < E ? row[e] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = t0 + u;
+    if (t >= T) break;
+    if (GROUPED)
+      topk_rounds<MAXV, GROUPED>(v[u], lane, t, E, k, renorm, G, idx_out, w_out);
+    else
+      topk_token<MAXV>(v[u], lane, t, E, k, renorm, idx_out, w_out, s_idx[wv], s_val[wv]);
+  }
+}
+
+// dlogits, TPW tokens per wave (TPW * k <= 64).  renorm: dL_m = w_m (dw_m -
+// <w, dw>) on the selected experts (local or not), 0 elsewhere.  raw softmax:
+// dL_e = p_e (g_e - <w, dw>) with g_e = dw_j at e = idx_j.  Lane u*k + j loads
+// slot j of the wave's token u, so one load of each input serves all TPW
+// tokens; a token's k selections are then read into scalar registers (their
+// lane is uniform) and scattered into the row held by the lanes: expert e is
+// element e/64 of lane e%64.
+template <int MAXV, int TPW>
 __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict__ logits,
                                                         const int32_t* __restrict__ idx,
                                                         const float* __restrict__ w,
                                                         const float* __restrict__ dw, int T, int E, int k,
                                                         int renorm, float* __restrict__ dlogits) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  if (t0 >= T) return;
   int my_i = -1;
   float my_w = 0.f, my_dw = 0.f;
-  if (lane < k) {
-    my_i = idx[(int64_t)t * k + lane];
-    my_w = w[(int64_t)t * k + lane];
-    my_dw = dw[(int64_t)t * k + lane];
+  const int64_t slot = (int64_t)t0 * k + lane;  // slot (lane % k) of token t0 + lane / k
+  if (lane < TPW * k && slot < (int64_t)T * k) {
+    my_i = idx[slot];
+    my_w = w[slot];
+    my_dw = dw[slot];
   }
-  const float s = wave_sum(my_w * my_dw);
-  // g[i]: for renorm w_j (dw_j - s) at the selected experts, else dw_j
-  float g[MAXV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) g[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int ij = __builtin_amdgcn_readlane(my_i, j);
-    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
-    const float dwj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dw), j));
-    const float val = renorm ? wj * (dwj - s) : dwj;
+  for (int u = 0; u < TPW; ++u) {
+    const int t = t0 + u;
+    if (t >= T) break;
+    float s = 0.f;  // <w, dw> of the token, summed in slot order
+    for (int j = 0; j < k; ++j)
+      s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), u * k + j)) *
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dw), u * k + j));
+    // g[i]: for renorm w_j (dw_j - s) at the selected experts, else dw_j
+    float g[MAXV];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i)
-      if (ij == i * 64 + lane) g[i] = val;
+    for (int i = 0; i < MAXV; ++i) g[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int ij = __builtin_amdgcn_readlane(my_i, u * k + j);
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), u * k + j));
+      const float dwj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dw), u * k + j));
+      const float val = renorm ? wj * (dwj - s) : dwj;
+      // expert ij is element ij / 64 of lane ij % 64; the element is uniform,
+      // so one select in one register instead of one per element
+      const int ie = ij >> 6;
+      const bool mine = (ij & 63) == lane;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i)
+        if (ie == i) g[i] = mine ? val : g[i];
+    }
+    float* out = dlogits + (int64_t)t * E;
+    if (renorm) {
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const int e = i * 64 + lane;
+        if (e < E) out[e] = g[i];
+      }
+    } else {
+      const float* row = logits + (int64_t)t * E;
+      float v[MAXV];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const int e = i * 64 + lane;
+        v[i] = e < E ? row[e] : -INFINITY;
+        mx = fmaxf(mx, v[i]);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i)
+        if (i * 64 + lane < E) z += expf(v[i] - mx);
+      z = wave_sum(z);
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const int e = i * 64 + lane;
+        if (e < E) out[e] = expf(v[i] - mx) / z * (g[i] - s);
+      }
+    }
   }
-  float* out = dlogits + (int64_t)t * E;
-  if (renorm) {
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int e = i * 64 + lane;
-      if (e < E) out[e] = g[i];
-    }
-  } else {
-    const float* row = logits + (int64_t)t * E;
-    float v[MAXV];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int e = i * 64 + lane;
-      v[i] = e < E ? row[e] : -INFINITY;
-      mx = fmaxf(mx, v[i]);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i)
-      if (i * 64 + lane < E) z += expf(v[i] - mx);
-    z = wave_sum(z);
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int e = i * 64 + lane;
-      if (e < E) out[e] = expf(v[i] - mx) / z * (g[i] - s);
-    }
+}
+
+// One instantiation per number of 64-wide slices of a logit row (1 .. 16 for
+// E <= 1024), so no slice is carried for nothing.
+template <int NV, bool GROUPED>
+static void route_nv(const moe_desc& d, int nv, const float* logits, int G, int32_t* idx, float* w,
+                     hipStream_t s) {
+  if constexpr (NV <= 16) {
+    if (nv > NV) return route_nv<NV + 1, GROUPED>(d, nv, logits, G, idx, w, s);
+    constexpr int TPW = 1;  // tokens per wave (2 measured no faster: the selection, not the loads, is the cost)
+    topk_route_kernel<NV, GROUPED, TPW><<<(d.T + 4 * TPW - 1) / (4 * TPW), 256, 0, s>>>(logits, d.T, d.E, d.k,
+                                                                                      d.renormalize, G, idx, w);
   }
 }
 
 template <bool GROUPED>
 static void route_dispatch(const moe_desc& d, const float* logits, int G, int32_t* idx, float* w, hipStream_t s) {
-  const dim3 grid((d.T + 3) / 4), block(256);
-  const int nv = (d.E + 63) / 64;
-  if (nv <= 1) topk_route_kernel<1, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
-  else if (nv <= 2) topk_route_kernel<2, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
-  else if (nv <= 4) topk_route_kernel<4, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
-  else if (nv <= 8) topk_route_kernel<8, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
-  else topk_route_kernel<16, GROUPED><<<grid, block, 0, s>>>(logits, d.T, d.E, d.k, d.renormalize, G, idx, w);
+  route_nv<1, GROUPED>(d, (d.E + 63) / 64, logits, G, idx, w, s);
+}
+
+template <int NV>
+static void route_bwd_nv(const moe_desc& d, int nv, const float* logits, const int32_t* idx, const float* w,
+                         const float* dw, float* dlogits, hipStream_t s) {
+  if constexpr (NV <= 16) {
+    if (nv > NV) return route_bwd_nv<NV + 1>(d, nv, logits, idx, w, dw, dlogits, s);
+    // one token per wave (4 per wave measured slower: 0.050 against 0.041 ms at T = 65536, E = 384)
+    route_bwd_kernel<NV, 1><<<(d.T + 3) / 4, 256, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize,
+                                                          dlogits);
+  }
 }
 
 hipError_t launch_route(const moe_desc& d, const float* logits, int n_groups, int32_t* idx, float* w,
@@ -282,13 +337,7 @@ hipError_t launch_route(const moe_desc& d, const float* logits, int n_groups, in
 
 hipError_t launch_route_bwd(const moe_desc& d, const float* logits, const int32_t* idx, const float* w,
                             const float* dw, float* dlogits, hipStream_t s) {
-  const dim3 grid((d.T + 3) / 4), block(256);
-  const int nv = (d.E + 63) / 64;
-  if (nv <= 1) route_bwd_kernel<1><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
-  else if (nv <= 2) route_bwd_kernel<2><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
-  else if (nv <= 4) route_bwd_kernel<4><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
-  else if (nv <= 8) route_bwd_kernel<8><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
-  else route_bwd_kernel<16><<<grid, block, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize, dlogits);
+  route_bwd_nv<1>(d, (d.E + 63) / 64, logits, idx, w, dw, dlogits, s);
   return hipGetLastError();
 }
 
