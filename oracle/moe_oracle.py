@@ -45,7 +45,7 @@ import numpy as np
 
 __all__ = [
     "router_logits", "topk_route", "topk_route_grouped", "fp8_e4m3_decode", "fp8_e4m3_encode",
-    "fp8_quantize_blocks", "fp8_dequantize_blocks", "bf16_round", "count_tokens", "generate_indices", "permute",
+    "fp8_quantize_blocks", "fp8_dequantize_blocks", "fp8_quantize_blocks_pow2", "fp8_dequantize_blocks_pow2", "bf16_round", "count_tokens", "generate_indices", "permute",
     "silu", "silu_grad", "expert_ffn_rows", "expert_ffn", "combine",
     "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd", "unpermute_bwd",
     "route_bwd", "router_bwd", "layer_forward", "layer_backward",
@@ -219,6 +219,45 @@ def fp8_dequantize_blocks(codes, scales, block=128):
     dec = fp8_e4m3_decode(codes).astype(np.float32).reshape(-1, block)
     v = (dec * np.asarray(scales, np.float32)[:, None]).astype(np.float32)
     return bf16_round(v).reshape(-1)
+
+
+def fp8_quantize_blocks_pow2(w, block=128):
+    """codes [n] uint8 and power-of-two block scales [n/block] of w [n] (any
+    shape, flattened), each scale given as its biased exponent e + 127 (the
+    E8M0 byte: scale = 2^(byte - 127)).
+
+    [Domyn] FP8 expert weights: blocks of 128 values scaled into the E4M3
+    range and cast, one scale per block.  This form takes as the scale the
+    smallest power of two 2^e with amax <= 448 * 2^e, so that the block
+    maximum lands in (224, 448] and the scaling itself is exact; it is the
+    scale a block-scaled FP8 matrix instruction applies (activations are
+    quantised the same way, in blocks of 128 along a row).  Each value
+    w * 2^-e is encoded to the nearest E4M3 code.  An all-zero block has
+    e = 0 and zero codes (the sign of -0 is kept).
+    """
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    if w.size % block:
+        raise ValueError("oracle: size must be a multiple of the block")
+    wb = w.reshape(-1, block).astype(np.float64)
+    amax = np.abs(wb).max(axis=1)
+    nz = amax > 0
+    # amax = f 2^x with f in [0.5, 1), and 448 2^e = 0.875 2^(e+9): the least
+    # e is x - 9 when f <= 0.875, else x - 8.
+    f, x = np.frexp(np.where(nz, amax, 1.0))
+    e = np.where(f <= 0.875, x - 9, x - 8)
+    e = np.where(nz, e, 0).astype(np.int64)
+    if np.any(e < -127) or np.any(e > 127):
+        raise ValueError("oracle: block scale outside the E8M0 range")
+    xs = wb * np.ldexp(1.0, -e)[:, None]                     # exact: a power of two
+    codes = fp8_e4m3_encode(xs).astype(np.uint8)
+    return codes.reshape(-1), (e + 127).astype(np.uint8)
+
+
+def fp8_dequantize_blocks_pow2(codes, e8, block=128):
+    """Values decode(code) * 2^(e8 - 127) of fp8_quantize_blocks_pow2's
+    output, exactly (float64)."""
+    dec = fp8_e4m3_decode(codes).reshape(-1, block)
+    return (dec * np.ldexp(1.0, np.asarray(e8, np.int64) - 127)[:, None]).reshape(-1)
 
 
 # --------------------------------------------------------------------------

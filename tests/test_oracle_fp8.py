@@ -108,3 +108,61 @@ def test_values_on_the_grid_survive_a_round_trip():
     assert (scales == np.float32(448 * 2.0 ** -8 / 448)).all()
     assert np.array_equal(oracle.fp8_e4m3_decode(codes[:127]), grid)
     assert np.array_equal(oracle.fp8_dequantize_blocks(codes, scales)[:127], w[:127])
+
+
+# ---------------------------------------------------------------------------
+# The power-of-two block scales (the scale a block-scaled FP8 matrix
+# instruction applies): scale = the least 2^e with amax <= 448 * 2^e.
+# ---------------------------------------------------------------------------
+def test_pow2_scale_puts_the_block_maximum_in_the_top_binade():
+    rng = np.random.default_rng(11)
+    w = (rng.normal(0, 1, (400, 128)) * 10.0 ** rng.uniform(-6, 4, (400, 1))).astype(np.float32)
+    codes, e8 = oracle.fp8_quantize_blocks_pow2(w)
+    e = e8.astype(np.int64) - 127
+    amax = np.abs(w.astype(np.float64)).max(axis=1)
+    scaled = amax * 2.0 ** -e
+    assert (scaled > 224).all() and (scaled <= 448).all()      # so e is the least such exponent
+
+
+@pytest.mark.parametrize("amax,e", [(448.0, 0), (449.0, 1), (224.0, -1), (224.5, 0), (1.0, -8), (0.875, -9),
+                                    (2.0 ** -20, -28), (3.5, -7)])
+def test_pow2_scale_of_hand_chosen_maxima(amax, e):
+    # 448 = 1.75 * 2^8: amax <= 448 * 2^e  <=>  e >= log2(amax / 448), and the least integer is taken.
+    w = np.zeros(128, np.float32)
+    w[3] = -amax
+    _, e8 = oracle.fp8_quantize_blocks_pow2(w)
+    assert int(e8[0]) - 127 == e
+
+
+def test_pow2_codes_match_the_library_cast_of_the_scaled_values():
+    rng = np.random.default_rng(12)
+    w = (rng.normal(0, 0.02, (300, 128))).astype(np.float32)
+    w[0] = 0.0
+    w[1, ::3] = -0.0
+    w[2] = rng.normal(0, 1e-30, 128).astype(np.float32)          # tiny values: subnormal codes
+    codes, e8 = oracle.fp8_quantize_blocks_pow2(w)
+    scaled = w.astype(np.float64) * 2.0 ** -(e8.astype(np.int64) - 127)[:, None]
+    assert np.array_equal(codes, _torch_e4m3(scaled.astype(np.float32)).reshape(-1))
+    assert (codes.reshape(300, 128)[0] == 0).all() and e8[0] == 127
+
+
+def test_pow2_round_trip_is_exact_on_the_grid_and_bounded_elsewhere():
+    finite = oracle.fp8_e4m3_decode(np.arange(127))               # non-negative codes, finite
+    rng = np.random.default_rng(13)
+    for e in (-10, 0, 5):
+        vals = rng.choice(finite, (50, 128)) * np.where(rng.random((50, 128)) < 0.5, -1, 1)
+        vals[:, 0] = 448.0                                         # the block maximum, already in range
+        w = (vals * 2.0 ** e).astype(np.float32)
+        codes, e8 = oracle.fp8_quantize_blocks_pow2(w)
+        assert (e8 == 127 + e).all()
+        assert np.array_equal(oracle.fp8_dequantize_blocks_pow2(codes, e8), w.reshape(-1).astype(np.float64))
+    w = rng.normal(0, 0.02, (500, 128)).astype(np.float32)
+    codes, e8 = oracle.fp8_quantize_blocks_pow2(w)
+    back = oracle.fp8_dequantize_blocks_pow2(codes, e8).reshape(500, 128)
+    amax = np.abs(w).max(axis=1, keepdims=True)
+    # half a step of a 3-bit mantissa is 1/16 of the value's binade; the largest binade reaches 448 * 2^e,
+    # and 448 * 2^e < 2 * amax, so every error is under amax / 8 and a relative 2^-4 in the normal range
+    err = np.abs(back - w)
+    assert (err <= amax / 8).all()
+    normal = np.abs(w) * 2.0 ** -(e8.astype(np.int64) - 127)[:, None] >= 2.0 ** -6
+    assert (err[normal] <= np.abs(w[normal]) * 2.0 ** -4).all()
