@@ -38,12 +38,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop/B where the two roofs meet
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwdbwd_1t_hbm_traffic.txt")
 GEMM_ROWS = ("A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw13", "B4_dw2")
-EXTRA_WORKLOADS = ("share_1t", "zipf_1t", "uniform_1t")
+EXTRA_WORKLOADS = ("share_1t", "share_1t_fp8mm", "zipf_1t", "uniform_1t")
 
 
 @dataclasses.dataclass
@@ -54,6 +55,7 @@ class Row:
     launches: int
     flops: float = 0.0
     nbytes: float = 0.0
+    peak_tflops: float = PEAK_BF16_TFLOPS   # the matrix-core peak of the row's operand type
 
 
 def pick_dominant(avg_ms, launches):
@@ -77,11 +79,12 @@ def pick_dominant(avg_ms, launches):
 
 def grade(row, ms):
     """Roofline of one launch: MFMA when its arithmetic intensity (algorithmic
-    flops per algorithmic byte) is at or above the ridge, else HBM."""
-    if row.flops and row.flops / row.nbytes >= RIDGE:
+    flops per algorithmic byte) is at or above the ridge of its operand
+    type's matrix-core peak and the HBM peak, else HBM."""
+    if row.flops and row.flops / row.nbytes >= row.peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9):
         ach = row.flops / ms / 1e9
-        return {"kernel": row.name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        return {"kernel": row.name, "bound": "mfma", "achieved": round(ach, 1), "peak": row.peak_tflops,
+                "unit": "TFLOP/s", "frac": round(ach / row.peak_tflops, 4)}
     ach = row.nbytes / ms / 1e6
     return {"kernel": row.name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
@@ -187,7 +190,9 @@ def _cpu_baseline(cfg, inp, sample_tokens, n_groups, extra_inputs):
 class Workload:
     """Device tensors and the ordered rows of one workload's step."""
 
-    def __init__(self, moe, torch, cfg, inp, args, dev):
+    def __init__(self, moe, torch, cfg, inp, args, dev, fp8mm=False):
+        """fp8mm: gate/up on the FP8 matrix cores (forward only): W1/W3 held as
+        E4M3 codes with power-of-two block scales, x quantised each step."""
         self.cfg = cfg
         T, d, f, E, k, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.num_local
 
@@ -204,7 +209,7 @@ class Workload:
         counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
         D = self.D = moe.make_desc(T, d, f, E, k, cfg.expert_begin, NL, cfg.dtype, cfg.renormalize,
                                    tile_counters=counters)
-        gather = args.x_path == "gather"
+        gather = args.x_path == "gather" or fp8mm
         gdy = args.dy_path == "gather" and cfg.dtype == "bf16"
         b = self.b = moe.Buffers(D, backward=cfg.backward, gather=gather, gather_dy=gdy)
         bb = 2 if cfg.dtype == "bf16" else 4
@@ -223,8 +228,8 @@ class Workload:
         idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
         rows = []
 
-        def add(name, fn, launches, flops=lambda R: 0.0, nbytes=lambda R: 0.0):
-            rows.append((name, fn, launches, flops, nbytes))
+        def add(name, fn, launches, flops=lambda R: 0.0, nbytes=lambda R: 0.0, peak=PEAK_BF16_TFLOPS):
+            rows.append((name, fn, launches, flops, nbytes, peak))
 
         nw = 3 * NL * d * f
         if args.fp8_weights and not (args.fp8_gemm and not cfg.backward):
@@ -250,7 +255,26 @@ class Workload:
             4 if gather else 5,
             nbytes=lambda R: (0 if gather else self.ntok_local * d * bb + R * d * bb) + T * k * 12 + R * 4)
         gu_bytes = (lambda R: R * 2 * f * bb) if cfg.backward else (lambda R: 0)
-        if args.fp8_gemm:
+        if fp8mm:
+            assert not cfg.backward and cfg.dtype == "bf16"
+            q8 = {}
+            for n in ("w1", "w3"):
+                qq = torch.empty(g[n].numel(), dtype=torch.uint8, device=dev)
+                ee = torch.empty(g[n].numel() // 128, dtype=torch.uint8, device=dev)
+                moe.fp8_quantize_pow2(g[n], qq, ee)
+                q8[n] = (qq, ee)
+            xq = torch.empty(T * d, dtype=torch.uint8, device=dev)
+            xe = torch.empty(T * d // 128, dtype=torch.uint8, device=dev)
+            add("A4_quant_x", lambda: moe.fp8_quantize_pow2(g["x"], xq, xe), 1,
+                nbytes=lambda R: T * d * (bb + 1) + T * d // 128)
+            add("A5_gate_up", lambda: moe.expert_gate_up_fp8mm(D, b.offsets, b.row_token, xq, xe, q8["w1"][0],
+                                                               q8["w1"][1], q8["w3"][0], q8["w3"][1], None, b.h), 1,
+                lambda R: 4.0 * R * d * f,
+                lambda R: R * d + R * d // 128 + 2 * NL * f * d + 2 * NL * f * d // 128 + R * f * bb,
+                peak=PEAK_FP8_TFLOPS)
+            add("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), 1,
+                lambda R: 2.0 * R * d * f, lambda R: R * f * bb + NL * f * d * bb + R * d * bb)
+        elif args.fp8_gemm:
             add("A5_gate_up", lambda: moe.expert_gate_up_fp8(
                 D, b.offsets, b.row_token if gather else None, g["x"] if gather else b.x_perm,
                 fp8["w1"][0], fp8["w1"][1], fp8["w3"][0], fp8["w3"][1], b.gu, b.h), 1,
@@ -312,12 +336,12 @@ class Workload:
 
     def steps(self):
         """(name, entry-point call) of each row, in step order."""
-        return [(n, fn) for n, fn, _, _, _ in self._rows]
+        return [(n, fn) for n, fn, _, _, _, _ in self._rows]
 
     def rows(self):
         """Every row with its algorithmic flops and bytes at the measured R."""
         R = self.R
-        return [Row(n, fn, l, fl(R), nb(R)) for n, fn, l, fl, nb in self._rows]
+        return [Row(n, fn, l, fl(R), nb(R), pk) for n, fn, l, fl, nb, pk in self._rows]
 
 
 def run(moe, torch, wl, args, steps, warmup, flush, note):
@@ -470,17 +494,20 @@ def main():
     extras, extra_inputs = {}, {}
     names = [] if args.extra_workloads == "none" else [n for n in args.extra_workloads.split(",") if n]
     for name in names:
-        c = synth.CONFIGS[name]
-        data = synth.make_inputs(c)
-        if name == "share_1t":             # reused by the CPU baseline's single-thread sample
-            extra_inputs[name] = data
-        w2 = Workload(moe, torch, c, data, args, dev)
+        fp8mm = name.endswith("_fp8mm")
+        base = name[:-len("_fp8mm")] if fp8mm else name
+        c = synth.CONFIGS[base]
+        data = extra_inputs.get(base) or synth.make_inputs(c)
+        if base == "share_1t":             # reused by the fp8 variant and the CPU baseline's sample
+            extra_inputs[base] = data
+        w2 = Workload(moe, torch, c, data, args, dev, fp8mm=fp8mm)
         torch.cuda.synchronize()
         a2, s2, wall2 = run(moe, torch, w2, args, args.extra_steps, args.warmup, flush, note)
         sm = summarize(w2, a2, s2, wall2, args.extra_steps, False)
         extras[name] = {
-            "workload": f"{name}: T={c.T} d={c.d} E={c.E} ({c.num_local} local) top-{c.k} f={c.f} fwd, "
-                        f"routing {c.routing}",
+            "workload": f"{base}: T={c.T} d={c.d} E={c.E} ({c.num_local} local) top-{c.k} f={c.f} fwd, "
+                        f"routing {c.routing}" + (", gate/up on the fp8 matrix cores (e4m3 x and W1/W3 with "
+                                                  "power-of-two block-128 scales)" if fp8mm else ""),
             "steps": args.extra_steps, "ms_per_step": round(sm["ms_per_step"], 4),
             "tokens/s": round(c.T / sm["ms_per_step"] * 1e3, 1), "routed_rows": sm["R"],
             "grouped_gemm_tflops": round(sm["gemm_tflops"], 1),

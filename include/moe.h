@@ -369,6 +369,20 @@ int moe_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* sca
  * even.  Same layouts and errors as moe_fp8_quantize. */
 int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, void* stream);
 
+/* E4M3 blocks of 128 with power-of-two scales (Domyn page, section "FP8
+ * expert weight all-gather", in the form a block-scaled FP8 matrix
+ * instruction applies; used for the weights and the activations of the FP8
+ * matrix-core GEMM below).  Per block: e = the least integer with
+ * amax <= 448 * 2^e (so the block maximum lands in (224, 448]); each code =
+ * the E4M3 value nearest to w * 2^-e (exact scaling; ties to even); the
+ * scale leaves as its E8M0 byte e8 = e + 127.  A block of zeros gets
+ * e8 = 127 and zero codes.
+ *   w [n] (MOE_BF16 or MOE_F32 as `dtype`), blocks of 128 consecutive values
+ *   (the rows of x [T][d] or W1/W3 [NL][f][d] when d is a multiple of 128);
+ *   q [n] uint8 codes; e8 [n/128] uint8.  Errors as moe_fp8_quantize. */
+int moe_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t* q, uint8_t* e8,
+                          void* stream);
+
 /* A5 and A6 on FP8 weights (the page's further step: the expert GEMMs take
  * the FP8 weights directly).  The weight tiles move as E4M3 codes - half the
  * bytes of bf16 - and are decoded to bf16 in the kernel where the MFMA
@@ -386,6 +400,22 @@ int moe_expert_gate_up_fp8(const moe_desc* desc, const int32_t* offsets, const i
                            const float* W3s, void* gu, void* h, void* stream);
 int moe_expert_down_fp8(const moe_desc* desc, const int32_t* offsets, const void* h, const uint8_t* W2q,
                         const float* W2s, void* y_perm, void* stream);
+
+/* A5 on the FP8 matrix cores (Domyn page, section "FP8 expert weight
+ * all-gather": the expert GEMMs in FP8 as the further step): the activations
+ * and the weights are both E4M3 codes with power-of-two block scales, as
+ * moe_fp8_quantize_pow2 writes them, and each 32 x 32 x 64 product applies
+ * the row's and the column's scale itself, accumulating in float32:
+ *   G[r] = sum over k of (xq * 2^xe)[row_token[r]][k] (W1q * 2^we)[n][k], U
+ *   likewise with W3, h = silu(G) * U, as moe_expert_gate_up_gather.
+ *   xq [T][d] codes, xs [T][d/128] E8M0 bytes (x quantised in blocks of 128
+ *   along a row); W1q, W3q [NL][f][d] codes, W1s, W3s [NL][f][d/128] bytes;
+ *   gu [R_cap][2f] (or NULL) and h [R_cap][f] bf16.  MOE_ERR_UNSUPPORTED
+ *   unless dtype is bf16, d is a multiple of 512 and T * d < 2^31. */
+int moe_expert_gate_up_fp8mm(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                             const uint8_t* xq, const uint8_t* xs, const uint8_t* W1q,
+                             const uint8_t* W1s, const uint8_t* W3q, const uint8_t* W3s, void* gu,
+                             void* h, void* stream);
 
 /* Measurement aid (Domyn page, section "Dynamic tile scheduling in
  * SonicMoE": the two tile orders are compared with and without a dummy

@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8", "fp8_quantize_pow2", "expert_gate_up_fp8mm",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine_bwd_gather", "expert_bwd_dh_gather", "expert_bwd_dw_down_gather", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -81,6 +81,7 @@ _SIGS = {
     "moe_expert_gate_up_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_gate_up_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_down_fp8": [_vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_gate_up_fp8mm": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_ffn_bwd_dw_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dh": [_vp, _vp, _vp, _vp, _vp, _vp],
@@ -100,7 +101,7 @@ _SIGS = {
     "moe_router_bwd_acc": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
 }
 EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error", "moe_hold_cus",
-                                 "moe_fp8_quantize", "moe_fp8_dequantize"])
+                                 "moe_fp8_quantize", "moe_fp8_dequantize", "moe_fp8_quantize_pow2"])
 
 _lib = None
 
@@ -123,6 +124,8 @@ def lib():
         l.moe_fp8_quantize.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp]
         l.moe_fp8_quantize.restype = ctypes.c_int
         l.moe_fp8_dequantize.argtypes = [_vp, _vp, ctypes.c_int64, _vp, _vp]
+        l.moe_fp8_quantize_pow2.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp]
+        l.moe_fp8_quantize_pow2.restype = ctypes.c_int
         l.moe_fp8_dequantize.restype = ctypes.c_int
         l.moe_hold_cus.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
         l.moe_hold_cus.restype = ctypes.c_int
@@ -208,6 +211,22 @@ def fp8_quantize(w, q, scales):
     rc = lib().moe_fp8_quantize(w.data_ptr(), dt, w.numel(), q.data_ptr(), scales.data_ptr(), _stream())
     if rc != MOE_OK:
         raise MoeError("moe_fp8_quantize", rc)
+
+
+def fp8_quantize_pow2(w, q, e8):
+    """E4M3 codes q (uint8, w's size) and power-of-two block scales e8 (uint8 E8M0 bytes, size/128) of w."""
+    dt = MOE_BF16 if w.dtype == torch.bfloat16 else MOE_F32
+    for t in (w, q, e8):
+        if not t.is_contiguous():
+            raise ValueError("libmoe needs contiguous tensors")
+    rc = lib().moe_fp8_quantize_pow2(w.data_ptr(), dt, w.numel(), q.data_ptr(), e8.data_ptr(), _stream())
+    if rc != MOE_OK:
+        raise MoeError("moe_fp8_quantize_pow2", rc)
+
+
+def expert_gate_up_fp8mm(desc, offsets, row_token, xq, xs, w1q, w1s, w3q, w3s, gu, h):
+    """gate/up + SwiGLU on the FP8 matrix cores: x and W1/W3 as codes with E8M0 block scales."""
+    _call("moe_expert_gate_up_fp8mm", desc, offsets, row_token, xq, xs, w1q, w1s, w3q, w3s, gu, h, _stream())
 
 
 def fp8_dequantize(q, scales, w):

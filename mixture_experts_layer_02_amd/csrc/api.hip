@@ -336,6 +336,12 @@ int moe_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* sca
   return finish(moe::launch_fp8_quantize(w, dtype, n, q, scales, S(stream)));
 }
 
+int moe_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t* q, uint8_t* e8, void* stream) {
+  if (!need(w) || !need(q) || !need(e8) || n < 0 || n % 128) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_fp8_quantize_pow2(w, dtype, n, q, e8, S(stream)));
+}
+
 int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, void* stream) {
   if (!need(w) || !need(q) || !need(scales) || n < 0 || n % 128) return MOE_ERR_INVALID_ARG;
   return finish(moe::launch_fp8_dequantize(q, scales, n, w, S(stream)));
@@ -364,6 +370,21 @@ int moe_expert_down_fp8(const moe_desc* desc, const int32_t* offsets, const void
   if (!need(offsets) || !need(h) || !need(W2q) || !need(W2s) || !need(y_perm)) return MOE_ERR_INVALID_ARG;
   if (!q8_ok(desc)) return MOE_ERR_UNSUPPORTED;
   return finish(moe::launch_down_q8(*desc, offsets, h, W2q, W2s, y_perm, S(stream)));
+}
+
+int moe_expert_gate_up_fp8mm(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
+                             const uint8_t* xq, const uint8_t* xs, const uint8_t* W1q, const uint8_t* W1s,
+                             const uint8_t* W3q, const uint8_t* W3s, void* gu, void* h, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(row_token) || !need(xq) || !need(xs) || !need(W1q) || !need(W1s) || !need(W3q) ||
+      !need(W3s) || !opt(gu) || !need(h))
+    return MOE_ERR_INVALID_ARG;
+  // bf16 outputs; d in whole groups of four 128-code blocks (so a row's scale
+  // bytes come as aligned dwords); the gathered codes addressed in 32 bits
+  if (desc->dtype != MOE_BF16 || desc->d % 512 || (int64_t)desc->T * desc->d >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_gate_up_f8(*desc, offsets, row_token, xq, xs, W1q, W1s, W3q, W3s, gu, h, S(stream)));
 }
 
 int moe_hold_cus(int workgroups, int lds_bytes, int microseconds, void* stream) {

@@ -55,7 +55,8 @@ constexpr int DMA_STAGES = DMA_BK == 64 ? 2 : 4;
 
 // bf16 products: the LDS-DMA kernel when every K-contiguous operand has K a
 // multiple of its 32-wide k-tile, else the register-staged kernel.
-template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE, bool BQ8 = false>
+template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE, bool BQ8 = false,
+          bool F8 = false>
 hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   // K-contiguous operands need whole 64-wide k-tiles: every K (GRP_M, plain)
   // or every K chunk (GRP_K split into kchunk pieces) a multiple of 64.
@@ -73,13 +74,13 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
     if (F32_ONLY && !p.c_f32) return hipErrorInvalidValue;
     const bool cf = (EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32;
     if (p.dyn) {
-      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, true, GATH, BQ8, F8><<<(unsigned)grid, 256, 0, s>>>(p);
       else if constexpr (!F32_ONLY)
-        gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+        gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, true, GATH, BQ8, F8><<<(unsigned)grid, 256, 0, s>>>(p);
     } else {
-      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+      if (cf) gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, true, false, GATH, BQ8, F8><<<(unsigned)grid, 256, 0, s>>>(p);
       else if constexpr (!F32_ONLY)
-        gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH, BQ8><<<(unsigned)grid, 256, 0, s>>>(p);
+        gemm_dma_kernel<DMA_BK, DMA_STAGES, ALAY, BLAY, GRP, EPI, DUAL, false, false, GATH, BQ8, F8><<<(unsigned)grid, 256, 0, s>>>(p);
     }
   }
   return hipGetLastError();
@@ -293,6 +294,37 @@ hipError_t launch_gate_up_q8(const moe_desc& d, const int32_t* offsets, const vo
   const int64_t ub = mtiles_ub(d, MT) * cdiv(d.f, MT / 2);
   if (row_token) return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true, GATH_A, true>(p, ub, s);
   return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true, GATH_NONE, true>(p, ub, s);
+}
+
+// gate/up on the FP8 matrix cores: x and W1/W3 as E4M3 codes with power-of-two
+// block scales (E8M0 bytes, one per 128 codes of a row), x read through
+// row_token; the block-scaled MFMA applies both scales.  Codes count in
+// pairs in the GEMM's units (a k-tile of 64 pairs is one scale block).
+hipError_t launch_gate_up_f8(const moe_desc& d, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
+                             const uint8_t* xs, const uint8_t* W1q, const uint8_t* W1s, const uint8_t* W3q,
+                             const uint8_t* W3s, void* gu, void* h, hipStream_t s) {
+  GemmParams p = blank(d);
+  p.A = xq;
+  p.lda = d.d / 2;
+  p.gather = row_token;
+  p.gather_rows = d.T;
+  p.B = W1q;
+  p.B2 = W3q;
+  p.ldb = d.d / 2;
+  p.b_gstride = (int64_t)d.f * d.d / 2;
+  p.a_scale = xs;
+  p.b_scale = W1s;
+  p.b2_scale = W3s;
+  p.sbytes = d.d / 128;
+  p.C = h;
+  p.ldc = d.f;
+  p.gu_out = gu;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.N = d.f;
+  p.K = d.d / 2;
+  return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_SWIGLU, true, GATH_A, false, true>(
+      p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
 }
 
 hipError_t launch_down_q8(const moe_desc& d, const int32_t* offsets, const void* h, const uint8_t* W2q,

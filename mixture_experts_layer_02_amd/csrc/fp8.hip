@@ -73,6 +73,43 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(const T* __restrict__ w,
   }
 }
 
+// Power-of-two block scales (the scale a block-scaled FP8 matrix instruction
+// applies): e = the least integer with amax <= 448 * 2^e, from amax = f 2^x
+// (f in [0.5, 1)): x - 9 when f <= 0.875, else x - 8; each value w * 2^-e
+// (exact) is cast; the scale leaves as its E8M0 byte e + 127.  An all-zero
+// block gets e = 0.
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_quant_pow2_kernel(const T* __restrict__ w, int64_t nblk,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; blk < nblk;
+       blk += ((int64_t)gridDim.x * 256) >> 4) {
+    float v[8];
+    load8(w + blk * 128 + sub * 8, v);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    int x = 0;
+    const float f = frexpf(amax, &x);
+    const int e = amax > 0.f ? (f <= 0.875f ? x - 9 : x - 8) : 0;
+    uint32_t c[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = ldexpf(v[4 * h + i], -e);
+      int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+      c[h] = (uint32_t)r;
+    }
+    const u32x2 out = {c[0], c[1]};
+    *reinterpret_cast<u32x2*>(q + blk * 128 + sub * 8) = out;
+    if (sub == 0) e8[blk] = (uint8_t)(e + 127);
+  }
+}
+
 // bf16 value = decode(code) * scale in float32, rounded to nearest even.
 __global__ void __launch_bounds__(256) fp8_dequant_kernel(const uint8_t* __restrict__ q, const float* __restrict__ scales,
                                                           int64_t nblk, uint16_t* __restrict__ w) {
@@ -107,6 +144,18 @@ hipError_t launch_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, 
                                                                          scales);
   else
     fp8_quant_kernel<float><<<(unsigned)grid_for(nblk), 256, 0, s>>>(reinterpret_cast<const float*>(w), nblk, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t* q, uint8_t* e8, hipStream_t s) {
+  const int64_t nblk = n / 128;
+  if (nblk == 0) return hipSuccess;
+  if (dtype == MOE_BF16)
+    fp8_quant_pow2_kernel<uint16_t><<<(unsigned)grid_for(nblk), 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w),
+                                                                              nblk, q, e8);
+  else
+    fp8_quant_pow2_kernel<float><<<(unsigned)grid_for(nblk), 256, 0, s>>>(reinterpret_cast<const float*>(w), nblk, q,
+                                                                           e8);
   return hipGetLastError();
 }
 

@@ -60,6 +60,10 @@ struct GemmParams {
   const float* bs;        // BQ8: float32 scale of each 128-value block of B's rows (B2's in bs2)
   const float* bs2;
   int band;               // GRP_K: m-tiles per band of the tile order (0 = m-tile fastest over all of M)
+  const uint8_t* a_scale;  // F8: E8M0 scale bytes of A's rows ([rows][sbytes], one per 128 codes of k)
+  const uint8_t* b_scale;  //     ... of B's rows (B2's in b2_scale), [groups * N][sbytes]
+  const uint8_t* b2_scale;
+  int sbytes;              //     scale bytes per row (K codes / 128, a multiple of 4)
   const float* row_scale; // EPI_SWIGLU_BWD with a gathered A: dH of row r is scaled by row_scale[r]
   void* h_out;            //   and, when set, row_scale[r] * silu(G) * U is written here ([rows][N])
 };

@@ -247,8 +247,18 @@ __device__ __forceinline__ void wait_stages(int later) {
 // decoded to bf16 when the MFMA fragments are read: decode * scale in
 // float32, rounded to nearest even, which is exactly what moe_fp8_dequantize
 // writes, so the product equals the bf16 product on dequantised weights.
+//
+// F8 (FP8 matrix cores): A and B hold E4M3 codes, two to a bf16 slot (K, lda,
+// ldb and the strides count pairs of codes, so a 64-wide k-tile is 128 codes),
+// with power-of-two block scales as E8M0 bytes, one per 128 codes of a row
+// (a_scale, b_scale, b2_scale; sbytes per row).  A k-tile is then one scale
+// block: each k-step is one v_mfma_scale_f32_32x32x64_f8f6f4 per 32 x 32
+// block, which applies the row's A and the column's B scale itself.  The
+// scale bytes of a k-tile's rows come with its operand tiles: one dword per
+// row (the four blocks k-tile & ~3 .. | 3) into a 2 KB area of the stage.
+// A is read through row_token (GATH_A).
 template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN, int GATH,
-          bool BQ8>
+          bool BQ8, bool F8 = false>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using namespace dma;
   static_assert(!DUAL || BLAY == LAY_K, "dual B is K-contiguous");
@@ -259,15 +269,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   static_assert(!BQ8 || (BLAY == LAY_K && GRP == GRP_M && (GATH == GATH_NONE || GATH == GATH_A) && BK == 64),
                 "FP8 B: K-contiguous B of GRP_M, 64-wide k-tiles (half a scale block)");
   static_assert(BK == 64 && STAGES == 2, "ring of two 64-wide k-tiles");
+  static_assert(!F8 || (ALAY == LAY_K && BLAY == LAY_K && GRP == GRP_M && !BQ8 && GATH == GATH_A),
+                "FP8 matrix cores: K-contiguous A (read through row_token) and B of GRP_M");
   // GKB: the k-rows of an MN-contiguous operand of a grouped-K product are
   // gathered (B for GATH_B, A for GATH_AK), through a ring of token copies.
   constexpr bool GKB = GATH == GATH_B || GATH == GATH_AK;
   constexpr int MI = 4, NI = 4;          // 32 x 32 blocks per wave (128 x 128)
+  typedef int i32x8f __attribute__((ext_vector_type(8)));
+  using Frag = typename std::conditional<F8, i32x8f, bf16x8>::type;  // one operand fragment of a k-step
   constexpr int TILE_ELEMS = 256 * BK;   // one operand tile
-  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
+  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS + (F8 ? 1024 : 0);  // (F8: + A and B scale dwords, 1 KB each)
+  constexpr int SCA = 2 * TILE_ELEMS * 2, SCB = SCA + 1024;        // their byte offsets in a stage
   constexpr int NJ = BK / 8;             // DMA instructions per wave per operand tile
   constexpr int NJB = BQ8 ? NJ / 2 : NJ;  // ... for B (FP8 B is half the bytes)
-  constexpr int KS = BK / 16;            // MFMA k-steps per k-tile
+  constexpr int KS = F8 ? 2 : BK / 16;   // MFMA k-steps per k-tile (F8: 64 codes per step)
   constexpr int WC = NI * 32;            // columns of a wave's block
   constexpr int SP = WC + 4;             // staging row pitch (floats)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][STAGE_ELEMS];
@@ -334,10 +349,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     int glim;
     int pfe;
     i32x4 rs;  // BQ8: the scales of the tile's B rows (of the second B for waves 2 and 3 with dual B)
+    uint32_t sbo;    // F8: the lane's B-row scale offset (bit 31 set past the tile's valid rows)
   };
   // GATH_A: the A offsets of the current and the next tile's rows (filled
   // from their tokens once these are in LDS).
   uint32_t gcur[GATH == GATH_A ? NJ : 1], gnext[GATH == GATH_A ? NJ : 1];
+  // F8: the lane's A-row scale offset (row 64 wave + lane of the tile) for
+  // the current and the next tile, and its B-row scale offset.
+  uint32_t gsc = 0x80000000u, gsn = 0x80000000u;
+  // F8: one resource over all of A's scale rows, one over all of the wave's B
+  // scale rows (B for waves 0 and 1, B2 for waves 2 and 3 with dual B).
+  const i32x4 rsa = F8 ? make_rsrc(p.a_scale, (uint64_t)p.gather_rows * p.sbytes) : make_rsrc(Ag, 0);
+  const i32x4 rsb = F8 ? make_rsrc(DUAL && wave >= 2 ? p.b2_scale : p.b_scale,
+                                   (uint64_t)p.ngroups * p.N * p.sbytes)
+                       : make_rsrc(Ag, 0);
   // L2 prefetch: one instruction per wave per operand, each lane touching one
   // 64-byte sector.  A tile is also loaded by the tiles of the same XCD that
   // run at the same time and share it: the tiles of one n-tile and
@@ -427,6 +452,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       L.pfe = e < ITEMS ? e : -1;
       L.pa = 0x7FFFFFF0u;
     }
+    if (F8) {  // B row (64 wave + lane) mod the rows of one B is row g N + n0 + r of its scale array
+      const int r = (wave * 64 + lane) & (DUAL ? 127 : 255);
+      L.sbo = ((uint32_t)((int64_t)t.g * p.N + t.n0 + r) * (uint32_t)p.sbytes) | (r < nlim_b ? 0u : 0x80000000u);
+    }
     if (GATH == GATH_B) {
       const int e = t.mtile % cB + cB * (wave * 64 + lane);
       L.glim = (int)klen;
@@ -442,6 +471,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   };
   Ld null_ld;  // loads nothing: every offset is outside its resources
   null_ld.ra = null_ld.rb = null_ld.rb2 = null_ld.rt = null_ld.rs = make_rsrc(Ag, 0);
+  null_ld.sbo = 0x80000000u;
   null_ld.nk = 0;
   null_ld.pa = null_ld.pb = 0x7FFFFFF0u;
   null_ld.glim = 0;
@@ -588,6 +618,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     L.pb = c ? cur.pb : nxt.pb;
     L.nk = 0;
     if (BQ8) L.rs = c ? cur.rs : nxt.rs;
+    if (F8) L.sbo = c ? cur.sbo : nxt.sbo;
     if (GATH != 0) {
       L.rt = c ? cur.rt : nxt.rt;
       L.glim = c ? cur.glim : nxt.glim;
@@ -602,6 +633,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     if (decltype(pure_c)::value) return gcur[GATH == GATH_A ? jj : 0];
     return pos < cur.nk ? gcur[GATH == GATH_A ? jj : 0] : gnext[GATH == GATH_A ? jj : 0];
   };
+  auto a_gs = [&](int pos, auto pure_c) __attribute__((always_inline)) -> uint32_t {
+    if (decltype(pure_c)::value) return gsc;
+    return pos < cur.nk ? gsc : gsn;
+  };
   // GATH_B (GATH_AK): the B (A) offsets of the position whose DMA is being
   // issued, and the L2-prefetch offset held for position kt+3 (see ktile).
   uint32_t gvb[GKB ? NJ : 1];
@@ -609,7 +644,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
 #pragma unroll
   for (int jj = 0; jj < (GKB ? NJ : 1); ++jj) gvb[jj] = 0x80000000u;
   // DMA instruction q (0 .. 2*NJ-1) of ring position pos: even q are A, odd q B.
-  auto dma_one = [&](int pos, int q, auto pure_c) {
+  auto dma_one = [&](int pos, int q, auto pure_c) __attribute__((always_inline)) {
     int k;
     const Ld L = pick(pos, k, pure_c);
     uint16_t* st = ring[(uint32_t)(gbase + pos) % STAGES];
@@ -633,6 +668,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
     constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
+    if (F8 && q >= 2 * NJ) {  // the scale dwords of the wave's 64 A rows, then of its 64 B rows
+      // (always five wait states: the compiler spills these resources to
+      // vector lanes and may reload one just before its use)
+      const uint32_t so = (uint32_t)(k >> 2) * 4u;
+      if (q == 2 * NJ) touch4u<false>(rsa, a_gs(pos, pure_c), so, stb + SCA + wave * 256);
+      else touch4u<false>(rsb, L.sbo, so, stb + SCB + wave * 256);
+      return;
+    }
     if ((q & 1) == 0 && GATH == GATH_AK) {
       dma16<LT>(L.ra, gvb[GKB ? jj : 0], 0u, stb + j * 1024);
     } else if ((q & 1) == 0) {
@@ -647,7 +690,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
   };
   // L2 prefetch instruction o (0: A, 1: B) of ring position pos.
-  auto pf_one = [&](int pos, int o, auto pure_c) {
+  auto pf_one = [&](int pos, int o, auto pure_c) __attribute__((always_inline)) {
     int k;
     const Ld L = pick(pos, k, pure_c);
     constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // as in dma_one
@@ -675,8 +718,13 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   };
   // GATH_A: the tile's A offsets and A prefetch offset from its tokens
   // (lane's rows 64w + 8jj + lane/8, and the prefetch sector's row pfe/2).
-  auto tok_fill_tile = [&](Ld& L, int slot, uint32_t (&gv)[GATH == GATH_A ? NJ : 1]) __attribute__((always_inline)) {
+  auto tok_fill_tile = [&](Ld& L, int slot, uint32_t (&gv)[GATH == GATH_A ? NJ : 1], uint32_t& gs)
+      __attribute__((always_inline)) {
     const int32_t* tk = s_tok[slot & (GATH == GATH_A ? 1 : 0)];
+    if (F8) {  // the scale row of tile row 64 wave + lane
+      const int row = wave * 64 + lane;
+      gs = ((uint32_t)tk[row] * (uint32_t)p.sbytes) | (row < L.glim ? 0u : 0x80000000u);
+    }
     constexpr int CPR = BK / 8, RPI = 64 / CPR;
 #pragma unroll
     for (int jj = 0; jj < (GATH == GATH_A ? NJ : 1); ++jj) {
@@ -724,15 +772,46 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   f32x16 acc[MI][NI];
   // Fragment f (0 .. MI+NI-1) of k-step kk of a ring stage, in the order the
   // MFMAs (mi-major) first use them: A0, B0 .. B3, A1 .. A3.
-  auto read_frag = [&](const uint16_t* st, int kk, int f, bf16x8(&a)[MI], bf16x8(&b)[NI]) {
+  // F8 fragment (K-contiguous rows of codes): row row0 + lane%32, the 32
+  // codes of 16-byte chunks 4 kk + 2 (lane/32) and the one after it, so that
+  // the two lanes of a row cover the k-step's 64 codes (the two operands of
+  // the instruction pair bytes the same way, measured on the MI355X).
+  auto frag8 = [&](const uint16_t* S, int row0, int kk) __attribute__((always_inline)) -> i32x8f {
+    const int r = row0 + (lane & 31);
+    const int c0 = 4 * kk + 2 * (lane >> 5);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(S + r * BK + ((c0 ^ swz_k<BK>(r)) * 8));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(S + r * BK + (((c0 + 1) ^ swz_k<BK>(r)) * 8));
+    const i32x8f v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return v;
+  };
+  auto read_frag = [&](const uint16_t* st, int kk, int f, Frag(&a)[MI], Frag(&b)[NI]) __attribute__((always_inline)) {
     static_assert(MI == 4 && NI == 4, "fragment order");
     if (f == 0 || f > NI) {
       const int mi = f == 0 ? 0 : f - NI;
-      a[mi] = frag<BK, ALAY>(st, wm * 128 + mi * 32, kk, lane);
+      if constexpr (F8) a[mi] = frag8(st, wm * 128 + mi * 32, kk);
+      else a[mi] = frag<BK, ALAY>(st, wm * 128 + mi * 32, kk, lane);
     } else {
       const int ni = f - 1;
       const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
-      b[ni] = BQ8 ? frag_q8(st + TILE_ELEMS, brow, kk, lane) : frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
+      if constexpr (F8) b[ni] = frag8(st + TILE_ELEMS, brow, kk);
+      else b[ni] = BQ8 ? frag_q8(st + TILE_ELEMS, brow, kk, lane) : frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
+    }
+  };
+  // F8: the E8M0 scale bytes of the wave's A rows and B columns for the k-tile
+  // in use (sA, sB) and for the next one (nsA, nsB, read with its first
+  // fragments): byte kb & 3 of each row's scale dword in stage st.
+  uint32_t sA[MI], sB[NI], nsA[MI], nsB[NI];
+  auto read_scales = [&](const uint16_t* st, int kb) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      const uint8_t* sa = reinterpret_cast<const uint8_t*>(st) + SCA + (kb & 3);
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(st) + SCB + (kb & 3);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) nsA[mi] = sa[(wm * 128 + mi * 32 + (lane & 31)) * 4];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
+        nsB[ni] = sb[(brow + (lane & 31)) * 4];
+      }
     }
   };
   // One k-step: the 16 MFMAs of fragments (a, b), with, in between, the
@@ -741,15 +820,29 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // position ppos, spread evenly.  The scheduling barriers pin this order, so
   // that the DMA issue never comes as a burst that would stall the wave's
   // MFMAs behind a full address queue.
-  auto kstep = [&](auto nd_c, auto np_c, auto pure_c, const bf16x8(&a)[MI], const bf16x8(&b)[NI],
-                   bf16x8(&na)[MI], bf16x8(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos) {
+  // (always_inline: out of line, the DMAs' scalar operands would arrive in
+  // vector registers, which the instruction does not take)
+  auto kstep = [&](auto nd_c, auto np_c, auto pure_c, const Frag(&a)[MI], const Frag(&b)[NI],
+                   Frag(&na)[MI], Frag(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos)
+      __attribute__((always_inline)) {
     constexpr int ND = decltype(nd_c)::value;
     constexpr int NO = ND + decltype(np_c)::value;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int mi = i / NI, ni = i % NI;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-      if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
+      if constexpr (F8) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mi], b[ni], acc[mi][ni], 0, 0, 0,
+                                                                      (int)sA[mi], 0, (int)sB[ni]);
+        // The next step's fragment of a row once this step's row is done, of
+        // a column after its last use (mi = 3): each then takes the registers
+        // of the one it replaces, so that about 9 rather than 16 fragments of
+        // 32 bytes are live at once.
+        if (ni == NI - 1) read_frag(rst, rkk, mi == 0 ? 0 : NI + mi, na, nb);
+        if (mi == MI - 1) read_frag(rst, rkk, 1 + ni, na, nb);
+      } else {
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
+      }
 #pragma unroll
       for (int o = (i * NO) / 16; o < ((i + 1) * NO) / 16; ++o) {
         if (o < ND) dma_one(dpos, q0 + o, pure_c);
@@ -765,7 +858,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // position kt+1 is waited for (one barrier per k-tile); the last step reads
   // position kt+1's first fragments and issues the first half of position
   // kt+2 (the last k-tile issues it whole, before the epilogue).
-  constexpr int PER = BQ8 ? NJ + NJB + 1 : 2 * NJ;  // DMA instructions per wave per ring position
+  constexpr int PER = BQ8 ? NJ + NJB + 1 : 2 * NJ + (F8 ? 2 : 0);  // DMA instructions per wave per ring position
   constexpr int PART = PER / 2;                      // first part; the second has PER - PART
   constexpr int PFD = 1;  // (measured: 1 beats 2 and 3 by 1-2% on the 1T shapes)
   // Memory instructions per lane of one epilogue (the buffer stores and
@@ -783,7 +876,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   using NDP1 = std::integral_constant<int, PER - PART>;
   using NDF = std::integral_constant<int, PER>;
   using NPP = std::integral_constant<int, NPF>;
-  bf16x8 fa[2][MI], fb[2][NI];
+  Frag fa[2][MI], fb[2][NI];
 
   // Dynamic order: the claim issued at the top of tile it resolves to tile
   // it+2's id, stored where the top of tile it+1 reads it.  k-tile pub_kt
@@ -819,18 +912,24 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   const int gat_kt = GATH == GATH_A ? __builtin_amdgcn_readfirstlane(p.ngroups >= 0 ? 1 : 2) : -1;
   auto gat_fill_next = [&]() __attribute__((always_inline)) {
     if (!gat_done) {
-      tok_fill_tile(lnext, it + 1, gnext);
+      tok_fill_tile(lnext, it + 1, gnext, gsn);
       if (pipe) nxt.pa = lnext.pa;
       gat_done = true;
     }
   };
 
   // PURE: every position the k-tile loads (kt+1 .. kt+1+PFD) is the current tile's.
-  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c) {
+  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     using PU = decltype(pure_c);
     const uint16_t* st = ring[(uint32_t)(gbase + kt) % STAGES];
+    if constexpr (F8) {  // this k-tile's scales, read with its first fragments
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) sA[mi] = nsA[mi];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) sB[ni] = nsB[ni];
+    }
     // GATH_B: the tokens of position kt+3+PFD (read two k-tiles later, after the
     // barriers that follow their wait).
     if (GKB) tok_dma_pos(kt + 3 + PFD);
@@ -860,6 +959,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // by now in every wave) give its A offsets.
     if (GATH == GATH_A && !FIRST && kt == gat_kt) gat_fill_next();
     const uint16_t* nst = ring[(uint32_t)(gbase + kt + 1) % STAGES];
+    if (F8) {  // the scales of position kt+1 (its k-tile index picks the byte)
+      int kn;
+      pick(kt + 1, kn, PU());
+      read_scales(nst, kn);
+    }
     if (LAST)
       kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
     else
@@ -879,7 +983,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     tok_dma_tile(cur, 0);
     wait_vm<0>();
     lds_barrier();
-    tok_fill_tile(cur, 0, gcur);
+    tok_fill_tile(cur, 0, gcur, gsc);
   }
   for (;;) {
     // The next tile of this workgroup, loaded ahead if it is long enough.
@@ -942,6 +1046,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         lds_barrier();
 #pragma unroll
         for (int f = 0; f < MI + NI; ++f) read_frag(ring[(uint32_t)gbase % STAGES], 0, f, fa[0], fb[0]);
+        read_scales(ring[(uint32_t)gbase % STAGES], 0);
       }
       using T_ = std::true_type;
       using F_ = std::false_type;
@@ -1219,6 +1324,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     if (GATH == GATH_A) {
 #pragma unroll
       for (int jj = 0; jj < (GATH == GATH_A ? NJ : 1); ++jj) gcur[jj] = gnext[jj];
+      gsc = gsn;
     }
     primed = pipe;
   }

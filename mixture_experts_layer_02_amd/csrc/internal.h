@@ -10,10 +10,14 @@ hipError_t launch_hold(int workgroups, int lds_bytes, int microseconds, hipStrea
 hipError_t launch_gate_up_q8(const moe_desc& d, const int32_t* offsets, const void* a, const int32_t* row_token,
                              const uint8_t* W1q, const float* s1, const uint8_t* W3q, const float* s3, void* gu,
                              void* h, hipStream_t s);
+hipError_t launch_gate_up_f8(const moe_desc& d, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
+                             const uint8_t* xs, const uint8_t* W1q, const uint8_t* W1s, const uint8_t* W3q,
+                             const uint8_t* W3s, void* gu, void* h, hipStream_t s);
 hipError_t launch_down_q8(const moe_desc& d, const int32_t* offsets, const void* h, const uint8_t* W2q,
                           const float* s2, void* y_perm, hipStream_t s);
 hipError_t launch_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, hipStream_t s);
+hipError_t launch_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t* q, uint8_t* e8, hipStream_t s);
 
 size_t permute_workspace(const moe_desc& d);
 // Size of the allocation-free permute's fixed device scratch (4 MiB per device).

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 33
+    assert len(names) == 35
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n

@@ -212,3 +212,131 @@ def test_fp8_gemms_match_the_oracle(gpu, scale, gather, dyn):
     assert max_row_rel_err(gu[:, f:], U) <= tol
     assert max_row_rel_err(to_host(b.h)[:R], H) <= tol
     assert max_row_rel_err(to_host(b.y_perm)[:R], Y) <= tol
+
+
+# ---------------------------------------------------------------------------
+# Power-of-two block scales and the gate/up GEMM on the FP8 matrix cores
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nblk", [1, 7, 1000, 40961])
+def test_quantize_pow2_matches_the_oracle(gpu, dtype, nblk):
+    rng = np.random.default_rng(100 + nblk)
+    w = _special_blocks(rng, max(nblk, 8))[:nblk].reshape(-1) if nblk >= 8 else \
+        (rng.normal(0, 1, nblk * 128) * 10.0 ** rng.uniform(-8, 6)).astype(np.float32)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(w)
+        w = synth.bf16_bits_to_f32(bits)
+        wd = to_dev(bits)
+    else:
+        wd = to_dev(w)
+    q = torch.empty(w.size, dtype=torch.uint8, device=gpu)
+    e8 = torch.empty(nblk, dtype=torch.uint8, device=gpu)
+    moe.fp8_quantize_pow2(wd, q, e8)
+    codes, e8_o = oracle.fp8_quantize_blocks_pow2(w)
+    np.testing.assert_array_equal(q.cpu().numpy(), codes)
+    np.testing.assert_array_equal(e8.cpu().numpy(), e8_o)
+
+
+def _quant_pow2(t, gpu):
+    q = torch.empty(t.numel(), dtype=torch.uint8, device=gpu)
+    e8 = torch.empty(t.numel() // 128, dtype=torch.uint8, device=gpu)
+    moe.fp8_quantize_pow2(t, q, e8)
+    return q, e8
+
+
+@pytest.mark.parametrize("dyn", [False, True])
+@pytest.mark.parametrize("scale", [
+    dict(T=1024, d=512, f=256, E=32, num_local=16, expert_begin=8, k=4),
+    dict(T=700, d=1024, f=384, E=64, num_local=24, expert_begin=40, k=6),    # ragged, empty experts, 3 n-tiles
+    dict(T=300, d=512, f=128, E=8, num_local=8, expert_begin=0, k=2),        # K of 4 k-tiles: no hand-over
+])
+def test_fp8mm_gate_up_matches_the_oracle(gpu, scale, dyn):
+    # x and W1/W3 quantised to E4M3 with power-of-two block scales; G, U and
+    # h against the oracle's expert MLP on the oracle's own dequantised x
+    # rows and weights (the codes and scales are first checked bit-exact).
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[fp8mm] {scale} dynamic={dyn}", flush=True)
+    T, d, f, E, k, e0, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local
+    inp = synth.make_inputs(cfg, want=("x", "w1", "w3"))
+    idx = random_routing(np.random.default_rng(T + d), T, E, k, skew=1.0)
+    D = moe.make_desc(T, d, f, E, k, e0, NL, "bf16", 1, tile_counters=moe.new_tile_counters(gpu) if dyn else None)
+    b = moe.Buffers(D, gather=True, backward=True)
+    moe.permute(D, to_dev(idx), None, b.counts, b.offsets, b.row_token, b.slot_row, None, b.ws_permute)
+    xq, xs = _quant_pow2(to_dev(inp["x"]), gpu)
+    wq = {n: _quant_pow2(to_dev(inp[n]), gpu) for n in ("w1", "w3")}
+    moe.expert_gate_up_fp8mm(D, b.offsets, b.row_token, xq, xs, wq["w1"][0], wq["w1"][1], wq["w3"][0],
+                             wq["w3"][1], b.gu, b.h)
+    torch.cuda.synchronize()
+    deq = {}
+    for n, a in (("x", inp["x"]), ("w1", inp["w1"]), ("w3", inp["w3"])):
+        c, e = oracle.fp8_quantize_blocks_pow2(synth.as_f32(a, "bf16"))
+        got = (xq, xs) if n == "x" else wq[n]
+        np.testing.assert_array_equal(got[0].cpu().numpy(), c)
+        np.testing.assert_array_equal(got[1].cpu().numpy(), e)
+        deq[n] = oracle.fp8_dequantize_blocks_pow2(c, e).reshape(a.shape)
+    _, off = oracle.count_tokens(idx, E, e0, NL)
+    rows, _ = oracle.generate_indices(idx, e0, NL, off)
+    np.testing.assert_array_equal(to_host(b.offsets), off)
+    R = int(off[-1])
+    xp = oracle.permute(deq["x"], rows)
+    G, U, H, _ = oracle.expert_ffn(xp, off, deq["w1"], deq["w3"], np.zeros((NL, d, f)))
+    tol = TOL["bf16"]
+    gu = to_host(b.gu)[:R]
+    assert max_row_rel_err(gu[:, :f], G) <= tol
+    assert max_row_rel_err(gu[:, f:], U) <= tol
+    assert max_row_rel_err(to_host(b.h)[:R], H) <= tol
+
+
+def test_fp8mm_rejects_unsupported_shapes(gpu):
+    z = torch.zeros(1 << 16, dtype=torch.float32, device=gpu)
+    D = _desc(64, 256, 128, 8, 2, 0, 8, "bf16")                 # d not a multiple of 512
+    with pytest.raises(moe.MoeError):
+        moe.expert_gate_up_fp8mm(D, z, z, z, z, z, z, z, z, z, z)
+    D = _desc(64, 512, 128, 8, 2, 0, 8, "f32")
+    with pytest.raises(moe.MoeError):
+        moe.expert_gate_up_fp8mm(D, z, z, z, z, z, z, z, z, z, z)
+
+
+def test_fp8mm_gate_up_at_full_size_sampled(gpu):
+    # The 1T expert-parallel share (T = 8192, d = 6144, 96 of 384 experts,
+    # f = 1792) in the benchmark's launch configuration; the oracle quantises
+    # and multiplies only what the sampled tokens' rows need (their x rows
+    # and their experts' W1 / W3).
+    cfg = synth.CONFIGS["share_1t"]
+    T, d, f, E, k, e0, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local
+    print(f"[fp8mm full size] T={T} d={d} f={f} E={E} NL={NL}", flush=True)
+    inp = synth.make_inputs(cfg, want=("x", "w1", "w3"))
+    idx = random_routing(np.random.default_rng(3), T, E, k)
+    D = _desc(T, d, f, E, k, e0, NL, "bf16")
+    b = moe.Buffers(D, gather=True)
+    moe.permute(D, to_dev(idx), None, b.counts, b.offsets, b.row_token, b.slot_row, None, b.ws_permute)
+    xq, xs = _quant_pow2(to_dev(inp["x"]), gpu)
+    wq = {n: _quant_pow2(to_dev(inp[n]), gpu) for n in ("w1", "w3")}
+    moe.expert_gate_up_fp8mm(D, b.offsets, b.row_token, xq, xs, wq["w1"][0], wq["w1"][1], wq["w3"][0],
+                             wq["w3"][1], None, b.h)
+    torch.cuda.synchronize()
+    _, off = oracle.count_tokens(idx, E, e0, NL)
+    rows, slot = oracle.generate_indices(idx, e0, NL, off)
+    np.testing.assert_array_equal(to_host(b.offsets), off)
+    np.testing.assert_array_equal(to_host(b.slot_row), slot)
+    # sampled tokens (the first and the last among them) with at least one local slot
+    has = (slot >= 0).any(axis=1)
+    cand = np.nonzero(has)[0]
+    toks = np.unique(np.concatenate([cand[[0, -1]], np.random.default_rng(5).choice(cand, 3, replace=False)]))
+    x32 = synth.as_f32(inp["x"], "bf16")
+    deq_w = {}
+    hg = to_host(b.h[torch.as_tensor(slot[toks][slot[toks] >= 0].astype(np.int64), device=b.h.device)])
+    want = []
+    for t in toks:
+        c, e = oracle.fp8_quantize_blocks_pow2(x32[t])
+        xr = oracle.fp8_dequantize_blocks_pow2(c, e)
+        for j in range(k):
+            if slot[t, j] < 0:
+                continue
+            n = int(idx[t, j]) - e0
+            if n not in deq_w:
+                deq_w[n] = [oracle.fp8_dequantize_blocks_pow2(*oracle.fp8_quantize_blocks_pow2(
+                    synth.as_f32(inp[w][n], "bf16"))).reshape(f, d) for w in ("w1", "w3")]
+            G, U, H, _ = oracle.expert_ffn_rows(xr[None, :], deq_w[n][0], deq_w[n][1], np.zeros((d, f)))
+            want.append(H[0])
+    assert max_row_rel_err(hg, np.array(want)) <= TOL["bf16"]
