@@ -799,20 +799,33 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   };
   // F8: the E8M0 scale bytes of the wave's A rows and B columns for the k-tile
   // in use (sA, sB) and for the next one (nsA, nsB, read with its first
-  // fragments): byte kb & 3 of each row's scale dword in stage st.
-  uint32_t sA[MI], sB[NI], nsA[MI], nsB[NI];
+  // fragments): byte kb & 3 of each row's scale dword in stage st.  Byte mi
+  // of sA is the scale of fragment row mi, byte ni of sB that of fragment
+  // column ni; the instruction's op_sel picks the byte.
+  uint32_t sA = 0, sB = 0, nsA = 0, nsB = 0;
   auto read_scales = [&](const uint16_t* st, int kb) __attribute__((always_inline)) {
     if constexpr (F8) {
       const uint8_t* sa = reinterpret_cast<const uint8_t*>(st) + SCA + (kb & 3);
       const uint8_t* sb = reinterpret_cast<const uint8_t*>(st) + SCB + (kb & 3);
+      uint32_t a = 0, b = 0;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) nsA[mi] = sa[(wm * 128 + mi * 32 + (lane & 31)) * 4];
+      for (int mi = 0; mi < MI; ++mi) a |= (uint32_t)sa[(wm * 128 + mi * 32 + (lane & 31)) * 4] << (8 * mi);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
-        nsB[ni] = sb[(brow + (lane & 31)) * 4];
+        b |= (uint32_t)sb[(brow + (lane & 31)) * 4] << (8 * ni);
       }
+      nsA = a;
+      nsB = b;
     }
+  };
+  // The block-scaled product of fragment row MI_ and column NI_ (op_sel must be a constant).
+  auto mfma8 = [&](auto mi_c, auto ni_c, const Frag& a, const Frag& b, f32x16 c) __attribute__((always_inline)) {
+    if constexpr (F8)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, decltype(mi_c)::value, (int)sA,
+                                                            decltype(ni_c)::value, (int)sB);
+    else
+      return c;
   };
   // One k-step: the 16 MFMAs of fragments (a, b), with, in between, the
   // reads of the next k-step's fragments (stage rst, step rkk), ND DMA
@@ -822,23 +835,33 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // MFMAs behind a full address queue.
   // (always_inline: out of line, the DMAs' scalar operands would arrive in
   // vector registers, which the instruction does not take)
+  // (F8, NOREAD: the step reads no fragments - the last k-step of a tile,
+  // whose successor reads its own after the epilogue)
   auto kstep = [&](auto nd_c, auto np_c, auto pure_c, const Frag(&a)[MI], const Frag(&b)[NI],
-                   Frag(&na)[MI], Frag(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos)
-      __attribute__((always_inline)) {
+                   Frag(&na)[MI], Frag(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos,
+                   auto noread_c) __attribute__((always_inline)) {
+    constexpr bool NOREAD = decltype(noread_c)::value;
     constexpr int ND = decltype(nd_c)::value;
     constexpr int NO = ND + decltype(np_c)::value;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int mi = i / NI, ni = i % NI;
       if constexpr (F8) {
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mi], b[ni], acc[mi][ni], 0, 0, 0,
-                                                                      (int)sA[mi], 0, (int)sB[ni]);
+        switch (i) {  // (i is a constant once the loop is unrolled)
+#define MOE_F8_CASE(I) \
+  case I: acc[I / NI][I % NI] = mfma8(std::integral_constant<int, I / NI>(), std::integral_constant<int, I % NI>(), \
+                                     a[I / NI], b[I % NI], acc[I / NI][I % NI]); break;
+          MOE_F8_CASE(0) MOE_F8_CASE(1) MOE_F8_CASE(2) MOE_F8_CASE(3) MOE_F8_CASE(4) MOE_F8_CASE(5)
+          MOE_F8_CASE(6) MOE_F8_CASE(7) MOE_F8_CASE(8) MOE_F8_CASE(9) MOE_F8_CASE(10) MOE_F8_CASE(11)
+          MOE_F8_CASE(12) MOE_F8_CASE(13) MOE_F8_CASE(14) MOE_F8_CASE(15)
+#undef MOE_F8_CASE
+        }
         // The next step's fragment of a row once this step's row is done, of
         // a column after its last use (mi = 3): each then takes the registers
         // of the one it replaces, so that about 9 rather than 16 fragments of
         // 32 bytes are live at once.
-        if (ni == NI - 1) read_frag(rst, rkk, mi == 0 ? 0 : NI + mi, na, nb);
-        if (mi == MI - 1) read_frag(rst, rkk, 1 + ni, na, nb);
+        if (!NOREAD && ni == NI - 1) read_frag(rst, rkk, mi == 0 ? 0 : NI + mi, na, nb);
+        if (!NOREAD && mi == MI - 1) read_frag(rst, rkk, 1 + ni, na, nb);
       } else {
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
         if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
@@ -925,10 +948,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     using PU = decltype(pure_c);
     const uint16_t* st = ring[(uint32_t)(gbase + kt) % STAGES];
     if constexpr (F8) {  // this k-tile's scales, read with its first fragments
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) sA[mi] = nsA[mi];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) sB[ni] = nsB[ni];
+      sA = nsA;
+      sB = nsB;
     }
     // GATH_B: the tokens of position kt+3+PFD (read two k-tiles later, after the
     // barriers that follow their wait).
@@ -937,15 +958,16 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     for (int s = 0; s < KS - 1; ++s) {
       if (s == 0) {
         if (FIRST)
-          kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD);
+          kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD, std::false_type());
         else
-          kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD);
+          kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD, std::false_type());
         // GATH_B: position kt+1 is issued whole; its offsets make way for
         // those of kt+2 (issued at this k-tile's end and the next's start),
         // and the prefetch offset for kt+2+PFD (next k-tile's prefetch).
         if (GKB) tok_fill_pos(kt + 2, kt + 2 + PFD);
       } else {
-        kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0);
+        kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0,
+              std::false_type());
       }
     }
     // Position kt+1 has landed: after its last DMA come only its prefetches,
@@ -959,15 +981,18 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // by now in every wave) give its A offsets.
     if (GATH == GATH_A && !FIRST && kt == gat_kt) gat_fill_next();
     const uint16_t* nst = ring[(uint32_t)(gbase + kt + 1) % STAGES];
-    if (F8) {  // the scales of position kt+1 (its k-tile index picks the byte)
+    if (F8 && !LAST) {  // the scales of position kt+1 (its k-tile index picks the byte)
       int kn;
       pick(kt + 1, kn, PU());
       read_scales(nst, kn);
     }
+    // (F8: the last k-tile leaves the next tile's first fragments and scales
+    // to be read after the epilogue, so they are not live through it)
+    using NR = std::integral_constant<bool, F8 && LAST>;
     if (LAST)
-      kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
+      kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR());
     else
-      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0);
+      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR());
   };
 
   // Epilogue resources: C (or C2 for rows past msplit) from the tile's
@@ -1044,6 +1069,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         for (int q = 0; q < PER; ++q) dma_one(1, q, std::false_type());
         wait_vm<PER + NPF>();  // position 0 has landed (then come its prefetch and position 1)
         lds_barrier();
+#pragma unroll
+        for (int f = 0; f < MI + NI; ++f) read_frag(ring[(uint32_t)gbase % STAGES], 0, f, fa[0], fb[0]);
+        read_scales(ring[(uint32_t)gbase % STAGES], 0);
+      } else if (F8) {  // primed: position 0 has landed (waited for before the previous tile's last step)
 #pragma unroll
         for (int f = 0; f < MI + NI; ++f) read_frag(ring[(uint32_t)gbase % STAGES], 0, f, fa[0], fb[0]);
         read_scales(ring[(uint32_t)gbase % STAGES], 0);
