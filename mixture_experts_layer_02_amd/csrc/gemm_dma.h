@@ -883,7 +883,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // kt+2 (the last k-tile issues it whole, before the epilogue).
   constexpr int PER = BQ8 ? NJ + NJB + 1 : 2 * NJ + (F8 ? 2 : 0);  // DMA instructions per wave per ring position
   constexpr int PART = PER / 2;                      // first part; the second has PER - PART
-  constexpr int PFD = 1;  // (measured: 1 beats 2 and 3 by 1-2% on the 1T shapes)
+  constexpr int PFD = 1;  // (measured: 1 beats 2 and 3 by 1-2% on the 1T shapes; for F8, 2 is within noise)
   // Memory instructions per lane of one epilogue (the buffer stores and
   // loads below, all unconditional).
   // (ROWSC: dH scaled per row, with the scales loaded and h_out stored: 32 more of each.)
