@@ -211,6 +211,7 @@ class Workload:
                                    tile_counters=counters)
         gather = args.x_path == "gather" or fp8mm
         gdy = args.dy_path == "gather" and cfg.dtype == "bf16"
+        fuse_rdx = args.router_dx == "fused" and bool(cfg.renormalize)
         b = self.b = moe.Buffers(D, backward=cfg.backward, gather=gather, gather_dy=gdy)
         bb = 2 if cfg.dtype == "bf16" else 4
         fp8 = self.fp8 = {}
@@ -325,9 +326,19 @@ class Workload:
             if routing is None:
                 add("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), 1,
                     nbytes=lambda R: T * E * 4 + T * k * 12)
-            add("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx), 1,
-                nbytes=lambda R: R * d * bb + T * d * bb + T * k * 4)
-            if routing is None:
+            if routing is None and fuse_rdx:
+                # dx = the unpermute sum + the k selected rows of Wr times dlogits, in one pass
+                add("B5_unpermute", lambda: moe.unpermute_router_bwd(D, b.slot_row, b.dx_perm, idx, b.dlogits,
+                                                                     g["wr"], b.dx), 1,
+                    nbytes=lambda R: R * d * bb + T * d * bb + T * k * 12 + E * d * bb)
+                # dlogits to bf16, dWr split-K partials, their sum
+                add("B5_router_bwd", lambda: moe.router_bwd_acc(D, g["x"], g["wr"], b.dlogits, None, b.dWr,
+                                                                b.ws_router_bwd), 3,
+                    lambda R: 2.0 * T * d * E, lambda R: T * d * bb + T * E * 4 + E * d * 4)
+            else:
+                add("B5_unpermute", lambda: moe.unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx), 1,
+                    nbytes=lambda R: R * d * bb + T * d * bb + T * k * 4)
+            if routing is None and not fuse_rdx:
                 # dlogits to bf16, dx += dlogits Wr, dWr split-K partials, their sum
                 add("B5_router_bwd", lambda: moe.router_bwd_acc(D, g["x"], g["wr"], b.dlogits, b.dx, b.dWr,
                                                                 b.ws_router_bwd), 4,
@@ -442,6 +453,9 @@ def main():
     ap.add_argument("--dy-path", choices=["perm", "gather"], default="gather",
                     help="gather: dH and dW2 read dy through row_token with the routing weight applied inside "
                          "(no dy_perm); perm: the combine backward writes dy_perm")
+    ap.add_argument("--router-dx", choices=["fused", "gemm"], default="fused",
+                    help="the router's share of dx: fused, k rows of Wr added in the unpermute pass (renormalised "
+                         "weights: dlogits is zero outside the selection); gemm, dx += dlogits Wr as a product")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights held as blockwise-128 E4M3 codes + scales, dequantised to bf16 each step")
     ap.add_argument("--fp8-gemm", action="store_true",
@@ -481,7 +495,8 @@ def main():
     note("inputs resident in HBM; warming up")
     avg, step_ms, wall = run(moe, torch, wl, args, args.steps, args.warmup, flush, note)
     peak_mem = torch.cuda.max_memory_allocated()
-    default_run = (cfg.name == "fwdbwd_1t" and args.x_path == "perm" and args.dy_path == "gather" and not (
+    default_run = (cfg.name == "fwdbwd_1t" and args.x_path == "perm" and args.dy_path == "gather"
+                   and args.router_dx == "fused" and not (
         args.fp8_weights or args.fp8_gemm or args.hold_cus or args.n_groups > 1 or args.schedule != "static"))
     main_sum = summarize(wl, avg, step_ms, wall, args.steps, default_run)
     ms_step = main_sum["ms_per_step"]
@@ -536,6 +551,8 @@ def main():
                    "x_path": ("x_perm copy" if args.x_path == "perm" else "x read through row_token"),
                    "dy_path": ("dy read through row_token, no dy_perm" if args.dy_path == "gather"
                                else "dy_perm copy"),
+                   "router_dx": ("k rows of Wr added in the unpermute pass" if args.router_dx == "fused"
+                                 and cfg.renormalize else "dx += dlogits Wr product"),
                    "expert_weights": ("bf16" if not args.fp8_weights else
                                       "fp8 e4m3 blocks of 128, read by the forward GEMMs" if args.fp8_gemm else
                                       "fp8 e4m3 blocks of 128, dequantised each step"),

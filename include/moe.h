@@ -344,6 +344,27 @@ int moe_router_bwd(const moe_desc* desc, const void* x, const void* Wr, const fl
 int moe_router_bwd_acc(const moe_desc* desc, const void* x, const void* Wr, const float* dlogits, void* dx,
                        float* dWr, void* ws, size_t ws_bytes, void* stream);
 
+/* B5a and the dx half of B5c in one pass, for renormalised weights:
+ *   dx[t] = sum over local slots j of dx_perm[slot_row[t][j]]
+ *         + sum over all k slots j of dlogits[t][e_j] * Wr[e_j],  e_j = topk_idx[t][j].
+ * With the weights renormalised over the selection (Aurora page, Algorithm
+ * 1, stage 1, as read with renormalisation), dlogits is zero outside the k
+ * selected experts (moe_route_bwd), so dlogits[t] Wr is that sum of k rows
+ * of Wr; this replaces moe_unpermute_bwd followed by moe_router_bwd_acc
+ * with dx (dWr still comes from moe_router_bwd_acc with dx NULL).
+ *   slot_row [T][k] int32, dx_perm [R_cap][d], topk_idx [T][k] int32 (the
+ *   selection moe_route wrote; entries outside [0, E) are clamped into it),
+ *   dlogits [T][E] float32 (moe_route_bwd's output), Wr [E][d], dx [T][d]
+ *   out, all but the index arrays and dlogits in the descriptor's dtype.
+ *   float32 sums (expert rows in slot order, then router rows in slot
+ *   order), one rounding at the store.
+ * Errors: MOE_ERR_UNSUPPORTED when desc->renormalize is 0 (dlogits is then
+ * dense: use moe_unpermute_bwd and moe_router_bwd_acc); MOE_ERR_INVALID_ARG
+ * for a NULL pointer or a bad descriptor. */
+int moe_unpermute_router_bwd(const moe_desc* desc, const int32_t* slot_row, const void* dx_perm,
+                             const int32_t* topk_idx, const float* dlogits, const void* Wr, void* dx,
+                             void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_str(int status);
 

@@ -99,6 +99,7 @@ _SIGS = {
     "moe_route_bwd": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_router_bwd_acc": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_unpermute_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
 }
 EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error", "moe_hold_cus",
                                  "moe_fp8_quantize", "moe_fp8_dequantize", "moe_fp8_quantize_pow2"])
@@ -348,6 +349,10 @@ def unpermute_bwd(desc, slot_row, dx_perm, dx_add, dx):
     _call("moe_unpermute_bwd", desc, slot_row, dx_perm, dx_add, dx, _stream())
 
 
+def unpermute_router_bwd(desc, slot_row, dx_perm, topk_idx, dlogits, wr, dx):
+    _call("moe_unpermute_router_bwd", desc, slot_row, dx_perm, topk_idx, dlogits, wr, dx, _stream())
+
+
 def route_bwd(desc, logits, topk_idx, topk_w, dtopk_w, dlogits):
     _call("moe_route_bwd", desc, logits, topk_idx, topk_w, dtopk_w, dlogits, _stream())
 
@@ -432,8 +437,11 @@ def forward(b: Buffers, x, wr, w1, w3, w2, bias=None, routing=None, n_groups=1):
     return b.y
 
 
-def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None):
-    """Stages B1-B5 for upstream gradient dy (needs Buffers(backward=True))."""
+def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None, fuse_router_dx=True):
+    """Stages B1-B5 for upstream gradient dy (needs Buffers(backward=True)).
+    fuse_router_dx: with renormalised weights, the router's share of dx is
+    added in the unpermute pass (unpermute_router_bwd) instead of by the
+    dx += dlogits Wr product."""
     D = b.desc
     idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
     if b.gather_dy:
@@ -453,6 +461,11 @@ def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None):
         combine_bwd(D, b.slot_row, w, b.y_perm, dy, b.dy_perm, b.dtopk_w)
         grouped_ffn_bwd_dx(D, b.offsets, w1, w3, w2, b.gu, b.dy_perm, b.dgu, b.dx_perm)
         grouped_ffn_bwd_dw(D, b.offsets, b.x_perm, b.h, b.dgu, b.dy_perm, b.dW1, b.dW3, b.dW2)
+    if routing is None and fuse_router_dx and D.renormalize:
+        route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits)
+        unpermute_router_bwd(D, b.slot_row, b.dx_perm, idx, b.dlogits, wr, b.dx)
+        router_bwd_acc(D, x, wr, b.dlogits, None, b.dWr, b.ws_router_bwd)
+        return b.dx
     unpermute_bwd(D, b.slot_row, b.dx_perm, None, b.dx)
     if routing is None:
         route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits)

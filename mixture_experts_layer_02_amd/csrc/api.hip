@@ -288,6 +288,17 @@ int moe_unpermute_bwd(const moe_desc* desc, const int32_t* slot_row, const void*
   return finish(moe::launch_unpermute_bwd(*desc, slot_row, dx_perm, dx_add, dx, S(stream)));
 }
 
+int moe_unpermute_router_bwd(const moe_desc* desc, const int32_t* slot_row, const void* dx_perm,
+                             const int32_t* topk_idx, const float* dlogits, const void* Wr, void* dx,
+                             void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(dx_perm) || !need(topk_idx) || !need(dlogits) || !need(Wr) || !need(dx))
+    return MOE_ERR_INVALID_ARG;
+  if (desc->renormalize != 1) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_unpermute_router_bwd(*desc, slot_row, dx_perm, topk_idx, dlogits, Wr, dx, S(stream)));
+}
+
 int moe_route_bwd(const moe_desc* desc, const float* logits, const int32_t* topk_idx, const float* topk_w,
                   const float* dtopk_w, float* dlogits, void* stream) {
   int rc = check_desc(desc);

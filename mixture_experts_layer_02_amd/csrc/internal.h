@@ -48,6 +48,9 @@ hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, cons
                                  const void* dy, const void* hw, float* dW2, hipStream_t s);
 hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
                                 const float* dx_add, void* dx, hipStream_t s);
+hipError_t launch_unpermute_router_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
+                                       const int32_t* topk_idx, const float* dlogits, const void* Wr, void* dx,
+                                       hipStream_t s);
 hipError_t launch_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* W1,
                           const void* W3, void* gu, void* h, hipStream_t s,
                           const int32_t* row_token = nullptr);

@@ -582,6 +582,107 @@ __global__ void __launch_bounds__(256) unpermute_bwd_kernel_b(const int32_t* __r
   }
 }
 
+// dx[t] = sum_j dx_perm[slot_row[t][j]] + sum_j dL[t][e_j] W_r[e_j], e_j =
+// topk_idx[t][j], dL the router-logit gradient.  With the weights
+// renormalised over the selection, dL is zero outside it, so the router's
+// share of dx, dlogits[t] W_r, is that sum of k rows of W_r: k multiply-adds
+// per element here instead of a T x d x E product.  Sums in float32, the
+// expert rows in slot order, then the router rows in slot order; one
+// rounding at the store.  W_r (E x d) is read by every token and stays in
+// the caches.  Each wave takes one token; per chunk of the row every load
+// (the live expert rows and the k router rows) is issued before any is used.
+template <typename T, int KB>
+__global__ void __launch_bounds__(256) unpermute_router_bwd_kernel_b(
+    const int32_t* __restrict__ slot_row, const T* __restrict__ dx_perm, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dlogits, const T* __restrict__ wr, int Tn, int k, int E, int d,
+    T* __restrict__ dx) {
+  using R = batched::Raw<T>;
+  constexpr int VN = R::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const int ex = lane < k ? min(max(topk_idx[(int64_t)t * k + lane], 0), E - 1) : 0;  // (clamped: no read outside W_r)
+  const float g = lane < k ? dlogits[(int64_t)t * E + ex] : 0.f;
+  const uint64_t live = __ballot(r >= 0);
+  int64_t rows[KB], erows[KB];
+  float gj[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    rows[j] = (int64_t)__shfl(r, j, 64) * d;
+    erows[j] = (int64_t)__shfl(ex, j, 64) * d;
+    gj[j] = __shfl(g, j, 64);
+  }
+  for (int c = lane * VN; c < d; c += 64 * VN) {
+    u32x4 q[KB], qw[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1) q[j] = batched::ld16(dx_perm + rows[j] + c);
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (j < k) qw[j] = batched::ld16(wr + erows[j] + c);
+    float acc[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if ((live >> j) & 1) {
+        float v[VN];
+        R::widen(q[j], v);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) acc[e] += v[e];
+      }
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (j < k) {
+        float v[VN];
+        R::widen(qw[j], v);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) acc[e] = fmaf(gj[j], v[e], acc[e]);
+      }
+    Vec16<T>::store(dx + (int64_t)t * d + c, acc);
+  }
+}
+
+// The same for any k <= 64, one slot at a time.
+template <typename T>
+__global__ void __launch_bounds__(256) unpermute_router_bwd_kernel(
+    const int32_t* __restrict__ slot_row, const T* __restrict__ dx_perm, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dlogits, const T* __restrict__ wr, int Tn, int k, int E, int d,
+    T* __restrict__ dx) {
+  using V = Vec16<T>;
+  constexpr int VN = V::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
+  const int ex = lane < k ? min(max(topk_idx[(int64_t)t * k + lane], 0), E - 1) : 0;  // (clamped: no read outside W_r)
+  const float g = lane < k ? dlogits[(int64_t)t * E + ex] : 0.f;
+  const uint64_t live = __ballot(r >= 0);
+  for (int c = lane * VN; c < d; c += 64 * VN) {
+    float acc[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) acc[e] = 0.f;
+    uint64_t m = live;
+    while (m) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      float v[VN];
+      V::load(dx_perm + (int64_t)__shfl(r, j, 64) * d + c, v);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] += v[e];
+    }
+    for (int j = 0; j < k; ++j) {
+      const float gs = __shfl(g, j, 64);
+      float v[VN];
+      V::load(wr + (int64_t)__shfl(ex, j, 64) * d + c, v);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] = fmaf(gs, v[e], acc[e]);
+    }
+    V::store(dx + (int64_t)t * d + c, acc);
+  }
+}
+
 hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
                           void* y, hipStream_t s) {
   const dim3 grid((d.T + 3) / 4), block(256);
@@ -645,6 +746,33 @@ hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, cons
     else
       unpermute_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, dx_add, d.T, d.k, d.d,
                                                          (float*)dx);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute_router_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
+                                       const int32_t* topk_idx, const float* dlogits, const void* Wr, void* dx,
+                                       hipStream_t s) {
+  const dim3 grid((d.T + 3) / 4), block(256);
+  const bool b8 = d.k <= 8;
+  if (d.dtype == MOE_BF16) {
+    if (b8)
+      unpermute_router_bwd_kernel_b<uint16_t, 8><<<grid, block, 0, s>>>(
+          slot_row, (const uint16_t*)dx_perm, topk_idx, dlogits, (const uint16_t*)Wr, d.T, d.k, d.E, d.d,
+          (uint16_t*)dx);
+    else
+      unpermute_router_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, (const uint16_t*)dx_perm, topk_idx,
+                                                                   dlogits, (const uint16_t*)Wr, d.T, d.k, d.E,
+                                                                   d.d, (uint16_t*)dx);
+  } else {
+    if (b8)
+      unpermute_router_bwd_kernel_b<float, 8><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, topk_idx,
+                                                                     dlogits, (const float*)Wr, d.T, d.k, d.E,
+                                                                     d.d, (float*)dx);
+    else
+      unpermute_router_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, topk_idx,
+                                                                dlogits, (const float*)Wr, d.T, d.k, d.E, d.d,
+                                                                (float*)dx);
   }
   return hipGetLastError();
 }

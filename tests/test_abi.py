@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 35
+    assert len(names) == 36
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n
@@ -179,3 +179,15 @@ def test_permute_noalloc_rejects_shapes_beyond_its_scratch():
     d = _d()
     assert l.moe_permute_noalloc(ctypes.byref(d), None, None, g, g, g, g, None, None) == moe.MOE_ERR_INVALID_ARG
     assert l.moe_permute_noalloc(ctypes.byref(d), g, g, g, g, g, g, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_unpermute_router_bwd_rejects_dense_dlogits_and_nulls():
+    # The router rows are summed over the selection only, which is dlogits'
+    # support when the weights are renormalised; renormalize = 0 is refused.
+    l = moe.lib()
+    g = 1 << 20
+    d0 = _d(renormalize=0)
+    assert l.moe_unpermute_router_bwd(ctypes.byref(d0), g, g, g, g, g, g, None) == moe.MOE_ERR_UNSUPPORTED
+    d = _d()
+    assert l.moe_unpermute_router_bwd(ctypes.byref(d), g, g, None, g, g, g, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_unpermute_router_bwd(ctypes.byref(d), g, g, g, g, None, g, None) == moe.MOE_ERR_INVALID_ARG

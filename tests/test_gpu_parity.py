@@ -210,6 +210,43 @@ def test_router_backward(gpu, T, d, E, dtype):
 
 
 # ---------------------------------------------------------------------------
+# B5 fused: the unpermute sum plus the router's share of dx, with dlogits
+# from the oracle's route backward (renormalised weights: zero outside the
+# selection).  k <= 8 takes the batched kernel, k > 8 the slot-loop one.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,k,e0,NL,dtype", [
+    (300, 256, 72, 8, 8, 24, "bf16"), (1000, 512, 384, 8, 0, 96, "bf16"), (513, 320, 64, 6, 40, 24, "bf16"),
+    (257, 128, 64, 12, 0, 64, "bf16"), (1, 128, 8, 1, 0, 8, "bf16"), (129, 128, 16, 4, 3, 5, "f32"),
+    (200, 192, 40, 10, 0, 40, "f32"),
+    (301, 2048, 64, 8, 16, 32, "bf16"), (130, 4096, 384, 8, 0, 96, "bf16"), (70, 2048, 16, 3, 0, 16, "f32")])
+def test_unpermute_router_backward(gpu, T, d, E, k, e0, NL, dtype):
+    rng = np.random.default_rng(T * 7 + E)
+    idx = random_routing(rng, T, E, k)
+    counts, off = oracle.count_tokens(idx, E, e0, NL)
+    _, slot = oracle.generate_indices(idx, e0, NL, off)
+    R = int(off[-1])
+    w = rng.dirichlet(np.ones(k), size=T)
+    dw = rng.standard_normal((T, k))
+    dl = oracle.route_bwd(idx, w, dw, E, 1).astype(np.float32)
+    cfg = synth.Config("t", 19, T, d, E, k, 64, e0, NL, dtype, 1.0, "router", False)
+    inp = synth.make_inputs(cfg, want=("wr",))
+    dxp = synth.normal_f32(T + 11, 3, (max(R, 1), d), 1.0)
+    dxp = synth.f32_to_bf16_bits(dxp) if dtype == "bf16" else dxp
+    D = _desc(T, d, 64, E, k, e0, NL, dtype)
+    dx = torch.full((T, d), 3.0, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=gpu)
+    moe.unpermute_router_bwd(D, to_dev(slot.astype(np.int32)), to_dev(dxp), to_dev(idx), to_dev(dl),
+                             to_dev(inp["wr"]), dx)
+    torch.cuda.synchronize()
+    ref_dxr, _ = oracle.router_bwd(np.zeros((T, d)), f64(inp["wr"], dtype), dl)
+    want = oracle.unpermute_bwd(f64(dxp, dtype)[:R], slot) + ref_dxr
+    assert max_row_rel_err(to_host(dx), want) <= TOL[dtype]
+    # renormalize = 0 gives a dense dlogits: refused
+    with pytest.raises(moe.MoeError):
+        moe.unpermute_router_bwd(_desc(T, d, 64, E, k, e0, NL, dtype, renorm=0), to_dev(slot.astype(np.int32)),
+                                 to_dev(dxp), to_dev(idx), to_dev(dl), to_dev(inp["wr"]), dx)
+
+
+# ---------------------------------------------------------------------------
 # A5 + A6: grouped SwiGLU MLP on a given routing
 # ---------------------------------------------------------------------------
 FFN_CASES = [
