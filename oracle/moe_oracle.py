@@ -46,7 +46,7 @@ import numpy as np
 __all__ = [
     "router_logits", "topk_route", "topk_route_grouped", "fp8_e4m3_decode", "fp8_e4m3_encode",
     "fp8_quantize_blocks", "fp8_dequantize_blocks", "fp8_quantize_blocks_pow2", "fp8_dequantize_blocks_pow2", "bf16_round", "count_tokens", "generate_indices", "permute",
-    "silu", "silu_grad", "expert_ffn_rows", "expert_ffn", "combine",
+    "silu", "silu_grad", "expert_ffn_rows", "expert_ffn", "expert_down", "combine",
     "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd", "unpermute_bwd",
     "route_bwd", "router_bwd", "layer_forward", "layer_backward",
 ]
@@ -381,6 +381,26 @@ def expert_ffn(x_perm, offsets, w1, w3, w2):
         if b > a:
             G[a:b], U[a:b], H[a:b], Y[a:b] = expert_ffn_rows(x_perm[a:b], w1[n], w3[n], w2[n])
     return G, U, H, Y
+
+
+def expert_down(h_perm, offsets, w2):
+    """The down projection of stage 4 alone: y_perm[r] = h_perm[r] W_down^T
+    with the weights of the expert whose segment holds row r.
+
+    [Aurora] Algorithm 1, stage 4 (mlp_out = mul_out W_down, one Grouped_mm
+    over the cum_token_counts segments); expert_ffn computes the same product
+    after gate/up and SwiGLU.  h_perm [R][f], w2 [NL][d][f]; returns [R][d].
+    """
+    h_perm = _f64(h_perm)
+    NL = len(offsets) - 1
+    R = int(offsets[NL])
+    d = np.asarray(w2).shape[1]
+    Y = np.zeros((R, d))
+    for n in range(NL):
+        a, b = int(offsets[n]), int(offsets[n + 1])
+        if b > a:
+            Y[a:b] = h_perm[a:b] @ _f64(w2[n]).T
+    return Y
 
 
 # --------------------------------------------------------------------------

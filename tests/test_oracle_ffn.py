@@ -4,7 +4,9 @@ Routes other than the oracle's own: a textbook triple-loop SwiGLU MLP, the
 identical-experts invariant (any routing reduces to the dense MLP because the
 renormalised weights sum to one), the expert-parallel partition identity
 (Algorithm 1 stage 5: the partial outputs of the ranks sum to the full
-output), zero down-projection, and closed forms of silu.
+output), zero down-projection, and closed forms of silu.  The down
+projection alone (expert_down) is pinned to the MLP's own output and to
+explicit loops.
 """
 import math
 
@@ -108,3 +110,24 @@ def test_silu_closed_forms():
     eps = 1e-6
     np.testing.assert_allclose(oracle.silu_grad(g), (oracle.silu(g + eps) - oracle.silu(g - eps)) / (2 * eps),
                                rtol=1e-7, atol=1e-9)
+
+
+def test_expert_down_alone_is_the_mlps_last_product():
+    # expert_down on the MLP's own H gives the MLP's y_perm; on tiny inputs it
+    # equals an explicit loop over rows, outputs and the inner dimension, with
+    # the right expert's weights for every segment (one empty).
+    rng = np.random.default_rng(21)
+    NL, d, f = 4, 6, 5
+    off = np.array([0, 3, 3, 7, 9])
+    x = rng.standard_normal((9, d))
+    w1, w3, w2 = (rng.standard_normal((NL, f, d)), rng.standard_normal((NL, f, d)),
+                  rng.standard_normal((NL, d, f)))
+    _, _, H, Y = oracle.expert_ffn(x, off, w1, w3, w2)
+    np.testing.assert_array_equal(oracle.expert_down(H, off, w2), Y)
+    h = rng.standard_normal((9, f))
+    got = oracle.expert_down(h, off, w2)
+    for n in range(NL):
+        for r in range(off[n], off[n + 1]):
+            for o in range(d):
+                want = sum(h[r][c] * w2[n][o][c] for c in range(f))
+                assert abs(got[r][o] - want) <= 1e-12 * (1 + abs(want))
