@@ -191,8 +191,9 @@ class Workload:
     """Device tensors and the ordered rows of one workload's step."""
 
     def __init__(self, moe, torch, cfg, inp, args, dev, fp8mm=False):
-        """fp8mm: gate/up on the FP8 matrix cores (forward only): W1/W3 held as
-        E4M3 codes with power-of-two block scales, x quantised each step."""
+        """fp8mm: gate/up and down on the FP8 matrix cores (forward only): W1,
+        W3 and W2 held as E4M3 codes with power-of-two block scales, x and h
+        quantised each step."""
         self.cfg = cfg
         T, d, f, E, k, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.num_local
 
@@ -273,8 +274,19 @@ class Workload:
                 lambda R: 4.0 * R * d * f,
                 lambda R: R * d + R * d // 128 + 2 * NL * f * d + 2 * NL * f * d // 128 + R * f * bb,
                 peak=PEAK_FP8_TFLOPS)
-            add("A6_down", lambda: moe.expert_down(D, b.offsets, b.h, g["w2"], b.y_perm), 1,
-                lambda R: 2.0 * R * d * f, lambda R: R * f * bb + NL * f * d * bb + R * d * bb)
+            # down on the FP8 matrix cores too: W2 quantised once by rows of f, h each step
+            S8 = moe.fp8_scale_row_bytes(f)
+            w2q = torch.empty(NL * d, f, dtype=torch.uint8, device=dev)
+            w2e = torch.empty(NL * d, S8, dtype=torch.uint8, device=dev)
+            moe.fp8_quantize_pow2_rows(g["w2"].view(NL * d, f), w2q, w2e)
+            Rc = D.R_cap
+            hq = torch.empty(Rc, f, dtype=torch.uint8, device=dev)
+            he = torch.empty(Rc, S8, dtype=torch.uint8, device=dev)
+            add("A6_quant_h", lambda: moe.fp8_quantize_pow2_rows(b.h, hq, he, b.offsets[NL:]), 1,
+                nbytes=lambda R: R * f * (bb + 1) + R * S8)
+            add("A6_down", lambda: moe.expert_down_fp8mm(D, b.offsets, hq, he, w2q, w2e, b.y_perm), 1,
+                lambda R: 2.0 * R * d * f, lambda R: R * f + R * S8 + NL * f * d + NL * d * S8 + R * d * bb,
+                peak=PEAK_FP8_TFLOPS)
         elif args.fp8_gemm:
             add("A5_gate_up", lambda: moe.expert_gate_up_fp8(
                 D, b.offsets, b.row_token if gather else None, g["x"] if gather else b.x_perm,
@@ -521,8 +533,8 @@ def main():
         sm = summarize(w2, a2, s2, wall2, args.extra_steps, False)
         extras[name] = {
             "workload": f"{base}: T={c.T} d={c.d} E={c.E} ({c.num_local} local) top-{c.k} f={c.f} fwd, "
-                        f"routing {c.routing}" + (", gate/up on the fp8 matrix cores (e4m3 x and W1/W3 with "
-                                                  "power-of-two block-128 scales)" if fp8mm else ""),
+                        f"routing {c.routing}" + (", gate/up and down on the fp8 matrix cores (e4m3 x, h and "
+                                                  "W1/W3/W2 with power-of-two block-128 scales)" if fp8mm else ""),
             "steps": args.extra_steps, "ms_per_step": round(sm["ms_per_step"], 4),
             "tokens/s": round(c.T / sm["ms_per_step"] * 1e3, 1), "routed_rows": sm["R"],
             "grouped_gemm_tflops": round(sm["gemm_tflops"], 1),

@@ -404,6 +404,19 @@ int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w
 int moe_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t* q, uint8_t* e8,
                           void* stream);
 
+/* moe_fp8_quantize_pow2 by rows, with the scales in rows of their own pitch
+ * (the layout the FP8 matrix-core GEMMs read):
+ *   w [rows][cols] (MOE_BF16 or MOE_F32), cols a multiple of 128; q
+ *   [rows][cols] codes; e8 [rows][e8_ld] E8M0 bytes, block j of row r at
+ *   e8[r * e8_ld + j], the bytes past cols/128 set to zero; e8_ld from
+ *   cols/128 to cols/128 + 15.  nrows (device int32, or NULL): rows at or
+ *   past *nrows are left alone (e.g. offsets + NL: the routed rows of a
+ *   [R_cap] buffer).  Errors: MOE_ERR_INVALID_ARG for a NULL pointer, w or q
+ *   not 16-byte aligned, nrows not 4-byte aligned, or sizes outside these
+ *   rules; MOE_ERR_UNSUPPORTED for another dtype. */
+int moe_fp8_quantize_pow2_rows(const void* w, int dtype, int64_t rows, int64_t cols, const int32_t* nrows,
+                               uint8_t* q, uint8_t* e8, int64_t e8_ld, void* stream);
+
 /* A5 and A6 on FP8 weights (the page's further step: the expert GEMMs take
  * the FP8 weights directly).  The weight tiles move as E4M3 codes - half the
  * bytes of bf16 - and are decoded to bf16 in the kernel where the MFMA
@@ -437,6 +450,19 @@ int moe_expert_gate_up_fp8mm(const moe_desc* desc, const int32_t* offsets, const
                              const uint8_t* xq, const uint8_t* xs, const uint8_t* W1q,
                              const uint8_t* W1s, const uint8_t* W3q, const uint8_t* W3s, void* gu,
                              void* h, void* stream);
+
+/* A6 on the FP8 matrix cores (same passage): y_perm = h W2^T with h and W2
+ * both E4M3 codes with power-of-two block scales along f, each 32 x 32 x 64
+ * product applying the row's and the column's scale, float32 sums:
+ *   y_perm[r][n] = sum over k of (hq * 2^hs)[r][k] (W2q * 2^ws)[g][n][k] for
+ *   row r of expert g's segment (offsets, as moe_expert_down).
+ *   hq [R_cap][f] codes and hs [R_cap][S] E8M0 bytes; W2q [NL][d][f] codes
+ *   and W2s [NL][d][S] bytes, with S = f/128 rounded up to a multiple of 4
+ *   (moe_fp8_quantize_pow2_rows with e8_ld = S writes both); y_perm
+ *   [R_cap][d] bf16.  MOE_ERR_UNSUPPORTED unless dtype is bf16, f is a
+ *   multiple of 128 and R_cap * f < 2^31. */
+int moe_expert_down_fp8mm(const moe_desc* desc, const int32_t* offsets, const uint8_t* hq, const uint8_t* hs,
+                          const uint8_t* W2q, const uint8_t* W2s, void* y_perm, void* stream);
 
 /* Measurement aid (Domyn page, section "Dynamic tile scheduling in
  * SonicMoE": the two tile orders are compared with and without a dummy

@@ -17,7 +17,7 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8", "fp8_quantize_pow2", "expert_gate_up_fp8mm",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8", "fp8_quantize_pow2", "expert_gate_up_fp8mm", "fp8_quantize_pow2_rows", "expert_down_fp8mm", "fp8_scale_row_bytes",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine_bwd_gather", "expert_bwd_dh_gather", "expert_bwd_dw_down_gather", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
     "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
@@ -82,6 +82,7 @@ _SIGS = {
     "moe_expert_gate_up_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_down_fp8": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_gate_up_fp8mm": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_down_fp8mm": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_ffn_bwd_dw_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dh": [_vp, _vp, _vp, _vp, _vp, _vp],
@@ -102,7 +103,8 @@ _SIGS = {
     "moe_unpermute_router_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
 }
 EXPORTS = sorted(list(_SIGS) + ["moe_workspace_size", "moe_status_str", "moe_last_error", "moe_hold_cus",
-                                 "moe_fp8_quantize", "moe_fp8_dequantize", "moe_fp8_quantize_pow2"])
+                                 "moe_fp8_quantize", "moe_fp8_dequantize", "moe_fp8_quantize_pow2",
+                                 "moe_fp8_quantize_pow2_rows"])
 
 _lib = None
 
@@ -127,6 +129,9 @@ def lib():
         l.moe_fp8_dequantize.argtypes = [_vp, _vp, ctypes.c_int64, _vp, _vp]
         l.moe_fp8_quantize_pow2.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp]
         l.moe_fp8_quantize_pow2.restype = ctypes.c_int
+        l.moe_fp8_quantize_pow2_rows.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp,
+                                                 ctypes.c_int64, _vp]
+        l.moe_fp8_quantize_pow2_rows.restype = ctypes.c_int
         l.moe_fp8_dequantize.restype = ctypes.c_int
         l.moe_hold_cus.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
         l.moe_hold_cus.restype = ctypes.c_int
@@ -223,6 +228,31 @@ def fp8_quantize_pow2(w, q, e8):
     rc = lib().moe_fp8_quantize_pow2(w.data_ptr(), dt, w.numel(), q.data_ptr(), e8.data_ptr(), _stream())
     if rc != MOE_OK:
         raise MoeError("moe_fp8_quantize_pow2", rc)
+
+
+def fp8_scale_row_bytes(n):
+    """Bytes per row of E8M0 block scales for rows of n codes, as the FP8 GEMMs read them."""
+    return (n // 128 + 3) // 4 * 4
+
+
+def fp8_quantize_pow2_rows(w, q, e8, nrows=None):
+    """fp8_quantize_pow2 by rows of w [rows][cols]: codes q [rows][cols] and
+    scales e8 [rows][e8_ld] (e8_ld = e8's row length, the bytes past cols/128
+    zero); rows at or past the device int32 nrows (if given) are left alone."""
+    dt = MOE_BF16 if w.dtype == torch.bfloat16 else MOE_F32
+    for t in (w, q, e8):
+        if not t.is_contiguous():
+            raise ValueError("libmoe needs contiguous tensors")
+    rows, cols = w.shape
+    rc = lib().moe_fp8_quantize_pow2_rows(w.data_ptr(), dt, rows, cols, None if nrows is None else nrows.data_ptr(),
+                                          q.data_ptr(), e8.data_ptr(), e8.shape[-1], _stream())
+    if rc != MOE_OK:
+        raise MoeError("moe_fp8_quantize_pow2_rows", rc)
+
+
+def expert_down_fp8mm(desc, offsets, hq, hs, w2q, w2s, y_perm):
+    """down on the FP8 matrix cores: h and W2 as codes with E8M0 block scales in rows of fp8_scale_row_bytes(f)."""
+    _call("moe_expert_down_fp8mm", desc, offsets, hq, hs, w2q, w2s, y_perm, _stream())
 
 
 def expert_gate_up_fp8mm(desc, offsets, row_token, xq, xs, w1q, w1s, w3q, w3s, gu, h):

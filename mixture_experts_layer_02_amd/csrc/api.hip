@@ -1,6 +1,7 @@
 // The extern "C" entry points of libmoe.so (declared in include/moe.h):
 // argument validation on the host, then the kernel launches of each step.
 #include <stdio.h>
+#include <algorithm>
 #include <string.h>
 
 #include "internal.h"
@@ -353,6 +354,15 @@ int moe_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t* q, uint8
   return finish(moe::launch_fp8_quantize_pow2(w, dtype, n, q, e8, S(stream)));
 }
 
+int moe_fp8_quantize_pow2_rows(const void* w, int dtype, int64_t rows, int64_t cols, const int32_t* nrows,
+                               uint8_t* q, uint8_t* e8, int64_t e8_ld, void* stream) {
+  if (!need(w) || !need(q) || !e8 || (reinterpret_cast<uintptr_t>(nrows) & 3u) || rows < 0 || cols < 128 || cols % 128 ||
+      e8_ld < cols / 128 || e8_ld > cols / 128 + 15)
+    return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_fp8_quantize_pow2_rows(w, dtype, rows, cols, nrows, q, e8, e8_ld, S(stream)));
+}
+
 int moe_fp8_dequantize(const uint8_t* q, const float* scales, int64_t n, void* w, void* stream) {
   if (!need(w) || !need(q) || !need(scales) || n < 0 || n % 128) return MOE_ERR_INVALID_ARG;
   return finish(moe::launch_fp8_dequantize(q, scales, n, w, S(stream)));
@@ -396,6 +406,18 @@ int moe_expert_gate_up_fp8mm(const moe_desc* desc, const int32_t* offsets, const
   if (desc->dtype != MOE_BF16 || desc->d % 512 || (int64_t)desc->T * desc->d >= (1ll << 31))
     return MOE_ERR_UNSUPPORTED;
   return finish(moe::launch_gate_up_f8(*desc, offsets, row_token, xq, xs, W1q, W1s, W3q, W3s, gu, h, S(stream)));
+}
+
+int moe_expert_down_fp8mm(const moe_desc* desc, const int32_t* offsets, const uint8_t* hq, const uint8_t* hs,
+                          const uint8_t* W2q, const uint8_t* W2s, void* y_perm, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(offsets) || !need(hq) || !need(hs) || !need(W2q) || !need(W2s) || !need(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  // bf16 output; f in whole 128-code blocks; h's codes addressed in 32 bits
+  const int64_t rc_rows = (int64_t)desc->T * std::min(desc->k, desc->num_local);
+  if (desc->dtype != MOE_BF16 || desc->f % 128 || rc_rows * desc->f >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  return finish(moe::launch_down_f8(*desc, offsets, hq, hs, W2q, W2s, y_perm, S(stream)));
 }
 
 int moe_hold_cus(int workgroups, int lds_bytes, int microseconds, void* stream) {

@@ -327,6 +327,31 @@ hipError_t launch_gate_up_f8(const moe_desc& d, const int32_t* offsets, const in
       p, mtiles_ub(d, MT) * cdiv(d.f, MT / 2), s);
 }
 
+// y_perm = h W2^T on the FP8 matrix cores: h [R_cap][f] and W2 [NL][d][f]
+// as E4M3 codes, their power-of-two block scales in rows of sb bytes (f/128
+// rounded up to a multiple of 4).
+hipError_t launch_down_f8(const moe_desc& d, const int32_t* offsets, const uint8_t* hq, const uint8_t* hs,
+                          const uint8_t* W2q, const uint8_t* W2s, void* y_perm, hipStream_t s) {
+  GemmParams p = blank(d);
+  p.A = hq;
+  p.lda = d.f / 2;
+  p.gather_rows = (int)r_cap(d);  // (the rows of A's scale array)
+  p.B = W2q;
+  p.ldb = d.f / 2;
+  p.b_gstride = (int64_t)d.d * d.f / 2;
+  p.a_scale = hs;
+  p.b_scale = W2s;
+  p.sbytes = fp8_scale_row_bytes(d.f);
+  p.C = y_perm;
+  p.ldc = d.d;
+  p.offsets = offsets;
+  p.ngroups = d.num_local;
+  p.N = d.d;
+  p.K = d.f / 2;
+  return run_bf16<LAY_K, LAY_K, uint16_t, GRP_M, EPI_STORE, false, GATH_NONE, false, true>(
+      p, mtiles_ub(d, MT) * cdiv(d.d, MT), s);
+}
+
 hipError_t launch_down_q8(const moe_desc& d, const int32_t* offsets, const void* h, const uint8_t* W2q,
                           const float* s2, void* y_perm, hipStream_t s) {
   GemmParams q = blank(d);

@@ -77,36 +77,64 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(const T* __restrict__ w,
 // applies): e = the least integer with amax <= 448 * 2^e, from amax = f 2^x
 // (f in [0.5, 1)): x - 9 when f <= 0.875, else x - 8; each value w * 2^-e
 // (exact) is cast; the scale leaves as its E8M0 byte e + 127.  An all-zero
-// block gets e = 0.
+// block gets e = 0.  One block per 16-lane group: src and dst its values and
+// codes; returns the scale byte (in every lane of the group).
+template <typename T>
+__device__ __forceinline__ uint8_t quant_pow2_block(const T* src, uint8_t* dst, int sub) {
+  float v[8];
+  load8(src + sub * 8, v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  int x = 0;
+  const float f = frexpf(amax, &x);
+  const int e = amax > 0.f ? (f <= 0.875f ? x - 9 : x - 8) : 0;
+  uint32_t c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = ldexpf(v[4 * h + i], -e);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+    c[h] = (uint32_t)r;
+  }
+  const u32x2 out = {c[0], c[1]};
+  *reinterpret_cast<u32x2*>(dst + sub * 8) = out;
+  return (uint8_t)(e + 127);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) fp8_quant_pow2_kernel(const T* __restrict__ w, int64_t nblk,
                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
   const int sub = threadIdx.x & 15;
   for (int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; blk < nblk;
        blk += ((int64_t)gridDim.x * 256) >> 4) {
-    float v[8];
-    load8(w + blk * 128 + sub * 8, v);
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-    int x = 0;
-    const float f = frexpf(amax, &x);
-    const int e = amax > 0.f ? (f <= 0.875f ? x - 9 : x - 8) : 0;
-    uint32_t c[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = ldexpf(v[4 * h + i], -e);
-      int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
-      c[h] = (uint32_t)r;
-    }
-    const u32x2 out = {c[0], c[1]};
-    *reinterpret_cast<u32x2*>(q + blk * 128 + sub * 8) = out;
-    if (sub == 0) e8[blk] = (uint8_t)(e + 127);
+    const uint8_t b = quant_pow2_block(w + blk * 128, q + blk * 128, sub);
+    if (sub == 0) e8[blk] = b;
+  }
+}
+
+// By rows: w [rows][cols], codes [rows][cols], scales [rows][e8_ld] (the
+// bytes past cols/128 set to zero); rows at or past *nrows (if given) are
+// left alone.
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_quant_pow2_rows_kernel(const T* __restrict__ w, int64_t rows, int64_t cols,
+                                                                  const int32_t* __restrict__ nrows,
+                                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ e8,
+                                                                  int64_t e8_ld) {
+  const int sub = threadIdx.x & 15;
+  const int64_t cb = cols / 128;
+  const int64_t lim = nrows ? min(rows, (int64_t)*nrows) : rows;
+  const int64_t nblk = lim * cb;
+  for (int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; blk < nblk;
+       blk += ((int64_t)gridDim.x * 256) >> 4) {
+    const int64_t r = blk / cb, j = blk - r * cb;
+    const uint8_t b = quant_pow2_block(w + r * cols + j * 128, q + r * cols + j * 128, sub);
+    if (sub == 0) e8[r * e8_ld + j] = b;
+    if (j == cb - 1 && sub > 0 && cb + sub - 1 < e8_ld) e8[r * e8_ld + cb + sub - 1] = 0;
   }
 }
 
@@ -156,6 +184,20 @@ hipError_t launch_fp8_quantize_pow2(const void* w, int dtype, int64_t n, uint8_t
   else
     fp8_quant_pow2_kernel<float><<<(unsigned)grid_for(nblk), 256, 0, s>>>(reinterpret_cast<const float*>(w), nblk, q,
                                                                            e8);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_pow2_rows(const void* w, int dtype, int64_t rows, int64_t cols, const int32_t* nrows,
+                                         uint8_t* q, uint8_t* e8, int64_t e8_ld, hipStream_t s) {
+  const int64_t nblk = rows * (cols / 128);
+  if (nblk == 0) return hipSuccess;
+  const unsigned g = (unsigned)grid_for(nblk);
+  if (dtype == MOE_BF16)
+    fp8_quant_pow2_rows_kernel<uint16_t><<<g, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w), rows, cols, nrows, q,
+                                                           e8, e8_ld);
+  else
+    fp8_quant_pow2_rows_kernel<float><<<g, 256, 0, s>>>(reinterpret_cast<const float*>(w), rows, cols, nrows, q, e8,
+                                                        e8_ld);
   return hipGetLastError();
 }
 

@@ -255,8 +255,9 @@ __device__ __forceinline__ void wait_stages(int later) {
 // block: each k-step is one v_mfma_scale_f32_32x32x64_f8f6f4 per 32 x 32
 // block, which applies the row's A and the column's B scale itself.  The
 // scale bytes of a k-tile's rows come with its operand tiles: one dword per
-// row (the four blocks k-tile & ~3 .. | 3) into a 2 KB area of the stage.
-// A is read through row_token (GATH_A).
+// row (the four blocks k-tile & ~3 .. | 3) into a 2 KB area of the stage,
+// so sbytes is a multiple of 4 (a row's scales padded when K/128 is not).
+// A is read through row_token (GATH_A) or in place (GATH_NONE).
 template <int BK, int STAGES, int ALAY, int BLAY, int GRP, int EPI, bool DUAL, bool CF32, bool DYN, int GATH,
           bool BQ8, bool F8 = false>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
@@ -269,8 +270,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   static_assert(!BQ8 || (BLAY == LAY_K && GRP == GRP_M && (GATH == GATH_NONE || GATH == GATH_A) && BK == 64),
                 "FP8 B: K-contiguous B of GRP_M, 64-wide k-tiles (half a scale block)");
   static_assert(BK == 64 && STAGES == 2, "ring of two 64-wide k-tiles");
-  static_assert(!F8 || (ALAY == LAY_K && BLAY == LAY_K && GRP == GRP_M && !BQ8 && GATH == GATH_A),
-                "FP8 matrix cores: K-contiguous A (read through row_token) and B of GRP_M");
+  static_assert(!F8 || (ALAY == LAY_K && BLAY == LAY_K && GRP == GRP_M && !BQ8 &&
+                        (GATH == GATH_A || GATH == GATH_NONE)),
+                "FP8 matrix cores: K-contiguous A (in place or read through row_token) and B of GRP_M");
   // GKB: the k-rows of an MN-contiguous operand of a grouped-K product are
   // gathered (B for GATH_B, A for GATH_AK), through a ring of token copies.
   constexpr bool GKB = GATH == GATH_B || GATH == GATH_AK;
@@ -350,6 +352,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     int pfe;
     i32x4 rs;  // BQ8: the scales of the tile's B rows (of the second B for waves 2 and 3 with dual B)
     uint32_t sbo;    // F8: the lane's B-row scale offset (bit 31 set past the tile's valid rows)
+    uint32_t sao;    // F8, A in place: the lane's A-row scale offset (bit 31 set past the valid rows)
   };
   // GATH_A: the A offsets of the current and the next tile's rows (filled
   // from their tokens once these are in LDS).
@@ -455,6 +458,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     if (F8) {  // B row (64 wave + lane) mod the rows of one B is row g N + n0 + r of its scale array
       const int r = (wave * 64 + lane) & (DUAL ? 127 : 255);
       L.sbo = ((uint32_t)((int64_t)t.g * p.N + t.n0 + r) * (uint32_t)p.sbytes) | (r < nlim_b ? 0u : 0x80000000u);
+      // A in place: tile row 64 wave + lane is A row m0 + that (read through
+      // row_token instead, its offset comes from the tile's tokens)
+      const int ra = wave * 64 + lane;
+      L.sao = GATH == GATH_NONE ? ((uint32_t)(t.m0 + ra) * (uint32_t)p.sbytes) | (ra < t.mlim ? 0u : 0x80000000u)
+                                : 0x80000000u;
     }
     if (GATH == GATH_B) {
       const int e = t.mtile % cB + cB * (wave * 64 + lane);
@@ -471,7 +479,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   };
   Ld null_ld;  // loads nothing: every offset is outside its resources
   null_ld.ra = null_ld.rb = null_ld.rb2 = null_ld.rt = null_ld.rs = make_rsrc(Ag, 0);
-  null_ld.sbo = 0x80000000u;
+  null_ld.sbo = null_ld.sao = 0x80000000u;
   null_ld.nk = 0;
   null_ld.pa = null_ld.pb = 0x7FFFFFF0u;
   null_ld.glim = 0;
@@ -618,7 +626,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     L.pb = c ? cur.pb : nxt.pb;
     L.nk = 0;
     if (BQ8) L.rs = c ? cur.rs : nxt.rs;
-    if (F8) L.sbo = c ? cur.sbo : nxt.sbo;
+    if (F8) {
+      L.sbo = c ? cur.sbo : nxt.sbo;
+      L.sao = c ? cur.sao : nxt.sao;
+    }
     if (GATH != 0) {
       L.rt = c ? cur.rt : nxt.rt;
       L.glim = c ? cur.glim : nxt.glim;
@@ -672,7 +683,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       // (always five wait states: the compiler spills these resources to
       // vector lanes and may reload one just before its use)
       const uint32_t so = (uint32_t)(k >> 2) * 4u;
-      if (q == 2 * NJ) touch4u<false>(rsa, a_gs(pos, pure_c), so, stb + SCA + wave * 256);
+      if (q == 2 * NJ) touch4u<false>(rsa, GATH == GATH_A ? a_gs(pos, pure_c) : L.sao, so, stb + SCA + wave * 256);
       else touch4u<false>(rsb, L.sbo, so, stb + SCB + wave * 256);
       return;
     }

@@ -13,6 +13,13 @@ hipError_t launch_gate_up_q8(const moe_desc& d, const int32_t* offsets, const vo
 hipError_t launch_gate_up_f8(const moe_desc& d, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
                              const uint8_t* xs, const uint8_t* W1q, const uint8_t* W1s, const uint8_t* W3q,
                              const uint8_t* W3s, void* gu, void* h, hipStream_t s);
+hipError_t launch_down_f8(const moe_desc& d, const int32_t* offsets, const uint8_t* hq, const uint8_t* hs,
+                          const uint8_t* W2q, const uint8_t* W2s, void* y_perm, hipStream_t s);
+// Bytes per row of power-of-two block scales for rows of n codes, as the FP8
+// GEMMs read them: n/128, rounded up to a multiple of 4.
+inline int fp8_scale_row_bytes(int64_t n) { return (int)(((n / 128) + 3) / 4 * 4); }
+hipError_t launch_fp8_quantize_pow2_rows(const void* w, int dtype, int64_t rows, int64_t cols, const int32_t* nrows,
+                                         uint8_t* q, uint8_t* e8, int64_t e8_ld, hipStream_t s);
 hipError_t launch_down_q8(const moe_desc& d, const int32_t* offsets, const void* h, const uint8_t* W2q,
                           const float* s2, void* y_perm, hipStream_t s);
 hipError_t launch_fp8_quantize(const void* w, int dtype, int64_t n, uint8_t* q, float* scales, hipStream_t s);

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 36
+    assert len(names) == 38
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n
@@ -191,3 +191,19 @@ def test_unpermute_router_bwd_rejects_dense_dlogits_and_nulls():
     d = _d()
     assert l.moe_unpermute_router_bwd(ctypes.byref(d), g, g, None, g, g, g, None) == moe.MOE_ERR_INVALID_ARG
     assert l.moe_unpermute_router_bwd(ctypes.byref(d), g, g, g, g, None, g, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_row_quantise_and_down_reject_bad_arguments():
+    l = moe.lib()
+    g = 1 << 20
+    # cols not a multiple of 128; a scale pitch below cols/128 or above it + 15; nrows misaligned
+    assert l.moe_fp8_quantize_pow2_rows(g, moe.MOE_BF16, 4, 200, None, g, g, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_fp8_quantize_pow2_rows(g, moe.MOE_BF16, 4, 256, None, g, g, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_fp8_quantize_pow2_rows(g, moe.MOE_BF16, 4, 256, None, g, g, 18, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_fp8_quantize_pow2_rows(g, moe.MOE_BF16, 4, 256, g + 2, g, g, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_fp8_quantize_pow2_rows(g, 7, 4, 256, None, g, g, 2, None) == moe.MOE_ERR_UNSUPPORTED
+    # the down product: bf16 only, f in whole 128-code blocks
+    assert l.moe_expert_down_fp8mm(ctypes.byref(_d(f=192)), g, g, g, g, g, g, None) == moe.MOE_ERR_UNSUPPORTED
+    assert l.moe_expert_down_fp8mm(ctypes.byref(_d(f=128, dtype=moe.MOE_F32)), g, g, g, g, g, g,
+                                   None) == moe.MOE_ERR_UNSUPPORTED
+    assert l.moe_expert_down_fp8mm(ctypes.byref(_d(f=128)), g, None, g, g, g, g, None) == moe.MOE_ERR_INVALID_ARG

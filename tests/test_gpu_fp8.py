@@ -340,3 +340,126 @@ def test_fp8mm_gate_up_at_full_size_sampled(gpu):
             G, U, H, _ = oracle.expert_ffn_rows(xr[None, :], deq_w[n][0], deq_w[n][1], np.zeros((d, f)))
             want.append(H[0])
     assert max_row_rel_err(hg, np.array(want)) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# A6 on the FP8 matrix cores: h and W2 quantised by rows, scales in rows of
+# fp8_scale_row_bytes(f) bytes (f/128 rounded up to a multiple of 4).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,ld,nrows", [(1, 128, 4, None), (37, 1792, 16, 20), (300, 640, 5, None),
+                                                (64, 6144, 48, 64), (50, 256, 17, 0), (129, 384, 3, 129)])
+def test_quantize_pow2_rows_matches_the_oracle(gpu, dtype, rows, cols, ld, nrows):
+    rng = np.random.default_rng(rows + cols)
+    w = (rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-4, 2, (rows, 1))).astype(np.float32)
+    w[0, :128] = 0.0                                         # a zero block
+    w = synth.as_f32(synth.f32_to_bf16_bits(w), "bf16") if dtype == "bf16" else w
+    wd = to_dev(w, dtype)
+    q = torch.full((rows, cols), 0xAB, dtype=torch.uint8, device=gpu)
+    e8 = torch.full((rows, ld), 0xCD, dtype=torch.uint8, device=gpu)
+    nr = None if nrows is None else torch.tensor([nrows], dtype=torch.int32, device=gpu)
+    moe.fp8_quantize_pow2_rows(wd, q, e8, nr)
+    torch.cuda.synchronize()
+    lim = rows if nrows is None else min(rows, nrows)
+    c, e = oracle.fp8_quantize_blocks_pow2(w[:lim])
+    qh, eh = q.cpu().numpy(), e8.cpu().numpy()
+    cb = cols // 128
+    np.testing.assert_array_equal(qh[:lim].reshape(-1), c)
+    np.testing.assert_array_equal(eh[:lim, :cb].reshape(-1), e)
+    assert (eh[:lim, cb:] == 0).all()                        # the padding
+    assert (qh[lim:] == 0xAB).all() and (eh[lim:] == 0xCD).all()   # rows past nrows untouched
+
+
+def test_quantize_pow2_rows_rejects_bad_pitches(gpu):
+    w = torch.zeros(4, 256, dtype=torch.bfloat16, device=gpu)
+    q = torch.empty(4, 256, dtype=torch.uint8, device=gpu)
+    for ld in (1, 18):                                       # below cols/128, above cols/128 + 15
+        with pytest.raises(moe.MoeError):
+            moe.fp8_quantize_pow2_rows(w, q, torch.empty(4, ld, dtype=torch.uint8, device=gpu))
+
+
+def _down_case(cfg, gpu, dyn, seed):
+    T, d, f, E, k, e0, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local
+    inp = synth.make_inputs(cfg, want=("w2",))
+    idx = random_routing(np.random.default_rng(seed), T, E, k, skew=1.0)
+    D = moe.make_desc(T, d, f, E, k, e0, NL, "bf16", 1, tile_counters=moe.new_tile_counters(gpu) if dyn else None)
+    b = moe.Buffers(D, gather=True)
+    moe.permute(D, to_dev(idx), None, b.counts, b.offsets, b.row_token, b.slot_row, None, b.ws_permute)
+    _, off = oracle.count_tokens(idx, E, e0, NL)
+    R = int(off[-1])
+    # h: seeded bf16 rows, like the SwiGLU outputs in scale; rows past R stay
+    # garbage and are left alone by the row quantiser
+    h = synth.as_f32(synth.f32_to_bf16_bits(synth.normal_f32(seed, 7, (max(R, 1), f), 0.5)), "bf16")
+    hd = torch.full((D.R_cap, f), float("nan"), dtype=torch.bfloat16, device=gpu)
+    hd[:R] = to_dev(h[:R], "bf16")
+    S8 = moe.fp8_scale_row_bytes(f)
+    hq = torch.empty(D.R_cap, f, dtype=torch.uint8, device=gpu)
+    hs = torch.empty(D.R_cap, S8, dtype=torch.uint8, device=gpu)
+    moe.fp8_quantize_pow2_rows(hd, hq, hs, b.offsets[NL:])
+    w2d = to_dev(inp["w2"])
+    w2q = torch.empty(NL * d, f, dtype=torch.uint8, device=gpu)
+    w2s = torch.empty(NL * d, S8, dtype=torch.uint8, device=gpu)
+    moe.fp8_quantize_pow2_rows(w2d.view(NL * d, f), w2q, w2s)
+    y = torch.empty(D.R_cap, d, dtype=torch.bfloat16, device=gpu)
+    moe.expert_down_fp8mm(D, b.offsets, hq, hs, w2q, w2s, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(b.offsets), off)
+    return inp, h[:R], off, R, (hq, hs, w2q, w2s), y
+
+
+@pytest.mark.parametrize("dyn", [False, True])
+@pytest.mark.parametrize("scale", [
+    dict(T=512, d=256, f=128, E=32, num_local=8, expert_begin=8),
+    dict(T=700, d=384, f=1792, E=16, num_local=16, expert_begin=0),      # 14 scale blocks per row: padded to 16
+    dict(T=1500, d=320, f=640, E=64, num_local=24, expert_begin=40, k=6),  # ragged, empty experts
+])
+def test_fp8mm_down_matches_the_oracle(gpu, scale, dyn):
+    # h and W2 quantised on the GPU (codes and scales checked bit-exact
+    # against the oracle's), then y_perm against the oracle's down projection
+    # on its own dequantised h and W2.
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[fp8mm down] {scale} dynamic={dyn}", flush=True)
+    d, f, NL = cfg.d, cfg.f, cfg.num_local
+    inp, h, off, R, (hq, hs, w2q, w2s), y = _down_case(cfg, gpu, dyn, cfg.T + f)
+    cb = f // 128
+    ch, eh = oracle.fp8_quantize_blocks_pow2(h)
+    np.testing.assert_array_equal(hq[:R].cpu().numpy().reshape(-1), ch)
+    np.testing.assert_array_equal(hs[:R, :cb].cpu().numpy().reshape(-1), eh)
+    w2 = synth.as_f32(inp["w2"], "bf16")
+    cw, ew = oracle.fp8_quantize_blocks_pow2(w2)
+    np.testing.assert_array_equal(w2q.cpu().numpy().reshape(-1), cw)
+    np.testing.assert_array_equal(w2s[:, :cb].cpu().numpy().reshape(-1), ew)
+    hdq = oracle.fp8_dequantize_blocks_pow2(ch, eh).reshape(R, f)
+    w2dq = oracle.fp8_dequantize_blocks_pow2(cw, ew).reshape(NL, d, f)
+    want = oracle.expert_down(hdq, off, w2dq)
+    assert max_row_rel_err(to_host(y)[:R], want) <= TOL["bf16"]
+
+
+def test_fp8mm_down_rejects_unsupported_shapes(gpu):
+    z = torch.zeros(1 << 16, dtype=torch.float32, device=gpu)
+    D = _desc(64, 256, 192, 8, 2, 0, 8, "bf16")                 # f not a multiple of 128
+    with pytest.raises(moe.MoeError):
+        moe.expert_down_fp8mm(D, z, z, z, z, z, z)
+    D = _desc(64, 256, 128, 8, 2, 0, 8, "f32")
+    with pytest.raises(moe.MoeError):
+        moe.expert_down_fp8mm(D, z, z, z, z, z, z)
+
+
+def test_fp8mm_down_at_full_size_sampled(gpu):
+    # The 1T share (T = 8192, d = 6144, 96 of 384 experts, f = 1792) in the
+    # benchmark's launch configuration; the oracle quantises and multiplies
+    # only what the sampled rows need (their h rows and their experts' W2).
+    cfg = synth.CONFIGS["share_1t"]
+    d, f, E, k, e0, NL = cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local
+    print(f"[fp8mm down full size] T={cfg.T} d={d} f={f} E={E} NL={NL}", flush=True)
+    inp, h, off, R, (hq, hs, w2q, w2s), y = _down_case(cfg, gpu, False, 3)
+    rs = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(6).choice(R, 6, replace=False)]))
+    seg = np.searchsorted(off, rs, side="right") - 1
+    want = []
+    for r, n in zip(rs, seg):
+        hr = oracle.fp8_dequantize_blocks_pow2(*oracle.fp8_quantize_blocks_pow2(h[r]))
+        w2n = synth.as_f32(inp["w2"][n], "bf16")
+        wn = oracle.fp8_dequantize_blocks_pow2(*oracle.fp8_quantize_blocks_pow2(w2n)).reshape(d, f)
+        want.append(oracle.expert_down(hr[None, :], np.array([0, 1]), wn[None])[0])
+    got = to_host(y[torch.as_tensor(rs, device=y.device)])
+    assert max_row_rel_err(got, np.array(want)) <= TOL["bf16"]
