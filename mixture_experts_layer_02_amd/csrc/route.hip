@@ -107,24 +107,30 @@ __device__ __forceinline__ void topk_token(const float (&v)[MAXV], int lane, int
                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                            int32_t* s_idx, float* s_val) {
   // Threshold selection.  theta = the k-th largest of the lanes' maximum keys
-  // (a binary search over the key bits, counting lanes with ballots): at
-  // least k elements have key >= theta, so every one of the k selections
-  // does, and the candidates (key >= theta) are usually few.  They are
-  // compacted through LDS, and a candidate's slot is the number of
+  // (a binary search over the key bits, counting lanes with ballots), or a
+  // key below it: at least k elements have key >= theta, so every one of the
+  // k selections does, and the candidates (key >= theta) are usually few.
+  // They are compacted through LDS, and a candidate's slot is the number of
   // candidates that come before it in the order (logit descending, expert
   // ascending).  With more than 64 candidates (heavy ties) the wave takes
-  // the k rounds instead.  Only the lane maxima need keys: theta is one of
-  // them, the k-th largest, so key >= theta is the float comparison
-  // v >= key_float(theta), under which -0.0 and +0.0 are equal too.
+  // the k rounds instead.  Only the lane maxima need keys: theta is the key
+  // of a float, so key >= theta is the float comparison v >= key_float(theta),
+  // under which -0.0 and +0.0 are equal too.
   float vmax = v[0];
 #pragma unroll
   for (int i = 1; i < MAXV; ++i) vmax = fmaxf(vmax, v[i]);
   const uint32_t kmax = lane < E ? order_key(vmax) : 0u;  // a lane holds an expert iff lane < E
+  // The search runs over the top 16 key bits only: theta is then the k-th
+  // largest lane maximum with its low 16 bits cleared, still at or below it,
+  // so the candidates still hold every selection; values within 2^-7 of it
+  // add the odd extra candidate.  (A theta below the key of -infinity would
+  // name a NaN; it is raised to that key, and every element is a candidate.)
   uint32_t theta = 0;
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= 16; --b) {
     const uint32_t c = theta | (1u << b);
     if ((int)__popcll(__ballot(kmax >= c)) >= k) theta = c;
   }
+  if (theta < 0x00800000u) theta = 0x007FFFFFu;
   const float thf = key_float(theta);
   uint64_t m[MAXV];
   int cnt = 0;
@@ -140,7 +146,7 @@ __device__ __forceinline__ void topk_token(const float (&v)[MAXV], int lane, int
   int base = 0;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    if ((m[i] >> lane) & 1ull) {
+    if (v[i] >= thf) {  // (this lane's bit of m[i])
       const int pos = base + (int)__popcll(m[i] & ((1ull << lane) - 1ull));
       s_idx[pos] = i * 64 + lane;
       s_val[pos] = v[i];
@@ -152,27 +158,33 @@ __device__ __forceinline__ void topk_token(const float (&v)[MAXV], int lane, int
   const bool cand = lane < cnt;
   const int ci = cand ? s_idx[lane] : 0x7fffffff;
   const float cv = cand ? s_val[lane] : 0.f;
+  // rank = candidates before this one in (logit descending, expert
+  // ascending): one unsigned compare of (key, ~expert) pairs
+  const uint32_t khi = order_key(cv), klo = ~(uint32_t)ci;
+  const uint64_t ck = ((uint64_t)khi << 32) | klo;
   int rank = 0;
   for (int j = 0; j < cnt; ++j) {
-    const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv), j));
-    const int ij = __builtin_amdgcn_readlane(ci, j);
-    rank += (vj > cv || (vj == cv && ij < ci)) ? 1 : 0;
+    const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
+    rank += kj > ck ? 1 : 0;
   }
   const bool sel = cand && rank < k;
   // the largest selected logit (slot 0)
   const uint64_t top = __ballot(cand && rank == 0);
   const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv), (int)__builtin_ctzll(top)));
+  // Weights with the hardware exp2 and reciprocal (a few ulp; their
+  // exponents x <= 0).
   float w;
   if (renorm) {
-    const float ex = sel ? expf(cv - v0) : 0.f;
-    w = ex / wave_sum(ex);
+    const float ex = sel ? __expf(cv - v0) : 0.f;
+    w = ex * __builtin_amdgcn_rcpf(wave_sum(ex));
   } else {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i)
-      if (i * 64 + lane < E) s += expf(v[i] - v0);
+      if (i * 64 + lane < E) s += __expf(v[i] - v0);
     s = wave_sum(s);
-    w = expf(cv - v0) / s;
+    w = __expf(cv - v0) * __builtin_amdgcn_rcpf(s);
   }
   if (sel) {
     idx_out[(int64_t)t * k + rank] = ci;
@@ -196,14 +208,20 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
   const int t0 = (blockIdx.x * 4 + wv) * TPW;
   if (t0 >= T) return;
   float v[TPW][MAXV];
+  const bool full = E == MAXV * 64;  // (uniform) every lane holds MAXV experts: no mask
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int t = min(t0 + u, T - 1);  // (a token past T re-reads the last row, unused)
     const float* row = logits + (int64_t)t * E;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int e = i * 64 + lane;
-      v[u][i] = e < E ? row[e] : -INFINITY;
+      for (int i = 0; i < MAXV; ++i) v[u][i] = row[i * 64 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const int e = i * 64 + lane;
+        v[u][i] = e < E ? row[e] : -INFINITY;
+      }
     }
   }
 #pragma unroll
@@ -217,84 +235,71 @@ __global__ void __launch_bounds__(256) topk_route_kernel(const float* __restrict
   }
 }
 
-// dlogits, TPW tokens per wave (TPW * k <= 64).  renorm: dL_m = w_m (dw_m -
-// <w, dw>) on the selected experts (local or not), 0 elsewhere.  raw softmax:
-// dL_e = p_e (g_e - <w, dw>) with g_e = dw_j at e = idx_j.  Lane u*k + j loads
-// slot j of the wave's token u, so one load of each input serves all TPW
-// tokens; a token's k selections are then read into scalar registers (their
-// lane is uniform) and scattered into the row held by the lanes: expert e is
-// element e/64 of lane e%64.
-template <int MAXV, int TPW>
+// dlogits, one wave per token.  renorm: dL_m = w_m (dw_m - <w, dw>) on the
+// selected experts (local or not), 0 elsewhere.  raw softmax: dL_e = p_e (g_e
+// - <w, dw>) with g_e = dw_j at e = idx_j.  Lane j (< k) holds slot j; <w, dw>
+// is a butterfly sum over the wave.  The k values are scattered into a
+// zeroed LDS copy of the token's row at their experts (the experts of a
+// token are distinct), which the lanes then read back in the order they
+// store the row: expert e is element e/64 of lane e%64.  (A wave's LDS
+// operations complete in order, so the zeroing lands before the scatter.)
+template <int MAXV>
 __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict__ logits,
                                                         const int32_t* __restrict__ idx,
                                                         const float* __restrict__ w,
                                                         const float* __restrict__ dw, int T, int E, int k,
                                                         int renorm, float* __restrict__ dlogits) {
+  __shared__ float s_g[4][MAXV * 64];
   const int lane = threadIdx.x & 63;
-  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
-  if (t0 >= T) return;
-  int my_i = -1;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float* gs = s_g[threadIdx.x >> 6];
+  int my_i = 0;
   float my_w = 0.f, my_dw = 0.f;
-  const int64_t slot = (int64_t)t0 * k + lane;  // slot (lane % k) of token t0 + lane / k
-  if (lane < TPW * k && slot < (int64_t)T * k) {
-    my_i = idx[slot];
-    my_w = w[slot];
-    my_dw = dw[slot];
+  if (lane < k) {
+    my_i = min(max(idx[(int64_t)t * k + lane], 0), E - 1);  // (clamped: no write outside the row)
+    my_w = w[(int64_t)t * k + lane];
+    my_dw = dw[(int64_t)t * k + lane];
   }
+  const float s = wave_sum(my_w * my_dw);  // <w, dw>
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = t0 + u;
-    if (t >= T) break;
-    float s = 0.f;  // <w, dw> of the token, summed in slot order
-    for (int j = 0; j < k; ++j)
-      s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), u * k + j)) *
-           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dw), u * k + j));
-    // g[i]: for renorm w_j (dw_j - s) at the selected experts, else dw_j
-    float g[MAXV];
+  for (int i = 0; i < MAXV; ++i) gs[i * 64 + lane] = 0.f;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < k) gs[my_i] = renorm ? my_w * (my_dw - s) : my_dw;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float g[MAXV];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) g[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int ij = __builtin_amdgcn_readlane(my_i, u * k + j);
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), u * k + j));
-      const float dwj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dw), u * k + j));
-      const float val = renorm ? wj * (dwj - s) : dwj;
-      // expert ij is element ij / 64 of lane ij % 64; the element is uniform,
-      // so one select in one register instead of one per element
-      const int ie = ij >> 6;
-      const bool mine = (ij & 63) == lane;
+  for (int i = 0; i < MAXV; ++i) g[i] = gs[i * 64 + lane];
+  float* out = dlogits + (int64_t)t * E;
+  if (renorm) {
 #pragma unroll
-      for (int i = 0; i < MAXV; ++i)
-        if (ie == i) g[i] = mine ? val : g[i];
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      if (e < E) out[e] = g[i];
     }
-    float* out = dlogits + (int64_t)t * E;
-    if (renorm) {
+  } else {
+    const float* row = logits + (int64_t)t * E;
+    float v[MAXV];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < MAXV; ++i) {
-        const int e = i * 64 + lane;
-        if (e < E) out[e] = g[i];
-      }
-    } else {
-      const float* row = logits + (int64_t)t * E;
-      float v[MAXV];
-      float mx = -INFINITY;
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      v[i] = e < E ? row[e] : -INFINITY;
+      mx = fmaxf(mx, v[i]);
+    }
 #pragma unroll
-      for (int i = 0; i < MAXV; ++i) {
-        const int e = i * 64 + lane;
-        v[i] = e < E ? row[e] : -INFINITY;
-        mx = fmaxf(mx, v[i]);
-      }
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float z = 0.f;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      float z = 0.f;
+    for (int i = 0; i < MAXV; ++i)
+      if (i * 64 + lane < E) z += expf(v[i] - mx);
+    z = wave_sum(z);
 #pragma unroll
-      for (int i = 0; i < MAXV; ++i)
-        if (i * 64 + lane < E) z += expf(v[i] - mx);
-      z = wave_sum(z);
-#pragma unroll
-      for (int i = 0; i < MAXV; ++i) {
-        const int e = i * 64 + lane;
-        if (e < E) out[e] = expf(v[i] - mx) / z * (g[i] - s);
-      }
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = i * 64 + lane;
+      if (e < E) out[e] = expf(v[i] - mx) / z * (g[i] - s);
     }
   }
 }
@@ -323,7 +328,7 @@ static void route_bwd_nv(const moe_desc& d, int nv, const float* logits, const i
   if constexpr (NV <= 16) {
     if (nv > NV) return route_bwd_nv<NV + 1>(d, nv, logits, idx, w, dw, dlogits, s);
     // one token per wave (4 per wave measured slower: 0.050 against 0.041 ms at T = 65536, E = 384)
-    route_bwd_kernel<NV, 1><<<(d.T + 3) / 4, 256, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize,
+    route_bwd_kernel<NV><<<(d.T + 3) / 4, 256, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize,
                                                           dlogits);
   }
 }

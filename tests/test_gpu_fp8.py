@@ -463,3 +463,61 @@ def test_fp8mm_down_at_full_size_sampled(gpu):
         want.append(oracle.expert_down(hr[None, :], np.array([0, 1]), wn[None])[0])
     got = to_host(y[torch.as_tensor(rs, device=y.device)])
     assert max_row_rel_err(got, np.array(want)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("scale", [
+    dict(T=600, d=512, f=256, E=32, num_local=8, expert_begin=8),
+    dict(T=700, d=512, f=1792, E=16, num_local=16, expert_begin=0),
+])
+def test_fp8mm_forward_layer_matches_the_oracle(gpu, scale):
+    # The whole forward with both expert products on the FP8 matrix cores, as
+    # the FP8 benchmark workload runs it: x, W1, W3, W2 and h quantised to
+    # E4M3 with power-of-two block scales.  The oracle quantises at the same
+    # points: x and the weights as given, and its own H after rounding it to
+    # bf16.  The GPU's h is the bf16 rounding of its own G and U, an ulp away
+    # from the oracle's here and there, and a value that sits near a code
+    # boundary then takes the neighbouring code: a full code step where the
+    # quantisation itself moves a value by at most half a step.  So y is held
+    # to the bf16 bound plus twice the quantisation's own effect on y, q (the
+    # oracle's y on quantised H against its y on the bf16 H); h itself, and
+    # each product on identical codes (the tests above), meet the bf16 bound.
+    cfg = synth.scaled(synth.CONFIGS["share_1t"], **scale)
+    T, d, f, E, k, e0, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local
+    print(f"[fp8mm layer] {scale}", flush=True)
+    inp = synth.make_inputs(cfg, want=("x", "w1", "w3", "w2"))
+    rng = np.random.default_rng(T + f)
+    idx = random_routing(rng, T, E, k)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    D = _desc(T, d, f, E, k, e0, NL, "bf16")
+    b = moe.Buffers(D, gather=True)
+    moe.permute(D, to_dev(idx), None, b.counts, b.offsets, b.row_token, b.slot_row, None, b.ws_permute)
+    xq, xs = _quant_pow2(to_dev(inp["x"]), gpu)
+    wq = {n: _quant_pow2(to_dev(inp[n]), gpu) for n in ("w1", "w3")}
+    moe.expert_gate_up_fp8mm(D, b.offsets, b.row_token, xq, xs, wq["w1"][0], wq["w1"][1], wq["w3"][0],
+                             wq["w3"][1], None, b.h)
+    S8 = moe.fp8_scale_row_bytes(f)
+    hq = torch.empty(D.R_cap, f, dtype=torch.uint8, device=gpu)
+    hs = torch.empty(D.R_cap, S8, dtype=torch.uint8, device=gpu)
+    moe.fp8_quantize_pow2_rows(b.h, hq, hs, b.offsets[NL:])
+    w2q = torch.empty(NL * d, f, dtype=torch.uint8, device=gpu)
+    w2s = torch.empty(NL * d, S8, dtype=torch.uint8, device=gpu)
+    moe.fp8_quantize_pow2_rows(to_dev(inp["w2"]).view(NL * d, f), w2q, w2s)
+    moe.expert_down_fp8mm(D, b.offsets, hq, hs, w2q, w2s, b.y_perm)
+    moe.combine(D, b.slot_row, to_dev(w), b.y_perm, b.y)
+    torch.cuda.synchronize()
+    deq = {}
+    for n in ("x", "w1", "w3", "w2"):
+        a = synth.as_f32(inp[n], "bf16")
+        deq[n] = oracle.fp8_dequantize_blocks_pow2(*oracle.fp8_quantize_blocks_pow2(a)).reshape(a.shape)
+    _, off = oracle.count_tokens(idx, E, e0, NL)
+    rows, slot = oracle.generate_indices(idx, e0, NL, off)
+    R = int(off[-1])
+    _, _, H, _ = oracle.expert_ffn(oracle.permute(deq["x"], rows), off, deq["w1"], deq["w3"], np.zeros((NL, d, f)))
+    assert max_row_rel_err(to_host(b.h)[:R], H) <= TOL["bf16"]
+    Hb = oracle.bf16_round(H)
+    Hq = oracle.fp8_dequantize_blocks_pow2(*oracle.fp8_quantize_blocks_pow2(Hb)).reshape(R, f)
+    y = oracle.combine(oracle.expert_down(Hq, off, deq["w2"]), slot, w)
+    q = max_row_rel_err(oracle.combine(oracle.expert_down(Hb, off, deq["w2"]), slot, w), y)
+    err = max_row_rel_err(to_host(b.y), y)
+    print(f"[fp8mm layer] y error {err:.4f}, quantisation effect q {q:.4f}", flush=True)
+    assert err <= TOL["bf16"] + 2 * q
