@@ -125,10 +125,12 @@ __device__ __forceinline__ void topk_token(const float (&v)[MAXV], int lane, int
   // so the candidates still hold every selection; values within 2^-7 of it
   // add the odd extra candidate.  (A theta below the key of -infinity would
   // name a NaN; it is raised to that key, and every element is a candidate.)
+  // (uicmp: the lanes' unsigned kmax >= c as a wave mask in one compare,
+  // without materialising the predicate first as a ballot does)
   uint32_t theta = 0;
   for (int b = 31; b >= 16; --b) {
     const uint32_t c = theta | (1u << b);
-    if ((int)__popcll(__ballot(kmax >= c)) >= k) theta = c;
+    if ((int)__popcll(__builtin_amdgcn_uicmp(kmax, c, 35 /* unsigned >= */)) >= k) theta = c;
   }
   if (theta < 0x00800000u) theta = 0x007FFFFFu;
   const float thf = key_float(theta);
@@ -146,8 +148,9 @@ __device__ __forceinline__ void topk_token(const float (&v)[MAXV], int lane, int
   int base = 0;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    if (v[i] >= thf) {  // (this lane's bit of m[i])
-      const int pos = base + (int)__popcll(m[i] & ((1ull << lane) - 1ull));
+    if (v[i] >= thf) {  // (this lane's bit of m[i]); pos = base + the set bits of m[i] below the lane
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[i] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m[i], 0u));
       s_idx[pos] = i * 64 + lane;
       s_val[pos] = v[i];
     }
