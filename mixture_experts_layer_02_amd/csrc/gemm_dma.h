@@ -1234,11 +1234,17 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
           }
           // Stage the next slab now: a wave's LDS operations run in order, so
           // these writes land after the reads above, and they issue while the
-          // reads return and this slab is converted and stored.
+          // reads return and this slab is converted and stored.  The reads
+          // and writes pass values between lanes, which the compiler does not
+          // see as a dependence: empty asm with a memory clobber on both sides
+          // keeps it from moving either across the other (a staging written by
+          // half of the lanes has been reordered without it).
+          asm volatile("" ::: "memory");
           if (sl < 3)
             stage_slab(mi, sl + 1);
           else if (mi + 1 < MI)
             stage_slab(mi + 1, 0);
+          asm volatile("" ::: "memory");
 #pragma unroll
           for (int vi = 0; vi < VPL; ++vi) {
             const int e = lane_e + vi * 64;
