@@ -305,9 +305,20 @@ class Workload:
                 lambda R: 2.0 * R * d * f, lambda R: R * f * bb + NL * f * d * bb + R * d * bb)
         add("A7_combine", lambda: moe.combine(D, b.slot_row, w, b.y_perm, b.y), 1,
             nbytes=lambda R: R * d * bb + T * d * bb + T * k * 8)
-        if cfg.backward and gdy:
+        NP = moe.dtopk_parts(D)
+        parts = cfg.backward and gdy and args.dtopk == "parts"
+        if cfg.backward and gdy and parts:
             # dy read in place: no dy_perm; the routing weight of each row is
-            # applied inside dH, which also writes hw = w silu(G) U for dW2
+            # applied inside dH, which also writes hw = w silu(G) U for dW2 and
+            # the rows' partial sums of <dy W2, h> = <dy, y_perm> (dtopk_w)
+            add("B1_row_weights", lambda: moe.row_weights(D, b.slot_row, w, b.row_w), 1,
+                nbytes=lambda R: T * k * 8 + R * 4)
+            add("B2_dh", lambda: moe.expert_bwd_dh_gather(D, b.offsets, b.row_token, b.row_w, g["dy"], g["w2"],
+                                                          b.gu, b.dgu, b.hw, b.dtopk_part), 1,
+                lambda R: 2.0 * R * d * f,
+                lambda R: R * d * bb + NL * f * d * bb + 2 * R * 2 * f * bb + R * f * bb + R * 4 + R * NP * 4)
+        elif cfg.backward and gdy:
+            # dy read in place, dtopk_w by dot products over dy and y_perm
             add("B1_combine_bwd", lambda: moe.combine_bwd_gather(D, b.slot_row, w, b.y_perm, g["dy"], b.row_w,
                                                                  b.dtopk_w), 1,
                 nbytes=lambda R: T * d * bb + R * d * bb + T * k * 8 + R * 4)
@@ -335,6 +346,9 @@ class Workload:
             else:
                 add("B4_dw2", lambda: moe.expert_bwd_dw_down(D, b.offsets, b.dy_perm, b.h, b.dW2), 1,
                     lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
+            if parts:
+                add("B5_dtopk_w", lambda: moe.dtopk_w_from_parts(D, b.slot_row, b.dtopk_part, b.dtopk_w), 1,
+                    nbytes=lambda R: T * k * 8 + R * NP * 4)
             if routing is None:
                 add("B5_route_bwd", lambda: moe.route_bwd(D, b.logits, idx, w, b.dtopk_w, b.dlogits), 1,
                     nbytes=lambda R: T * E * 4 + T * k * 12)
@@ -465,6 +479,9 @@ def main():
     ap.add_argument("--dy-path", choices=["perm", "gather"], default="gather",
                     help="gather: dH and dW2 read dy through row_token with the routing weight applied inside "
                          "(no dy_perm); perm: the combine backward writes dy_perm")
+    ap.add_argument("--dtopk", choices=["parts", "dot"], default="parts",
+                    help="dtopk_w with dy read in place: parts, partial sums of <dy W2, h> from the dH product "
+                         "(y_perm is not read); dot, dot products of dy and y_perm in the combine backward")
     ap.add_argument("--router-dx", choices=["fused", "gemm"], default="fused",
                     help="the router's share of dx: fused, k rows of Wr added in the unpermute pass (renormalised "
                          "weights: dlogits is zero outside the selection); gemm, dx += dlogits Wr as a product")
@@ -508,7 +525,7 @@ def main():
     avg, step_ms, wall = run(moe, torch, wl, args, args.steps, args.warmup, flush, note)
     peak_mem = torch.cuda.max_memory_allocated()
     default_run = (cfg.name == "fwdbwd_1t" and args.x_path == "perm" and args.dy_path == "gather"
-                   and args.router_dx == "fused" and not (
+                   and args.router_dx == "fused" and args.dtopk == "parts" and not (
         args.fp8_weights or args.fp8_gemm or args.hold_cus or args.n_groups > 1 or args.schedule != "static"))
     main_sum = summarize(wl, avg, step_ms, wall, args.steps, default_run)
     ms_step = main_sum["ms_per_step"]
@@ -565,6 +582,8 @@ def main():
                                else "dy_perm copy"),
                    "router_dx": ("k rows of Wr added in the unpermute pass" if args.router_dx == "fused"
                                  and cfg.renormalize else "dx += dlogits Wr product"),
+                   "dtopk_w": ("partial sums of <dy W2, h> in the dH product" if args.dtopk == "parts"
+                               else "dot products of dy and y_perm"),
                    "expert_weights": ("bf16" if not args.fp8_weights else
                                       "fp8 e4m3 blocks of 128, read by the forward GEMMs" if args.fp8_gemm else
                                       "fp8 e4m3 blocks of 128, dequantised each step"),

@@ -293,13 +293,31 @@ int moe_combine_bwd_gather(const moe_desc* desc, const int32_t* slot_row, const 
                            const void* y_perm, const void* dy, float* row_w, float* dtopk_w,
                            void* stream);
 
+/* B1 without the dot products: row_w [R_cap] float32, row_w[slot_row[t][j]]
+ *   = topk_w[t][j] for every local slot (the weight row r carries), for the
+ *   dH product below; dtopk_w then comes from that product's partial sums
+ *   (moe_dtopk_w_from_parts), since <dy[t], y_perm[r]> = <dy[t] W2[n], h[r]>
+ *   for row r = slot_row[t][j] of expert n (y_perm[r] = h[r] W2[n]^T). */
+int moe_row_weights(const moe_desc* desc, const int32_t* slot_row, const float* topk_w, float* row_w,
+                    void* stream);
+
 /* B2: dH[r] = row_w[r] * (dy[row_token[r]] W2[n]) with the SwiGLU backward
  *   fused as in moe_expert_bwd_dh -> dgu [R_cap][2f]; and, when hw is not
  *   NULL, hw[r] = row_w[r] * silu(G) * U [R_cap][f] bf16 from the saved
- *   G | U (gu), the operand of the dW2 product below.  dy [T][d]. */
+ *   G | U (gu), the operand of the dW2 product below; and, when dtopk_part
+ *   is not NULL, dtopk_part [R_cap][P] float32, P = 2 * ceil(f / 256): the
+ *   sums of (dy[row_token[r]] W2[n]) * silu(G) * U over consecutive 128-wide
+ *   column blocks of f (with G, U the saved bf16 values).  dy [T][d]. */
 int moe_expert_bwd_dh_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
                              const float* row_w, const void* dy, const void* W2, const void* gu,
-                             void* dgu, void* hw, void* stream);
+                             void* dgu, void* hw, float* dtopk_part, void* stream);
+
+/* B1's dot products from B2's partial sums: dtopk_w[t][j] = the sum, in
+ *   order, of dtopk_part[slot_row[t][j]][0 .. P-1] for a local slot, 0 for a
+ *   slot whose expert is not local (as moe_combine_bwd).  dtopk_w [T][k]
+ *   float32. */
+int moe_dtopk_w_from_parts(const moe_desc* desc, const int32_t* slot_row, const float* dtopk_part,
+                           float* dtopk_w, void* stream);
 
 /* B4, dW2 with dy read in place: dW2[n] = sum over rows r of expert n of
  *   dy[row_token[r]]^T hw[r]  ([NL][d][f] float32, overwritten; exact zeros

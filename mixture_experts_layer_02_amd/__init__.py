@@ -17,9 +17,9 @@ import os
 import torch  # imported before libmoe.so so that the process holds one HIP runtime
 
 __all__ = [
-    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8", "fp8_quantize_pow2", "expert_gate_up_fp8mm", "fp8_quantize_pow2_rows", "expert_down_fp8mm", "fp8_scale_row_bytes",
+    "MoeError", "MoeDesc", "lib", "make_desc", "new_tile_counters", "SCHEDULE_STATIC", "SCHEDULE_DYNAMIC", "workspace_size", "router_logits", "route", "route_grouped", "hold_cus", "fp8_quantize", "fp8_dequantize", "permute", "permute_noalloc", "expert_gate_up_gather", "grouped_ffn_bwd_dw_gather", "expert_gate_up_fp8", "expert_down_fp8", "fp8_quantize_pow2", "expert_gate_up_fp8mm", "fp8_quantize_pow2_rows", "expert_down_fp8mm", "fp8_scale_row_bytes", "row_weights", "dtopk_w_from_parts", "dtopk_parts",
     "grouped_ffn", "expert_gate_up", "expert_down", "expert_bwd_dh", "expert_bwd_dx", "expert_bwd_dw_gate_up", "expert_bwd_dw_down", "combine_bwd_gather", "expert_bwd_dh_gather", "expert_bwd_dw_down_gather", "combine", "combine_bwd", "grouped_ffn_bwd_dx", "grouped_ffn_bwd_dw",
-    "unpermute_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
+    "unpermute_bwd", "unpermute_router_bwd", "route_bwd", "router_bwd", "router_bwd_acc", "Buffers", "forward", "backward",
     "MOE_F32", "MOE_BF16",
 ]
 
@@ -90,7 +90,9 @@ _SIGS = {
     "moe_expert_bwd_dw_gate_up": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_expert_bwd_dw_down": [_vp, _vp, _vp, _vp, _vp],
     "moe_combine_bwd_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
-    "moe_expert_bwd_dh_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_expert_bwd_dh_gather": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_row_weights": [_vp, _vp, _vp, _vp],
+    "moe_dtopk_w_from_parts": [_vp, _vp, _vp, _vp],
     "moe_expert_bwd_dw_down_gather": [_vp, _vp, _vp, _vp, _vp, _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _vp],
     "moe_combine_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -347,9 +349,25 @@ def combine_bwd_gather(desc, slot_row, topk_w, y_perm, dy, row_w, dtopk_w):
     _call("moe_combine_bwd_gather", desc, slot_row, topk_w, y_perm, dy, row_w, dtopk_w, _stream())
 
 
-def expert_bwd_dh_gather(desc, offsets, row_token, row_w, dy, w2, gu, dgu, hw):
-    """dH from dy read through row_token, scaled by row_w, SwiGLU backward -> dgu; hw = row_w silu(G) U."""
-    _call("moe_expert_bwd_dh_gather", desc, offsets, row_token, row_w, dy, w2, gu, dgu, hw, _stream())
+def expert_bwd_dh_gather(desc, offsets, row_token, row_w, dy, w2, gu, dgu, hw, dtopk_part=None):
+    """dH from dy read through row_token, scaled by row_w, SwiGLU backward -> dgu; hw = row_w silu(G) U;
+    dtopk_part: the rows' partial sums of (dy W2) silu(G) U (dtopk_parts(desc) per row)."""
+    _call("moe_expert_bwd_dh_gather", desc, offsets, row_token, row_w, dy, w2, gu, dgu, hw, dtopk_part, _stream())
+
+
+def dtopk_parts(desc):
+    """Partial sums per row written by expert_bwd_dh_gather: two per 256-wide n-tile of f."""
+    return 2 * ((desc.f + 255) // 256)
+
+
+def row_weights(desc, slot_row, topk_w, row_w):
+    """row_w[slot_row[t][j]] = topk_w[t][j] for every local slot."""
+    _call("moe_row_weights", desc, slot_row, topk_w, row_w, _stream())
+
+
+def dtopk_w_from_parts(desc, slot_row, dtopk_part, dtopk_w):
+    """dtopk_w[t][j] = the sum of slot j's row's partial sums (0 for a non-local slot)."""
+    _call("moe_dtopk_w_from_parts", desc, slot_row, dtopk_part, dtopk_w, _stream())
 
 
 def expert_bwd_dw_down_gather(desc, offsets, row_token, dy, hw, dw2):
@@ -431,6 +449,7 @@ class Buffers:
             self.dy_perm = None if gdy else torch.empty(Rc, d, dtype=dt, **z)
             self.row_w = torch.empty(Rc, dtype=torch.float32, **z) if gdy else None
             self.hw = torch.empty(Rc, f, dtype=dt, **z) if gdy else None
+            self.dtopk_part = torch.empty(Rc, dtopk_parts(desc), dtype=torch.float32, **z) if gdy else None
             self.dtopk_w = torch.empty(T, k, dtype=torch.float32, **z)
             self.dgu = torch.empty(Rc, 2 * f, dtype=dt, **z)
             self.dx_perm = torch.empty(Rc, d, dtype=dt, **z)
@@ -475,8 +494,11 @@ def backward(b: Buffers, x, wr, w1, w3, w2, dy, routing=None, fuse_router_dx=Tru
     D = b.desc
     idx, w = (b.topk_idx, b.topk_w) if routing is None else routing
     if b.gather_dy:
-        combine_bwd_gather(D, b.slot_row, w, b.y_perm, dy, b.row_w, b.dtopk_w)
-        expert_bwd_dh_gather(D, b.offsets, b.row_token, b.row_w, dy, w2, b.gu, b.dgu, b.hw)
+        # dtopk_w = <dy, y_perm> = <dy W2, h>: the row weights first, the dot
+        # products as partial sums inside dH (y_perm is not read)
+        row_weights(D, b.slot_row, w, b.row_w)
+        expert_bwd_dh_gather(D, b.offsets, b.row_token, b.row_w, dy, w2, b.gu, b.dgu, b.hw, b.dtopk_part)
+        dtopk_w_from_parts(D, b.slot_row, b.dtopk_part, b.dtopk_w)
         expert_bwd_dx(D, b.offsets, w1, w3, b.dgu, b.dx_perm)
         if b.gather:
             expert_bwd_dw_gate_up(D, b.offsets, b.row_token, x, b.dgu, b.dW1, b.dW3)

@@ -262,14 +262,31 @@ int moe_combine_bwd_gather(const moe_desc* desc, const int32_t* slot_row, const 
 
 int moe_expert_bwd_dh_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
                              const float* row_w, const void* dy, const void* W2, const void* gu, void* dgu,
-                             void* hw, void* stream) {
+                             void* hw, float* dtopk_part, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(offsets) || !need(row_token) || !need(row_w) || !need(dy) || !need(W2) || !need(gu) || !need(dgu) ||
-      !opt(hw))
+      !opt(hw) || !opt(dtopk_part))
     return MOE_ERR_INVALID_ARG;
   if (!gather_ok(desc)) return MOE_ERR_UNSUPPORTED;
-  return finish(moe::launch_bwd_dh_gather(*desc, offsets, row_token, row_w, dy, W2, gu, dgu, hw, S(stream)));
+  return finish(
+      moe::launch_bwd_dh_gather(*desc, offsets, row_token, row_w, dy, W2, gu, dgu, hw, dtopk_part, S(stream)));
+}
+
+int moe_row_weights(const moe_desc* desc, const int32_t* slot_row, const float* topk_w, float* row_w,
+                    void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(topk_w) || !need(row_w)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_row_weights(*desc, slot_row, topk_w, row_w, S(stream)));
+}
+
+int moe_dtopk_w_from_parts(const moe_desc* desc, const int32_t* slot_row, const float* dtopk_part,
+                           float* dtopk_w, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!need(slot_row) || !need(dtopk_part) || !need(dtopk_w)) return MOE_ERR_INVALID_ARG;
+  return finish(moe::launch_dtopk_from_parts(*desc, slot_row, dtopk_part, dtopk_w, S(stream)));
 }
 
 int moe_expert_bwd_dw_down_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,

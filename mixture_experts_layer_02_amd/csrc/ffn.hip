@@ -418,8 +418,9 @@ hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* 
 // (bf16) for the dW2 product.
 hipError_t launch_bwd_dh_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
                                 const float* row_w, const void* dy, const void* W2, const void* gu, void* dgu,
-                                void* hw, hipStream_t s) {
+                                void* hw, float* dtopk_part, hipStream_t s) {
   GemmParams p = blank(d);
+  p.dw_part = dtopk_part;
   p.A = dy;
   p.lda = d.d;
   p.gather = row_token;

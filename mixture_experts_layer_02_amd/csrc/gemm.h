@@ -66,6 +66,8 @@ struct GemmParams {
   int sbytes;              //     scale bytes per row (K codes / 128, a multiple of 4)
   const float* row_scale; // EPI_SWIGLU_BWD with a gathered A: dH of row r is scaled by row_scale[r]
   void* h_out;            //   and, when set, row_scale[r] * silu(G) * U is written here ([rows][N])
+  float* dw_part;         //   and, when set, row r's partial sums of dH * silu(G) * U (unscaled dH)
+                          //   over each wave's 128 columns: [rows][2 * n-tiles], entry 2 n-tile + wn
 };
 
 struct TileCtx {

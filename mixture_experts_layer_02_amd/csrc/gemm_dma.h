@@ -897,9 +897,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   constexpr int PFD = 1;  // (measured: 1 beats 2 and 3 by 1-2% on the 1T shapes; for F8, 2 is within noise)
   // Memory instructions per lane of one epilogue (the buffer stores and
   // loads below, all unconditional).
-  // (ROWSC: dH scaled per row, with the scales loaded and h_out stored: 32 more of each.)
+  // (ROWSC: dH scaled per row, with the scales loaded and h_out and the rows'
+  // partial dot products stored: 32 more of each.)
   constexpr bool ROWSC = EPI == EPI_SWIGLU_BWD && GATH == GATH_A;
-  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? (ROWSC ? 192 : 128)
+  constexpr int EPI_OPS = (EPI == EPI_SWIGLU) ? 48 : (EPI == EPI_SWIGLU_BWD) ? (ROWSC ? 224 : 128)
                           : (EPI == EPI_ADD ? 2 : 1) * (CF32 ? 64 : 32);
   // (+1: a gathered operand's token copy is issued between the epilogue and
   // the prefetches.)
@@ -1153,12 +1154,16 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         r1 = c_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.gu_in)) + (m0g * ld2 + t.n0) * 2, ld2, 2);
         ldo = ld2;
       }
-      // ROWSC: the rows' scales (float) and h_out ([rows][N] bf16, or nothing).
-      __amdgpu_buffer_rsrc_t rsc = r0, rho = r0;
+      // ROWSC: the rows' scales (float), h_out ([rows][N] bf16, or nothing) and
+      // the rows' partial dot products ([rows][NP] float, or nothing).
+      __amdgpu_buffer_rsrc_t rsc = r0, rho = r0, rdw = r0;
+      const int NP = 2 * sched.NT;
       if (ROWSC) {
         rsc = c_rsrc(const_cast<float*>(p.row_scale) + m0g, 1, 4);
         rho = p.h_out ? c_rsrc(reinterpret_cast<char*>(p.h_out) + (m0g * p.N + t.n0) * 2, p.N, 2)
                       : __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(p.C), (short)0, 0, 0x00020000);
+        rdw = p.dw_part ? c_rsrc(p.dw_part + m0g * NP, NP, 4)
+                        : __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(p.C), (short)0, 0, 0x00020000);
       }
       // Values the epilogue reads are loaded in batches ahead of the stores
       // that use them: a load waits for every memory instruction issued
@@ -1326,6 +1331,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 sc = __uint_as_float(sw);
               }
               float dg[8], du[8], hs[8];
+              float dot = 0.f;  // ROWSC: sum over the vector of unscaled dH * silu(G) U
 #pragma unroll
               for (int q = 0; q < 8; ++q) {
                 const uint32_t gw = gq[q >> 1], uw = uq[q >> 1];
@@ -1336,8 +1342,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 du[q] = dh * g * sg;
                 dg[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
                 hs[q] = g * sg * u * sc;
+                if (ROWSC) dot = fmaf(v[q], g * sg * u, dot);
               }
               if (ROWSC) {
+                // The row's CPR = 16 vectors are held by 16 consecutive lanes:
+                // a butterfly over them, and the first of them writes the sum
+                // over this wave's 128 columns (rows past mlim fall outside rdw).
+                static_assert(!ROWSC || CPR == 16, "one row per 16 lanes");
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 16);
+                // (issued by every lane, so the epilogue's store count stays fixed;
+                // the other lanes' offsets lie outside rdw)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(dot), rdw,
+                    (lane_e & 15) == 0 ? (uint32_t)(row * NP + 2 * t.ntile + wn) * 4u : 0x80000000u, 0, 0);
                 const u32x4_t dhw = {pack_bf2(hs[0], hs[1]), pack_bf2(hs[2], hs[3]), pack_bf2(hs[4], hs[5]),
                                      pack_bf2(hs[6], hs[7])};
                 const int64_t eh = (int64_t)row * p.N + col;

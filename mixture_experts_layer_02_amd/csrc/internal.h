@@ -50,7 +50,14 @@ hipError_t launch_combine_bwd(const moe_desc& d, const int32_t* slot_row, const 
                               const void* dy, void* dy_perm, float* dw, hipStream_t s, float* row_w = nullptr);
 hipError_t launch_bwd_dh_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
                                 const float* row_w, const void* dy, const void* W2, const void* gu, void* dgu,
-                                void* hw, hipStream_t s);
+                                void* hw, float* dtopk_part, hipStream_t s);
+hipError_t launch_row_weights(const moe_desc& d, const int32_t* slot_row, const float* w, float* row_w,
+                              hipStream_t s);
+hipError_t launch_dtopk_from_parts(const moe_desc& d, const int32_t* slot_row, const float* part, float* dtopk_w,
+                                   hipStream_t s);
+// Partial sums per row written by the dH product with dy read in place: two per
+// 256-wide n-tile of f.
+inline int dtopk_parts(const moe_desc& d) { return 2 * (int)((d.f + 255) / 256); }
 hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
                                  const void* dy, const void* hw, float* dW2, hipStream_t s);
 hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,

@@ -683,6 +683,30 @@ __global__ void __launch_bounds__(256) unpermute_router_bwd_kernel(
   }
 }
 
+// row_w[slot_row[i]] = w[i] for every local slot i of the T x k selections.
+__global__ void __launch_bounds__(256) row_weights_kernel(const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ w, int64_t n,
+                                                          float* __restrict__ row_w) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int r = slot_row[i];
+    if (r >= 0) row_w[r] = w[i];
+  }
+}
+
+// dtopk_w[i] = the sum, in order, of the P partial sums of slot i's row (0
+// for a slot whose expert is not local).
+__global__ void __launch_bounds__(256) dtopk_parts_kernel(const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ part, int P, int64_t n,
+                                                          float* __restrict__ dtopk_w) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int r = slot_row[i];
+    float s = 0.f;
+    if (r >= 0)
+      for (int q = 0; q < P; ++q) s += part[(int64_t)r * P + q];
+    dtopk_w[i] = s;
+  }
+}
+
 hipError_t launch_combine(const moe_desc& d, const int32_t* slot_row, const float* w, const void* y_perm,
                           void* y, hipStream_t s) {
   const dim3 grid((d.T + 3) / 4), block(256);
@@ -774,6 +798,22 @@ hipError_t launch_unpermute_router_bwd(const moe_desc& d, const int32_t* slot_ro
                                                                 dlogits, (const float*)Wr, d.T, d.k, d.E, d.d,
                                                                 (float*)dx);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_weights(const moe_desc& d, const int32_t* slot_row, const float* w, float* row_w,
+                              hipStream_t s) {
+  const int64_t n = (int64_t)d.T * d.k;
+  const int64_t g = std::min<int64_t>((n + 255) / 256, (int64_t)num_cus() * 8);
+  row_weights_kernel<<<(unsigned)g, 256, 0, s>>>(slot_row, w, n, row_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_dtopk_from_parts(const moe_desc& d, const int32_t* slot_row, const float* part, float* dtopk_w,
+                                   hipStream_t s) {
+  const int64_t n = (int64_t)d.T * d.k;
+  const int64_t g = std::min<int64_t>((n + 255) / 256, (int64_t)num_cus() * 8);
+  dtopk_parts_kernel<<<(unsigned)g, 256, 0, s>>>(slot_row, part, dtopk_parts(d), n, dtopk_w);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     l = moe.lib()
     names = _declared()
-    assert len(names) == 38
+    assert len(names) == 40
     assert names == moe.EXPORTS
     for n in names:
         assert hasattr(l, n), n
@@ -207,3 +207,15 @@ def test_fp8_row_quantise_and_down_reject_bad_arguments():
     assert l.moe_expert_down_fp8mm(ctypes.byref(_d(f=128, dtype=moe.MOE_F32)), g, g, g, g, g, g,
                                    None) == moe.MOE_ERR_UNSUPPORTED
     assert l.moe_expert_down_fp8mm(ctypes.byref(_d(f=128)), g, None, g, g, g, g, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_row_weights_and_dtopk_parts_reject_nulls():
+    l = moe.lib()
+    g = 1 << 20
+    d = _d()
+    assert l.moe_row_weights(ctypes.byref(d), None, g, g, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_row_weights(ctypes.byref(d), g, g, g + 4, None) == moe.MOE_ERR_INVALID_ARG
+    assert l.moe_dtopk_w_from_parts(ctypes.byref(d), g, None, g, None) == moe.MOE_ERR_INVALID_ARG
+    # the dH product's partial sums are optional, but aligned when given
+    assert l.moe_expert_bwd_dh_gather(ctypes.byref(d), g, g, g, g, g, g, g, None, g + 4, None) == \
+        moe.MOE_ERR_INVALID_ARG

@@ -128,3 +128,43 @@ def test_gather_rejects_fp32_and_oversized_x(gpu):
         moe.expert_bwd_dh_gather(D, z, z, z, z, z, z, z, z)
     with pytest.raises(moe.MoeError):
         moe.expert_bwd_dw_down_gather(D, z, z, z, z, z)
+
+
+@pytest.mark.parametrize("scale", [
+    dict(T=512, d=256, f=128, E=32, num_local=8, expert_begin=8),
+    dict(T=1500, d=320, f=192, E=64, num_local=24, expert_begin=40, k=6),     # ragged, empty experts
+])
+def test_dtopk_w_two_ways_against_oracle(gpu, scale):
+    # dtopk_w[t][j] = <dy[t], y_perm[row]> (the stage-5 backward) from the
+    # combine backward's dot products, and = <dy[t] W2, h[row]> from the dH
+    # product's partial sums (the layer's default); both against the oracle
+    # on the layer's own forward, and row_weights against the weights.
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[dtopk_w] {scale}", flush=True)
+    inp = synth.make_inputs(cfg)
+    dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
+    args = (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.dtype, cfg.renormalize)
+    D = moe.make_desc(*args)
+    b = moe.Buffers(D, backward=True, gather=False, gather_dy=True)
+    moe.forward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"])
+    moe.backward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], dev["dy"])
+    dw_parts = b.dtopk_w.clone()
+    rw_parts = b.row_w.clone()
+    dw_dot = torch.empty_like(b.dtopk_w)
+    rw_dot = torch.empty_like(b.row_w)
+    moe.combine_bwd_gather(D, b.slot_row, b.topk_w, b.y_perm, dev["dy"], rw_dot, dw_dot)
+    torch.cuda.synchronize()
+    R = int(b.offsets[-1].item())
+    assert torch.equal(rw_parts[:R], rw_dot[:R])
+    dt = cfg.dtype
+    ref = oracle.layer_forward(f64(inp["x"], dt), f64(inp["wr"], dt), f64(inp["w1"], dt), f64(inp["w3"], dt),
+                               f64(inp["w2"], dt), cfg.k, cfg.expert_begin, cfg.num_local, cfg.renormalize)
+    idx_g = to_host(b.topk_idx)
+    agree = (idx_g == ref["idx"]).all(axis=1)      # tokens routed alike (near-ties aside)
+    _, dw_ref = oracle.combine_bwd(f64(inp["dy"], dt), ref["y_perm"], ref["slot_row"], ref["w"])
+    for got in (dw_parts, dw_dot):
+        g = to_host(got)[agree]
+        assert whole_rel_err(g, dw_ref[agree]) <= TOL[dt]
+    # non-local slots are exactly zero
+    sl = to_host(b.slot_row)
+    assert (to_host(dw_parts)[sl < 0] == 0).all()
