@@ -588,19 +588,57 @@ __global__ void __launch_bounds__(256) unpermute_bwd_kernel_b(const int32_t* __r
 // share of dx, dlogits[t] W_r, is that sum of k rows of W_r: k multiply-adds
 // per element here instead of a T x d x E product.  Sums in float32, the
 // expert rows in slot order, then the router rows in slot order; one
-// rounding at the store.  W_r (E x d) is read by every token and stays in
-// the caches.  Each wave takes one token; per chunk of the row every load
-// (the live expert rows and the k router rows) is issued before any is used.
+// rounding at the store.
+//
+// W_r (E x d) is read by every token; at E = 384, d = 6144 it is 4.7 MB, more
+// than one XCD's 4 MB L2.  So the columns are cut into 2^lg_s slices: block
+// b takes slice b mod 2^lg_s of four tokens, and as consecutive blocks go to
+// consecutive XCDs, each XCD reads only its slices' columns of W_r, which
+// then fit in its L2.  The streamed operands (dx_perm in, dx out) carry the
+// non-temporal hint so that they do not push W_r out.  Each wave takes one
+// token's slice; per chunk of it every load (the live expert rows and the k
+// router rows) is issued before any is used.
+//
+// With 96 of 384 experts local, about two of a token's eight slots have a
+// local row, so the k rows of W_r are most of what a token reads (6.4 GB from
+// L2 per pass at T = 65536, against 1.6 GB of dx_perm from HBM): the pass is
+// bound by those L2 reads, not by HBM.  Measured at that shape: 0.747 ms with
+// one slice, 0.691 with the hint, 0.672 with two slices and the hint, 0.695
+// with four, 0.86 with eight.
+constexpr bool kUnpermStreamHint = true;
+namespace batched {
+template <typename T>
+__device__ __forceinline__ u32x4 ld16_stream(const T* p) {
+  if constexpr (kUnpermStreamHint) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+template <typename T, int N>
+__device__ __forceinline__ void st16_stream(T* p, const float (&v)[N]) {
+  u32x4 q;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = pack_bf2(v[2 * i], v[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = __float_as_uint(v[i]);
+  }
+  if constexpr (kUnpermStreamHint) __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = q;
+}
+}  // namespace batched
+
 template <typename T, int KB>
 __global__ void __launch_bounds__(256) unpermute_router_bwd_kernel_b(
     const int32_t* __restrict__ slot_row, const T* __restrict__ dx_perm, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ dlogits, const T* __restrict__ wr, int Tn, int k, int E, int d,
+    const float* __restrict__ dlogits, const T* __restrict__ wr, int Tn, int k, int E, int d, int lg_s,
     T* __restrict__ dx) {
   using R = batched::Raw<T>;
   constexpr int VN = R::N;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = (int)(blockIdx.x >> lg_s) * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
+  const int sw = d >> lg_s;  // a multiple of VN (d % 64 == 0, lg_s <= 3)
+  const int c0 = (int)(blockIdx.x & ((1u << lg_s) - 1)) * sw, c1 = c0 + sw;
   const int r = lane < k ? slot_row[(int64_t)t * k + lane] : -1;
   const int ex = lane < k ? min(max(topk_idx[(int64_t)t * k + lane], 0), E - 1) : 0;  // (clamped: no read outside W_r)
   const float g = lane < k ? dlogits[(int64_t)t * E + ex] : 0.f;
@@ -613,11 +651,11 @@ __global__ void __launch_bounds__(256) unpermute_router_bwd_kernel_b(
     erows[j] = (int64_t)__shfl(ex, j, 64) * d;
     gj[j] = __shfl(g, j, 64);
   }
-  for (int c = lane * VN; c < d; c += 64 * VN) {
+  for (int c = c0 + lane * VN; c < c1; c += 64 * VN) {
     u32x4 q[KB], qw[KB];
 #pragma unroll
     for (int j = 0; j < KB; ++j)
-      if ((live >> j) & 1) q[j] = batched::ld16(dx_perm + rows[j] + c);
+      if ((live >> j) & 1) q[j] = batched::ld16_stream(dx_perm + rows[j] + c);
 #pragma unroll
     for (int j = 0; j < KB; ++j)
       if (j < k) qw[j] = batched::ld16(wr + erows[j] + c);
@@ -640,7 +678,7 @@ __global__ void __launch_bounds__(256) unpermute_router_bwd_kernel_b(
 #pragma unroll
         for (int e = 0; e < VN; ++e) acc[e] = fmaf(gj[j], v[e], acc[e]);
       }
-    Vec16<T>::store(dx + (int64_t)t * d + c, acc);
+    batched::st16_stream<T, VN>(dx + (int64_t)t * d + c, acc);
   }
 }
 
@@ -774,15 +812,23 @@ hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, cons
   return hipGetLastError();
 }
 
+// Column slices per token in the unpermute + router pass: up to 2, each at
+// least one wave-wide chunk.
+constexpr int kUnpermMaxLgSlices = 1;
+
 hipError_t launch_unpermute_router_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
                                        const int32_t* topk_idx, const float* dlogits, const void* Wr, void* dx,
                                        hipStream_t s) {
-  const dim3 grid((d.T + 3) / 4), block(256);
+  const dim3 block(256);
+  const int vn = d.dtype == MOE_BF16 ? 8 : 4;
+  int lg_s = 0;
+  while (lg_s < kUnpermMaxLgSlices && (d.d >> (lg_s + 1)) >= 64 * vn) ++lg_s;
+  const dim3 gridb((unsigned)((d.T + 3) / 4) << lg_s), grid((d.T + 3) / 4);
   const bool b8 = d.k <= 8;
   if (d.dtype == MOE_BF16) {
     if (b8)
-      unpermute_router_bwd_kernel_b<uint16_t, 8><<<grid, block, 0, s>>>(
-          slot_row, (const uint16_t*)dx_perm, topk_idx, dlogits, (const uint16_t*)Wr, d.T, d.k, d.E, d.d,
+      unpermute_router_bwd_kernel_b<uint16_t, 8><<<gridb, block, 0, s>>>(
+          slot_row, (const uint16_t*)dx_perm, topk_idx, dlogits, (const uint16_t*)Wr, d.T, d.k, d.E, d.d, lg_s,
           (uint16_t*)dx);
     else
       unpermute_router_bwd_kernel<uint16_t><<<grid, block, 0, s>>>(slot_row, (const uint16_t*)dx_perm, topk_idx,
@@ -790,9 +836,9 @@ hipError_t launch_unpermute_router_bwd(const moe_desc& d, const int32_t* slot_ro
                                                                    d.d, (uint16_t*)dx);
   } else {
     if (b8)
-      unpermute_router_bwd_kernel_b<float, 8><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, topk_idx,
-                                                                     dlogits, (const float*)Wr, d.T, d.k, d.E,
-                                                                     d.d, (float*)dx);
+      unpermute_router_bwd_kernel_b<float, 8><<<gridb, block, 0, s>>>(slot_row, (const float*)dx_perm, topk_idx,
+                                                                      dlogits, (const float*)Wr, d.T, d.k, d.E,
+                                                                      d.d, lg_s, (float*)dx);
     else
       unpermute_router_bwd_kernel<float><<<grid, block, 0, s>>>(slot_row, (const float*)dx_perm, topk_idx,
                                                                 dlogits, (const float*)Wr, d.T, d.k, d.E, d.d,
