@@ -134,6 +134,41 @@ def _copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def _vendor_gemm(torch, dev, NL, R, d, f, ours):
+    """The vendor's bf16 GEMM (torch.bmm, hipBLASLt) on the products of the grouped GEMM rows, with
+    equal segments of R / NL rows per expert, for comparison with the grouped kernels' own times.
+    Every operand is a contiguous tensor; outputs are bf16 (the weight gradients here are fp32)."""
+    m = max(1, round(R / NL))
+    g = torch.Generator(device=dev).manual_seed(5)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=torch.bfloat16, generator=g)
+
+    shapes = {"A5_gate_up": (m, d, 2 * f), "A6_down": (m, f, d), "B2_dh": (m, d, f), "B3_dx": (m, 2 * f, d),
+              "B4_dw13": (2 * f, m, d), "B4_dw2": (d, m, f)}
+    out = {}
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for row, (a0, k0, n0) in shapes.items():
+        a, b = rnd(NL, a0, k0), rnd(NL, k0, n0)
+        for _ in range(3):
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        st.record()
+        for _ in range(5):
+            torch.bmm(a, b)
+        en.record()
+        torch.cuda.synchronize()
+        ms = st.elapsed_time(en) / 5
+        fl = 2.0 * NL * a0 * k0 * n0
+        out[row] = {"bmm": f"{NL} x [{a0} x {k0}] . [{k0} x {n0}]", "vendor_ms": round(ms, 4),
+                    "vendor_tflops": round(fl / ms / 1e9, 1),
+                    "ours_ms": round(ours[row]["ms"], 4) if row in ours else None}
+        del a, b
+    torch.cuda.empty_cache()
+    return {"what": f"torch.bmm bf16 (hipBLASLt) on the same products, {NL} equal segments of {m} rows",
+            "rows": out}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -491,6 +526,8 @@ def main():
                     help="with --fp8-weights: the forward expert GEMMs read the FP8 weights directly")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip timing the vendor bf16 GEMM (torch.bmm) on the grouped GEMMs' products")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -561,6 +598,11 @@ def main():
         del w2
         torch.cuda.empty_cache()
 
+    vendor = None
+    if not args.no_vendor_gemm and cfg.backward:
+        vendor = _vendor_gemm(torch, dev, cfg.num_local, main_sum["R"], d, f, main_sum["rows"])
+        note("vendor gemm: " + ", ".join(f"{k} {v['vendor_ms']:.3f} ms" for k, v in vendor["rows"].items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         note(f"cpu baseline: oracle on {min(args.cpu_sample_tokens, cfg.T)} tokens")
@@ -599,6 +641,7 @@ def main():
         "cpu_baseline": cpu,
         "rows": main_sum["rows"],
         "workloads": extras,
+        "vendor_gemm": vendor,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out), flush=True)
