@@ -307,6 +307,18 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA operands scalar
   const int wm = wave >> 1, wn = wave & 1;
+  // Half tiles (row-grouped products in bf16): a tile with at most 128 valid
+  // rows - an expert's last, partial m-tile - would spend wave row 1's
+  // MFMAs on padding.  There wave row wm computes rows 64 wm .. 64 wm + 63
+  // instead (arow, the A row base of its fragment reads), its row blocks 0
+  // and 1 only: each wave then holds half the MFMAs of a full tile, and the
+  // outputs stay disjoint.
+  constexpr bool HALFM = GRP == GRP_M && !F8;
+  // The steady k-loop's DMAs take one wait state (see dma16), except in the
+  // gathered-B weight-gradient kernels, whose k-loop reloads spilled SGPRs
+  // next to its DMAs: they take five.
+  constexpr bool LIGHT_K = MOE_LIGHT_DMA && GATH != GATH_B;
+  int arow = wm * 128, arow_next = wm * 128;
   const uint16_t* Ag = reinterpret_cast<const uint16_t*>(p.A);
   const uint16_t* Bg = reinterpret_cast<const uint16_t*>(p.B);
   const uint16_t* B2g = reinterpret_cast<const uint16_t*>(p.B2);
@@ -662,7 +674,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // the stage's LDS byte address in scalar arithmetic; element offsets x2
     const uint32_t stb = ring_lds + ((uint32_t)(gbase + pos) % STAGES) * STAGE_ELEMS * 2;
     if (BQ8) {  // q < NJ: A; then NJB FP8 B instructions; then the B rows' scales
-      constexpr bool LTQ = MOE_LIGHT_DMA && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
+      constexpr bool LTQ = LIGHT_K && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
       if (q < NJ) {
         dma16<LTQ>(L.ra, GATH == GATH_A ? a_gv(pos, q, pure_c) : va[q], a_so(k), stb + (wave * NJ + q) * 1024);
       } else if (q < NJ + NJB) {
@@ -678,7 +690,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     }
     const int jj = q >> 1;
     const int j = wave * NJ + jj;
-    constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
+    constexpr bool LT = LIGHT_K && decltype(pure_c)::value;  // the steady k-loop: one wait state (checked at build)
     if (F8 && q >= 2 * NJ) {  // the scale dwords of the wave's 64 A rows, then of its 64 B rows
       // (always five wait states: the compiler spills these resources to
       // vector lanes and may reload one just before its use)
@@ -704,7 +716,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   auto pf_one = [&](int pos, int o, auto pure_c) __attribute__((always_inline)) {
     int k;
     const Ld L = pick(pos, k, pure_c);
-    constexpr bool LT = MOE_LIGHT_DMA && decltype(pure_c)::value;  // as in dma_one
+    constexpr bool LT = LIGHT_K && decltype(pure_c)::value;  // as in dma_one
     if (o == 0 && GATH == GATH_AK) {
       touch4u(L.ra, gpb, __builtin_amdgcn_readfirstlane(0u), junk_lds);  // (a readfirstlane just before)
     } else if (o == 0) {
@@ -800,7 +812,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     if (f == 0 || f > NI) {
       const int mi = f == 0 ? 0 : f - NI;
       if constexpr (F8) a[mi] = frag8(st, wm * 128 + mi * 32, kk);
-      else a[mi] = frag<BK, ALAY>(st, wm * 128 + mi * 32, kk, lane);
+      else a[mi] = frag<BK, ALAY>(st, (HALFM ? arow : wm * 128) + mi * 32, kk, lane);
     } else {
       const int ni = f - 1;
       const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
@@ -848,10 +860,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // vector registers, which the instruction does not take)
   // (F8, NOREAD: the step reads no fragments - the last k-step of a tile,
   // whose successor reads its own after the epilogue)
+  // (MIA: the wave's active row blocks, MI, or 2 in a half tile, whose
+  // MFMAs the step computes; RIA: the row blocks whose next fragments it
+  // reads - MIA, or MI where the next step is the next tile's)
   auto kstep = [&](auto nd_c, auto np_c, auto pure_c, const Frag(&a)[MI], const Frag(&b)[NI],
                    Frag(&na)[MI], Frag(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos,
-                   auto noread_c) __attribute__((always_inline)) {
+                   auto noread_c, auto mia_c, auto ria_c) __attribute__((always_inline)) {
     constexpr bool NOREAD = decltype(noread_c)::value;
+    constexpr int MIA = decltype(mia_c)::value;
+    constexpr int RIA = decltype(ria_c)::value;
     constexpr int ND = decltype(nd_c)::value;
     constexpr int NO = ND + decltype(np_c)::value;
 #pragma unroll
@@ -874,8 +891,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         if (!NOREAD && ni == NI - 1) read_frag(rst, rkk, mi == 0 ? 0 : NI + mi, na, nb);
         if (!NOREAD && mi == MI - 1) read_frag(rst, rkk, 1 + ni, na, nb);
       } else {
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-        if ((i & 1) == 0 && (i >> 1) < MI + NI) read_frag(rst, rkk, i >> 1, na, nb);
+        if (mi < MIA) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        // (fragment f: a[0], then b[0..NI-1], then a[1..MI-1])
+        if ((i & 1) == 0 && (i >> 1) < MI + NI && ((i >> 1) <= NI || (i >> 1) - NI < RIA))
+          read_frag(rst, rkk, i >> 1, na, nb);
       }
 #pragma unroll
       for (int o = (i * NO) / 16; o < ((i + 1) * NO) / 16; ++o) {
@@ -954,10 +973,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   };
 
   // PURE: every position the k-tile loads (kt+1 .. kt+1+PFD) is the current tile's.
-  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c) __attribute__((always_inline)) {
+  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c, auto mia_c) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     using PU = decltype(pure_c);
+    using MIA = decltype(mia_c);
     const uint16_t* st = ring[(uint32_t)(gbase + kt) % STAGES];
     if constexpr (F8) {  // this k-tile's scales, read with its first fragments
       sA = nsA;
@@ -970,16 +990,18 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     for (int s = 0; s < KS - 1; ++s) {
       if (s == 0) {
         if (FIRST)
-          kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD, std::false_type());
+          kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD, std::false_type(), MIA(),
+                MIA());
         else
-          kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD, std::false_type());
+          kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD,
+                std::false_type(), MIA(), MIA());
         // GATH_B: position kt+1 is issued whole; its offsets make way for
         // those of kt+2 (issued at this k-tile's end and the next's start),
         // and the prefetch offset for kt+2+PFD (next k-tile's prefetch).
         if (GKB) tok_fill_pos(kt + 2, kt + 2 + PFD);
       } else {
         kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0,
-              std::false_type());
+              std::false_type(), MIA(), MIA());
       }
     }
     // Position kt+1 has landed: after its last DMA come only its prefetches,
@@ -1001,10 +1023,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // (F8: the last k-tile leaves the next tile's first fragments and scales
     // to be read after the epilogue, so they are not live through it)
     using NR = std::integral_constant<bool, F8 && LAST>;
-    if (LAST)
-      kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR());
-    else
-      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR());
+    if (LAST) {
+      // (this step reads the next tile's first fragments: at that tile's A
+      // rows, and all its row blocks, for a full tile may follow a half one)
+      if constexpr (HALFM) arow = arow_next;
+      kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR(), MIA(),
+            std::integral_constant<int, MI>());
+    } else {
+      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR(), MIA(), MIA());
+    }
   };
 
   // Epilogue resources: C (or C2 for rows past msplit) from the tile's
@@ -1054,6 +1081,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
     // more hands over early.)
     pipe = has_next && lnext.nk >= STAGES && cur.nk >= (GATH != 0 ? 5 : 1);
     nxt = pipe ? lnext : null_ld;
+    // Half tiles: this tile's A row base, and the next tile's, at which the
+    // last k-step reads its first fragments when it is loaded ahead.  (When
+    // this tile was loaded ahead, its first fragments were read at the
+    // arow_next set here one tile earlier, for the same tile.)
+    const bool half = HALFM && t.mlim <= 128;
+    if constexpr (HALFM) {
+      arow = half ? wm * 64 : wm * 128;
+      arow_next = (pipe && tn.mlim <= 128) ? wm * 64 : wm * 128;
+    }
 
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -1091,16 +1127,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       }
       using T_ = std::true_type;
       using F_ = std::false_type;
-      if (cur.nk == 1) {
-        ktile(0, T_(), T_(), F_());
-      } else {
-        ktile(0, T_(), F_(), F_());
-        // k-tiles whose positions kt+1 .. kt+1+PFD are all the current tile's
-        const int pure_end = max(1, cur.nk - 1 - PFD);
-        for (int kt = 1; kt < pure_end; ++kt) ktile(kt, F_(), F_(), T_());
-        for (int kt = pure_end; kt < cur.nk - 1; ++kt) ktile(kt, F_(), F_(), F_());
-        ktile(cur.nk - 1, F_(), T_(), F_());
-      }
+      auto kloop = [&](auto mia_c) __attribute__((always_inline)) {
+        if (cur.nk == 1) {
+          ktile(0, T_(), T_(), F_(), mia_c);
+        } else {
+          ktile(0, T_(), F_(), F_(), mia_c);
+          // k-tiles whose positions kt+1 .. kt+1+PFD are all the current tile's
+          const int pure_end = max(1, cur.nk - 1 - PFD);
+          for (int kt = 1; kt < pure_end; ++kt) ktile(kt, F_(), F_(), T_(), mia_c);
+          for (int kt = pure_end; kt < cur.nk - 1; ++kt) ktile(kt, F_(), F_(), F_(), mia_c);
+          ktile(cur.nk - 1, F_(), T_(), F_(), mia_c);
+        }
+      };
+      if (HALFM && half) kloop(std::integral_constant<int, 2>());
+      else kloop(std::integral_constant<int, MI>());
     }
 
     // Epilogue.  Each wave stages its 32 x 128 block acc[mi] eight rows at a
@@ -1186,7 +1226,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       };
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const int rowb = wm * 128 + mi * 32;  // the block's first row in the tile
+        // the block's first row in the tile (a half tile's inactive blocks 2
+        // and 3 are placed past its 256 rows, where every access is out of
+        // range; arow already holds the next tile's base here)
+        const int rowb = (HALFM && half) ? (mi < 2 ? wm * 64 + mi * 32 : 256 + mi * 32) : wm * 128 + mi * 32;
         // Rows of this block lie on one side of msplit (a multiple of 32).
         const bool side2 = PLAIN && p.msplit && m0g + rowb >= p.msplit;
         if (EPI == EPI_ADD && mi % AB == 0) {
