@@ -171,6 +171,10 @@ struct Scheduler {
       // together and A (T x d) streams from memory once, not once per n-tile.
       const bool nf = GRP == GRP_NONE && MT >= NT;
       int mt = nf ? local / NT : local % MT, nt = nf ? local % NT : local / MT;
+      // With two n-tiles (the second often narrower: E = 384 is 256 + 128)
+      // a workgroup would take the same n-tile in every round of the static
+      // order; swapping them in odd rounds gives each one both in turn.
+      if (GRP == GRP_NONE && BANDED && nf && NT == 2 && ((id / (int)gridDim.x) & 1)) nt ^= 1;
       t.mtile = mt;
       t.mtiles = MT;
       if (GRP == GRP_K && BANDED && p.band > 0 && p.band < MT) {

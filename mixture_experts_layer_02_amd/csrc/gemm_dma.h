@@ -314,11 +314,17 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // and 1 only: each wave then holds half the MFMAs of a full tile, and the
   // outputs stay disjoint.
   constexpr bool HALFM = GRP == GRP_M && !F8;
+  // Likewise across columns for plain products (the router's logits, N = E =
+  // 384): a tile with at most 128 valid columns has wave column wn compute
+  // columns 64 wn .. 64 wn + 63 (bcol, the B row base of its fragment reads)
+  // with its column blocks 0 and 1 only.
+  constexpr bool HALFN = GRP == GRP_NONE && !DUAL && !F8 && !BQ8;
   // The steady k-loop's DMAs take one wait state (see dma16), except in the
   // gathered-B weight-gradient kernels, whose k-loop reloads spilled SGPRs
   // next to its DMAs: they take five.
   constexpr bool LIGHT_K = MOE_LIGHT_DMA && GATH != GATH_B;
   int arow = wm * 128, arow_next = wm * 128;
+  int bcol = wn * 128, bcol_next = wn * 128;
   const uint16_t* Ag = reinterpret_cast<const uint16_t*>(p.A);
   const uint16_t* Bg = reinterpret_cast<const uint16_t*>(p.B);
   const uint16_t* B2g = reinterpret_cast<const uint16_t*>(p.B2);
@@ -815,7 +821,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       else a[mi] = frag<BK, ALAY>(st, (HALFM ? arow : wm * 128) + mi * 32, kk, lane);
     } else {
       const int ni = f - 1;
-      const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : wn * 128 + ni * 32;
+      const int brow = DUAL ? (ni / 2) * 128 + wn * 64 + (ni % 2) * 32 : (HALFN ? bcol : wn * 128) + ni * 32;
       if constexpr (F8) b[ni] = frag8(st + TILE_ELEMS, brow, kk);
       else b[ni] = BQ8 ? frag_q8(st + TILE_ELEMS, brow, kk, lane) : frag<BK, BLAY>(st + TILE_ELEMS, brow, kk, lane);
     }
@@ -860,15 +866,18 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   // vector registers, which the instruction does not take)
   // (F8, NOREAD: the step reads no fragments - the last k-step of a tile,
   // whose successor reads its own after the epilogue)
-  // (MIA: the wave's active row blocks, MI, or 2 in a half tile, whose
-  // MFMAs the step computes; RIA: the row blocks whose next fragments it
-  // reads - MIA, or MI where the next step is the next tile's)
+  // (MIA, NIA: the wave's active row and column blocks - MI and NI, or 2 in
+  // a half tile - whose MFMAs the step computes; RIA, RNIA: the blocks whose
+  // next fragments it reads - the active ones, or all where the next step is
+  // the next tile's)
   auto kstep = [&](auto nd_c, auto np_c, auto pure_c, const Frag(&a)[MI], const Frag(&b)[NI],
                    Frag(&na)[MI], Frag(&nb)[NI], const uint16_t* rst, int rkk, int dpos, int q0, int ppos,
-                   auto noread_c, auto mia_c, auto ria_c) __attribute__((always_inline)) {
+                   auto noread_c, auto mia_c, auto ria_c, auto nia_c, auto rnia_c) __attribute__((always_inline)) {
     constexpr bool NOREAD = decltype(noread_c)::value;
     constexpr int MIA = decltype(mia_c)::value;
     constexpr int RIA = decltype(ria_c)::value;
+    constexpr int NIA = decltype(nia_c)::value;
+    constexpr int RNIA = decltype(rnia_c)::value;
     constexpr int ND = decltype(nd_c)::value;
     constexpr int NO = ND + decltype(np_c)::value;
 #pragma unroll
@@ -891,9 +900,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
         if (!NOREAD && ni == NI - 1) read_frag(rst, rkk, mi == 0 ? 0 : NI + mi, na, nb);
         if (!NOREAD && mi == MI - 1) read_frag(rst, rkk, 1 + ni, na, nb);
       } else {
-        if (mi < MIA) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        if (mi < MIA && ni < NIA)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
         // (fragment f: a[0], then b[0..NI-1], then a[1..MI-1])
-        if ((i & 1) == 0 && (i >> 1) < MI + NI && ((i >> 1) <= NI || (i >> 1) - NI < RIA))
+        if ((i & 1) == 0 && (i >> 1) < MI + NI &&
+            ((i >> 1) == 0 || ((i >> 1) <= NI ? (i >> 1) - 1 < RNIA : (i >> 1) - NI < RIA)))
           read_frag(rst, rkk, i >> 1, na, nb);
       }
 #pragma unroll
@@ -973,11 +984,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
   };
 
   // PURE: every position the k-tile loads (kt+1 .. kt+1+PFD) is the current tile's.
-  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c, auto mia_c) __attribute__((always_inline)) {
+  auto ktile = [&](int kt, auto first_c, auto last_c, auto pure_c, auto mia_c, auto nia_c) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     using PU = decltype(pure_c);
     using MIA = decltype(mia_c);
+    using NIA = decltype(nia_c);
     const uint16_t* st = ring[(uint32_t)(gbase + kt) % STAGES];
     if constexpr (F8) {  // this k-tile's scales, read with its first fragments
       sA = nsA;
@@ -991,17 +1003,17 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       if (s == 0) {
         if (FIRST)
           kstep(N0(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, 0, 0, kt + 1 + PFD, std::false_type(), MIA(),
-                MIA());
+                MIA(), NIA(), NIA());
         else
           kstep(NDP1(), NPP(), PU(), fa[0], fb[0], fa[1], fb[1], st, 1, kt + 1, PART, kt + 1 + PFD,
-                std::false_type(), MIA(), MIA());
+                std::false_type(), MIA(), MIA(), NIA(), NIA());
         // GATH_B: position kt+1 is issued whole; its offsets make way for
         // those of kt+2 (issued at this k-tile's end and the next's start),
         // and the prefetch offset for kt+2+PFD (next k-tile's prefetch).
         if (GKB) tok_fill_pos(kt + 2, kt + 2 + PFD);
       } else {
         kstep(N0(), N0(), PU(), fa[s & 1], fb[s & 1], fa[(s + 1) & 1], fb[(s + 1) & 1], st, s + 1, 0, 0, 0,
-              std::false_type(), MIA(), MIA());
+              std::false_type(), MIA(), MIA(), NIA(), NIA());
       }
     }
     // Position kt+1 has landed: after its last DMA come only its prefetches,
@@ -1027,10 +1039,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       // (this step reads the next tile's first fragments: at that tile's A
       // rows, and all its row blocks, for a full tile may follow a half one)
       if constexpr (HALFM) arow = arow_next;
+      if constexpr (HALFN) bcol = bcol_next;
       kstep(NDF(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR(), MIA(),
-            std::integral_constant<int, MI>());
+            std::integral_constant<int, MI>(), NIA(), std::integral_constant<int, NI>());
     } else {
-      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR(), MIA(), MIA());
+      kstep(NDP(), N0(), PU(), fa[1], fb[1], fa[0], fb[0], nst, 0, kt + 2, 0, 0, NR(), MIA(), MIA(), NIA(), NIA());
     }
   };
 
@@ -1090,6 +1103,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       arow = half ? wm * 64 : wm * 128;
       arow_next = (pipe && tn.mlim <= 128) ? wm * 64 : wm * 128;
     }
+    const bool halfn = HALFN && t.nlim <= 128;
+    if constexpr (HALFN) {
+      bcol = halfn ? wn * 64 : wn * 128;
+      bcol_next = (pipe && tn.nlim <= 128) ? wn * 64 : wn * 128;
+    }
 
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -1127,20 +1145,24 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       }
       using T_ = std::true_type;
       using F_ = std::false_type;
-      auto kloop = [&](auto mia_c) __attribute__((always_inline)) {
+      auto kloop = [&](auto mia_c, auto nia_c) __attribute__((always_inline)) {
         if (cur.nk == 1) {
-          ktile(0, T_(), T_(), F_(), mia_c);
+          ktile(0, T_(), T_(), F_(), mia_c, nia_c);
         } else {
-          ktile(0, T_(), F_(), F_(), mia_c);
+          ktile(0, T_(), F_(), F_(), mia_c, nia_c);
           // k-tiles whose positions kt+1 .. kt+1+PFD are all the current tile's
           const int pure_end = max(1, cur.nk - 1 - PFD);
-          for (int kt = 1; kt < pure_end; ++kt) ktile(kt, F_(), F_(), T_(), mia_c);
-          for (int kt = pure_end; kt < cur.nk - 1; ++kt) ktile(kt, F_(), F_(), F_(), mia_c);
-          ktile(cur.nk - 1, F_(), T_(), F_(), mia_c);
+          for (int kt = 1; kt < pure_end; ++kt) ktile(kt, F_(), F_(), T_(), mia_c, nia_c);
+          for (int kt = pure_end; kt < cur.nk - 1; ++kt) ktile(kt, F_(), F_(), F_(), mia_c, nia_c);
+          ktile(cur.nk - 1, F_(), T_(), F_(), mia_c, nia_c);
         }
       };
-      if (HALFM && half) kloop(std::integral_constant<int, 2>());
-      else kloop(std::integral_constant<int, MI>());
+      using IMI = std::integral_constant<int, MI>;
+      using INI = std::integral_constant<int, NI>;
+      using I2 = std::integral_constant<int, 2>;
+      if (HALFM && half) kloop(I2(), INI());
+      else if (HALFN && halfn) kloop(IMI(), I2());
+      else kloop(IMI(), INI());
     }
 
     // Epilogue.  Each wave stages its 32 x 128 block acc[mi] eight rows at a
@@ -1166,7 +1188,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       constexpr int CPR = OC / W;               // vectors per row
       constexpr int VPL = 8 * CPR / 64;          // vectors per lane_e per slab
       static_assert(8 * CPR % 64 == 0, "whole vectors per lane_e");
-      const int col_base = (DUAL ? wn * 64 : wn * 128);
+      // (a half-N tile's wave column covers 64 columns; its vectors past them,
+      // from the inactive column blocks, are masked below)
+      const int col_base = DUAL ? wn * 64 : (HALFN && halfn) ? wn * 64 : wn * 128;
+      const int cvlim = (HALFN && halfn) ? 64 : OC;
       // Resources (row 0 = the tile's first row, element 0 = its first column).
       const int64_t m0g = t.m0;
       __amdgpu_buffer_rsrc_t r0, r1;
@@ -1246,7 +1271,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 const int row = rowb2 + sl * 8 + rl, col = col_base + cv;
                 const int64_t eo = (int64_t)row * ldo + col;
                 oldc[m2][sl][vi] = __builtin_amdgcn_raw_buffer_load_b128(
-                    side2b ? r1 : r0, col < t.nlim ? (uint32_t)(eo * (CF32 ? 4 : 2)) : 0x80000000u, 0, 0);
+                    side2b ? r1 : r0, col < t.nlim && cv < cvlim ? (uint32_t)(eo * (CF32 ? 4 : 2)) : 0x80000000u, 0,
+                    0);
               }
           }
         }
@@ -1305,7 +1331,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             }
             const int row = rowb + sl * 8 + rl;  // row in the tile
             const int col = col_base + cv;       // column in the tile
-            const bool ok = col < t.nlim;
+            const bool ok = col < t.nlim && cv < cvlim;
             const int64_t eo = (int64_t)row * ldo + col;  // element offset from the corner
             if (PLAIN) {
               const __amdgpu_buffer_rsrc_t rc = side2 ? r1 : r0;
