@@ -1235,11 +1235,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
       // before it, so each batch costs one round trip after the previous
       // batch's stores. EPI_ADD: the old C values of two 32-row blocks (one
       // for fp32 C, whose two would not fit in registers). EPI_SWIGLU_BWD: G
-      // and U of the four 8-row slabs of one block.
+      // and U (and the row scales) of one 8-row slab, two slabs ahead of its
+      // use, in a window of three (load_gu below).
       constexpr int AB = VPL <= 2 ? 2 : 1;
       u32x4_t oldc[AB][4][VPL];
-      u32x4_t gup[4][VPL][2];
-      uint32_t rsv[4][VPL];
+      u32x4_t gup[3][VPL][2];
+      uint32_t rsv[3][VPL];
       // Rows 8 sl .. 8 sl + 7 of the wave's 32-row block mi, as fp32, into the
       // wave's staging area.
       auto stage_slab = [&](int mi_, int sl_) __attribute__((always_inline)) {
@@ -1249,6 +1250,32 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
           for (int r4 = 0; r4 < 4; ++r4)
             stage[((lane_e >> 5) * 4 + r4) * SP + ni * 32 + (lane_e & 31)] = acc[mi_][ni][sl_ * 4 + r4];
       };
+      // EPI_SWIGLU_BWD: G and U (ROWSC: and the rows' scales) of slab j = 4 mi
+      // + sl into gup[j % 3], issued two slabs before slab j is stored.  Their
+      // wait then covers the stores of slab j - 2 and earlier, which have had
+      // two slabs' time to drain, not those of slab j - 1 (with a batch per
+      // 32-row block, each batch waited for the previous block's stores and
+      // then made a round trip of its own).
+      auto load_gu = [&](int j) __attribute__((always_inline)) {
+        const int mi_ = j >> 2, sl_ = j & 3;
+        const int rowb_ = (HALFM && half) ? (mi_ < 2 ? wm * 64 + mi_ * 32 : 256 + mi_ * 32) : wm * 128 + mi_ * 32;
+#pragma unroll
+        for (int vi = 0; vi < VPL; ++vi) {
+          const int e = lane_e + vi * 64;
+          const int rl = e / CPR, cv = (e % CPR) * W;
+          const int row = rowb_ + sl_ * 8 + rl, col = col_base + cv;
+          const int64_t eo = (int64_t)row * ldo + col;
+          const bool ok = col < t.nlim;
+          gup[j % 3][vi][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+          gup[j % 3][vi][1] =
+              __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
+          if (ROWSC) rsv[j % 3][vi] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)row * 4u, 0, 0);
+        }
+      };
+      if (EPI == EPI_SWIGLU_BWD) {
+        load_gu(0);
+        load_gu(1);
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         // the block's first row in the tile (a half tile's inactive blocks 2
@@ -1276,24 +1303,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
               }
           }
         }
-        if (EPI == EPI_SWIGLU_BWD) {
-#pragma unroll
-          for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-            for (int vi = 0; vi < VPL; ++vi) {
-              const int e = lane_e + vi * 64;
-              const int rl = e / CPR, cv = (e % CPR) * W;
-              const int row = rowb + sl * 8 + rl, col = col_base + cv;
-              const int64_t eo = (int64_t)row * ldo + col;
-              const bool ok = col < t.nlim;
-              gup[sl][vi][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
-              gup[sl][vi][1] =
-                  __builtin_amdgcn_raw_buffer_load_b128(r1, ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u, 0, 0);
-              if (ROWSC) rsv[sl][vi] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)row * 4u, 0, 0);
-            }
-        }
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
+          if (EPI == EPI_SWIGLU_BWD && mi * 4 + sl + 2 < MI * 4) load_gu(mi * 4 + sl + 2);
           if (mi == 0 && sl == 0) stage_slab(0, 0);  // later slabs are staged one ahead, below
           float vv[VPL][W], vv2[VPL][W];
 #pragma unroll
@@ -1390,12 +1402,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
             } else {  // EPI_SWIGLU_BWD: v = dH
               const uint32_t og = ok ? (uint32_t)(eo * 2) : 0x80000000u;
               const uint32_t ou = ok ? (uint32_t)((eo + p.N) * 2) : 0x80000000u;
-              u32x4_t gq = gup[sl][vi][0];
-              u32x4_t uq = gup[sl][vi][1];
+              u32x4_t gq = gup[(mi * 4 + sl) % 3][vi][0];
+              u32x4_t uq = gup[(mi * 4 + sl) % 3][vi][1];
               asm volatile("" : "+v"(gq), "+v"(uq));  // used here, not hoisted to their loads
               float sc = 1.0f;
               if (ROWSC) {
-                uint32_t sw = rsv[sl][vi];
+                uint32_t sw = rsv[(mi * 4 + sl) % 3][vi];
                 asm volatile("" : "+v"(sw));
                 sc = __uint_as_float(sw);
               }
