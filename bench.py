@@ -44,7 +44,7 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop/B where the two 
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwdbwd_1t_hbm_traffic.txt")
 GEMM_ROWS = ("A5_gate_up", "A6_down", "B2_dh", "B3_dx", "B4_dw13", "B4_dw2")
-EXTRA_WORKLOADS = ("share_1t", "share_1t_fp8mm", "zipf_1t", "uniform_1t")
+EXTRA_WORKLOADS = ("fwdbwd_1t_wgrad_f32", "share_1t", "share_1t_fp8mm", "zipf_1t", "uniform_1t")
 
 
 @dataclasses.dataclass
@@ -137,7 +137,7 @@ def _copy_calibration(nbytes):
 def _vendor_gemm(torch, dev, NL, R, d, f, ours):
     """The vendor's bf16 GEMM (torch.bmm, hipBLASLt) on the products of the grouped GEMM rows, with
     equal segments of R / NL rows per expert, for comparison with the grouped kernels' own times.
-    Every operand is a contiguous tensor; outputs are bf16 (the weight gradients here are fp32)."""
+    Every operand is a contiguous tensor; outputs are bf16 (the weight gradients here as --wgrad-dtype)."""
     m = max(1, round(R / NL))
     g = torch.Generator(device=dev).manual_seed(5)
 
@@ -225,10 +225,11 @@ def _cpu_baseline(cfg, inp, sample_tokens, n_groups, extra_inputs):
 class Workload:
     """Device tensors and the ordered rows of one workload's step."""
 
-    def __init__(self, moe, torch, cfg, inp, args, dev, fp8mm=False):
+    def __init__(self, moe, torch, cfg, inp, args, dev, fp8mm=False, wgrad=None):
         """fp8mm: gate/up and down on the FP8 matrix cores (forward only): W1,
         W3 and W2 held as E4M3 codes with power-of-two block scales, x and h
-        quantised each step."""
+        quantised each step.  wgrad: the expert weight gradients' type, "bf16"
+        or "f32" (default --wgrad-dtype; fp32 layers always write fp32)."""
         self.cfg = cfg
         T, d, f, E, k, NL = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.num_local
 
@@ -243,8 +244,11 @@ class Workload:
         bias = up(inp["bias"]) if "bias" in inp else None
         routing = (up(inp["idx"]), up(inp["w"])) if cfg.routing == "roundrobin" else None
         counters = moe.new_tile_counters(dev) if args.schedule == "dynamic" else None
+        wgrad = (wgrad or args.wgrad_dtype) if cfg.dtype == "bf16" else "f32"
+        self.wgrad = wgrad
+        wb = 2 if wgrad == "bf16" else 4   # bytes per weight-gradient element written
         D = self.D = moe.make_desc(T, d, f, E, k, cfg.expert_begin, NL, cfg.dtype, cfg.renormalize,
-                                   tile_counters=counters)
+                                   tile_counters=counters, wgrad_dtype=wgrad)
         gather = args.x_path == "gather" or fp8mm
         gdy = args.dy_path == "gather" and cfg.dtype == "bf16"
         fuse_rdx = args.router_dx == "fused" and bool(cfg.renormalize)
@@ -373,14 +377,14 @@ class Workload:
             add("B4_dw13", lambda: moe.expert_bwd_dw_gate_up(D, b.offsets, b.row_token if gather else None,
                                                              g["x"] if gather else b.x_perm, b.dgu, b.dW1,
                                                              b.dW3), 1,
-                lambda R: 4.0 * R * d * f, lambda R: R * d * bb + R * 2 * f * bb + 2 * NL * f * d * 4)
+                lambda R: 4.0 * R * d * f, lambda R: R * d * bb + R * 2 * f * bb + 2 * NL * f * d * wb)
             if gdy:
                 add("B4_dw2", lambda: moe.expert_bwd_dw_down_gather(D, b.offsets, b.row_token, g["dy"], b.hw,
                                                                     b.dW2), 1,
-                    lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
+                    lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * wb)
             else:
                 add("B4_dw2", lambda: moe.expert_bwd_dw_down(D, b.offsets, b.dy_perm, b.h, b.dW2), 1,
-                    lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * 4)
+                    lambda R: 2.0 * R * d * f, lambda R: R * d * bb + R * f * bb + NL * f * d * wb)
             if parts:
                 add("B5_dtopk_w", lambda: moe.dtopk_w_from_parts(D, b.slot_row, b.dtopk_part, b.dtopk_w), 1,
                     nbytes=lambda R: T * k * 8 + R * NP * 4)
@@ -524,6 +528,9 @@ def main():
                     help="expert weights held as blockwise-128 E4M3 codes + scales, dequantised to bf16 each step")
     ap.add_argument("--fp8-gemm", action="store_true",
                     help="with --fp8-weights: the forward expert GEMMs read the FP8 weights directly")
+    ap.add_argument("--wgrad-dtype", choices=["bf16", "f32"], default="bf16",
+                    help="type of the expert weight gradients dW1, dW3, dW2: bf16 (float32 sums rounded once at "
+                         "the store; gradients computed in bf16 and reduced in fp32, as on the pages) or f32")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vendor-gemm", action="store_true",
@@ -562,7 +569,7 @@ def main():
     avg, step_ms, wall = run(moe, torch, wl, args, args.steps, args.warmup, flush, note)
     peak_mem = torch.cuda.max_memory_allocated()
     default_run = (cfg.name == "fwdbwd_1t" and args.x_path == "perm" and args.dy_path == "gather"
-                   and args.router_dx == "fused" and args.dtopk == "parts" and not (
+                   and args.router_dx == "fused" and args.dtopk == "parts" and args.wgrad_dtype == "bf16" and not (
         args.fp8_weights or args.fp8_gemm or args.hold_cus or args.n_groups > 1 or args.schedule != "static"))
     main_sum = summarize(wl, avg, step_ms, wall, args.steps, default_run)
     ms_step = main_sum["ms_per_step"]
@@ -571,24 +578,30 @@ def main():
     del wl
     torch.cuda.empty_cache()
 
-    # forward-only 1T workloads after the main one
+    # the other 1T workloads after the main one: the same step with fp32 weight
+    # gradients (on the main step's inputs), then forward-only ones
     extras, extra_inputs = {}, {}
     names = [] if args.extra_workloads == "none" else [n for n in args.extra_workloads.split(",") if n]
     for name in names:
         fp8mm = name.endswith("_fp8mm")
-        base = name[:-len("_fp8mm")] if fp8mm else name
+        wf32 = name.endswith("_wgrad_f32")
+        base = name[:-len("_fp8mm")] if fp8mm else name[:-len("_wgrad_f32")] if wf32 else name
         c = synth.CONFIGS[base]
-        data = extra_inputs.get(base) or synth.make_inputs(c)
+        if wf32 and (base != cfg.name or args.wgrad_dtype == "f32" or c.dtype != "bf16"):
+            continue                       # only beside a bf16-gradient run of the same workload
+        data = inp if base == cfg.name else extra_inputs.get(base) or synth.make_inputs(c)
         if base == "share_1t":             # reused by the fp8 variant and the CPU baseline's sample
             extra_inputs[base] = data
-        w2 = Workload(moe, torch, c, data, args, dev, fp8mm=fp8mm)
+        w2 = Workload(moe, torch, c, data, args, dev, fp8mm=fp8mm, wgrad="f32" if wf32 else None)
         torch.cuda.synchronize()
         a2, s2, wall2 = run(moe, torch, w2, args, args.extra_steps, args.warmup, flush, note)
         sm = summarize(w2, a2, s2, wall2, args.extra_steps, False)
         extras[name] = {
-            "workload": f"{base}: T={c.T} d={c.d} E={c.E} ({c.num_local} local) top-{c.k} f={c.f} fwd, "
-                        f"routing {c.routing}" + (", gate/up and down on the fp8 matrix cores (e4m3 x, h and "
-                                                  "W1/W3/W2 with power-of-two block-128 scales)" if fp8mm else ""),
+            "workload": f"{base}: T={c.T} d={c.d} E={c.E} ({c.num_local} local) top-{c.k} f={c.f} "
+                        f"{'fwd+bwd' if c.backward else 'fwd'}, routing {c.routing}"
+                        + (", gate/up and down on the fp8 matrix cores (e4m3 x, h and W1/W3/W2 with "
+                           "power-of-two block-128 scales)" if fp8mm else "")
+                        + (", weight gradients dW1, dW3, dW2 in fp32" if wf32 else ""),
             "steps": args.extra_steps, "ms_per_step": round(sm["ms_per_step"], 4),
             "tokens/s": round(c.T / sm["ms_per_step"] * 1e3, 1), "routed_rows": sm["R"],
             "grouped_gemm_tflops": round(sm["gemm_tflops"], 1),
@@ -626,6 +639,10 @@ def main():
                                  and cfg.renormalize else "dx += dlogits Wr product"),
                    "dtopk_w": ("partial sums of <dy W2, h> in the dH product" if args.dtopk == "parts"
                                else "dot products of dy and y_perm"),
+                   "weight_grads": ("bf16: float32 sums rounded once at the store (the pages compute "
+                                    "gradients in bf16 and reduce them in fp32); the same step with fp32 "
+                                    "weight gradients is workloads.fwdbwd_1t_wgrad_f32"
+                                    if args.wgrad_dtype == "bf16" and cfg.dtype == "bf16" else "fp32"),
                    "expert_weights": ("bf16" if not args.fp8_weights else
                                       "fp8 e4m3 blocks of 128, read by the forward GEMMs" if args.fp8_gemm else
                                       "fp8 e4m3 blocks of 128, dequantised each step"),

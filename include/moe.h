@@ -92,6 +92,12 @@ typedef struct moe_desc {
                                every GEMM launch leaves them zero again.  Calls that share one array
                                must not run concurrently (same stream, or ordered by events).  Ignored
                                (may be NULL) for MOE_SCHEDULE_STATIC. */
+  int32_t wgrad_dtype;      /* enum moe_dtype of the expert weight gradients dW1, dW3, dW2 written by
+                               the B4 calls: MOE_F32 (0) float32, or MOE_BF16 (dtype MOE_BF16 only,
+                               else MOE_ERR_UNSUPPORTED) bf16 - each sum accumulated in float32 and
+                               rounded once to bf16 (nearest, ties to even) at the store, the
+                               gradients computed in bf16 and reduced in fp32 of the Domyn page,
+                               section "BF16 gradient all-to-all with FP32 accumulation" */
 } moe_desc;
 
 /* Host-only query: bytes of device workspace that call `op` needs for desc
@@ -248,13 +254,14 @@ int moe_expert_bwd_dx(const moe_desc* desc, const int32_t* offsets, const void* 
                       const void* dgu, void* dx_perm, void* stream);
 
 /* B4, weight gradients of the expert MLP (variable-K grouped GEMMs):
- *   dW1[n] = dG_n^T x_perm_n, dW3[n] = dU_n^T x_perm_n  ([NL][f][d] float32),
- *   dW2[n] = dy_perm_n^T h_n                           ([NL][d][f] float32),
- *   where _n is the row segment of expert n.  They are overwritten, not
- *   accumulated; an expert with no rows gets exact zeros. */
+ *   dW1[n] = dG_n^T x_perm_n, dW3[n] = dU_n^T x_perm_n  ([NL][f][d]),
+ *   dW2[n] = dy_perm_n^T h_n                           ([NL][d][f]),
+ *   where _n is the row segment of expert n, as float32 or bf16 by
+ *   desc->wgrad_dtype (here and in every B4 call below).  They are
+ *   overwritten, not accumulated; an expert with no rows gets exact zeros. */
 int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const void* x_perm,
-                           const void* h, const void* dgu, const void* dy_perm, float* dW1,
-                           float* dW3, float* dW2, void* ws, size_t ws_bytes, void* stream);
+                           const void* h, const void* dgu, const void* dy_perm, void* dW1,
+                           void* dW3, void* dW2, void* ws, size_t ws_bytes, void* stream);
 
 /* B4 with the gather fused (as moe_expert_gate_up_gather): dW1 and dW3 read
  * the rows of x_perm as x[row_token[r]] inside the GEMM's operand loads.
@@ -262,23 +269,23 @@ int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const v
  *   conditions as moe_expert_gate_up_gather. */
 int moe_grouped_ffn_bwd_dw_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
                                   const void* x, const void* h, const void* dgu, const void* dy_perm,
-                                  float* dW1, float* dW3, float* dW2, void* stream);
+                                  void* dW1, void* dW3, void* dW2, void* stream);
 
 /* B4, first launch alone: dW1[n] = dG_n^T a_n and dW3[n] = dU_n^T a_n
- * ([NL][f][d] float32, overwritten; exact zeros for an expert with no rows).
+ * ([NL][f][d], overwritten; exact zeros for an expert with no rows).
  *   row_token NULL: a is x_perm [R_cap][d]; else a is x [T][d] and k-row r
  *   of the product reads x[row_token[r]] (bf16 only, x under 2 GiB, else
  *   MOE_ERR_UNSUPPORTED).  dgu [R_cap][2f] as written by the dH step.
  *   Results are bitwise those of moe_grouped_ffn_bwd_dw's dW1 and dW3. */
 int moe_expert_bwd_dw_gate_up(const moe_desc* desc, const int32_t* offsets,
                               const int32_t* row_token, const void* a, const void* dgu,
-                              float* dW1, float* dW3, void* stream);
+                              void* dW1, void* dW3, void* stream);
 
-/* B4, second launch alone: dW2[n] = dy_perm_n^T h_n ([NL][d][f] float32,
+/* B4, second launch alone: dW2[n] = dy_perm_n^T h_n ([NL][d][f],
  * overwritten; exact zeros for an expert with no rows); bitwise
  * moe_grouped_ffn_bwd_dw's dW2. */
 int moe_expert_bwd_dw_down(const moe_desc* desc, const int32_t* offsets, const void* dy_perm,
-                           const void* h, float* dW2, void* stream);
+                           const void* h, void* dW2, void* stream);
 
 /* The backward with dy read in place (Domyn page, section "Dynamic tile
  * scheduling in SonicMoE": the expert GEMMs run on the dispatch layout, with
@@ -320,12 +327,12 @@ int moe_dtopk_w_from_parts(const moe_desc* desc, const int32_t* slot_row, const 
                            float* dtopk_w, void* stream);
 
 /* B4, dW2 with dy read in place: dW2[n] = sum over rows r of expert n of
- *   dy[row_token[r]]^T hw[r]  ([NL][d][f] float32, overwritten; exact zeros
+ *   dy[row_token[r]]^T hw[r]  ([NL][d][f], overwritten; exact zeros
  *   for an expert with no rows).  dW1 | dW3 come from
  *   moe_expert_bwd_dw_gate_up with row_token. */
 int moe_expert_bwd_dw_down_gather(const moe_desc* desc, const int32_t* offsets,
                                   const int32_t* row_token, const void* dy, const void* hw,
-                                  float* dW2, void* stream);
+                                  void* dW2, void* stream);
 
 /* B5a, backward of the gather: dx[t] = dx_add[t] + sum over local slots j of
  *   dx_perm[slot_row[t][j]], summed in float32; dx [T][d] dtype out;

@@ -48,6 +48,7 @@ class MoeDesc(ctypes.Structure):
         ("renormalize", ctypes.c_int32),
         ("tile_schedule", ctypes.c_int32),
         ("tile_counters", ctypes.c_void_p),
+        ("wgrad_dtype", ctypes.c_int32),
     ]
 
     @property
@@ -144,14 +145,17 @@ def lib():
 
 
 def make_desc(T, d, f, E, k, expert_begin=0, num_local=None, dtype=MOE_BF16, renormalize=1,
-              tile_counters=None) -> MoeDesc:
+              tile_counters=None, wgrad_dtype=MOE_F32) -> MoeDesc:
     """The layer descriptor.  ``tile_counters`` (a zeroed int32 device tensor of
     16 elements, see new_tile_counters) selects the dynamic tile order of the
-    grouped GEMMs; the descriptor keeps a reference to it."""
+    grouped GEMMs; the descriptor keeps a reference to it.  ``wgrad_dtype``:
+    the type of the expert weight gradients dW1, dW3, dW2 ("f32" or "bf16")."""
     if isinstance(dtype, str):
         dtype = MOE_BF16 if dtype == "bf16" else MOE_F32
+    if isinstance(wgrad_dtype, str):
+        wgrad_dtype = MOE_BF16 if wgrad_dtype == "bf16" else MOE_F32
     D = MoeDesc(ctypes.sizeof(MoeDesc), T, d, f, E, k, expert_begin, E if num_local is None else num_local,
-                dtype, renormalize, SCHEDULE_STATIC, None)
+                dtype, renormalize, SCHEDULE_STATIC, None, wgrad_dtype)
     if tile_counters is not None:
         if tile_counters.dtype != torch.int32 or tile_counters.numel() < 16 or not tile_counters.is_cuda:
             raise ValueError("tile_counters must be an int32 device tensor of 16 elements")
@@ -453,9 +457,10 @@ class Buffers:
             self.dtopk_w = torch.empty(T, k, dtype=torch.float32, **z)
             self.dgu = torch.empty(Rc, 2 * f, dtype=dt, **z)
             self.dx_perm = torch.empty(Rc, d, dtype=dt, **z)
-            self.dW1 = torch.empty(NL, f, d, dtype=torch.float32, **z)
-            self.dW3 = torch.empty(NL, f, d, dtype=torch.float32, **z)
-            self.dW2 = torch.empty(NL, d, f, dtype=torch.float32, **z)
+            wdt = torch.bfloat16 if desc.wgrad_dtype == MOE_BF16 else torch.float32
+            self.dW1 = torch.empty(NL, f, d, dtype=wdt, **z)
+            self.dW3 = torch.empty(NL, f, d, dtype=wdt, **z)
+            self.dW2 = torch.empty(NL, d, f, dtype=wdt, **z)
             self.dlogits = torch.empty(T, E, dtype=torch.float32, **z)
             self.dWr = torch.empty(E, d, dtype=torch.float32, **z)
             self.dx = torch.empty(T, d, dtype=dt, **z)

@@ -32,6 +32,8 @@ int check_desc(const moe_desc* d) {
   if (d->tile_schedule != MOE_SCHEDULE_STATIC && d->tile_schedule != MOE_SCHEDULE_DYNAMIC)
     return MOE_ERR_INVALID_ARG;
   if (d->tile_schedule == MOE_SCHEDULE_DYNAMIC && !need(d->tile_counters)) return MOE_ERR_INVALID_ARG;
+  if (d->wgrad_dtype != MOE_F32 && d->wgrad_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->wgrad_dtype == MOE_BF16 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->d % 64 || d->f % 64 || d->E % 8 || d->E > 1024 || d->k > 32) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->T * d->k >= (1ll << 31) || (int64_t)d->T * d->E >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -209,8 +211,8 @@ int moe_expert_gate_up_gather(const moe_desc* desc, const int32_t* offsets, cons
 }
 
 int moe_grouped_ffn_bwd_dw_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
-                                  const void* x, const void* h, const void* dgu, const void* dy_perm, float* dW1,
-                                  float* dW3, float* dW2, void* stream) {
+                                  const void* x, const void* h, const void* dgu, const void* dy_perm, void* dW1,
+                                  void* dW3, void* dW2, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(offsets) || !need(row_token) || !need(x) || !need(h) || !need(dgu) || !need(dy_perm) || !need(dW1) ||
@@ -221,7 +223,7 @@ int moe_grouped_ffn_bwd_dw_gather(const moe_desc* desc, const int32_t* offsets, 
 }
 
 int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const void* x_perm, const void* h,
-                           const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2, void* ws,
+                           const void* dgu, const void* dy_perm, void* dW1, void* dW3, void* dW2, void* ws,
                            size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
@@ -234,7 +236,7 @@ int moe_grouped_ffn_bwd_dw(const moe_desc* desc, const int32_t* offsets, const v
 }
 
 int moe_expert_bwd_dw_gate_up(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token, const void* a,
-                              const void* dgu, float* dW1, float* dW3, void* stream) {
+                              const void* dgu, void* dW1, void* dW3, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(offsets) || !opt(row_token) || !need(a) || !need(dgu) || !need(dW1) || !need(dW3))
@@ -244,7 +246,7 @@ int moe_expert_bwd_dw_gate_up(const moe_desc* desc, const int32_t* offsets, cons
 }
 
 int moe_expert_bwd_dw_down(const moe_desc* desc, const int32_t* offsets, const void* dy_perm, const void* h,
-                           float* dW2, void* stream) {
+                           void* dW2, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(offsets) || !need(dy_perm) || !need(h) || !need(dW2)) return MOE_ERR_INVALID_ARG;
@@ -290,7 +292,7 @@ int moe_dtopk_w_from_parts(const moe_desc* desc, const int32_t* slot_row, const 
 }
 
 int moe_expert_bwd_dw_down_gather(const moe_desc* desc, const int32_t* offsets, const int32_t* row_token,
-                                  const void* dy, const void* hw, float* dW2, void* stream) {
+                                  const void* dy, const void* hw, void* dW2, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!need(offsets) || !need(row_token) || !need(dy) || !need(hw) || !need(dW2)) return MOE_ERR_INVALID_ARG;

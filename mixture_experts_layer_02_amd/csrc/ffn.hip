@@ -55,8 +55,11 @@ constexpr int DMA_STAGES = DMA_BK == 64 ? 2 : 4;
 
 // bf16 products: the LDS-DMA kernel when every K-contiguous operand has K a
 // multiple of its 32-wide k-tile, else the register-staged kernel.
+// KB16: a grouped-K product that may write bf16 (the weight gradients); the
+// other grouped-K products (the router's split-K partials) write fp32 only,
+// and no bf16-output kernel is built for them.
 template <int ALAY, int BLAY, typename AT, int GRP, int EPI, bool DUAL, int GATH = GATH_NONE, bool BQ8 = false,
-          bool F8 = false>
+          bool F8 = false, bool KB16 = false>
 hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   // K-contiguous operands need whole 64-wide k-tiles: every K (GRP_M, plain)
   // or every K chunk (GRP_K split into kchunk pieces) a multiple of 64.
@@ -68,9 +71,7 @@ hipError_t run_bf16(const GemmParams& p, int64_t ub_tiles, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;
   if (grid <= 0) return hipSuccess;
   if constexpr (std::is_same<AT, uint16_t>::value) {
-    // Grouped-K products (weight gradients, split-K partials) write fp32 only,
-    // so no bf16-output kernel is built for them.
-    constexpr bool F32_ONLY = GRP == GRP_K;
+    constexpr bool F32_ONLY = GRP == GRP_K && !KB16;
     if (F32_ONLY && !p.c_f32) return hipErrorInvalidValue;
     const bool cf = (EPI == EPI_STORE || EPI == EPI_ADD) && p.c_f32;
     if (p.dyn) {
@@ -444,7 +445,7 @@ hipError_t launch_bwd_dh_gather(const moe_desc& d, const int32_t* offsets, const
 // dW2 [d][f] = dy_perm^T hw with dy read in place: k-row r of the A operand
 // is dy[row_token[r]] (bf16); hw carries the routing weight.
 hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
-                                 const void* dy, const void* hw, float* dW2, hipStream_t s) {
+                                 const void* dy, const void* hw, void* dW2, hipStream_t s) {
   GemmParams q = blank(d);
   q.A = dy;
   q.lda = d.d;
@@ -459,9 +460,9 @@ hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, cons
   q.ngroups = d.num_local;
   q.M = d.d;
   q.N = d.f;
-  q.c_f32 = 1;
+  q.c_f32 = d.wgrad_dtype == MOE_F32;
   q.band = k_band(cdiv(d.d, MT));
-  return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_AK>(
+  return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_AK, false, false, true>(
       q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
 }
 
@@ -492,7 +493,7 @@ hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void*
 // product with M = 2f split at f).  row_token != NULL: x_perm is x itself and
 // k-row r reads x[row_token[r]] (the gather fused into the B operand; bf16 only).
 hipError_t launch_dw_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* dgu,
-                             float* dW1, float* dW3, hipStream_t s, const int32_t* row_token) {
+                             void* dW1, void* dW3, hipStream_t s, const int32_t* row_token) {
   const bool bf = d.dtype == MOE_BF16;
   GemmParams p = blank(d);
   p.A = dgu;
@@ -510,17 +511,18 @@ hipError_t launch_dw_gate_up(const moe_desc& d, const int32_t* offsets, const vo
   p.ngroups = d.num_local;
   p.M = 2 * d.f;
   p.N = d.d;
-  p.c_f32 = 1;
+  p.c_f32 = d.wgrad_dtype == MOE_F32;
   const int64_t tiles = (int64_t)d.num_local * cdiv(2 * d.f, MT) * cdiv(d.d, MT);
   if (bf) p.band = k_band(cdiv(2 * d.f, MT));
-  if (bf && row_token) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_B>(p, tiles, s);
+  if (bf && row_token)
+    return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_B, false, false, true>(p, tiles, s);
   if (row_token) return hipErrorNotSupported;
-  if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(p, tiles, s);
+  if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_NONE, false, false, true>(p, tiles, s);
   return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(p, (int64_t)d.num_local * cdiv(2 * d.f, 64) * cdiv(d.d, 64), s);
 }
 
 // dW2 [d][f] = dy_perm^T h over each expert's rows.
-hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void* dy_perm, const void* h, float* dW2,
+hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void* dy_perm, const void* h, void* dW2,
                           hipStream_t s) {
   const bool bf = d.dtype == MOE_BF16;
   GemmParams q = blank(d);
@@ -535,14 +537,16 @@ hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void*
   q.ngroups = d.num_local;
   q.M = d.d;
   q.N = d.f;
-  q.c_f32 = 1;
+  q.c_f32 = d.wgrad_dtype == MOE_F32;
   if (bf) q.band = k_band(cdiv(d.d, MT));
-  if (bf) return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
+  if (bf)
+    return run_bf16<LAY_MN, LAY_MN, uint16_t, GRP_K, EPI_STORE, false, GATH_NONE, false, false, true>(
+        q, (int64_t)d.num_local * cdiv(d.d, MT) * cdiv(d.f, MT), s);
   return run_f32<LAY_MN, LAY_MN, GRP_K, EPI_STORE, false>(q, (int64_t)d.num_local * cdiv(d.d, 64) * cdiv(d.f, 64), s);
 }
 
 hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
-                             const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
+                             const void* dgu, const void* dy_perm, void* dW1, void* dW3, void* dW2,
                              hipStream_t s, const int32_t* row_token) {
   hipError_t e = launch_dw_gate_up(d, offsets, x_perm, dgu, dW1, dW3, s, row_token);
   if (e != hipSuccess) return e;

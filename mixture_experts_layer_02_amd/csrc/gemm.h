@@ -173,8 +173,10 @@ struct Scheduler {
       int mt = nf ? local / NT : local % MT, nt = nf ? local % NT : local / MT;
       // With two n-tiles (the second often narrower: E = 384 is 256 + 128)
       // a workgroup would take the same n-tile in every round of the static
-      // order; swapping them in odd rounds gives each one both in turn.
-      if (GRP == GRP_NONE && BANDED && nf && NT == 2 && ((id / (int)gridDim.x) & 1)) nt ^= 1;
+      // order; swapping them in odd rounds gives each one both in turn.  (A
+      // tile pair 2m, 2m + 1 lies in one round when the grid is even, so the
+      // swap maps the round's tiles onto themselves.)
+      if (GRP == GRP_NONE && BANDED && nf && NT == 2 && !(gridDim.x & 1u) && ((id / (int)gridDim.x) & 1)) nt ^= 1;
       t.mtile = mt;
       t.mtiles = MT;
       if (GRP == GRP_K && BANDED && p.band > 0 && p.band < MT) {

@@ -1384,7 +1384,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmParams p) {
                 }
                 const u32x4_t d = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]),
                                    pack_bf2(o[6], o[7])};
-                __builtin_amdgcn_raw_buffer_store_b128(d, rc, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0, 0);
+                // (bf16 weight gradients: non-temporal as their fp32 form)
+                __builtin_amdgcn_raw_buffer_store_b128(d, rc, ok ? (uint32_t)(eo * 2) : 0x80000000u, 0,
+                                                       GRP == GRP_K ? 2 : 0);
               }
             } else if (EPI == EPI_SWIGLU) {
               float h[8];

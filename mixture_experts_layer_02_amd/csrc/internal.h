@@ -59,7 +59,7 @@ hipError_t launch_dtopk_from_parts(const moe_desc& d, const int32_t* slot_row, c
 // 256-wide n-tile of f.
 inline int dtopk_parts(const moe_desc& d) { return 2 * (int)((d.f + 255) / 256); }
 hipError_t launch_dw_down_gather(const moe_desc& d, const int32_t* offsets, const int32_t* row_token,
-                                 const void* dy, const void* hw, float* dW2, hipStream_t s);
+                                 const void* dy, const void* hw, void* dW2, hipStream_t s);
 hipError_t launch_unpermute_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
                                 const float* dx_add, void* dx, hipStream_t s);
 hipError_t launch_unpermute_router_bwd(const moe_desc& d, const int32_t* slot_row, const void* dx_perm,
@@ -75,12 +75,12 @@ hipError_t launch_bwd_dh(const moe_desc& d, const int32_t* offsets, const void* 
 hipError_t launch_bwd_dxp(const moe_desc& d, const int32_t* offsets, const void* W1, const void* W3,
                           const void* dgu, void* dx_perm, hipStream_t s);
 hipError_t launch_ffn_bwd_dw(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* h,
-                             const void* dgu, const void* dy_perm, float* dW1, float* dW3, float* dW2,
+                             const void* dgu, const void* dy_perm, void* dW1, void* dW3, void* dW2,
                              hipStream_t s,
                              const int32_t* row_token = nullptr);
 hipError_t launch_dw_gate_up(const moe_desc& d, const int32_t* offsets, const void* x_perm, const void* dgu,
-                             float* dW1, float* dW3, hipStream_t s, const int32_t* row_token = nullptr);
-hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void* dy_perm, const void* h, float* dW2,
+                             void* dW1, void* dW3, hipStream_t s, const int32_t* row_token = nullptr);
+hipError_t launch_dw_down(const moe_desc& d, const int32_t* offsets, const void* dy_perm, const void* h, void* dW2,
                           hipStream_t s);
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const void* Wr, const float* dlogits,
                              float* dx_router, void* dx_acc, float* dWr, void* ws, hipStream_t s);

@@ -24,8 +24,9 @@ def random_routing(rng, T, E, k, skew=0.0):
     return np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
 
 
-def _desc(T, d, f, E, k, e0, NL, dtype, renorm=1):
-    return moe.make_desc(T, d, f, E, k, e0, NL, moe.MOE_BF16 if dtype == "bf16" else moe.MOE_F32, renorm)
+def _desc(T, d, f, E, k, e0, NL, dtype, renorm=1, wgrad="f32", tile_counters=None):
+    return moe.make_desc(T, d, f, E, k, e0, NL, moe.MOE_BF16 if dtype == "bf16" else moe.MOE_F32, renorm,
+                         tile_counters=tile_counters, wgrad_dtype=wgrad)
 
 
 def _routing_agreement(idx_g, L_ref, idx_ref):
@@ -47,10 +48,12 @@ def _routing_agreement(idx_g, L_ref, idx_ref):
     return same
 
 
-def _run_layer(cfg, backward, gpu, n_groups=1, gather=False, inp=None, gather_dy=None):
+def _run_layer(cfg, backward, gpu, n_groups=1, gather=False, inp=None, gather_dy=None, wgrad="f32",
+               tile_counters=None):
     inp = synth.make_inputs(cfg) if inp is None else inp
     dt = cfg.dtype
-    D = _desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, dt, cfg.renormalize)
+    D = _desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, dt, cfg.renormalize, wgrad,
+              tile_counters)
     b = moe.Buffers(D, backward=backward, gather=gather, gather_dy=gather_dy)
     dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
     bias = to_dev(inp["bias"]) if "bias" in inp else None

@@ -27,14 +27,16 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_desc_struct_matches_header_size():
-    # 11 x 4-byte fields, 4 bytes of padding, one 8-byte pointer
-    assert ctypes.sizeof(moe.MoeDesc) == 56
+    # 11 x 4-byte fields, 4 bytes of padding, one 8-byte pointer, one 4-byte
+    # field and 4 bytes of tail padding
+    assert ctypes.sizeof(moe.MoeDesc) == 64
     assert moe.MoeDesc.tile_counters.offset == 48
+    assert moe.MoeDesc.wgrad_dtype.offset == 56
 
 
 def _d(**kw):
     base = dict(T=64, d=128, f=64, E=8, k=2, expert_begin=0, num_local=8, dtype=moe.MOE_BF16)
-    extra = {n: kw.pop(n) for n in ("tile_schedule", "tile_counters") if n in kw}
+    extra = {n: kw.pop(n) for n in ("tile_schedule", "tile_counters", "wgrad_dtype") if n in kw}
     base.update(kw)
     d = moe.make_desc(**base)
     for n, v in extra.items():
@@ -57,6 +59,8 @@ def _d(**kw):
     (dict(tile_schedule=2), moe.MOE_ERR_INVALID_ARG),
     (dict(tile_schedule=1), moe.MOE_ERR_INVALID_ARG),    # dynamic order without counters
     (dict(tile_schedule=1, tile_counters=8), moe.MOE_ERR_INVALID_ARG),  # misaligned counters
+    (dict(wgrad_dtype=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(wgrad_dtype=moe.MOE_BF16, dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),  # bf16 gradients of fp32 weights
 ])
 def test_invalid_descriptors_are_rejected(kw, rc):
     n = ctypes.c_size_t(0)
@@ -65,7 +69,7 @@ def test_invalid_descriptors_are_rejected(kw, rc):
 
 def test_wrong_struct_size_and_null_desc():
     d = _d()
-    d.struct_size = 40                                  # the descriptor before the tile-order fields
+    d.struct_size = 56                                  # the descriptor before the gradient type
     n = ctypes.c_size_t(0)
     assert moe.lib().moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_route(None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG

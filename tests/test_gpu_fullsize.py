@@ -79,17 +79,18 @@ def _check_index_maps(cfg, idx, counts, offsets, row_token, slot_row):
     assert (r[order] == np.arange(len(r))).all()
 
 
-@pytest.mark.parametrize("name,gather,gather_dy", [
-    ("share_1t", False, False), ("zipf_1t", False, False), ("uniform_1t", False, False),
-    ("fwdbwd_1t", False, False),
-    ("fwdbwd_1t", False, True),    # the benchmark's configuration: x_perm, dy read in place
-    ("fwdbwd_1t", True, True)])
-def test_full_size_layer_sampled(gpu, name, gather, gather_dy):
+@pytest.mark.parametrize("name,gather,gather_dy,wgrad", [
+    ("share_1t", False, False, "f32"), ("zipf_1t", False, False, "f32"), ("uniform_1t", False, False, "f32"),
+    ("fwdbwd_1t", False, False, "f32"),
+    ("fwdbwd_1t", False, True, "f32"),
+    ("fwdbwd_1t", False, True, "bf16"),  # the benchmark's configuration: x_perm, dy read in place, bf16 dW
+    ("fwdbwd_1t", True, True, "f32")])
+def test_full_size_layer_sampled(gpu, name, gather, gather_dy, wgrad):
     cfg = synth.CONFIGS[name]
     back = cfg.backward
     print(f"[fullsize] {name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} NL={cfg.num_local} k={cfg.k} "
-          f"backward={back} gather={gather} gather_dy={gather_dy}", flush=True)
-    inp, b = _run_layer(cfg, back, gpu, gather=gather, gather_dy=gather_dy)
+          f"backward={back} gather={gather} gather_dy={gather_dy} wgrad={wgrad}", flush=True)
+    inp, b = _run_layer(cfg, back, gpu, gather=gather, gather_dy=gather_dy, wgrad=wgrad)
     dt, tol = cfg.dtype, TOL[cfg.dtype]
     T, E, k, e0, NL, f = cfg.T, cfg.E, cfg.k, cfg.expert_begin, cfg.num_local, cfg.f
     x32 = synth.as_f32(inp["x"], dt)

@@ -336,13 +336,14 @@ def test_layer_backward(gpu, name, scale):
     check_layer_backward(cfg, inp, b)
 
 
-def test_zero_row_experts_get_exact_zero_gradients(gpu):
+@pytest.mark.parametrize("wgrad", ["f32", "bf16"])
+def test_zero_row_experts_get_exact_zero_gradients(gpu, wgrad):
     T, d, f, E, k = 64, 128, 64, 8, 2
     cfg = synth.Config("t", 13, T, d, E, k, f, 0, E, "bf16", 1.0, "router", True)
     inp = synth.make_inputs(cfg)
     idx = np.stack([np.array([0, 1], np.int32)] * T)        # experts 2..7 get no rows
     w = np.full((T, k), 0.5, np.float32)
-    D = _desc(T, d, f, E, k, 0, E, "bf16")
+    D = _desc(T, d, f, E, k, 0, E, "bf16", wgrad=wgrad)
     b = moe.Buffers(D, backward=True)
     dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
     b.dW1.fill_(7.0)
@@ -353,6 +354,27 @@ def test_zero_row_experts_get_exact_zero_gradients(gpu):
     moe.backward(b, dev["x"], dev["wr"], dev["w1"], dev["w3"], dev["w2"], dev["dy"], routing=r)
     assert (to_host(b.dW1)[2:] == 0).all() and (to_host(b.dW3)[2:] == 0).all() and (to_host(b.dW2)[2:] == 0).all()
     assert (to_host(b.dW1)[:2] != 0).any()
+
+
+# ---------------------------------------------------------------------------
+# B4 with bf16 weight gradients (float32 sums rounded once at the store) on
+# every operand path: x_perm and dy_perm copies, x_perm with dy read in place
+# (the benchmark's), and both read in place; static and dynamic tile order.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dyn", [False, True])
+@pytest.mark.parametrize("gather,gather_dy", [(False, False), (False, True), (True, True)])
+@pytest.mark.parametrize("scale", [
+    dict(T=512, d=256, f=128, E=32, num_local=8, expert_begin=8),
+    dict(T=1500, d=320, f=192, E=64, num_local=24, expert_begin=40, k=6),     # ragged, empty experts
+    dict(T=777, d=256, f=128, E=64, num_local=3, expert_begin=61, k=8),       # few local experts
+])
+def test_layer_backward_bf16_weight_gradients(gpu, scale, gather, gather_dy, dyn):
+    cfg = synth.scaled(synth.CONFIGS["fwdbwd_1t"], **scale)
+    print(f"[bf16 dW] {scale} gather={gather} gather_dy={gather_dy} dynamic={dyn}", flush=True)
+    inp, b = _run_layer(cfg, True, gpu, gather=gather, gather_dy=gather_dy, wgrad="bf16",
+                        tile_counters=moe.new_tile_counters(gpu) if dyn else None)
+    assert b.dW1.dtype == b.dW3.dtype == b.dW2.dtype == torch.bfloat16
+    check_layer_backward(cfg, inp, b)
 
 
 def test_forward_backward_is_deterministic(gpu):
@@ -371,8 +393,9 @@ def test_forward_backward_is_deterministic(gpu):
 # k-tile counts 0, 1, 2, 3, ... and consecutive output tiles alternate
 # between loading their successor ahead and starting cold.
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wgrad", ["f32", "bf16"])
 @pytest.mark.parametrize("d,f", [(192, 128), (320, 192)])
-def test_expert_path_ragged_segments(gpu, d, f):
+def test_expert_path_ragged_segments(gpu, d, f, wgrad):
     counts = [0, 1, 63, 64, 65, 128, 129, 200, 0, 300, 2, 511, 512, 513, 0, 70]  # E a multiple of 8
     E = NL = len(counts)
     T, k = sum(counts), 1
@@ -381,7 +404,7 @@ def test_expert_path_ragged_segments(gpu, d, f):
     w = np.ones((T, 1), np.float32)
     cfg = synth.Config("ragged", 21, T, d, E, k, f, 0, NL, "bf16", 1.0, "router", True)
     inp = synth.make_inputs(cfg)
-    D = _desc(T, d, f, E, k, 0, NL, "bf16")
+    D = _desc(T, d, f, E, k, 0, NL, "bf16", wgrad=wgrad)
     b = moe.Buffers(D, backward=True)
     dev = {n: to_dev(inp[n]) for n in ("x", "wr", "w1", "w3", "w2", "dy")}
     r = (to_dev(idx), to_dev(w))
