@@ -307,6 +307,52 @@ __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict_
   }
 }
 
+// dlogits with renormalised weights, two tokens per wave: lanes 0-31 take
+// token 2w and lanes 32-63 token 2w+1 (k <= 32), each half summing its own
+// <w, dw> (the same additions as wave_sum, whose first step over the upper
+// half's zeros is exact).  Both rows are zeroed in LDS, the selections
+// scattered into them, and the two rows - contiguous in dlogits - written as
+// 16-byte vectors (E a multiple of 8: no vector straddles two rows, and row
+// 2w starts 16-byte aligned).  E2: 2 E rounded up to 256 floats (LDS per wave).
+template <int E2>
+__global__ void __launch_bounds__(256) route_bwd_renorm2_kernel(const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ w,
+                                                                const float* __restrict__ dw, int T, int E, int k,
+                                                                float* __restrict__ dlogits) {
+  __shared__ __attribute__((aligned(16))) float s_g[4][E2];
+  const int lane = threadIdx.x & 63, l = lane & 31, half = lane >> 5;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+  if (t0 >= T) return;
+  const int t = t0 + half;
+  float* gs = s_g[threadIdx.x >> 6];
+  const bool mine = l < k && t < T;
+  int my_i = 0;
+  float my_w = 0.f, my_dw = 0.f;
+  if (mine) {
+    my_i = min(max(idx[(int64_t)t * k + l], 0), E - 1);  // (clamped: no write outside the row)
+    my_w = w[(int64_t)t * k + l];
+    my_dw = dw[(int64_t)t * k + l];
+  }
+  float s = my_w * my_dw;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);  // within each half
+  const int n4 = E >> 1;  // 16-byte vectors in the two rows
+  float4* g4 = reinterpret_cast<float4*>(gs);
+#pragma unroll
+  for (int q = lane; q < E2 / 4; q += 64)
+    if (q < n4) g4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (mine) gs[half * E + my_i] = my_w * (my_dw - s);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int nv = (t0 + 1 < T) ? n4 : n4 >> 1;  // the second row only if token 2w+1 exists
+  float4* out = reinterpret_cast<float4*>(dlogits + (int64_t)t0 * E);
+#pragma unroll
+  for (int q = lane; q < E2 / 4; q += 64)
+    if (q < nv) out[q] = g4[q];
+}
+
 // One instantiation per number of 64-wide slices of a logit row (1 .. 16 for
 // E <= 1024), so no slice is carried for nothing.
 template <int NV, bool GROUPED>
@@ -330,6 +376,11 @@ static void route_bwd_nv(const moe_desc& d, int nv, const float* logits, const i
                          const float* dw, float* dlogits, hipStream_t s) {
   if constexpr (NV <= 16) {
     if (nv > NV) return route_bwd_nv<NV + 1>(d, nv, logits, idx, w, dw, dlogits, s);
+    if (d.renormalize) {  // two tokens per wave, E <= 64 NV
+      constexpr int E2 = (2 * 64 * NV + 255) / 256 * 256;
+      route_bwd_renorm2_kernel<E2><<<(d.T + 7) / 8, 256, 0, s>>>(idx, w, dw, d.T, d.E, d.k, dlogits);
+      return;
+    }
     // one token per wave (4 per wave measured slower: 0.050 against 0.041 ms at T = 65536, E = 384)
     route_bwd_kernel<NV><<<(d.T + 3) / 4, 256, 0, s>>>(logits, idx, w, dw, d.T, d.E, d.k, d.renormalize,
                                                           dlogits);

@@ -210,6 +210,38 @@ def test_router_backward(gpu, T, d, E, dtype):
 
 
 # ---------------------------------------------------------------------------
+# B5 route backward alone: dlogits from dtopk_w against the oracle, with
+# renormalised weights (two tokens per wave; an odd T leaves the last wave one
+# token) and with the raw softmax; k up to 32, E up to 1024.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("renorm", [1, 0])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 1), (3, 8, 2), (777, 384, 8), (1000, 64, 32), (257, 1024, 8),
+                                   (130, 72, 5)])
+def test_route_backward(gpu, T, E, k, renorm):
+    rng = np.random.default_rng(T + 3 * E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx = np.argsort(-logits, axis=1)[:, :k].astype(np.int32)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(p, idx, axis=1)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    w = w.astype(np.float32)
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    D = _desc(T, 128, 64, E, k, 0, E, "bf16", renorm)
+    dl = torch.full((T, E), 5.0, dtype=torch.float32, device=gpu)
+    moe.route_bwd(D, to_dev(logits), to_dev(idx), to_dev(w), to_dev(dw), dl)
+    torch.cuda.synchronize()
+    want = oracle.route_bwd(idx, w, dw, E, renorm, logits=logits)
+    assert whole_rel_err(to_host(dl), want) <= 1e-5
+    if renorm:  # exact zeros outside the selection
+        got = to_host(dl)
+        mask = np.ones((T, E), bool)
+        np.put_along_axis(mask, idx.astype(np.int64), False, axis=1)
+        assert (got[mask] == 0).all()
+
+
+# ---------------------------------------------------------------------------
 # B5 fused: the unpermute sum plus the router's share of dx, with dlogits
 # from the oracle's route backward (renormalised weights: zero outside the
 # selection).  k <= 8 takes the batched kernel, k > 8 the slot-loop one.
