@@ -164,9 +164,13 @@ def test_permute(gpu, T, E, k, e0, NL, d, dtype, skew):
 # A1: router logits
 # ---------------------------------------------------------------------------
 # (bf16 shapes with fewer than 256 output tiles are split over d: 300 x 256 x 72 in 4 chunks,
-# 1000 x 512 x 384 in 8, 11008 x 640 x 384 in 3 of 256, 256 and 128; 1 x 64 x 8 is not split)
+# 1000 x 512 x 384 in 8, 11008 x 640 x 384 in 3 of 256, 256 and 128; 1 x 64 x 8 is not split.
+# 70000 x 256 x 384 takes the persistent product: 548 tiles in three rounds, the second with the
+# two n-tiles swapped, the last partial, every second n-tile 128 columns wide (half-N); 66000 x
+# 192 x 320 the same with a 64-column second n-tile.)
 @pytest.mark.parametrize("T,d,E,dtype,bias", [(1, 64, 8, "bf16", False), (300, 256, 72, "bf16", True),
                                              (1000, 512, 384, "bf16", False), (11008, 640, 384, "bf16", True),
+                                             (70000, 256, 384, "bf16", True), (66000, 192, 320, "bf16", False),
                                              (129, 128, 8, "f32", True), (333, 192, 96, "f32", False)])
 def test_router_logits(gpu, T, d, E, dtype, bias):
     cfg = synth.Config("t", 11, T, d, E, 2, 64, 0, E, dtype, 1.0, "router", False)
